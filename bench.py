@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark one batched verification step on one MI355X.
+
+Workload: B=64 requests, K=4 drafts, V=128256, bf16 logits (target ~ N(0, 3^2)
+plus a +6 spike per row, draft = target + N(0, 0.7^2)), T = 1, no filters,
+seeded synthetic inputs.  A "step" is one full call: row statistics, accept
+scan and the float64 residual / bonus draw for every request.
+
+Output: exactly one JSON line on stdout (progress goes to stderr):
+  value            verified draft positions per second (sum of draft lengths / step time)
+  ms_per_step      mean step time over the timed region (HIP events on the call's stream)
+  roofline         the dominant kernel (row statistics): algorithmic bytes per launch
+                   over its mean duration, against the 8 TB/s HBM peak
+  cpu_baseline     the fp64 oracle on this host, on a bounded sample of the same workload
+Inputs rotate over several independent sets whose total exceeds twice the
+256 MB last-level cache, so reads come from HBM.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = 3
+METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,K=4,V=128k"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw HIP events (the call records them on its own stream)."""
+
+    def __init__(self, n):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = h
+
+    def elapsed_ms(self, i, j):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], self.arr[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.arr:
+            self.lib.hipEventDestroy(h)
+
+
+def cpu_baseline(w, budget_s):
+    """Time the fp64 oracle on whole calls of the same workload, single core."""
+    import oracle as O
+    reps, t_total, positions = 0, 0.0, 0
+    reqs = list(range(w.B))
+    while t_total < budget_s:
+        t0 = time.perf_counter()
+        O.verify(w.target, w.draft, w.draft_tokens, w.draft_len, w.u, w.u_final, w.T, w.top_k,
+                 w.top_p, w.eos_id, w.dtype, requests=reqs)
+        t_total += time.perf_counter() - t0
+        positions += w.positions
+        reps += 1
+    return {"value": positions / t_total, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} whole calls of the same workload (B={w.B}, K={w.K}, V={w.V}), "
+                      f"{t_total:.1f} s of single-threaded numpy fp64",
+            "seconds_per_call": t_total / reps}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="input sets rotated through")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle timing budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        log("multi-GPU runs are not part of this build: the path would shard over requests "
+            "with no communication (see the design notes); run with --gpus 1")
+        sys.exit(2)
+
+    import torch
+    from speculative_decoding_sampling_amd import binding
+    from speculative_decoding_sampling_amd.build import LIB
+    from speculative_decoding_sampling_amd.workloads import WORKLOADS, make_workload, upload
+
+    if not os.path.exists(LIB):
+        from speculative_decoding_sampling_amd.build import build
+        build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    sets, hosts = [], []
+    for i in range(args.sets):
+        t0 = time.perf_counter()
+        w = make_workload(WORKLOAD, seed=1000 + WORKLOAD + 100 * i)
+        hosts.append(w)
+        a = upload(w, dev)
+        a["out_tokens"] = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
+        a["n_emitted"] = torch.empty((w.B,), dtype=torch.int32, device=dev)
+        sets.append(a)
+        log(f"input set {i}: {w.algorithmic_bytes / 1e6:.1f} MB needed rows, "
+            f"{w.positions} positions ({time.perf_counter() - t0:.1f} s to generate)")
+    w0 = hosts[0]
+    positions = w0.positions
+    alg_bytes = w0.algorithmic_bytes
+    assert all(h.positions == positions and h.algorithmic_bytes == alg_bytes for h in hosts)
+
+    stream = torch.cuda.current_stream(dev)
+    ws = torch.empty(binding.workspace_bytes(w0.B, w0.K, w0.V, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i, events=None):
+        binding.verify(**sets[i % len(sets)], workspace=ws, stream=stream, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    # Timed region: the plain entry point, K steps bracketed by synchronisation.
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev.lib.hipEventRecord(ev.arr[0], stream.cuda_stream)
+    for i in range(args.steps):
+        step(i)
+    ev.lib.hipEventRecord(ev.arr[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = ev.elapsed_ms(0, 1) / args.steps
+    ev.close()
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step "
+        f"(host wall {wall / args.steps * 1e6:.2f} us/step)")
+
+    # Per-kernel durations: the same steps through the timing entry point.
+    names = binding.stage_names()
+    nst = len(names)
+    evs = [HipEvents(nst + 1) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, events=evs[i].arr)
+    torch.cuda.synchronize()
+    stage_ms = np.array([[e.elapsed_ms(j, j + 1) for j in range(nst)] for e in evs])
+    timed_total = float(np.mean([e.elapsed_ms(0, nst) for e in evs]))
+    for e in evs:
+        e.close()
+    stage_us = {n: float(stage_ms[:, j].mean() * 1e3) for j, n in enumerate(names)}
+    log("stage means (us): " + ", ".join(f"{k}={v:.2f}" for k, v in stage_us.items())
+        + f"; evented step {timed_total * 1e3:.2f} us")
+
+    # Result sanity: every request emitted a legal count.
+    n = sets[0]["n_emitted"].cpu().numpy()
+    assert np.all((n >= 1) & (n <= w0.draft_len + 1)), n
+
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 copies of {args.copy_calibration_mib} MiB")
+
+    dominant = "row_stats"
+    k1_us = stage_us[dominant]
+    achieved = alg_bytes / (k1_us * 1e-6) / 1e9
+    step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": positions / (ms_per_step * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[WORKLOAD]["name"], "B": w0.B, "K": w0.K, "V": w0.V,
+                   "logits": "bf16", "temperature": w0.T, "top_k": 0, "top_p": 1.0,
+                   "input_sets": args.sets, "positions_per_step": positions,
+                   "algorithmic_bytes_per_step": alg_bytes},
+        "hbm_gbps_whole_step": step_gbps,
+        "hbm_frac_whole_step": step_gbps / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "launch_us": k1_us,
+                     "bytes_per_launch": alg_bytes},
+        "stages_us": stage_us,
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle for about {args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * libspecverify: batched rejection-sampling verification for speculative
+ * decoding on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For each request b, a draft model proposed draft_len[b]
+ * tokens x_0 .. x_{n-1}; the target model produced logits for the n+1
+ * positions that follow the committed prefix.  Target row k verifies draft
+ * token k, and target row n supplies a bonus token when every draft survives
+ * (nickwang.xyz, "推测解码：草稿、验证与实际加速", section "候选已知，验证才能并行").
+ * p_k and q_k are the target and draft distributions after temperature and
+ * the optional top-k / top-p filters, applied the same way to both rows
+ * (same page, section "接受与拒绝怎样保住分布").  Scanning k = 0, 1, ..., the
+ * call accepts x_k when u[b][k] < alpha_k = min(1, p_k(x_k) / q_k(x_k))
+ * (eq. a(x) there; tbxsx.cn "推测解码采样验证优化策略 —— 深度调研报告", formula 1
+ * and section "4. 实现逻辑"), stops at the first rejection j and replaces
+ * x_j by a draw from max(p_j - q_j, 0) renormalised (eq. r(x); bowenzhou.top
+ * "投机采样", section "深入推导"), or, when all n drafts are accepted, draws
+ * a bonus token from p_n.  Both draws are inverse-CDF draws at u_final[b] over
+ * token ids in ascending order (nickwang.xyz, section "算完三个 token 的全部概率",
+ * function sample()).  The library draws no random numbers: the caller
+ * supplies every uniform, so results are reproducible.
+ *
+ * Conventions for every entry point below.
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no pointer after it returns.
+ *  - The call is asynchronous on `stream`; outputs are valid once the caller
+ *    has synchronised that stream.  The library is stateless and reentrant;
+ *    calls that share a workspace must not overlap.
+ *  - Host-checkable argument errors return a status and enqueue nothing.
+ *  - Per-request precondition violations found on the device (draft_len
+ *    outside [0, K], a draft token outside [0, V), q(x) == 0, a uniform
+ *    outside [0, 1), a needed row with no finite logit) set n_emitted[b] = -1
+ *    and out_tokens[b][*] = -1; other requests are not affected.
+ *  - Logits must be finite or -inf (-inf masks a token out).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define SPECV_API __attribute__((visibility("default")))
+#else
+#define SPECV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPECV_OK = 0,
+  SPECV_EINVAL = 1,       /* bad argument (null/misaligned pointer, bad size or parameter) */
+  SPECV_EWORKSPACE = 2,   /* workspace missing, misaligned (16 B) or smaller than specv_workspace_bytes() */
+  SPECV_EHIP = 3,         /* a HIP launch failed */
+  SPECV_EUNSUPPORTED = 4  /* valid request this build does not implement (see specv_verify) */
+} specv_status_t;
+
+typedef enum {
+  SPECV_F32 = 0,          /* IEEE float32 logits */
+  SPECV_BF16 = 1          /* bfloat16 logits (upper half of a float32) */
+} specv_dtype_t;
+
+/* Largest draft length K the call accepts. */
+#define SPECV_MAX_K 63
+/* Largest top_k the filter path accepts (candidates per row are held on chip). */
+#define SPECV_MAX_TOPK 1024
+
+/*
+ * Bytes of device workspace specv_verify needs for these sizes.  Returns 0
+ * for sizes specv_verify would reject.  The workspace holds per-row
+ * statistics, per-request decisions and fp64 chunk partials; its contents
+ * need no initialisation and are meaningless after the call.
+ */
+SPECV_API size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype, int top_k, float top_p);
+
+/*
+ * One batched verification step: target logits, draft logits, draft tokens,
+ * draft lengths and uniforms in; emitted tokens and their count out.
+ *
+ *  target_logits  [B][K+1][V] of `dtype`, row-major, contiguous; element-aligned
+ *                 (16-byte alignment of rows enables vector loads).
+ *  draft_logits   [B][K][V] of `dtype`; may be NULL when K == 0.
+ *  draft_tokens   [B][K] int32; entry k is read only when k < draft_len[b].
+ *  draft_len      [B] int32, each in [0, K].
+ *  u              [B][K] float32 in [0, 1): the accept test of position k.
+ *  u_final        [B] float32 in [0, 1): the one correction or bonus draw.
+ *  B >= 1, 0 <= K <= SPECV_MAX_K, V >= 1 (V * (K+1) * B below 2^62).
+ *  temperature    > 0 and finite; logits are divided by it before filtering.
+ *  top_k          0 = off; otherwise keep logits >= the top_k-th largest (ties
+ *                 kept).  top_k >= V is the same as off.
+ *  top_p          1 = off; otherwise in (0, 1): keep the shortest prefix of
+ *                 the top-k renormalised distribution, by logit descending,
+ *                 whose mass reaches top_p (crossing token and its ties kept).
+ *                 top_p < 1 needs 0 < top_k <= SPECV_MAX_TOPK, and top_k alone
+ *                 needs top_k <= SPECV_MAX_TOPK (else SPECV_EUNSUPPORTED).
+ *  eos_id         -1 = off; else in [0, V): the round stops right after the
+ *                 first emitted EOS (accepted draft or drawn token).
+ *  out_tokens     [B][K+1] int32 output: emitted tokens, -1 beyond n_emitted.
+ *  n_emitted      [B] int32 output: 1 .. draft_len[b] + 1, or -1 on a
+ *                 per-request error.
+ *  workspace      device buffer of at least specv_workspace_bytes(...) bytes,
+ *                 16-byte aligned.
+ */
+SPECV_API specv_status_t specv_verify(const void *target_logits, const void *draft_logits,
+                            specv_dtype_t dtype, const int32_t *draft_tokens,
+                            const int32_t *draft_len, const float *u, const float *u_final,
+                            int B, int K, int V, float temperature, int top_k, float top_p,
+                            int eos_id, int32_t *out_tokens, int32_t *n_emitted,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * specv_verify plus diagnostic outputs, each nullable:
+ *  accept_prob    [B][K] float32: alpha_k for k < draft_len[b], -1 otherwise
+ *                 (and -1 for error requests).
+ *  residual_mass  [B] float64: sum_v max(p_j - q_j, 0) on the rejection path
+ *                 (nickwang.xyz, section "算完三个 token 的全部概率": it equals one
+ *                 minus the acceptance rate), 0 on other paths.
+ *  stop_pos       [B] int32: the rejected position, the EOS position, or
+ *                 draft_len[b] when every draft was accepted; -1 on error.
+ *  path           [B] int32: 0 rejection + correction, 1 bonus, 2 EOS, -1 error.
+ */
+SPECV_API specv_status_t specv_verify_debug(const void *target_logits, const void *draft_logits,
+                                  specv_dtype_t dtype, const int32_t *draft_tokens,
+                                  const int32_t *draft_len, const float *u,
+                                  const float *u_final, int B, int K, int V,
+                                  float temperature, int top_k, float top_p, int eos_id,
+                                  int32_t *out_tokens, int32_t *n_emitted, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream,
+                                  float *accept_prob, double *residual_mass,
+                                  int32_t *stop_pos, int32_t *path);
+
+/*
+ * Timing variant of specv_verify, for benchmarks: identical work, plus
+ * hipEventRecord on `stream` of events[0] before the first kernel launch and
+ * of events[i+1] after kernel stage i.  `events` holds specv_num_stages() + 1
+ * caller-created HIP events (SPECV_EINVAL if NULL or any entry is NULL); the
+ * caller reads stage durations with hipEventElapsedTime after synchronising.
+ */
+SPECV_API specv_status_t specv_verify_timed(const void *target_logits, const void *draft_logits,
+                                            specv_dtype_t dtype, const int32_t *draft_tokens,
+                                            const int32_t *draft_len, const float *u,
+                                            const float *u_final, int B, int K, int V,
+                                            float temperature, int top_k, float top_p,
+                                            int eos_id, int32_t *out_tokens, int32_t *n_emitted,
+                                            void *workspace, size_t workspace_bytes,
+                                            hipStream_t stream, hipEvent_t *events);
+
+/* Number of kernel stages one call launches, and the static name of stage i
+ * (NULL when out of range). */
+SPECV_API int specv_num_stages(void);
+SPECV_API const char *specv_stage_name(int i);
+
+/* Static, human-readable name of a status code. */
+SPECV_API const char *specv_status_string(specv_status_t status);
+
+/* Library version, 100 * major + minor. */
+SPECV_API int specv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

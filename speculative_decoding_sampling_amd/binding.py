@@ -1,0 +1,183 @@
+"""ctypes binding for libspecverify (argument marshalling only).
+
+Every step of the verification runs in the HIP library; this module checks
+tensor shapes and dtypes, allocates outputs and a workspace with torch, and
+passes raw device pointers plus the current HIP stream through the C ABI
+declared in ``include/specverify.h``.  If the library is not built the
+binding raises: there is no fallback.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+
+SPECV_F32, SPECV_BF16 = 0, 1
+SPECV_OK, SPECV_EINVAL, SPECV_EWORKSPACE, SPECV_EHIP, SPECV_EUNSUPPORTED = 0, 1, 2, 3, 4
+MAX_K = 63
+
+PATH_ERROR, PATH_REJECT, PATH_BONUS, PATH_EOS = -1, 0, 1, 2
+
+_lib = None
+_lock = threading.Lock()
+_workspaces = {}
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"specv_verify failed with status {status}: {msg}")
+        self.status = status
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libspecverify.so and declare its C signatures (once)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is not built; run `python -m speculative_decoding_sampling_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        c_int, c_float, c_vp, c_size = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+        lib.specv_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_float]
+        lib.specv_workspace_bytes.restype = c_size
+        common = [c_vp, c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_float, c_int,
+                  c_float, c_int, c_vp, c_vp, c_vp, c_size, c_vp]
+        lib.specv_verify.argtypes = common
+        lib.specv_verify.restype = c_int
+        lib.specv_verify_debug.argtypes = common + [c_vp, c_vp, c_vp, c_vp]
+        lib.specv_verify_debug.restype = c_int
+        lib.specv_verify_timed.argtypes = common + [c_vp]
+        lib.specv_verify_timed.restype = c_int
+        lib.specv_num_stages.argtypes = []
+        lib.specv_num_stages.restype = c_int
+        lib.specv_stage_name.argtypes = [c_int]
+        lib.specv_stage_name.restype = ctypes.c_char_p
+        lib.specv_status_string.argtypes = [c_int]
+        lib.specv_status_string.restype = ctypes.c_char_p
+        lib.specv_version.argtypes = []
+        lib.specv_version.restype = c_int
+        _lib = lib
+        return lib
+
+
+def status_string(status):
+    return load_library().specv_status_string(int(status)).decode()
+
+
+def stage_names():
+    """Names of the kernel stages one call launches, in order."""
+    lib = load_library()
+    return [lib.specv_stage_name(i).decode() for i in range(lib.specv_num_stages())]
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SPECV_BF16
+    if t.dtype == torch.float32:
+        return SPECV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def workspace_bytes(B, K, V, dtype, top_k=0, top_p=1.0):
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load_library().specv_workspace_bytes(int(B), int(K), int(V), code, int(top_k),
+                                                   float(top_p)))
+
+
+def _workspace(device, nbytes):
+    key = (device.index if device.index is not None else torch.cuda.current_device())
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _check(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def verify(target_logits, draft_logits, draft_tokens, draft_len, u, u_final, temperature=1.0,
+           top_k=0, top_p=1.0, eos_id=-1, *, out_tokens=None, n_emitted=None, workspace=None,
+           debug=False, stream=None, events=None):
+    """Run one batched verification step on the GPU.
+
+    Shapes: target_logits [B, K+1, V] (bf16 or fp32), draft_logits [B, K, V]
+    (same dtype), draft_tokens [B, K] int32, draft_len [B] int32, u [B, K]
+    fp32, u_final [B] fp32.  Returns a dict with ``out_tokens`` [B, K+1] and
+    ``n_emitted`` [B] (int32), plus ``accept_prob``, ``residual_mass``,
+    ``stop_pos`` and ``path`` when ``debug`` is true.  The call is
+    asynchronous on ``stream`` (default: the current stream).  ``events``, a
+    ctypes array of ``len(stage_names()) + 1`` HIP event handles, selects the
+    timing entry point, which records them around every kernel stage.
+    """
+    lib = load_library()
+    dev = target_logits.device
+    if dev.type != "cuda":
+        raise ValueError("target_logits must be a GPU tensor")
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits", None, (B, K + 1, V), dev)
+    _check(draft_logits, "draft_logits", target_logits.dtype, (B, K, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(draft_len, "draft_len", torch.int32, (B,), dev)
+    _check(u, "u", torch.float32, (B, K), dev)
+    _check(u_final, "u_final", torch.float32, (B,), dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if n_emitted is None:
+        n_emitted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+    _check(n_emitted, "n_emitted", torch.int32, (B,), dev)
+    nbytes = int(lib.specv_workspace_bytes(B, K, V, code, int(top_k), float(top_p)))
+    if workspace is None:
+        workspace = _workspace(dev, nbytes)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    args = [_ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(draft_len),
+            _ptr(u), _ptr(u_final), B, K, V, float(temperature), int(top_k), float(top_p),
+            int(eos_id), _ptr(out_tokens), _ptr(n_emitted), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), sptr]
+    res = {"out_tokens": out_tokens, "n_emitted": n_emitted}
+    if events is not None:
+        if debug:
+            raise ValueError("events and debug are exclusive")
+        status = lib.specv_verify_timed(*args, ctypes.cast(events, ctypes.c_void_p))
+    elif debug:
+        res["accept_prob"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+        res["residual_mass"] = torch.empty((B,), dtype=torch.float64, device=dev)
+        res["stop_pos"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        res["path"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        status = lib.specv_verify_debug(*args, _ptr(res["accept_prob"]), _ptr(res["residual_mass"]),
+                                        _ptr(res["stop_pos"]), _ptr(res["path"]))
+    else:
+        status = lib.specv_verify(*args)
+    if status != SPECV_OK:
+        raise SpecVerifyError(status, status_string(status))
+    return res

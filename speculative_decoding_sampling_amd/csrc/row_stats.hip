@@ -1,0 +1,102 @@
+// Row statistics: per (request, needed row, vocabulary chunk), the chunk's
+// maximum logit m and its partial normaliser s = sum 2^(z*c - fl(m*c)), with
+// c = log2(e) / T in float32 and fl() the float32 product (never fused).
+// These give the softmax normaliser of the target and draft distributions
+// (tbxsx.cn "推测解码采样验证优化策略 —— 深度调研报告", section
+// "4. 实现逻辑": softmax of logits over temperature; nickwang.xyz
+// "推测解码：草稿、验证与实际加速", section "接受与拒绝怎样保住分布").
+//
+// This pass reads every needed row once and carries nearly all of the call's
+// HBM traffic.  Each workgroup streams one chunk with coalesced 16-byte loads
+// issued up front, reduces with wave64 shuffles and combines its four waves
+// in LDS.  Partials are combined later in a fixed order, so the result is
+// deterministic and a draft row equal to its target row gets bit-identical
+// statistics.
+#include "common.h"
+
+namespace specv {
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
+    const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
+    int K, int V, int nchunk, float c, float2* __restrict__ part) {
+  constexpr int N = Elem<T>::kPerVec;
+  constexpr int kChunk = kRowThreads * kRowVecs * N;
+  const int R = 2 * K + 1;
+  const int chunk = blockIdx.x % nchunk;
+  const int rr = blockIdx.x / nchunk;
+  const int r = rr % R;
+  const int b = rr / R;
+  const int nb = draft_len[b];
+  if (nb < 0 || nb > K) return;                      // the accept scan reports the error
+  const bool is_target = r <= K;
+  const int k = is_target ? r : r - (K + 1);
+  if (k > (is_target ? nb : nb - 1)) return;         // row not needed for this request
+  const T* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+
+  float v[kRowVecs][N];
+  const long e_base = (long)chunk * kChunk;
+#pragma unroll
+  for (int j = 0; j < kRowVecs; ++j)
+    load_vec(row, e_base + ((long)j * kRowThreads + threadIdx.x) * N, V, aligned, v[j]);
+
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kRowVecs; ++j)
+#pragma unroll
+    for (int i = 0; i < N; ++i) m = fmaxf(m, v[j][i]);
+  m = wave_max(m);
+
+  float s = 0.f;
+  if (m != -INFINITY) {
+    const float mc = __fmul_rn(m, c);                // the exact reference fl(m*c)
+#pragma unroll
+    for (int j = 0; j < kRowVecs; ++j)
+#pragma unroll
+      for (int i = 0; i < N; ++i) s += __builtin_amdgcn_exp2f(fmaf(v[j][i], c, -mc));
+  }
+  s = wave_sum(s);
+
+  __shared__ float2 red[kRowThreads / kWave];
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  if (lane == 0) red[wid] = make_float2(m, s);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kRowThreads / kWave; ++w) M = fmaxf(M, red[w].x);
+    float S = 0.f;
+    if (M != -INFINITY) {
+      const float Mc = __fmul_rn(M, c);
+#pragma unroll
+      for (int w = 0; w < kRowThreads / kWave; ++w)
+        if (red[w].x != -INFINITY)
+          S += red[w].y * __builtin_amdgcn_exp2f(__fmul_rn(red[w].x, c) - Mc);
+    }
+    part[(size_t)rr * nchunk + chunk] = make_float2(M, S);
+  }
+}
+
+int row_stats_chunk(bool bf16) {
+  return kRowThreads * kRowVecs * (bf16 ? Elem<bf16_t>::kPerVec : Elem<float>::kPerVec);
+}
+
+hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
+                            int B, int K, int V, int nchunk, float c, float2* part,
+                            hipStream_t stream) {
+  const size_t blocks = (size_t)B * (2 * K + 1) * nchunk;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  if (bf16)
+    row_stats_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
+        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V, nchunk,
+        c, part);
+  else
+    row_stats_kernel<float><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
+        static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, nchunk,
+        c, part);
+  return hipGetLastError();
+}
+
+}  // namespace specv

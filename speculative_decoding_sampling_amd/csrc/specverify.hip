@@ -1,0 +1,216 @@
+// C ABI of libspecverify: argument checks, workspace layout and the launch
+// sequence on the caller's stream.  The declarations and their contract live
+// in include/specverify.h.
+#include "specverify.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "common.h"
+
+namespace specv {
+int row_stats_chunk(bool bf16);
+hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
+                            int B, int K, int V, int nchunk, float c, float2* part,
+                            hipStream_t stream);
+hipError_t launch_accept(bool bf16, const void* tgt, const void* dft, const int* tokens,
+                         const int* draft_len, const float* u, const float* u_final, int B,
+                         int K, int V, int nchunk, float c, int eos_id, const float2* part,
+                         Plan* plan, int* out_tokens, int* n_emitted, float* alpha_out,
+                         double* rmass_out, int* stop_out, int* path_out, hipStream_t stream);
+hipError_t launch_sample_norm(bool bf16, const void* tgt, const void* dft, int B, int K, int V,
+                              int nch, double invT, const Plan* plan, double2* norm_part,
+                              hipStream_t stream);
+hipError_t launch_sample_resid(bool bf16, const void* tgt, const void* dft, int B, int K, int V,
+                               int nch, double invT, const Plan* plan, const double2* norm_part,
+                               double* resid_part, hipStream_t stream);
+hipError_t launch_sample_draw(bool bf16, const void* tgt, const void* dft, const float* u_final,
+                              int B, int K, int V, int nch, double invT, const Plan* plan,
+                              const double2* norm_part, const double* resid_part,
+                              int* out_tokens, double* rmass_out, hipStream_t stream);
+
+// Kernel stages of one call, in launch order (specv_verify_timed records an
+// event after each).
+const char* const kStageNames[] = {"row_stats", "accept", "sample_norm", "sample_resid",
+                                   "sample_draw"};
+constexpr int kNumStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace regions, each 256-byte aligned:
+//   row partials   float2  [B][2K+1][nch_row]    (max, partial normaliser)
+//   plans          Plan    [B]
+//   norm partials  double2 [B][nch_samp]         (target, draft fp64 normalisers)
+//   resid partials double  [B][nch_samp]         (fp64 residual mass per chunk)
+struct Layout {
+  int nch_row = 0, nch_samp = 0;
+  size_t off_row = 0, off_plan = 0, off_norm = 0, off_resid = 0, total = 0;
+};
+
+Layout make_layout(int B, int K, int V, bool bf16) {
+  Layout L;
+  const int ch = row_stats_chunk(bf16);
+  L.nch_row = (V + ch - 1) / ch;
+  L.nch_samp = (V + kSampChunk - 1) / kSampChunk;
+  size_t off = 0;
+  L.off_row = off;
+  off = align_up(off + (size_t)B * (2 * K + 1) * L.nch_row * sizeof(float2));
+  L.off_plan = off;
+  off = align_up(off + (size_t)B * sizeof(Plan));
+  L.off_norm = off;
+  off = align_up(off + (size_t)B * L.nch_samp * sizeof(double2));
+  L.off_resid = off;
+  off = align_up(off + (size_t)B * L.nch_samp * sizeof(double));
+  L.total = off;
+  return L;
+}
+
+bool filters_on(int V, int top_k, float top_p) { return (top_k > 0 && top_k < V) || top_p < 1.0f; }
+
+specv_status_t check_sizes(int B, int K, int V, specv_dtype_t dtype, int top_k, float top_p) {
+  if (B < 1 || K < 0 || K > SPECV_MAX_K || V < 1) return SPECV_EINVAL;
+  if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_EINVAL;
+  if (top_k < 0) return SPECV_EINVAL;
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return SPECV_EINVAL;
+  // B * (K+1) * V elements must index without overflow.
+  if ((double)B * (double)(K + 1) * (double)V > 4.0e18) return SPECV_EINVAL;
+  if ((size_t)B * (2 * K + 1) * (size_t)((V + 1023) / 1024) > 0x7fffffffu) return SPECV_EINVAL;
+  if (filters_on(V, top_k, top_p)) return SPECV_EUNSUPPORTED;
+  return SPECV_OK;
+}
+
+bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
+                   const int32_t* tokens, const int32_t* draft_len, const float* u,
+                   const float* u_final, int B, int K, int V, float temperature, int top_k,
+                   float top_p, int eos_id, int32_t* out_tokens, int32_t* n_emitted,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream,
+                   float* alpha_out, double* rmass_out, int32_t* stop_out, int32_t* path_out,
+                   hipEvent_t* events) {
+  specv_status_t st = check_sizes(B, K, V, dtype, top_k, top_p);
+  if (st != SPECV_OK) return st;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SPECV_EINVAL;
+  if (eos_id < -1 || eos_id >= V) return SPECV_EINVAL;
+  const size_t esz = dtype == SPECV_BF16 ? 2 : 4;
+  if (!target || !draft_len || !u_final || !out_tokens || !n_emitted) return SPECV_EINVAL;
+  if (K > 0 && (!draft || !tokens || !u)) return SPECV_EINVAL;
+  if (misaligned(target, esz) || (draft && misaligned(draft, esz))) return SPECV_EINVAL;
+  if (misaligned(draft_len, 4) || misaligned(u_final, 4) || misaligned(out_tokens, 4) ||
+      misaligned(n_emitted, 4) || (tokens && misaligned(tokens, 4)) || (u && misaligned(u, 4)))
+    return SPECV_EINVAL;
+  if ((alpha_out && misaligned(alpha_out, 4)) || (rmass_out && misaligned(rmass_out, 8)) ||
+      (stop_out && misaligned(stop_out, 4)) || (path_out && misaligned(path_out, 4)))
+    return SPECV_EINVAL;
+  const bool bf16 = dtype == SPECV_BF16;
+  const Layout L = make_layout(B, K, V, bf16);
+  if (!workspace || misaligned(workspace, 16) || workspace_bytes < L.total) return SPECV_EWORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
+  Plan* plan = reinterpret_cast<Plan*>(ws + L.off_plan);
+  double2* norm_part = reinterpret_cast<double2*>(ws + L.off_norm);
+  double* resid_part = reinterpret_cast<double*>(ws + L.off_resid);
+
+  // log2(e) / T rounded once to float32; every float32 exponent uses it.
+  const float c = (float)(1.4426950408889634 / (double)temperature);
+  const double invT = 1.0 / (double)temperature;
+
+  // Events (timing variant only): events[0] before the first launch, events[i+1]
+  // after stage i.
+  auto mark = [&](int i) -> bool {
+    return !events || hipEventRecord(events[i], stream) == hipSuccess;
+  };
+  if (!mark(0)) return SPECV_EHIP;
+  hipError_t e = launch_row_stats(bf16, target, draft, draft_len, B, K, V, L.nch_row, c,
+                                  row_part, stream);
+  if (e != hipSuccess || !mark(1)) return SPECV_EHIP;
+  e = launch_accept(bf16, target, draft, tokens, draft_len, u, u_final, B, K, V, L.nch_row, c,
+                    eos_id, row_part, plan, out_tokens, n_emitted, alpha_out, rmass_out, stop_out,
+                    path_out, stream);
+  if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
+  e = launch_sample_norm(bf16, target, draft, B, K, V, L.nch_samp, invT, plan, norm_part, stream);
+  if (e != hipSuccess || !mark(3)) return SPECV_EHIP;
+  e = launch_sample_resid(bf16, target, draft, B, K, V, L.nch_samp, invT, plan, norm_part,
+                          resid_part, stream);
+  if (e != hipSuccess || !mark(4)) return SPECV_EHIP;
+  e = launch_sample_draw(bf16, target, draft, u_final, B, K, V, L.nch_samp, invT, plan, norm_part,
+                         resid_part, out_tokens, rmass_out, stream);
+  if (e != hipSuccess || !mark(5)) return SPECV_EHIP;
+  return SPECV_OK;
+}
+
+}  // namespace
+}  // namespace specv
+
+extern "C" {
+
+size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype, int top_k, float top_p) {
+  if (specv::check_sizes(B, K, V, dtype, top_k, top_p) != SPECV_OK) return 0;
+  return specv::make_layout(B, K, V, dtype == SPECV_BF16).total;
+}
+
+specv_status_t specv_verify(const void* target_logits, const void* draft_logits,
+                            specv_dtype_t dtype, const int32_t* draft_tokens,
+                            const int32_t* draft_len, const float* u, const float* u_final,
+                            int B, int K, int V, float temperature, int top_k, float top_p,
+                            int eos_id, int32_t* out_tokens, int32_t* n_emitted, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return specv::run(target_logits, draft_logits, dtype, draft_tokens, draft_len, u, u_final, B,
+                    K, V, temperature, top_k, top_p, eos_id, out_tokens, n_emitted, workspace,
+                    workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr, nullptr);
+}
+
+specv_status_t specv_verify_debug(const void* target_logits, const void* draft_logits,
+                                  specv_dtype_t dtype, const int32_t* draft_tokens,
+                                  const int32_t* draft_len, const float* u,
+                                  const float* u_final, int B, int K, int V, float temperature,
+                                  int top_k, float top_p, int eos_id, int32_t* out_tokens,
+                                  int32_t* n_emitted, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, float* accept_prob, double* residual_mass,
+                                  int32_t* stop_pos, int32_t* path) {
+  return specv::run(target_logits, draft_logits, dtype, draft_tokens, draft_len, u, u_final, B,
+                    K, V, temperature, top_k, top_p, eos_id, out_tokens, n_emitted, workspace,
+                    workspace_bytes, stream, accept_prob, residual_mass, stop_pos, path,
+                    nullptr);
+}
+
+specv_status_t specv_verify_timed(const void* target_logits, const void* draft_logits,
+                                  specv_dtype_t dtype, const int32_t* draft_tokens,
+                                  const int32_t* draft_len, const float* u,
+                                  const float* u_final, int B, int K, int V, float temperature,
+                                  int top_k, float top_p, int eos_id, int32_t* out_tokens,
+                                  int32_t* n_emitted, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, hipEvent_t* events) {
+  if (!events) return SPECV_EINVAL;
+  for (int i = 0; i <= specv::kNumStages; ++i)
+    if (!events[i]) return SPECV_EINVAL;
+  return specv::run(target_logits, draft_logits, dtype, draft_tokens, draft_len, u, u_final, B,
+                    K, V, temperature, top_k, top_p, eos_id, out_tokens, n_emitted, workspace,
+                    workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr, events);
+}
+
+int specv_num_stages(void) { return specv::kNumStages; }
+
+const char* specv_stage_name(int i) {
+  return (i >= 0 && i < specv::kNumStages) ? specv::kStageNames[i] : nullptr;
+}
+
+const char* specv_status_string(specv_status_t status) {
+  switch (status) {
+    case SPECV_OK: return "ok";
+    case SPECV_EINVAL: return "invalid argument";
+    case SPECV_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case SPECV_EHIP: return "HIP launch failed";
+    case SPECV_EUNSUPPORTED: return "unsupported parameter combination";
+  }
+  return "unknown status";
+}
+
+int specv_version(void) { return 100; }
+
+}  // extern "C"

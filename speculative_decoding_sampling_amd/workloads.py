@@ -200,3 +200,26 @@ def make_workload(cfg, seed=None, B=None, draft_sampler=None):
                     top_p=top_p, eos_id=eos_id, target=np.ascontiguousarray(target_arr),
                     draft=np.ascontiguousarray(draft_arr), draft_tokens=tokens,
                     draft_len=draft_len, u=u, u_final=u_final, classes=classes)
+
+
+def upload(w, device="cuda"):
+    """Copy a workload's arrays to the GPU as the tensors ``binding.verify`` takes."""
+    import torch
+
+    def logits(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(a).to(device)
+
+    return dict(
+        target_logits=logits(w.target),
+        draft_logits=logits(w.draft),
+        draft_tokens=torch.from_numpy(w.draft_tokens).to(device),
+        draft_len=torch.from_numpy(w.draft_len).to(device),
+        u=torch.from_numpy(w.u).to(device),
+        u_final=torch.from_numpy(w.u_final).to(device),
+        temperature=w.T,
+        top_k=w.top_k,
+        top_p=w.top_p,
+        eos_id=w.eos_id,
+    )

@@ -1,0 +1,191 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI (GPU only).
+
+Bars: tokens and counts bit-exact except where the oracle flags a decision
+as within rounding reach; accept probabilities and residual masses within
+1e-5 absolute.  Sizes keep the oracle to seconds yet span many chunks and a
+ragged tail (V is never a multiple of the chunk sizes used here).
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+from speculative_decoding_sampling_amd import binding  # noqa: E402
+from speculative_decoding_sampling_amd.workloads import make_workload, upload  # noqa: E402
+from tests.parity import compare, to_numpy  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def oracle_sampler(z, T, k, p, uni):
+    P, _ = O.processed_distribution(z, T, k, p)
+    return O.icdf(P, uni)[0]
+
+
+def run_gpu(w, **kw):
+    args = upload(w, DEV)
+    args.update(kw)
+    res = binding.verify(**args, debug=True)
+    torch.cuda.synchronize()
+    return to_numpy(res)
+
+
+def run_oracle(w, requests=None, **kw):
+    p = dict(temperature=w.T, top_k=w.top_k, top_p=w.top_p, eos_id=w.eos_id)
+    p.update(kw)
+    return O.verify(w.target, w.draft, w.draft_tokens, w.draft_len, w.u, w.u_final,
+                    p["temperature"], p["top_k"], p["top_p"], p["eos_id"], w.dtype,
+                    requests=requests)
+
+
+def assert_parity(w, requests=None, label=""):
+    print(f"[parity] cfg={w.cfg} seed={w.seed} B={w.B} K={w.K} V={w.V} {w.dtype} {label}",
+          flush=True)
+    g = run_gpu(w)
+    o = run_oracle(w, requests)
+    rep = compare(g, o, w.K)
+    print(f"  requests={rep['requests']} positions={rep['positions']} flagged={rep['flagged']} "
+          f"kinds={rep['flag_kinds']} max_alpha_err={rep['max_alpha_err']:.2e} "
+          f"max_mass_err={rep['max_mass_err']:.2e}", flush=True)
+    assert not rep["mismatches"], rep["mismatches"][:5]
+    return rep, g, o
+
+
+@pytest.mark.parametrize("cfg,B", [(1, None), (2, None), (3, 8), (5, 16)])
+def test_parity_reduced_batch(cfg, B):
+    assert_parity(make_workload(cfg, B=B))
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_parity_seed_sweep(cfg):
+    flagged = positions = 0
+    for i in range(12):
+        rep, _, _ = assert_parity(make_workload(cfg, seed=1000 + cfg + 100 * i))
+        flagged += rep["flagged"]
+        positions += rep["positions"]
+    print(f"  sweep cfg={cfg}: flagged {flagged} of {positions} positions")
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_parity_full_size(cfg):
+    w = make_workload(cfg)
+    rep, g, o = assert_parity(w, label="full size")
+    # every request took one of the four paths and emitted a sane count
+    n = g["n_emitted"]
+    assert np.all((n == -1) | ((n >= 1) & (n <= w.draft_len + 1)))
+
+
+def test_p_equals_q_is_always_bonus_with_alpha_exactly_one():
+    # EOS off: with p == q an accepted draft may itself be the EOS token.
+    w = make_workload(5, B=16)
+    w.draft[:] = w.target[:, :w.K]
+    g = run_gpu(w, eos_id=-1)
+    assert np.array_equal(g["path"], np.full(w.B, binding.PATH_BONUS))
+    assert np.array_equal(g["n_emitted"], w.draft_len + 1)
+    for b in range(w.B):
+        assert np.all(g["accept_prob"][b, :w.draft_len[b]] == 1.0)
+    rep = compare(g, run_oracle(w, eos_id=-1), w.K)
+    assert not rep["mismatches"], rep["mismatches"][:3]
+
+
+def test_deterministic_bitwise():
+    w = make_workload(3, B=8)
+    a, b = run_gpu(w), run_gpu(w)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+def test_per_request_errors_are_isolated():
+    w = make_workload(1)
+    w.draft_len[0] = 5                       # draft_len > K
+    w.draft_len[1] = -1                      # negative draft_len
+    w.draft_tokens[2, 3] = w.V               # token out of range
+    w.u[3, 1] = 1.0                          # uniform outside [0, 1)
+    w.u_final[4] = np.nan                    # final uniform not a number
+    w.draft[5, 2, w.draft_tokens[5, 2]] = -np.inf   # q(x) == 0
+    g = run_gpu(w)
+    for b in range(6):
+        assert g["n_emitted"][b] == -1 and np.all(g["out_tokens"][b] == -1)
+        assert g["path"][b] == binding.PATH_ERROR
+    rep = compare(g, run_oracle(w), w.K)
+    assert not rep["mismatches"], rep["mismatches"][:3]
+
+
+def test_draft_len_zero_and_k_zero():
+    w = make_workload(1)
+    w.draft_len[:] = 0
+    assert_parity(w, label="draft_len=0")
+    # K = 0: only the bonus row exists
+    t = torch.from_numpy(w.target[:, :1].copy()).to(DEV)
+    d = torch.empty((w.B, 0, w.V), dtype=torch.float32, device=DEV)
+    res = binding.verify(t, d, torch.empty((w.B, 0), dtype=torch.int32, device=DEV),
+                         torch.zeros(w.B, dtype=torch.int32, device=DEV),
+                         torch.empty((w.B, 0), dtype=torch.float32, device=DEV),
+                         torch.from_numpy(w.u_final).to(DEV), 1.0, debug=True)
+    torch.cuda.synchronize()
+    o = O.verify(w.target[:, :1], w.draft[:, :0], w.draft_tokens[:, :0], np.zeros(w.B, np.int32),
+                 w.u[:, :0], w.u_final, 1.0)
+    assert np.array_equal(res["out_tokens"].cpu().numpy(), o["out_tokens"])
+    assert np.array_equal(res["n_emitted"].cpu().numpy(), o["n_emitted"])
+
+
+@pytest.mark.parametrize("V", [1, 3, 4097, 10007])
+def test_unaligned_and_tiny_vocabularies(V):
+    rng = np.random.default_rng(V)
+    B, K = 6, 3
+    t = rng.normal(0, 2, size=(B, K + 1, V)).astype(np.float32)
+    d = (t[:, :K] + rng.normal(0, 0.6, size=(B, K, V))).astype(np.float32)
+    toks = np.array([[int(np.argmax(d[b, k] + rng.gumbel(size=V))) for k in range(K)]
+                     for b in range(B)], dtype=np.int32)
+    from speculative_decoding_sampling_amd.workloads import Workload, to_bf16_bits, uniforms
+    for dtype in ("f32", "bf16"):
+        tt = to_bf16_bits(t) if dtype == "bf16" else t
+        dd = to_bf16_bits(d) if dtype == "bf16" else d
+        w = Workload(cfg=0, seed=V, B=B, K=K, V=V, dtype=dtype, T=0.9, top_k=0, top_p=1.0,
+                     eos_id=-1, target=np.ascontiguousarray(tt), draft=np.ascontiguousarray(dd),
+                     draft_tokens=toks, draft_len=np.array([3, 2, 1, 0, 3, 3], np.int32),
+                     u=uniforms(rng, (B, K)), u_final=uniforms(rng, (B,)))
+        assert_parity(w, label=f"V={V}")
+
+
+def test_exhaustive_cells_match_oracle():
+    # Thousands of random V=3, K=2 requests over the worked example's
+    # distributions: tokens must match the oracle request for request.
+    p_rows = [np.array([0.5, 0.3, 0.2]), np.array([0.1, 0.6, 0.3]), np.array([0.25, 0.25, 0.5])]
+    q_rows = [np.array([0.6, 0.1, 0.3]), np.array([0.3, 0.3, 0.4])]
+    K, V = 2, 3
+    rng = np.random.default_rng(0)
+    B = 4000
+    toks = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    u = rng.random((B, K)).astype(np.float32)
+    uf = rng.random(B).astype(np.float32)
+    t = np.broadcast_to(np.log(np.array(p_rows, dtype=np.float32)), (B, K + 1, V)).copy()
+    d = np.broadcast_to(np.log(np.array(q_rows, dtype=np.float32)), (B, K, V)).copy()
+    from speculative_decoding_sampling_amd.workloads import Workload
+    w = Workload(cfg=0, seed=0, B=B, K=K, V=V, dtype="f32", T=1.0, top_k=0, top_p=1.0,
+                 eos_id=-1, target=t, draft=d, draft_tokens=toks,
+                 draft_len=np.full(B, K, np.int32), u=u, u_final=uf)
+    assert_parity(w, label="tiny-V exhaustive")
+
+
+def test_host_argument_errors():
+    w = make_workload(1)
+    a = upload(w, DEV)
+    bad = [
+        dict(temperature=0.0), dict(temperature=-1.0), dict(temperature=float("inf")),
+        dict(top_p=0.0), dict(top_p=1.5), dict(top_k=-1), dict(eos_id=w.V), dict(eos_id=-2),
+    ]
+    for kw in bad:
+        args = dict(a)
+        args.update(kw)
+        with pytest.raises(binding.SpecVerifyError) as e:
+            binding.verify(**args)
+        assert e.value.status == binding.SPECV_EINVAL, kw
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(binding.SpecVerifyError) as e:
+        binding.verify(**a, workspace=small)
+    assert e.value.status == binding.SPECV_EWORKSPACE

@@ -1,0 +1,111 @@
+"""The C-ABI library builds, loads and exports every symbol its header declares.
+
+CPU only: nothing here launches a kernel.  Calls that return before any HIP
+work (argument validation, workspace sizing, status strings) are exercised.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from speculative_decoding_sampling_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    return ctypes.CDLL(build.LIB)
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"SPECV_API\s+[\w\s\*]+?\b(specv_\w+)\s*\(", text)
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    assert set(names) == {"specv_workspace_bytes", "specv_verify", "specv_verify_debug",
+                          "specv_verify_timed", "specv_num_stages", "specv_stage_name",
+                          "specv_status_string", "specv_version"}, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_the_c_api_is_exported(lib):
+    import subprocess
+    from speculative_decoding_sampling_amd import build
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True,
+                         text=True).stdout
+    funcs = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert funcs == set(declared_functions()), funcs
+
+
+def test_workspace_sizes(lib):
+    f = lib.specv_workspace_bytes
+    f.argtypes = [ctypes.c_int] * 5 + [ctypes.c_float]
+    f.restype = ctypes.c_size_t
+    n3 = f(64, 4, 128256, 1, 0, 1.0)
+    assert n3 > 0 and n3 % 256 == 0
+    assert f(64, 4, 128256, 1, 0, 1.0) == n3                      # pure function of sizes
+    assert f(128, 4, 128256, 1, 0, 1.0) > n3
+    assert f(0, 4, 100, 0, 0, 1.0) == 0                           # B < 1
+    assert f(1, 64, 100, 0, 0, 1.0) == 0                          # K > SPECV_MAX_K
+    assert f(1, 4, 0, 0, 0, 1.0) == 0                             # V < 1
+    assert f(1, 4, 100, 7, 0, 1.0) == 0                           # unknown dtype
+    assert f(1, 4, 100, 0, 0, 0.0) == 0                           # top_p out of range
+
+
+def test_validation_returns_before_any_gpu_work(lib):
+    v = lib.specv_verify
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    v.argtypes = [vp, vp, ci, vp, vp, vp, vp, ci, ci, ci, cf, ci, cf, ci, vp, vp, vp,
+                  ctypes.c_size_t, vp]
+    v.restype = ci
+    dummy = ctypes.c_void_p(4096)
+    base = [dummy, dummy, 1, dummy, dummy, dummy, dummy, 4, 4, 1000, 1.0, 0, 1.0, -1,
+            dummy, dummy, dummy, 1 << 20, None]
+
+    def call(**kw):
+        args = list(base)
+        idx = {"B": 7, "K": 8, "V": 9, "T": 10, "top_k": 11, "top_p": 12, "eos": 13,
+               "target": 0, "ws_bytes": 17}
+        for k, val in kw.items():
+            args[idx[k]] = val
+        return v(*args)
+
+    assert call(B=0) == 1
+    assert call(K=64) == 1
+    assert call(V=0) == 1
+    assert call(T=0.0) == 1
+    assert call(T=float("nan")) == 1
+    assert call(top_p=0.0) == 1
+    assert call(eos=1000) == 1
+    assert call(target=None) == 1
+    assert call(top_k=10) == 4                 # filters: unsupported in this build
+    assert call(ws_bytes=16) == 2              # workspace too small
+
+
+def test_stage_names(lib):
+    lib.specv_stage_name.argtypes = [ctypes.c_int]
+    lib.specv_stage_name.restype = ctypes.c_char_p
+    n = lib.specv_num_stages()
+    names = [lib.specv_stage_name(i) for i in range(n)]
+    assert n >= 1 and names[0] == b"row_stats" and all(names)
+    assert lib.specv_stage_name(n) is None and lib.specv_stage_name(-1) is None
+
+
+def test_status_strings(lib):
+    s = lib.specv_status_string
+    s.argtypes = [ctypes.c_int]
+    s.restype = ctypes.c_char_p
+    assert s(0) == b"ok" and s(1) == b"invalid argument"
+    assert lib.specv_version() == 100
