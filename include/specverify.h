@@ -65,6 +65,8 @@ typedef enum {
 
 /* Largest draft length K the call accepts. */
 #define SPECV_MAX_K 63
+/* Largest vocabulary the call accepts (larger V returns SPECV_EUNSUPPORTED). */
+#define SPECV_MAX_V 4194304
 /* Largest top_k the filter path accepts (candidates per row are held on chip). */
 #define SPECV_MAX_TOPK 1024
 
@@ -87,7 +89,7 @@ SPECV_API size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype,
  *  draft_len      [B] int32, each in [0, K].
  *  u              [B][K] float32 in [0, 1): the accept test of position k.
  *  u_final        [B] float32 in [0, 1): the one correction or bonus draw.
- *  B >= 1, 0 <= K <= SPECV_MAX_K, V >= 1 (V * (K+1) * B below 2^62).
+ *  B >= 1, 0 <= K <= SPECV_MAX_K, 1 <= V <= SPECV_MAX_V (B * (K+1) * V below 2^62).
  *  temperature    > 0 and finite; logits are divided by it before filtering.
  *  top_k          0 = off; otherwise keep logits >= the top_k-th largest (ties
  *                 kept).  top_k >= V is the same as off.

@@ -63,6 +63,8 @@ def load_library():
         lib.specv_stage_name.restype = ctypes.c_char_p
         lib.specv_status_string.argtypes = [c_int]
         lib.specv_status_string.restype = ctypes.c_char_p
+        lib.specv_selftest_exp64.argtypes = [c_vp, c_vp, c_int, c_vp]
+        lib.specv_selftest_exp64.restype = c_int
         lib.specv_version.argtypes = []
         lib.specv_version.restype = c_int
         _lib = lib
@@ -77,6 +79,19 @@ def stage_names():
     """Names of the kernel stages one call launches, in order."""
     lib = load_library()
     return [lib.specv_stage_name(i).decode() for i in range(lib.specv_num_stages())]
+
+
+def selftest_exp64(x):
+    """The sampler's device float64 exp applied to a float64 GPU tensor (test hook)."""
+    lib = load_library()
+    if x.dtype != torch.float64 or x.device.type != "cuda" or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float64 GPU tensor")
+    y = torch.empty_like(x)
+    st = lib.specv_selftest_exp64(_ptr(x), _ptr(y), x.numel(),
+                                  ctypes.c_void_p(torch.cuda.current_stream(x.device).cuda_stream))
+    if st != SPECV_OK:
+        raise SpecVerifyError(st, status_string(st))
+    return y
 
 
 def _dtype_code(t):

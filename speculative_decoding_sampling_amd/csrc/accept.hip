@@ -1,33 +1,51 @@
 // Gather-and-accept scan: one wave64 per request, lane k owns draft position k.
 //
 // Lane k combines the chunk partials of target row k and draft row k into
-// exact row maxima and float64 normalisers, gathers p_k(x_k) and q_k(x_k),
-// forms alpha_k = min(1, p/q) and tests u[b][k] < alpha_k (nickwang.xyz
-// "推测解码：草稿、验证与实际加速", section "接受与拒绝怎样保住分布", eq. a(x); the
-// strict comparison of that page's replay code).  A ballot finds the first
-// rejection: every earlier draft is emitted and every later one discarded
-// (section "候选已知，验证才能并行"; tbxsx.cn "推测解码采样验证优化策略 ——
-// 深度调研报告", section "4. 实现逻辑").  A second ballot finds the first
-// accepted EOS, which ends the round early.  The lane at the stop position
-// records what the sampler must draw: a correction from max(p_j - q_j, 0)
-// after a rejection, or a bonus from target row draft_len when all drafts
-// pass.
+// the exact row maxima and the normalisers, gathers p_k(x_k) and q_k(x_k) in
+// float64, forms alpha_k = min(1, p/q) and tests u[b][k] < alpha_k
+// (nickwang.xyz "推测解码：草稿、验证与实际加速", section "接受与拒绝怎样保住分布",
+// eq. a(x); the strict comparison of that page's replay code).  A ballot
+// finds the first rejection: every earlier draft is emitted and every later
+// one discarded (section "候选已知，验证才能并行"; tbxsx.cn
+// "推测解码采样验证优化策略 —— 深度调研报告", section "4. 实现逻辑").  A second
+// ballot finds the first accepted EOS, which ends the round early.  The lane
+// at the stop position records what the sampler must draw: a correction from
+// max(p_j - q_j, 0) after a rejection, or a bonus from target row draft_len
+// when all drafts pass.
+//
+// Latency: the kernel is a short dependency chain per request, so every load
+// that does not depend on another (draft_len, u_final, tokens, uniforms and
+// the partials of all K+1 target and K draft rows) is issued up front; rows
+// beyond draft_len are loaded but never used.
 #include "common.h"
 
 namespace specv {
 
-// Combine one row's chunk partials in chunk order.  The partial s of a chunk
-// with maximum m is relative to 2^fl(m*c); the row normaliser is returned
-// relative to 2^fl(M*c) with M the row maximum, in float64.
+constexpr int kCombineBatch = 16;
+
+// Combine one row's chunk partials, in chunk order.  A chunk partial s with
+// maximum m is relative to 2^fl(m*c); the result S is relative to 2^fl(M*c)
+// with M the row maximum.  The partials are float32 sums, so float32 scale
+// factors add no meaningful error.
 __device__ __forceinline__ void combine_row(const float2* __restrict__ p, int n, float c,
-                                            float& M, double& S) {
-  float m = -INFINITY;
-  for (int i = 0; i < n; ++i) m = fmaxf(m, p[i].x);
-  double s = 0.0;
-  if (m != -INFINITY) {
-    const double Mc = (double)__fmul_rn(m, c);
-    for (int i = 0; i < n; ++i)
-      if (p[i].x != -INFINITY) s += (double)p[i].y * exp2((double)__fmul_rn(p[i].x, c) - Mc);
+                                            float& M, float& S) {
+  float m = -INFINITY, s = 0.f;
+  for (int base = 0; base < n; base += kCombineBatch) {
+    float2 v[kCombineBatch];
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j)
+      v[j] = base + j < n ? p[base + j] : make_float2(-INFINITY, 0.f);
+    float mb = m;
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) mb = fmaxf(mb, v[j].x);
+    if (mb != -INFINITY) {
+      const float mbc = __fmul_rn(mb, c);
+      if (m != -INFINITY) s *= __builtin_amdgcn_exp2f(__fmul_rn(m, c) - mbc);
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j)
+        if (v[j].x != -INFINITY) s += v[j].y * __builtin_amdgcn_exp2f(__fmul_rn(v[j].x, c) - mbc);
+    }
+    m = mb;
   }
   M = m;
   S = s;
@@ -46,28 +64,29 @@ __global__ __launch_bounds__(kWave) void accept_kernel(
   const int R = 2 * K + 1;
   const int nb_raw = draft_len[b];
   const float uf = u_final[b];
+  int x = -1;
+  float uk = 0.f;
+  if (lane < K) {
+    x = tokens[(size_t)b * K + lane];
+    uk = u[(size_t)b * K + lane];
+  }
+  float Mt = -INFINITY, Md = -INFINITY, St = 0.f, Sd = 0.f;
+  const float2* prow = part + (size_t)b * R * nchunk;
+  if (lane <= K) combine_row(prow + (size_t)lane * nchunk, nchunk, c, Mt, St);
+  if (lane < K) combine_row(prow + (size_t)(K + 1 + lane) * nchunk, nchunk, c, Md, Sd);
+
   bool bad = nb_raw < 0 || nb_raw > K || !(uf >= 0.f && uf < 1.f);
   const int nb = bad ? 0 : nb_raw;
-
-  float Mt = -INFINITY, Md = -INFINITY;
-  double St = 0.0, Sd = 0.0;
-  const float2* prow = part + (size_t)b * R * nchunk;
-  if (!bad && lane <= nb) combine_row(prow + (size_t)lane * nchunk, nchunk, c, Mt, St);
-  if (!bad && lane < nb) combine_row(prow + (size_t)(K + 1 + lane) * nchunk, nchunk, c, Md, Sd);
-
   bool ok = true, accept = false;
   double alpha = -1.0;
-  int x = -1;
   if (!bad && lane <= nb) ok = Mt != -INFINITY;            // target row has a finite logit
   if (!bad && lane < nb) {
-    x = tokens[(size_t)b * K + lane];
-    const float uk = u[(size_t)b * K + lane];
     ok = ok && Md != -INFINITY && x >= 0 && x < V && uk >= 0.f && uk < 1.f;
     if (ok) {
       const float zt = to_f32(tgt[target_row_off(b, lane, K, V) + x]);
       const float zd = to_f32(dft[draft_row_off(b, lane, K, V) + x]);
-      const double pt = exp2((double)zt * c - (double)__fmul_rn(Mt, c)) / St;
-      const double qd = exp2((double)zd * c - (double)__fmul_rn(Md, c)) / Sd;
+      const double pt = exp2((double)zt * c - (double)__fmul_rn(Mt, c)) / (double)St;
+      const double qd = exp2((double)zd * c - (double)__fmul_rn(Md, c)) / (double)Sd;
       ok = qd > 0.0;                                         // x was drawn from q: q(x) > 0
       const double ratio = pt / qd;
       alpha = ratio < 1.0 ? ratio : 1.0;
@@ -112,6 +131,15 @@ __global__ __launch_bounds__(kWave) void accept_kernel(
     pl.mt = Mt;
     pl.md = Md;
     pl.pad0 = pl.pad1 = 0;
+    // S_t / S_d in natural-exp units: each base-2 normaliser is relative to
+    // 2^fl(M*c); undo that offset exactly (M*c is exact in float64).
+    pl.g = 0.0;
+    if (path == kPathReject) {
+      const double off_t = (double)__fmul_rn(Mt, c) - (double)Mt * (double)c;
+      const double off_d = (double)__fmul_rn(Md, c) - (double)Md * (double)c;
+      pl.g = ((double)St / (double)Sd) * exp2(off_t - off_d);
+    }
+    pl.pad2 = 0.0;
     plan[b] = pl;
     n_emitted[b] = stop + 1;
     if (rmass_out) rmass_out[b] = 0.0;

@@ -28,8 +28,27 @@ struct Plan {
   float mt;   // exact max logit of target row trow
   float md;   // exact max logit of draft row drow
   int pad0, pad1;
+  double g;   // estimate of S_t / S_d, the two rows' natural-exp normalisers (reject only)
+  double pad2;
 };
-static_assert(sizeof(Plan) == 32, "Plan is 32 bytes");
+static_assert(sizeof(Plan) == 48, "Plan is 48 bytes");
+
+// fp64 sampler: per-chunk record and near-tie slots.
+constexpr int kTieCap = 32;                  // near ties recorded per chunk
+constexpr double kTieWindow = 1.0 / 16384.0; // relative width of the near-tie band
+constexpr int kMaxSampChunks = 2048;        // V <= kMaxSampChunks * kSampChunk
+struct ChunkRec {
+  double et, ed;   // sum of e_t, e_d over the chunk
+  double at, ad;   // sum of e_t, e_d over tokens certainly having p > q
+  int ntie;        // near ties found (may exceed kTieCap: then the exact path runs)
+  int pad[7];
+};
+static_assert(sizeof(ChunkRec) == 64, "ChunkRec is 64 bytes");
+struct Tie {
+  double et, ed;
+  int v, pad;
+};
+static_assert(sizeof(Tie) == 24, "Tie is 24 bytes");
 
 // bf16 logits travel as their 16-bit patterns.
 using bf16_t = uint16_t;
@@ -56,20 +75,47 @@ __device__ __forceinline__ void unpack(const uint4 w, float* out, bf16_t) {
   }
 }
 
-// Load the 16-byte vector of elements [e0, e0 + kPerVec) of `row` as floats.
-// Elements at or beyond V read as -inf (they carry no probability mass).
-// `aligned` says the row start is 16-byte aligned; e0 is a multiple of kPerVec.
+// Unconditional 16-byte load of elements [e0, e0 + kPerVec) of a 16-byte
+// aligned row, as floats.  Callers use it only on chunks they have checked,
+// uniformly for the whole workgroup, to be aligned and inside the row: a
+// per-lane bounds branch around each load would split the loads into
+// exec-masked regions and serialise them.
 template <typename T>
-__device__ __forceinline__ void load_vec(const T* __restrict__ row, long e0, int V, bool aligned,
-                                         float* out) {
+__device__ __forceinline__ void load_vec_fast(const T* __restrict__ row, long e0, float* out) {
+  const uint4 w = *reinterpret_cast<const uint4*>(row + e0);
+  unpack(w, out, T{});
+}
+
+// Same, with the nontemporal hint: for logits streamed exactly once.
+template <typename T>
+__device__ __forceinline__ void load_vec_stream(const T* __restrict__ row, long e0, float* out) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(row + e0);
+  uint4 w;
+  w.x = __builtin_nontemporal_load(p);
+  w.y = __builtin_nontemporal_load(p + 1);
+  w.z = __builtin_nontemporal_load(p + 2);
+  w.w = __builtin_nontemporal_load(p + 3);
+  unpack(w, out, T{});
+}
+
+// Checked load of the same elements for tail or unaligned chunks: a whole
+// 16-byte vector when it is aligned and inside the row, element by element
+// only for the one vector that straddles V.  Elements at or beyond V read as
+// -inf (they carry no probability mass).
+template <typename T>
+__device__ __forceinline__ void load_vec_checked(const T* __restrict__ row, long e0, int V,
+                                                 bool aligned, float* out) {
   constexpr int N = Elem<T>::kPerVec;
   if (aligned && e0 + N <= V) {
-    const uint4 w = *reinterpret_cast<const uint4*>(row + e0);
-    unpack(w, out, T{});
+    load_vec_fast(row, e0, out);
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) out[i] = (e0 + i < V) ? to_f32(row[e0 + i]) : -INFINITY;
   }
+}
+
+__device__ __forceinline__ bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 }
 
 // Butterfly reductions: every lane ends with the same, bit-identical value

@@ -16,12 +16,12 @@
 
 namespace specv {
 
-template <typename T>
+template <typename T, int VECS>
 __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
     int K, int V, int nchunk, float c, float2* __restrict__ part) {
   constexpr int N = Elem<T>::kPerVec;
-  constexpr int kChunk = kRowThreads * kRowVecs * N;
+  constexpr int kChunk = kRowThreads * VECS * N;
   const int R = 2 * K + 1;
   const int chunk = blockIdx.x % nchunk;
   const int rr = blockIdx.x / nchunk;
@@ -33,17 +33,27 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   const int k = is_target ? r : r - (K + 1);
   if (k > (is_target ? nb : nb - 1)) return;         // row not needed for this request
   const T* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
-  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
 
-  float v[kRowVecs][N];
+  // Each wave reads one contiguous segment of VECS * 1 KB: its loads are
+  // 1 KB apart, so concurrent loads spread over the HBM channels instead of
+  // striding by the workgroup width.
+  float v[VECS][N];
   const long e_base = (long)chunk * kChunk;
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  const long e_wave = e_base + (long)wid * VECS * kWave * N + (long)lane * N;
+  const bool aligned = aligned16(row);
+  if (aligned && e_base + kChunk <= V) {              // uniform: interior chunk
 #pragma unroll
-  for (int j = 0; j < kRowVecs; ++j)
-    load_vec(row, e_base + ((long)j * kRowThreads + threadIdx.x) * N, V, aligned, v[j]);
+    for (int j = 0; j < VECS; ++j) load_vec_stream(row, e_wave + (long)j * kWave * N, v[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < VECS; ++j)
+      load_vec_checked(row, e_wave + (long)j * kWave * N, V, aligned, v[j]);
+  }
 
   float m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kRowVecs; ++j)
+  for (int j = 0; j < VECS; ++j)
 #pragma unroll
     for (int i = 0; i < N; ++i) m = fmaxf(m, v[j][i]);
   m = wave_max(m);
@@ -52,14 +62,13 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   if (m != -INFINITY) {
     const float mc = __fmul_rn(m, c);                // the exact reference fl(m*c)
 #pragma unroll
-    for (int j = 0; j < kRowVecs; ++j)
+    for (int j = 0; j < VECS; ++j)
 #pragma unroll
       for (int i = 0; i < N; ++i) s += __builtin_amdgcn_exp2f(fmaf(v[j][i], c, -mc));
   }
   s = wave_sum(s);
 
   __shared__ float2 red[kRowThreads / kWave];
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   if (lane == 0) red[wid] = make_float2(m, s);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -89,11 +98,11 @@ hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const i
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   if (bf16)
-    row_stats_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
+    row_stats_kernel<bf16_t, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
         static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V, nchunk,
         c, part);
   else
-    row_stats_kernel<float><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
+    row_stats_kernel<float, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
         static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, nchunk,
         c, part);
   return hipGetLastError();

@@ -2,6 +2,7 @@
 // sequence on the caller's stream.  The declarations and their contract live
 // in include/specverify.h.
 #include "specverify.h"
+#include "specverify_selftest.h"
 
 #include <cmath>
 #include <cstdint>
@@ -18,21 +19,18 @@ hipError_t launch_accept(bool bf16, const void* tgt, const void* dft, const int*
                          int K, int V, int nchunk, float c, int eos_id, const float2* part,
                          Plan* plan, int* out_tokens, int* n_emitted, float* alpha_out,
                          double* rmass_out, int* stop_out, int* path_out, hipStream_t stream);
-hipError_t launch_sample_norm(bool bf16, const void* tgt, const void* dft, int B, int K, int V,
-                              int nch, double invT, const Plan* plan, double2* norm_part,
+hipError_t launch_sample_pass(bool bf16, const void* tgt, const void* dft, int B, int K, int V,
+                              int nch, double invT, const Plan* plan, ChunkRec* recs, Tie* ties,
                               hipStream_t stream);
-hipError_t launch_sample_resid(bool bf16, const void* tgt, const void* dft, int B, int K, int V,
-                               int nch, double invT, const Plan* plan, const double2* norm_part,
-                               double* resid_part, hipStream_t stream);
-hipError_t launch_sample_draw(bool bf16, const void* tgt, const void* dft, const float* u_final,
-                              int B, int K, int V, int nch, double invT, const Plan* plan,
-                              const double2* norm_part, const double* resid_part,
-                              int* out_tokens, double* rmass_out, hipStream_t stream);
+hipError_t launch_sample_finish(bool bf16, const void* tgt, const void* dft, const float* u_final,
+                                int B, int K, int V, int nch, double invT, const Plan* plan,
+                                const ChunkRec* recs, const Tie* ties, int* out_tokens,
+                                double* rmass_out, hipStream_t stream);
+hipError_t launch_exp64_selftest(const double* x, double* y, int n, hipStream_t stream);
 
 // Kernel stages of one call, in launch order (specv_verify_timed records an
 // event after each).
-const char* const kStageNames[] = {"row_stats", "accept", "sample_norm", "sample_resid",
-                                   "sample_draw"};
+const char* const kStageNames[] = {"row_stats", "accept", "sample_pass", "sample_finish"};
 constexpr int kNumStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
 
 namespace {
@@ -42,13 +40,13 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace regions, each 256-byte aligned:
-//   row partials   float2  [B][2K+1][nch_row]    (max, partial normaliser)
-//   plans          Plan    [B]
-//   norm partials  double2 [B][nch_samp]         (target, draft fp64 normalisers)
-//   resid partials double  [B][nch_samp]         (fp64 residual mass per chunk)
+//   row partials   float2   [B][2K+1][nch_row]        (max, partial normaliser)
+//   plans          Plan     [B]
+//   chunk records  ChunkRec [B][nch_samp]             (fp64 sums per sampler chunk)
+//   near ties      Tie      [B][nch_samp][kTieCap]
 struct Layout {
   int nch_row = 0, nch_samp = 0;
-  size_t off_row = 0, off_plan = 0, off_norm = 0, off_resid = 0, total = 0;
+  size_t off_row = 0, off_plan = 0, off_recs = 0, off_ties = 0, total = 0;
 };
 
 Layout make_layout(int B, int K, int V, bool bf16) {
@@ -61,10 +59,10 @@ Layout make_layout(int B, int K, int V, bool bf16) {
   off = align_up(off + (size_t)B * (2 * K + 1) * L.nch_row * sizeof(float2));
   L.off_plan = off;
   off = align_up(off + (size_t)B * sizeof(Plan));
-  L.off_norm = off;
-  off = align_up(off + (size_t)B * L.nch_samp * sizeof(double2));
-  L.off_resid = off;
-  off = align_up(off + (size_t)B * L.nch_samp * sizeof(double));
+  L.off_recs = off;
+  off = align_up(off + (size_t)B * L.nch_samp * sizeof(ChunkRec));
+  L.off_ties = off;
+  off = align_up(off + (size_t)B * L.nch_samp * kTieCap * sizeof(Tie));
   L.total = off;
   return L;
 }
@@ -73,6 +71,7 @@ bool filters_on(int V, int top_k, float top_p) { return (top_k > 0 && top_k < V)
 
 specv_status_t check_sizes(int B, int K, int V, specv_dtype_t dtype, int top_k, float top_p) {
   if (B < 1 || K < 0 || K > SPECV_MAX_K || V < 1) return SPECV_EINVAL;
+  if (V > SPECV_MAX_V) return SPECV_EUNSUPPORTED;
   if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_EINVAL;
   if (top_k < 0) return SPECV_EINVAL;
   if (!(top_p > 0.0f && top_p <= 1.0f)) return SPECV_EINVAL;
@@ -113,8 +112,8 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
   char* ws = static_cast<char*>(workspace);
   float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
   Plan* plan = reinterpret_cast<Plan*>(ws + L.off_plan);
-  double2* norm_part = reinterpret_cast<double2*>(ws + L.off_norm);
-  double* resid_part = reinterpret_cast<double*>(ws + L.off_resid);
+  ChunkRec* recs = reinterpret_cast<ChunkRec*>(ws + L.off_recs);
+  Tie* ties = reinterpret_cast<Tie*>(ws + L.off_ties);
 
   // log2(e) / T rounded once to float32; every float32 exponent uses it.
   const float c = (float)(1.4426950408889634 / (double)temperature);
@@ -133,14 +132,11 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
                     eos_id, row_part, plan, out_tokens, n_emitted, alpha_out, rmass_out, stop_out,
                     path_out, stream);
   if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
-  e = launch_sample_norm(bf16, target, draft, B, K, V, L.nch_samp, invT, plan, norm_part, stream);
+  e = launch_sample_pass(bf16, target, draft, B, K, V, L.nch_samp, invT, plan, recs, ties, stream);
   if (e != hipSuccess || !mark(3)) return SPECV_EHIP;
-  e = launch_sample_resid(bf16, target, draft, B, K, V, L.nch_samp, invT, plan, norm_part,
-                          resid_part, stream);
+  e = launch_sample_finish(bf16, target, draft, u_final, B, K, V, L.nch_samp, invT, plan, recs,
+                           ties, out_tokens, rmass_out, stream);
   if (e != hipSuccess || !mark(4)) return SPECV_EHIP;
-  e = launch_sample_draw(bf16, target, draft, u_final, B, K, V, L.nch_samp, invT, plan, norm_part,
-                         resid_part, out_tokens, rmass_out, stream);
-  if (e != hipSuccess || !mark(5)) return SPECV_EHIP;
   return SPECV_OK;
 }
 
@@ -195,6 +191,11 @@ specv_status_t specv_verify_timed(const void* target_logits, const void* draft_l
 }
 
 int specv_num_stages(void) { return specv::kNumStages; }
+
+specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream_t stream) {
+  if (n < 0 || (n > 0 && (!x || !y))) return SPECV_EINVAL;
+  return specv::launch_exp64_selftest(x, y, n, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
+}
 
 const char* specv_stage_name(int i) {
   return (i >= 0 && i < specv::kNumStages) ? specv::kStageNames[i] : nullptr;

@@ -189,3 +189,40 @@ def test_host_argument_errors():
     with pytest.raises(binding.SpecVerifyError) as e:
         binding.verify(**a, workspace=small)
     assert e.value.status == binding.SPECV_EWORKSPACE
+
+
+def test_exp64_against_numpy():
+    # The sampler's float64 exp (table-driven, Tang 1989) within 2 ulp of
+    # numpy's exp over the range the sampler uses, and 0 at and below -745.2.
+    rng = np.random.default_rng(5)
+    x = np.concatenate([-rng.random(400000) * 745.0, -rng.random(200000) * 40.0,
+                        -rng.random(50000) * 1e-3, rng.random(50000) * 700.0,
+                        [0.0, -0.0, -1e-300, -708.39, -709.0, -744.0, -745.0]])
+    y = binding.selftest_exp64(torch.from_numpy(x).to(DEV)).cpu().numpy()
+    ref = np.exp(x)
+    normal = ref > 2.3e-308
+    ulp = np.abs(y[normal] - ref[normal]) / np.spacing(ref[normal])
+    print(f"  exp64: max {ulp.max():.2f} ulp, mean {ulp.mean():.3f} ulp over {normal.sum()} values")
+    assert ulp.max() <= 2.0
+    sub = ~normal
+    assert np.all(np.abs(y[sub] - ref[sub]) <= 2 * 5e-324)
+    z = binding.selftest_exp64(torch.tensor([-np.inf, -746.0, -1e6], dtype=torch.float64,
+                                            device=DEV)).cpu().numpy()
+    assert np.all(z == 0.0)
+
+
+def test_sampler_exact_path_with_many_near_ties():
+    # Draft = target + N(0, 1e-4^2): nearly every token is a near tie, so the
+    # chunks overflow their tie slots and the sampler takes its exact path.
+    # u close to 1 forces rejections whenever p(x) < q(x).
+    w = make_workload(3, B=8)
+    from speculative_decoding_sampling_amd.workloads import from_bf16_bits
+    rng = np.random.default_rng(9)
+    t = from_bf16_bits(w.target).astype(np.float32)
+    w.dtype = "f32"
+    w.target = np.ascontiguousarray(t)
+    w.draft = np.ascontiguousarray(t[:, :w.K] + rng.normal(0, 1e-4, size=t[:, :w.K].shape)
+                                   .astype(np.float32))
+    w.u[:] = np.float32(1.0 - 2.0 ** -24)
+    rep, g, o = assert_parity(w, label="near-identical rows")
+    assert (o["path"] == O.PATH_REJECT).sum() >= 4
