@@ -68,7 +68,7 @@ typedef enum {
 /* Largest vocabulary the call accepts (larger V returns SPECV_EUNSUPPORTED). */
 #define SPECV_MAX_V 4194304
 /* Largest top_k the filter path accepts (candidates per row are held on chip). */
-#define SPECV_MAX_TOPK 1024
+#define SPECV_MAX_TOPK 128
 
 /*
  * Bytes of device workspace specv_verify needs for these sizes.  Returns 0
@@ -96,8 +96,15 @@ SPECV_API size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype,
  *  top_p          1 = off; otherwise in (0, 1): keep the shortest prefix of
  *                 the top-k renormalised distribution, by logit descending,
  *                 whose mass reaches top_p (crossing token and its ties kept).
- *                 top_p < 1 needs 0 < top_k <= SPECV_MAX_TOPK, and top_k alone
- *                 needs top_k <= SPECV_MAX_TOPK (else SPECV_EUNSUPPORTED).
+ *                 Filters are supported (else SPECV_EUNSUPPORTED) when
+ *                 0 < top_k <= SPECV_MAX_TOPK, top_k < V, V <= 262144 and the
+ *                 row's candidate slots fit on chip: (ceil(V / 8192) - 1) * c
+ *                 + max(c, 256) <= 4096 with c = 8 * ceil((1.5 * top_k + 40) / 8)
+ *                 (top_k = 50 at V = 152064 uses 2416).  top_p < 1 without an active top-k is
+ *                 not supported.  A request whose filtered row keeps more than
+ *                 512 tokens, or whose 8192-token chunk holds more candidates
+ *                 than its slot (massive ties), is reported as a per-request
+ *                 error (n_emitted = -1, debug path -1).
  *  eos_id         -1 = off; else in [0, V): the round stops right after the
  *                 first emitted EOS (accepted draft or drawn token).
  *  out_tokens     [B][K+1] int32 output: emitted tokens, -1 beyond n_emitted.
@@ -140,6 +147,7 @@ SPECV_API specv_status_t specv_verify_debug(const void *target_logits, const voi
  * of events[i+1] after kernel stage i.  `events` holds specv_num_stages() + 1
  * caller-created HIP events (SPECV_EINVAL if NULL or any entry is NULL); the
  * caller reads stage durations with hipEventElapsedTime after synchronising.
+ * The stages differ with and without filters (specv_stage_name).
  */
 SPECV_API specv_status_t specv_verify_timed(const void *target_logits, const void *draft_logits,
                                             specv_dtype_t dtype, const int32_t *draft_tokens,
@@ -151,9 +159,10 @@ SPECV_API specv_status_t specv_verify_timed(const void *target_logits, const voi
                                             hipStream_t stream, hipEvent_t *events);
 
 /* Number of kernel stages one call launches, and the static name of stage i
- * (NULL when out of range). */
-SPECV_API int specv_num_stages(void);
-SPECV_API const char *specv_stage_name(int i);
+ * (NULL when out of range); `filtered` is nonzero for calls with top-k /
+ * top-p active. */
+SPECV_API int specv_num_stages(int filtered);
+SPECV_API const char *specv_stage_name(int filtered, int i);
 
 /* Static, human-readable name of a status code. */
 SPECV_API const char *specv_status_string(specv_status_t status);

@@ -57,9 +57,9 @@ def load_library():
         lib.specv_verify_debug.restype = c_int
         lib.specv_verify_timed.argtypes = common + [c_vp]
         lib.specv_verify_timed.restype = c_int
-        lib.specv_num_stages.argtypes = []
+        lib.specv_num_stages.argtypes = [c_int]
         lib.specv_num_stages.restype = c_int
-        lib.specv_stage_name.argtypes = [c_int]
+        lib.specv_stage_name.argtypes = [c_int, c_int]
         lib.specv_stage_name.restype = ctypes.c_char_p
         lib.specv_status_string.argtypes = [c_int]
         lib.specv_status_string.restype = ctypes.c_char_p
@@ -75,10 +75,11 @@ def status_string(status):
     return load_library().specv_status_string(int(status)).decode()
 
 
-def stage_names():
+def stage_names(filtered=False):
     """Names of the kernel stages one call launches, in order."""
     lib = load_library()
-    return [lib.specv_stage_name(i).decode() for i in range(lib.specv_num_stages())]
+    f = 1 if filtered else 0
+    return [lib.specv_stage_name(f, i).decode() for i in range(lib.specv_num_stages(f))]
 
 
 def selftest_exp64(x):

@@ -51,14 +51,23 @@ __device__ __forceinline__ void combine_row(const float2* __restrict__ p, int n,
   S = s;
 }
 
-template <typename T>
+// Probability of token x in a filtered row: exp((z - m)/T) / S if z is kept.
+__device__ __forceinline__ double filt_prob(float z, const FiltRow& fr, double invT) {
+  if (!(z >= fr.tau) || z == -INFINITY) return 0.0;
+  return exp(((double)z - (double)fr.m) * invT) / fr.S;
+}
+
+// FILT selects the row statistics: chunk partials of the unfiltered path, or
+// the per-row (max, threshold, float64 normaliser) of the top-k / top-p path.
+template <typename T, bool FILT>
 __global__ __launch_bounds__(kWave) void accept_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ tokens,
     const int* __restrict__ draft_len, const float* __restrict__ u,
-    const float* __restrict__ u_final, int K, int V, int nchunk, float c, int eos_id,
-    const float2* __restrict__ part, Plan* __restrict__ plan, int* __restrict__ out_tokens,
-    int* __restrict__ n_emitted, float* __restrict__ alpha_out, double* __restrict__ rmass_out,
-    int* __restrict__ stop_out, int* __restrict__ path_out) {
+    const float* __restrict__ u_final, int K, int V, int nchunk, float c, double invT,
+    int eos_id, const float2* __restrict__ part, const FiltRow* __restrict__ frows,
+    Plan* __restrict__ plan, int* __restrict__ out_tokens, int* __restrict__ n_emitted,
+    float* __restrict__ alpha_out, double* __restrict__ rmass_out, int* __restrict__ stop_out,
+    int* __restrict__ path_out) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const int R = 2 * K + 1;
@@ -71,22 +80,39 @@ __global__ __launch_bounds__(kWave) void accept_kernel(
     uk = u[(size_t)b * K + lane];
   }
   float Mt = -INFINITY, Md = -INFINITY, St = 0.f, Sd = 0.f;
-  const float2* prow = part + (size_t)b * R * nchunk;
-  if (lane <= K) combine_row(prow + (size_t)lane * nchunk, nchunk, c, Mt, St);
-  if (lane < K) combine_row(prow + (size_t)(K + 1 + lane) * nchunk, nchunk, c, Md, Sd);
+  FiltRow ft, fd;
+  if constexpr (FILT) {
+    if (lane <= K) ft = frows[(size_t)b * R + lane];
+    if (lane < K) fd = frows[(size_t)b * R + K + 1 + lane];
+  } else {
+    const float2* prow = part + (size_t)b * R * nchunk;
+    if (lane <= K) combine_row(prow + (size_t)lane * nchunk, nchunk, c, Mt, St);
+    if (lane < K) combine_row(prow + (size_t)(K + 1 + lane) * nchunk, nchunk, c, Md, Sd);
+  }
 
   bool bad = nb_raw < 0 || nb_raw > K || !(uf >= 0.f && uf < 1.f);
   const int nb = bad ? 0 : nb_raw;
   bool ok = true, accept = false;
   double alpha = -1.0;
-  if (!bad && lane <= nb) ok = Mt != -INFINITY;            // target row has a finite logit
+  if (!bad && lane <= nb) {                                  // target row usable
+    if constexpr (FILT) ok = ft.status == 0;
+    else ok = Mt != -INFINITY;
+  }
   if (!bad && lane < nb) {
-    ok = ok && Md != -INFINITY && x >= 0 && x < V && uk >= 0.f && uk < 1.f;
+    if constexpr (FILT) ok = ok && fd.status == 0;
+    else ok = ok && Md != -INFINITY;
+    ok = ok && x >= 0 && x < V && uk >= 0.f && uk < 1.f;
     if (ok) {
       const float zt = to_f32(tgt[target_row_off(b, lane, K, V) + x]);
       const float zd = to_f32(dft[draft_row_off(b, lane, K, V) + x]);
-      const double pt = exp2((double)zt * c - (double)__fmul_rn(Mt, c)) / (double)St;
-      const double qd = exp2((double)zd * c - (double)__fmul_rn(Md, c)) / (double)Sd;
+      double pt, qd;
+      if constexpr (FILT) {
+        pt = filt_prob(zt, ft, invT);
+        qd = filt_prob(zd, fd, invT);
+      } else {
+        pt = exp2((double)zt * c - (double)__fmul_rn(Mt, c)) / (double)St;
+        qd = exp2((double)zd * c - (double)__fmul_rn(Md, c)) / (double)Sd;
+      }
       ok = qd > 0.0;                                         // x was drawn from q: q(x) > 0
       const double ratio = pt / qd;
       alpha = ratio < 1.0 ? ratio : 1.0;
@@ -134,7 +160,7 @@ __global__ __launch_bounds__(kWave) void accept_kernel(
     // S_t / S_d in natural-exp units: each base-2 normaliser is relative to
     // 2^fl(M*c); undo that offset exactly (M*c is exact in float64).
     pl.g = 0.0;
-    if (path == kPathReject) {
+    if (!FILT && path == kPathReject) {
       const double off_t = (double)__fmul_rn(Mt, c) - (double)Mt * (double)c;
       const double off_d = (double)__fmul_rn(Md, c) - (double)Md * (double)c;
       pl.g = ((double)St / (double)Sd) * exp2(off_t - off_d);
@@ -148,21 +174,23 @@ __global__ __launch_bounds__(kWave) void accept_kernel(
   }
 }
 
-hipError_t launch_accept(bool bf16, const void* tgt, const void* dft, const int* tokens,
+hipError_t launch_accept(bool bf16, bool filt, const void* tgt, const void* dft, const int* tokens,
                          const int* draft_len, const float* u, const float* u_final, int B,
-                         int K, int V, int nchunk, float c, int eos_id, const float2* part,
-                         Plan* plan, int* out_tokens, int* n_emitted, float* alpha_out,
-                         double* rmass_out, int* stop_out, int* path_out, hipStream_t stream) {
-  if (bf16)
-    accept_kernel<bf16_t><<<dim3(B), dim3(kWave), 0, stream>>>(
-        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), tokens, draft_len, u,
-        u_final, K, V, nchunk, c, eos_id, part, plan, out_tokens, n_emitted, alpha_out,
-        rmass_out, stop_out, path_out);
-  else
-    accept_kernel<float><<<dim3(B), dim3(kWave), 0, stream>>>(
-        static_cast<const float*>(tgt), static_cast<const float*>(dft), tokens, draft_len, u,
-        u_final, K, V, nchunk, c, eos_id, part, plan, out_tokens, n_emitted, alpha_out,
-        rmass_out, stop_out, path_out);
+                         int K, int V, int nchunk, float c, double invT, int eos_id,
+                         const float2* part, const FiltRow* frows, Plan* plan, int* out_tokens,
+                         int* n_emitted, float* alpha_out, double* rmass_out, int* stop_out,
+                         int* path_out, hipStream_t stream) {
+#define SPECV_ACCEPT(TT, FF)                                                                     \
+  accept_kernel<TT, FF><<<dim3(B), dim3(kWave), 0, stream>>>(                                    \
+      static_cast<const TT*>(tgt), static_cast<const TT*>(dft), tokens, draft_len, u, u_final, K, \
+      V, nchunk, c, invT, eos_id, part, frows, plan, out_tokens, n_emitted, alpha_out, rmass_out, \
+      stop_out, path_out)
+  if (bf16) {
+    if (filt) SPECV_ACCEPT(bf16_t, true); else SPECV_ACCEPT(bf16_t, false);
+  } else {
+    if (filt) SPECV_ACCEPT(float, true); else SPECV_ACCEPT(float, false);
+  }
+#undef SPECV_ACCEPT
   return hipGetLastError();
 }
 

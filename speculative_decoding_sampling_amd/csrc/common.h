@@ -50,6 +50,28 @@ struct Tie {
 };
 static_assert(sizeof(Tie) == 24, "Tie is 24 bytes");
 
+// Top-k / top-p path: candidate select, per-row merge, kept lists.
+constexpr int kFiltThreads = 256;
+constexpr int kFiltPerThread = 32;
+constexpr int kFiltChunk = kFiltThreads * kFiltPerThread;   // 8192 tokens per chunk
+constexpr int kFiltSortMax = 4096;          // candidates a row merge can sort in LDS
+constexpr int kFiltMaxChunks = 32;          // V <= 32 * 8192 on the filter path
+constexpr int kKeptCap = 512;               // kept tokens per row after top-k / top-p
+constexpr int kFiltMaxTopK = 128;           // candidate slots stay ~1.5 k only up to here
+struct FiltRow {
+  float m;      // row maximum (exact)
+  float tau;    // final threshold: a token is kept iff its logit >= tau
+  double S;     // float64 normaliser sum_{kept} exp((z - m) / T)
+  int count;    // kept tokens (list length)
+  int status;   // 0 ok; 1 capacity exceeded; 2 no finite logit
+  long pad;
+};
+static_assert(sizeof(FiltRow) == 32, "FiltRow is 32 bytes");
+struct Kept {
+  int id;
+  float z;
+};
+
 // bf16 logits travel as their 16-bit patterns.
 using bf16_t = uint16_t;
 

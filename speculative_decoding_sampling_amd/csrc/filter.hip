@@ -1,0 +1,484 @@
+// Top-k / top-p filtering and the sampler over the kept tokens.
+//
+// p and q are the target's and the draft's distributions after temperature,
+// top-k and top-p, each row filtered on its own (nickwang.xyz
+// "推测解码：草稿、验证与实际加速", section "接受与拒绝怎样保住分布": both already
+// include those settings).  top-k keeps every logit >= the k-th largest;
+// top-p then keeps the shortest prefix of the renormalised top-k
+// distribution, ordered by logit (descending) then token id, whose mass
+// reaches top_p, with the crossing token and its ties.
+//
+// One pass over HBM.  filter_cand streams each needed row in 8192-token
+// chunks and keeps a superset of the chunk's top-k: every thread takes the
+// max of its 32 logits and T_c is the k-th largest of the 256 thread maxima,
+// so the chunk has >= k logits >= T_c; the chunk's k-th largest logit is
+// >= T_c, and the row's k-th largest is at least the chunk's, so every logit
+// the row keeps is a candidate.  The candidates (~1.1 k per chunk on random
+// data) go to a per-chunk slot.  filter_merge
+// sorts a row's candidates in LDS by (logit desc, id asc), reads tau_k at
+// rank k, runs top-p in float64 over the sorted prefix, and writes the row
+// maximum, the final threshold, the float64 normaliser over the kept set and
+// the kept tokens sorted by id.  Nothing downstream reads the full rows
+// again: acceptance needs two gathers per position, and the residual or
+// bonus draw walks the target row's kept list (p is zero elsewhere).
+#include <climits>
+
+#include "common.h"
+#include "exp64.h"
+
+namespace specv {
+
+// Order-preserving 32-bit key of a float (larger float -> larger key).
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+constexpr uint32_t kNegInfKey = 0x007fffffu;   // fkey(-inf)
+
+// Descending sort of one key per lane across a wave (bitonic network).
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t key) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      const uint32_t other = __shfl_xor(key, stride, kWave);
+      const bool up = (lane & size) == 0;
+      const bool lower = (lane & stride) == 0;
+      key = (lower == up) ? max(key, other) : min(key, other);
+    }
+  }
+  return key;
+}
+
+template <typename V>
+__device__ __forceinline__ V block_scan_excl(V v, V* lds, V& total) {
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  V x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const V y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  V excl = __shfl_up(x, 1, kWave);
+  if (lane == 0) excl = V(0);
+  __syncthreads();
+  if (lane == kWave - 1) lds[wid] = x;
+  __syncthreads();
+  V off = V(0);
+  total = V(0);
+#pragma unroll
+  for (int w = 0; w < kFiltThreads / kWave; ++w) {
+    if (w < wid) off += lds[w];
+    total += lds[w];
+  }
+  return off + excl;
+}
+
+__device__ __forceinline__ int block_min_i(int v, int* lds) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) lds[wid] = v;
+  __syncthreads();
+  int r = lds[0];
+#pragma unroll
+  for (int w = 1; w < kFiltThreads / kWave; ++w) r = min(r, lds[w]);
+  return r;
+}
+
+// Row index r in [0, 2K+1) of request b: needed when it is target row
+// k <= n_b or draft row k < n_b.
+__device__ __forceinline__ bool row_needed(int r, int K, int nb, bool& is_target, int& k) {
+  is_target = r <= K;
+  k = is_target ? r : r - (K + 1);
+  return k <= (is_target ? nb : nb - 1);
+}
+
+// ---------------------------------------------------------------------------
+// filter_cand: per (request, needed row, 8192-token chunk).  Thread t holds
+// tokens e_base + 256 j + t, j = 0..31: loads are coalesced, issued
+// back-to-back (the address is clamped instead of branched on), and any
+// chunk with 256 or more valid tokens gives every thread data, so every
+// wave's threshold is a real logit.  A chunk with at most `slot` valid tokens
+// (only a row's last chunk can have so few) keeps all of them.
+template <typename T>
+__global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
+    const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
+    int K, int V, int nch, int top_k, int cap, int row_stride, uint64_t* __restrict__ cand,
+    int* __restrict__ counts) {
+  __shared__ uint32_t tw[kFiltThreads / kWave];
+  __shared__ uint32_t lists[kFiltThreads];
+  __shared__ int il[kFiltThreads / kWave];
+  const int R = 2 * K + 1;
+  const int chunk = blockIdx.x % nch;
+  const int rr = blockIdx.x / nch;
+  const int r = rr % R, b = rr / R;
+  const int nb = draft_len[b];
+  if (nb < 0 || nb > K) return;
+  bool is_target;
+  int k;
+  if (!row_needed(r, K, nb, is_target, k)) return;
+  const T* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  const long e_base = (long)chunk * kFiltChunk;
+  const int n_valid = (int)min((long)kFiltChunk, (long)V - e_base);
+  const int slot = chunk == nch - 1 ? row_stride - (nch - 1) * cap : cap;
+  float v[kFiltPerThread];
+  if (n_valid == kFiltChunk) {
+#pragma unroll
+    for (int j = 0; j < kFiltPerThread; ++j)
+      v[j] = to_f32(row[e_base + (long)j * kFiltThreads + threadIdx.x]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kFiltPerThread; ++j) {
+      const long e = e_base + (long)j * kFiltThreads + threadIdx.x;
+      const float x = to_f32(row[e < V ? e : (long)V - 1]);
+      v[j] = e < V ? x : -INFINITY;
+    }
+  }
+  uint32_t tc = kNegInfKey;                          // keep every valid logit ...
+  if (n_valid > slot) {                              // ... unless the chunk is larger than its slot
+    // T_c = the top_k-th largest of the 256 thread maxima: top_k distinct
+    // threads each hold a logit >= T_c.  Each wave sorts its maxima; every
+    // thread ranks its own maximum against the four sorted lists.
+    uint32_t tmax = kNegInfKey;
+#pragma unroll
+    for (int j = 0; j < kFiltPerThread; ++j) tmax = max(tmax, fkey(v[j]));
+    lists[threadIdx.x] = wave_sort_desc(tmax);        // wave w's list at [64w, 64w + 64)
+    __syncthreads();
+    int rank = 0;                                    // thread maxima >= tmax
+#pragma unroll
+    for (int w = 0; w < kFiltThreads / kWave; ++w) {
+      int lo = 0, hi = kWave;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (lists[w * kWave + mid] >= tmax) lo = mid + 1;
+        else hi = mid;
+      }
+      rank += lo;
+    }
+    uint32_t best = rank >= top_k ? tmax : 0u;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) best = max(best, (uint32_t)__shfl_xor(best, o, kWave));
+    if (lane == 0) tw[wid] = best;
+    __syncthreads();
+    tc = tw[0];
+#pragma unroll
+    for (int w = 1; w < kFiltThreads / kWave; ++w) tc = max(tc, tw[w]);
+  }
+  // candidates: finite logits with key >= tc, written in thread order
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < kFiltPerThread; ++j) {
+    const uint32_t kk = fkey(v[j]);
+    mine += (kk >= tc && kk > kNegInfKey) ? 1 : 0;
+  }
+  int total;
+  int off = block_scan_excl<int>(mine, il, total);
+  uint64_t* dst = cand + (size_t)rr * row_stride + (size_t)chunk * cap;
+#pragma unroll
+  for (int j = 0; j < kFiltPerThread; ++j) {
+    const uint32_t kk = fkey(v[j]);
+    if (kk >= tc && kk > kNegInfKey) {
+      if (off < slot) {
+        const uint32_t id = (uint32_t)(e_base + (long)j * kFiltThreads + threadIdx.x);
+        dst[off] = ((uint64_t)kk << 32) | (uint64_t)(0xffffffffu - id);
+      }
+      ++off;
+    }
+  }
+  if (threadIdx.x == 0) counts[(size_t)rr * nch + chunk] = total;
+}
+
+// ---------------------------------------------------------------------------
+// filter_merge: per (request, needed row).
+__device__ __forceinline__ void lds_bitonic_desc(uint64_t* a, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < n / 2; idx += kFiltThreads) {
+        const int lo = 2 * stride * (idx / stride) + (idx % stride);
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t x = a[lo], y = a[hi];
+        if ((x < y) == up) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
+    const int* __restrict__ draft_len, int K, int nch, int cap, int row_stride, int top_k,
+    float top_p, double invT, const uint64_t* __restrict__ cand, const int* __restrict__ counts,
+    FiltRow* __restrict__ rows, Kept* __restrict__ kept) {
+  __shared__ uint64_t keys[kFiltSortMax];
+  __shared__ double tbl[SPECV_EXP64_N];
+  __shared__ double dl[kFiltThreads / kWave];
+  __shared__ int il[kFiltThreads / kWave];
+  __shared__ int s_off[kFiltMaxChunks + 1];
+  __shared__ int s_status;
+  const int R = 2 * K + 1;
+  const int rr = blockIdx.x;
+  const int r = rr % R, b = rr / R;
+  exp64_stage_table(tbl);
+  const int nb = draft_len[b];
+  if (nb < 0 || nb > K) return;
+  bool is_target;
+  int k;
+  if (!row_needed(r, K, nb, is_target, k)) return;
+
+  // gather the row's candidates into LDS
+  if (threadIdx.x == 0) {
+    int acc = 0, st = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int n = counts[(size_t)rr * nch + c];
+      const int slot = c == nch - 1 ? row_stride - (nch - 1) * cap : cap;
+      if (n > slot) st = 1;
+      s_off[c] = acc;
+      acc += min(n, slot);
+    }
+    s_off[nch] = acc;
+    s_status = st;
+  }
+  __syncthreads();
+  const int n_all = s_off[nch];
+  int P = 2;
+  while (P < n_all) P <<= 1;
+  for (int c = 0; c < nch; ++c) {
+    const int base = s_off[c], n = s_off[c + 1] - base;
+    for (int i = threadIdx.x; i < n; i += kFiltThreads)
+      keys[base + i] = cand[(size_t)rr * row_stride + (size_t)c * cap + i];
+  }
+  for (int i = n_all + threadIdx.x; i < P; i += kFiltThreads) keys[i] = 0ull;   // sorts last
+  lds_bitonic_desc(keys, P);
+
+  FiltRow out;
+  out.status = s_status;
+  if (n_all == 0) out.status = 2;                    // no finite logit in the row
+  // tau_k: the top_k-th largest logit (top_k < V here), ties kept
+  const int kk = min(top_k, n_all);
+  const uint32_t tau_k = n_all > 0 ? (uint32_t)(keys[max(kk, 1) - 1] >> 32) : 0u;
+  // L = number of candidates with key >= tau_k: first index below it
+  int cand_i = INT_MAX;
+  for (int i = threadIdx.x; i < n_all; i += kFiltThreads)
+    if ((uint32_t)(keys[i] >> 32) < tau_k) cand_i = min(cand_i, i);
+  int L = block_min_i(cand_i, il);
+  if (L == INT_MAX) L = n_all;
+  const float m = n_all > 0 ? unkey((uint32_t)(keys[0] >> 32)) : -INFINITY;
+  const double md = (double)m;
+
+  // float64 weights of the sorted prefix, blocked scan in sorted order
+  const int q = (L + kFiltThreads - 1) / kFiltThreads;
+  const int i_lo = min(L, (int)threadIdx.x * q), i_hi = min(L, i_lo + q);
+  double mine = 0.0;
+  for (int i = i_lo; i < i_hi; ++i)
+    mine += exp64(((double)unkey((uint32_t)(keys[i] >> 32)) - md) * invT, tbl);
+  double tot;
+  const double excl = block_scan_excl<double>(mine, dl, tot);
+  int Lk = L;                                        // kept prefix length
+  uint32_t tau = tau_k;
+  if (top_p < 1.0f && L > 0) {
+    // M = first sorted index whose running mass reaches top_p of the total
+    int hit = INT_MAX;
+    double run = excl;
+    for (int i = i_lo; i < i_hi; ++i) {
+      run += exp64(((double)unkey((uint32_t)(keys[i] >> 32)) - md) * invT, tbl);
+      if (hit == INT_MAX && run / tot >= (double)top_p) hit = i;
+    }
+    int M = block_min_i(hit, il);
+    if (M == INT_MAX) M = L - 1;
+    tau = (uint32_t)(keys[M] >> 32);
+    int first_below = INT_MAX;
+    for (int i = threadIdx.x; i < L; i += kFiltThreads)
+      if ((uint32_t)(keys[i] >> 32) < tau) first_below = min(first_below, i);
+    Lk = block_min_i(first_below, il);
+    if (Lk == INT_MAX) Lk = L;
+  }
+  // normaliser over the kept prefix, same blocked order
+  double keep_sum = 0.0;
+  {
+    const int j_lo = min(Lk, (int)threadIdx.x * q), j_hi = min(Lk, j_lo + q);
+    for (int i = j_lo; i < j_hi; ++i)
+      keep_sum += exp64(((double)unkey((uint32_t)(keys[i] >> 32)) - md) * invT, tbl);
+    double stot;
+    (void)block_scan_excl<double>(keep_sum, dl, stot);
+    keep_sum = stot;
+  }
+  if (Lk > kKeptCap) out.status = 1;
+
+  // kept tokens re-sorted by id ascending: key (~id << 32 | logit bits), descending
+  __syncthreads();
+  int P2 = 2;
+  while (P2 < Lk) P2 <<= 1;
+  if (Lk <= kKeptCap) {
+    for (int i = threadIdx.x; i < P2; i += kFiltThreads) {
+      uint64_t x = 0ull;
+      if (i < Lk) {
+        const uint64_t e = keys[i];
+        const uint32_t id = 0xffffffffu - (uint32_t)e;
+        x = ((uint64_t)(0xffffffffu - id) << 32) | (uint64_t)__float_as_uint(unkey((uint32_t)(e >> 32)));
+      }
+      keys[kFiltSortMax / 2 + i] = x;
+    }
+    lds_bitonic_desc(keys + kFiltSortMax / 2, P2);
+    Kept* dst = kept + (size_t)rr * kKeptCap;
+    for (int i = threadIdx.x; i < Lk; i += kFiltThreads) {
+      const uint64_t x = keys[kFiltSortMax / 2 + i];
+      Kept e;
+      e.id = (int)(0xffffffffu - (uint32_t)(x >> 32));
+      e.z = __uint_as_float((uint32_t)x);
+      dst[i] = e;
+    }
+  }
+  if (threadIdx.x == 0) {
+    out.m = m;
+    out.tau = unkey(tau);
+    out.S = keep_sum;
+    out.count = Lk;
+    out.pad = 0;
+    rows[rr] = out;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// sample_list: per request, the residual or bonus draw over the target row's
+// kept tokens in id order.
+template <typename T>
+__global__ __launch_bounds__(kFiltThreads) void sample_list_kernel(
+    const T* __restrict__ dft, const float* __restrict__ u_final, int K, int V, double invT,
+    const Plan* __restrict__ plan, const FiltRow* __restrict__ rows, const Kept* __restrict__ kept,
+    int* __restrict__ out_tokens, double* __restrict__ rmass_out) {
+  __shared__ double tbl[SPECV_EXP64_N];
+  __shared__ double dl[kFiltThreads / kWave];
+  __shared__ int il[kFiltThreads / kWave];
+  const int b = blockIdx.x;
+  exp64_stage_table(tbl);
+  const Plan pl = plan[b];
+  if (pl.path != kPathReject && pl.path != kPathBonus) return;   // uniform per block
+  const int R = 2 * K + 1;
+  const FiltRow tr = rows[(size_t)b * R + pl.trow];
+  const bool rej = pl.path == kPathReject;
+  FiltRow dr;
+  dr.m = 0.f; dr.tau = 0.f; dr.S = 1.0; dr.count = 0; dr.status = 0; dr.pad = 0;
+  if (rej) dr = rows[(size_t)b * R + K + 1 + pl.drow];
+  const Kept* list = kept + ((size_t)b * R + pl.trow) * kKeptCap;
+  const T* drow = rej ? dft + draft_row_off(b, pl.drow, K, V) : nullptr;
+  __syncthreads();
+  const int n = tr.count;
+  const int q = (n + kFiltThreads - 1) / kFiltThreads;
+  const int i_lo = min(n, (int)threadIdx.x * q), i_hi = min(n, i_lo + q);
+  constexpr int kMaxPer = (kKeptCap + kFiltThreads - 1) / kFiltThreads;
+  double w[kMaxPer];
+  int ids[kMaxPer];
+  double wp[kMaxPer];
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    w[j] = wp[j] = 0.0;
+    ids[j] = -1;
+    const int i = i_lo + j;
+    if (i < i_hi) {
+      const Kept e = list[i];
+      ids[j] = e.id;
+      wp[j] = exp64(((double)e.z - (double)tr.m) * invT, tbl);
+      w[j] = wp[j];
+      if (rej) {
+        const float zd = to_f32(drow[e.id]);
+        double qv = 0.0;
+        if (zd >= dr.tau && zd > -INFINITY) qv = exp64(((double)zd - (double)dr.m) * invT, tbl) / dr.S;
+        const double r = wp[j] / tr.S - qv;
+        w[j] = r > 0.0 ? r : 0.0;
+      }
+    }
+  }
+  double mine = 0.0;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) mine += w[j];
+  double total;
+  double excl = block_scan_excl<double>(mine, dl, total);
+  bool resid = rej;
+  if (resid && !(total > 0.0)) {                     // unreachable in exact arithmetic: draw from p_j
+    resid = false;
+    mine = 0.0;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      w[j] = wp[j];
+      mine += w[j];
+    }
+    excl = block_scan_excl<double>(mine, dl, total);
+  }
+  const double t = (double)u_final[b] * total;
+  int hit = INT_MAX, last = -1;
+  double run = excl;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    if (ids[j] < 0) continue;
+    run += w[j];
+    if (hit == INT_MAX && t < run) hit = ids[j];
+    if (w[j] > 0.0) last = ids[j];
+  }
+  int y = block_min_i(hit, il);
+  if (y == INT_MAX) y = -block_min_i(-last, il);     // rounding fall-through: last positive
+  if (threadIdx.x == 0) {
+    out_tokens[(size_t)b * (K + 1) + pl.stop] = y;
+    if (rmass_out) rmass_out[b] = (rej && resid) ? total : 0.0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+int filter_cap(int top_k) { return ((3 * top_k) / 2 + 40 + 7) / 8 * 8; }
+
+// Candidate slots of one row: cap per chunk, at least 256 for the last one
+// (it keeps every valid token when it has 256 or fewer).
+int filter_row_stride(int nch, int top_k) {
+  const int cap = filter_cap(top_k);
+  return (nch - 1) * cap + (cap > 256 ? cap : 256);
+}
+
+hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int* draft_len, int B,
+                         int K, int V, int nch, int top_k, float top_p, double invT,
+                         uint64_t* cand, int* counts, FiltRow* rows, Kept* kept,
+                         hipStream_t stream, hipEvent_t mid) {
+  const int cap = filter_cap(top_k);
+  const int stride = filter_row_stride(nch, top_k);
+  const size_t blocks = (size_t)B * (2 * K + 1) * nch;
+  if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  if (bf16)
+    filter_cand_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
+        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V, nch,
+        top_k, cap, stride, cand, counts);
+  else
+    filter_cand_kernel<float><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
+        static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, nch,
+        top_k, cap, stride, cand, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (mid && (e = hipEventRecord(mid, stream)) != hipSuccess) return e;
+  filter_merge_kernel<<<dim3((unsigned)((size_t)B * (2 * K + 1))), dim3(kFiltThreads), 0, stream>>>(
+      draft_len, K, nch, cap, stride, top_k, top_p, invT, cand, counts, rows, kept);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_list(bool bf16, const void* dft, const float* u_final, int B, int K, int V,
+                              double invT, const Plan* plan, const FiltRow* rows, const Kept* kept,
+                              int* out_tokens, double* rmass_out, hipStream_t stream) {
+  if (bf16)
+    sample_list_kernel<bf16_t><<<dim3(B), dim3(kFiltThreads), 0, stream>>>(
+        static_cast<const bf16_t*>(dft), u_final, K, V, invT, plan, rows, kept, out_tokens,
+        rmass_out);
+  else
+    sample_list_kernel<float><<<dim3(B), dim3(kFiltThreads), 0, stream>>>(
+        static_cast<const float*>(dft), u_final, K, V, invT, plan, rows, kept, out_tokens,
+        rmass_out);
+  return hipGetLastError();
+}
+
+}  // namespace specv

@@ -14,11 +14,21 @@ int row_stats_chunk(bool bf16);
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                             int B, int K, int V, int nchunk, float c, float2* part,
                             hipStream_t stream);
-hipError_t launch_accept(bool bf16, const void* tgt, const void* dft, const int* tokens,
+hipError_t launch_accept(bool bf16, bool filt, const void* tgt, const void* dft, const int* tokens,
                          const int* draft_len, const float* u, const float* u_final, int B,
-                         int K, int V, int nchunk, float c, int eos_id, const float2* part,
-                         Plan* plan, int* out_tokens, int* n_emitted, float* alpha_out,
-                         double* rmass_out, int* stop_out, int* path_out, hipStream_t stream);
+                         int K, int V, int nchunk, float c, double invT, int eos_id,
+                         const float2* part, const FiltRow* frows, Plan* plan, int* out_tokens,
+                         int* n_emitted, float* alpha_out, double* rmass_out, int* stop_out,
+                         int* path_out, hipStream_t stream);
+int filter_cap(int top_k);
+int filter_row_stride(int nch, int top_k);
+hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int* draft_len, int B,
+                         int K, int V, int nch, int top_k, float top_p, double invT,
+                         uint64_t* cand, int* counts, FiltRow* rows, Kept* kept,
+                         hipStream_t stream, hipEvent_t mid);
+hipError_t launch_sample_list(bool bf16, const void* dft, const float* u_final, int B, int K, int V,
+                              double invT, const Plan* plan, const FiltRow* rows, const Kept* kept,
+                              int* out_tokens, double* rmass_out, hipStream_t stream);
 hipError_t launch_sample_pass(bool bf16, const void* tgt, const void* dft, int B, int K, int V,
                               int nch, double invT, const Plan* plan, ChunkRec* recs, Tie* ties,
                               hipStream_t stream);
@@ -29,9 +39,11 @@ hipError_t launch_sample_finish(bool bf16, const void* tgt, const void* dft, con
 hipError_t launch_exp64_selftest(const double* x, double* y, int n, hipStream_t stream);
 
 // Kernel stages of one call, in launch order (specv_verify_timed records an
-// event after each).
-const char* const kStageNames[] = {"row_stats", "accept", "sample_pass", "sample_finish"};
-constexpr int kNumStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
+// event after each): without filters, and with top-k / top-p.
+const char* const kStageNames[2][4] = {
+    {"row_stats", "accept", "sample_pass", "sample_finish"},
+    {"filter_cand", "filter_merge", "accept", "sample_list"}};
+constexpr int kNumStages = 4;
 
 namespace {
 
@@ -39,46 +51,79 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace regions, each 256-byte aligned:
+// Workspace regions, each 256-byte aligned.
+// Without filters:
 //   row partials   float2   [B][2K+1][nch_row]        (max, partial normaliser)
 //   plans          Plan     [B]
 //   chunk records  ChunkRec [B][nch_samp]             (fp64 sums per sampler chunk)
 //   near ties      Tie      [B][nch_samp][kTieCap]
+// With top-k / top-p:
+//   plans          Plan     [B]
+//   candidates     uint64   [B][2K+1][row_stride]     (key, id); cap per chunk, >= 256 last
+//   counts         int      [B][2K+1][nch_filt]
+//   filtered rows  FiltRow  [B][2K+1]
+//   kept lists     Kept     [B][2K+1][kKeptCap]
 struct Layout {
-  int nch_row = 0, nch_samp = 0;
-  size_t off_row = 0, off_plan = 0, off_recs = 0, off_ties = 0, total = 0;
+  bool filt = false;
+  int nch_row = 0, nch_samp = 0, nch_filt = 0, cap = 0;
+  size_t off_row = 0, off_plan = 0, off_recs = 0, off_ties = 0;
+  size_t off_cand = 0, off_counts = 0, off_frows = 0, off_kept = 0, total = 0;
 };
 
-Layout make_layout(int B, int K, int V, bool bf16) {
+bool filters_on(int V, int top_k, float top_p) { return (top_k > 0 && top_k < V) || top_p < 1.0f; }
+
+Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p) {
   Layout L;
-  const int ch = row_stats_chunk(bf16);
-  L.nch_row = (V + ch - 1) / ch;
-  L.nch_samp = (V + kSampChunk - 1) / kSampChunk;
+  const size_t R = (size_t)(2 * K + 1);
   size_t off = 0;
-  L.off_row = off;
-  off = align_up(off + (size_t)B * (2 * K + 1) * L.nch_row * sizeof(float2));
-  L.off_plan = off;
-  off = align_up(off + (size_t)B * sizeof(Plan));
-  L.off_recs = off;
-  off = align_up(off + (size_t)B * L.nch_samp * sizeof(ChunkRec));
-  L.off_ties = off;
-  off = align_up(off + (size_t)B * L.nch_samp * kTieCap * sizeof(Tie));
+  L.filt = filters_on(V, top_k, top_p);
+  if (!L.filt) {
+    const int ch = row_stats_chunk(bf16);
+    L.nch_row = (V + ch - 1) / ch;
+    L.nch_samp = (V + kSampChunk - 1) / kSampChunk;
+    L.off_row = off;
+    off = align_up(off + (size_t)B * R * L.nch_row * sizeof(float2));
+    L.off_plan = off;
+    off = align_up(off + (size_t)B * sizeof(Plan));
+    L.off_recs = off;
+    off = align_up(off + (size_t)B * L.nch_samp * sizeof(ChunkRec));
+    L.off_ties = off;
+    off = align_up(off + (size_t)B * L.nch_samp * kTieCap * sizeof(Tie));
+  } else {
+    L.nch_filt = (V + kFiltChunk - 1) / kFiltChunk;
+    L.cap = filter_cap(top_k);
+    L.off_plan = off;
+    off = align_up(off + (size_t)B * sizeof(Plan));
+    L.off_cand = off;
+    off = align_up(off + (size_t)B * R * filter_row_stride(L.nch_filt, top_k) * sizeof(uint64_t));
+    L.off_counts = off;
+    off = align_up(off + (size_t)B * R * L.nch_filt * sizeof(int));
+    L.off_frows = off;
+    off = align_up(off + (size_t)B * R * sizeof(FiltRow));
+    L.off_kept = off;
+    off = align_up(off + (size_t)B * R * kKeptCap * sizeof(Kept));
+  }
   L.total = off;
   return L;
 }
 
-bool filters_on(int V, int top_k, float top_p) { return (top_k > 0 && top_k < V) || top_p < 1.0f; }
-
 specv_status_t check_sizes(int B, int K, int V, specv_dtype_t dtype, int top_k, float top_p) {
   if (B < 1 || K < 0 || K > SPECV_MAX_K || V < 1) return SPECV_EINVAL;
-  if (V > SPECV_MAX_V) return SPECV_EUNSUPPORTED;
   if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_EINVAL;
   if (top_k < 0) return SPECV_EINVAL;
   if (!(top_p > 0.0f && top_p <= 1.0f)) return SPECV_EINVAL;
   // B * (K+1) * V elements must index without overflow.
   if ((double)B * (double)(K + 1) * (double)V > 4.0e18) return SPECV_EINVAL;
-  if ((size_t)B * (2 * K + 1) * (size_t)((V + 1023) / 1024) > 0x7fffffffu) return SPECV_EINVAL;
-  if (filters_on(V, top_k, top_p)) return SPECV_EUNSUPPORTED;
+  if (V > SPECV_MAX_V) return SPECV_EUNSUPPORTED;
+  if ((size_t)B * (2 * K + 1) * (size_t)((V + 1023) / 1024) > 0x7fffffffu) return SPECV_EUNSUPPORTED;
+  if (filters_on(V, top_k, top_p)) {
+    // top-p needs an active top-k; the candidate select handles k <= 256 and
+    // a row's candidates must fit the LDS merge.
+    if (!(top_k > 0 && top_k < V) || top_k > SPECV_MAX_TOPK) return SPECV_EUNSUPPORTED;
+    const int nch = (V + kFiltChunk - 1) / kFiltChunk;
+    if (nch > kFiltMaxChunks || filter_row_stride(nch, top_k) > kFiltSortMax)
+      return SPECV_EUNSUPPORTED;
+  }
   return SPECV_OK;
 }
 
@@ -106,14 +151,11 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
       (stop_out && misaligned(stop_out, 4)) || (path_out && misaligned(path_out, 4)))
     return SPECV_EINVAL;
   const bool bf16 = dtype == SPECV_BF16;
-  const Layout L = make_layout(B, K, V, bf16);
+  const Layout L = make_layout(B, K, V, bf16, top_k, top_p);
   if (!workspace || misaligned(workspace, 16) || workspace_bytes < L.total) return SPECV_EWORKSPACE;
 
   char* ws = static_cast<char*>(workspace);
-  float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
   Plan* plan = reinterpret_cast<Plan*>(ws + L.off_plan);
-  ChunkRec* recs = reinterpret_cast<ChunkRec*>(ws + L.off_recs);
-  Tie* ties = reinterpret_cast<Tie*>(ws + L.off_ties);
 
   // log2(e) / T rounded once to float32; every float32 exponent uses it.
   const float c = (float)(1.4426950408889634 / (double)temperature);
@@ -125,18 +167,39 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
     return !events || hipEventRecord(events[i], stream) == hipSuccess;
   };
   if (!mark(0)) return SPECV_EHIP;
-  hipError_t e = launch_row_stats(bf16, target, draft, draft_len, B, K, V, L.nch_row, c,
-                                  row_part, stream);
-  if (e != hipSuccess || !mark(1)) return SPECV_EHIP;
-  e = launch_accept(bf16, target, draft, tokens, draft_len, u, u_final, B, K, V, L.nch_row, c,
-                    eos_id, row_part, plan, out_tokens, n_emitted, alpha_out, rmass_out, stop_out,
-                    path_out, stream);
-  if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
-  e = launch_sample_pass(bf16, target, draft, B, K, V, L.nch_samp, invT, plan, recs, ties, stream);
-  if (e != hipSuccess || !mark(3)) return SPECV_EHIP;
-  e = launch_sample_finish(bf16, target, draft, u_final, B, K, V, L.nch_samp, invT, plan, recs,
-                           ties, out_tokens, rmass_out, stream);
-  if (e != hipSuccess || !mark(4)) return SPECV_EHIP;
+  hipError_t e;
+  if (!L.filt) {
+    float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
+    ChunkRec* recs = reinterpret_cast<ChunkRec*>(ws + L.off_recs);
+    Tie* ties = reinterpret_cast<Tie*>(ws + L.off_ties);
+    e = launch_row_stats(bf16, target, draft, draft_len, B, K, V, L.nch_row, c, row_part, stream);
+    if (e != hipSuccess || !mark(1)) return SPECV_EHIP;
+    e = launch_accept(bf16, false, target, draft, tokens, draft_len, u, u_final, B, K, V,
+                      L.nch_row, c, invT, eos_id, row_part, nullptr, plan, out_tokens, n_emitted,
+                      alpha_out, rmass_out, stop_out, path_out, stream);
+    if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
+    e = launch_sample_pass(bf16, target, draft, B, K, V, L.nch_samp, invT, plan, recs, ties,
+                           stream);
+    if (e != hipSuccess || !mark(3)) return SPECV_EHIP;
+    e = launch_sample_finish(bf16, target, draft, u_final, B, K, V, L.nch_samp, invT, plan, recs,
+                             ties, out_tokens, rmass_out, stream);
+    if (e != hipSuccess || !mark(4)) return SPECV_EHIP;
+  } else {
+    uint64_t* cand = reinterpret_cast<uint64_t*>(ws + L.off_cand);
+    int* counts = reinterpret_cast<int*>(ws + L.off_counts);
+    FiltRow* frows = reinterpret_cast<FiltRow*>(ws + L.off_frows);
+    Kept* kept = reinterpret_cast<Kept*>(ws + L.off_kept);
+    e = launch_filter(bf16, target, draft, draft_len, B, K, V, L.nch_filt, top_k, top_p, invT,
+                      cand, counts, frows, kept, stream, events ? events[1] : nullptr);
+    if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
+    e = launch_accept(bf16, true, target, draft, tokens, draft_len, u, u_final, B, K, V, 0, c,
+                      invT, eos_id, nullptr, frows, plan, out_tokens, n_emitted, alpha_out,
+                      rmass_out, stop_out, path_out, stream);
+    if (e != hipSuccess || !mark(3)) return SPECV_EHIP;
+    e = launch_sample_list(bf16, draft, u_final, B, K, V, invT, plan, frows, kept, out_tokens,
+                           rmass_out, stream);
+    if (e != hipSuccess || !mark(4)) return SPECV_EHIP;
+  }
   return SPECV_OK;
 }
 
@@ -147,7 +210,7 @@ extern "C" {
 
 size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype, int top_k, float top_p) {
   if (specv::check_sizes(B, K, V, dtype, top_k, top_p) != SPECV_OK) return 0;
-  return specv::make_layout(B, K, V, dtype == SPECV_BF16).total;
+  return specv::make_layout(B, K, V, dtype == SPECV_BF16, top_k, top_p).total;
 }
 
 specv_status_t specv_verify(const void* target_logits, const void* draft_logits,
@@ -190,15 +253,18 @@ specv_status_t specv_verify_timed(const void* target_logits, const void* draft_l
                     workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr, events);
 }
 
-int specv_num_stages(void) { return specv::kNumStages; }
+int specv_num_stages(int filtered) {
+  (void)filtered;
+  return specv::kNumStages;
+}
 
 specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream_t stream) {
   if (n < 0 || (n > 0 && (!x || !y))) return SPECV_EINVAL;
   return specv::launch_exp64_selftest(x, y, n, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }
 
-const char* specv_stage_name(int i) {
-  return (i >= 0 && i < specv::kNumStages) ? specv::kStageNames[i] : nullptr;
+const char* specv_stage_name(int filtered, int i) {
+  return (i >= 0 && i < specv::kNumStages) ? specv::kStageNames[filtered ? 1 : 0][i] : nullptr;
 }
 
 const char* specv_status_string(specv_status_t status) {

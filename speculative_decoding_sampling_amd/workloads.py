@@ -74,6 +74,11 @@ class Workload:
         return int(((2 * n + 1) * self.V * self.elem_bytes).sum())
 
 
+def f32(x):
+    """x rounded to the nearest float32, as a Python float."""
+    return float(np.float32(x))
+
+
 def to_bf16_bits(x):
     """float32 -> bf16 bit patterns (uint16), round to nearest even."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
@@ -114,7 +119,9 @@ def make_workload(cfg, seed=None, B=None, draft_sampler=None):
     seed = 1000 + cfg if seed is None else int(seed)
     B = spec["B"] if B is None else int(B)
     K, V, dtype = spec["K"], spec["V"], spec["dtype"]
-    T, top_k, top_p = spec["T"], spec["top_k"], spec["top_p"]
+    # The call takes temperature and top_p as float32: keep the values both
+    # sides see identical.
+    T, top_k, top_p = f32(spec["T"]), spec["top_k"], f32(spec["top_p"])
     filtered = (0 < top_k < V) or top_p < 1.0
     if filtered and draft_sampler is None:
         raise ValueError("filtered workloads need a draft_sampler for the processed draft distribution")

@@ -13,7 +13,7 @@ torch = pytest.importorskip("torch")
 
 import oracle as O  # noqa: E402
 from speculative_decoding_sampling_amd import binding  # noqa: E402
-from speculative_decoding_sampling_amd.workloads import make_workload, upload  # noqa: E402
+from speculative_decoding_sampling_amd.workloads import f32, make_workload, upload  # noqa: E402
 from tests.parity import compare, to_numpy  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -22,7 +22,7 @@ DEV = "cuda:0"
 
 
 def oracle_sampler(z, T, k, p, uni):
-    P, _ = O.processed_distribution(z, T, k, p)
+    P, _ = O.processed_distribution(z, f32(T), k, f32(p))
     return O.icdf(P, uni)[0]
 
 
@@ -37,8 +37,9 @@ def run_gpu(w, **kw):
 def run_oracle(w, requests=None, **kw):
     p = dict(temperature=w.T, top_k=w.top_k, top_p=w.top_p, eos_id=w.eos_id)
     p.update(kw)
+    # The call receives temperature and top_p as float32; the oracle gets the same values.
     return O.verify(w.target, w.draft, w.draft_tokens, w.draft_len, w.u, w.u_final,
-                    p["temperature"], p["top_k"], p["top_p"], p["eos_id"], w.dtype,
+                    f32(p["temperature"]), p["top_k"], f32(p["top_p"]), p["eos_id"], w.dtype,
                     requests=requests)
 
 
@@ -145,7 +146,7 @@ def test_unaligned_and_tiny_vocabularies(V):
     for dtype in ("f32", "bf16"):
         tt = to_bf16_bits(t) if dtype == "bf16" else t
         dd = to_bf16_bits(d) if dtype == "bf16" else d
-        w = Workload(cfg=0, seed=V, B=B, K=K, V=V, dtype=dtype, T=0.9, top_k=0, top_p=1.0,
+        w = Workload(cfg=0, seed=V, B=B, K=K, V=V, dtype=dtype, T=f32(0.9), top_k=0, top_p=1.0,
                      eos_id=-1, target=np.ascontiguousarray(tt), draft=np.ascontiguousarray(dd),
                      draft_tokens=toks, draft_len=np.array([3, 2, 1, 0, 3, 3], np.int32),
                      u=uniforms(rng, (B, K)), u_final=uniforms(rng, (B,)))
@@ -226,3 +227,61 @@ def test_sampler_exact_path_with_many_near_ties():
     w.u[:] = np.float32(1.0 - 2.0 ** -24)
     rep, g, o = assert_parity(w, label="near-identical rows")
     assert (o["path"] == O.PATH_REJECT).sum() >= 4
+
+
+# ---------------------------------------------------------------------------
+# top-k / top-p path
+# ---------------------------------------------------------------------------
+
+def redraw_tokens(w, seed):
+    """Draft tokens from the processed draft distribution (the oracle's)."""
+    from speculative_decoding_sampling_amd.workloads import uniforms
+    rng = np.random.default_rng(seed)
+    uni = uniforms(rng, (w.B, w.K))
+    for b in range(w.B):
+        for k in range(w.K):
+            z = O.widen_row(w.draft[b, k], w.dtype)
+            w.draft_tokens[b, k] = oracle_sampler(z, w.T, w.top_k, w.top_p, float(uni[b, k]))
+
+
+def test_parity_topk_topp_reduced():
+    w = make_workload(4, B=12, draft_sampler=oracle_sampler)
+    rep, g, o = assert_parity(w)
+    assert rep["positions"] > 0
+
+
+def test_parity_topk_topp_full_size_sampled():
+    w = make_workload(4, draft_sampler=oracle_sampler)          # B=256, K=8, V=152064 fp32
+    rep, g, o = assert_parity(w, requests=list(range(0, w.B, 5)), label="full size, sampled")
+    assert rep["requests"] == len(range(0, w.B, 5))
+
+
+@pytest.mark.parametrize("top_k,top_p", [(40, 1.0), (7, 0.8), (128, 0.95), (1, 1.0)])
+def test_parity_topk_bf16_with_ties(top_k, top_p):
+    # bf16 logits repeat values, so the k-th logit is often tied: all ties stay.
+    w = make_workload(3, B=6)
+    w.top_k, w.top_p, w.T = top_k, f32(top_p), f32(0.9)
+    redraw_tokens(w, top_k)
+    assert_parity(w, label=f"bf16 top_k={top_k} top_p={top_p}")
+
+
+def test_filter_capacity_limit_is_a_request_error():
+    # A row whose logits are all equal keeps every token under top-k (ties
+    # kept): more than the 512-token kept list, so that request is reported
+    # as an error while the others are unaffected.
+    w = make_workload(4, B=4, draft_sampler=oracle_sampler)
+    w.target[2, 0, :] = 0.0
+    g = run_gpu(w)
+    o = run_oracle(w)
+    assert g["n_emitted"][2] == -1 and o["n_emitted"][2] > 0
+    for b in (0, 1, 3):
+        assert g["n_emitted"][b] == o["n_emitted"][b] or o["flag_kind"][b] != O.FLAG_NONE
+
+
+def test_many_draws_large_vocabulary_non_unit_temperature():
+    # ~1000 inverse-CDF draws over V = 32000 at T = 0.8: a draw moves if the
+    # two sides' CDFs differ by more than about 1e-10, e.g. through a
+    # temperature that is not the same float on both sides.
+    w = make_workload(2, B=1024)
+    rep, g, o = assert_parity(w, label="1024 draws")
+    assert rep["requests"] == 1024

@@ -65,6 +65,8 @@ def test_workspace_sizes(lib):
     assert f(1, 4, 0, 0, 0, 1.0) == 0                             # V < 1
     assert f(1, 4, 100, 7, 0, 1.0) == 0                           # unknown dtype
     assert f(1, 4, 100, 0, 0, 0.0) == 0                           # top_p out of range
+    assert f(256, 8, 152064, 0, 50, 0.9) > 0                      # the top-k/top-p workload
+    assert f(1, 4, 300000, 0, 50, 0.9) == 0                       # V above the filter limit
 
 
 def test_validation_returns_before_any_gpu_work(lib):
@@ -93,17 +95,22 @@ def test_validation_returns_before_any_gpu_work(lib):
     assert call(top_p=0.0) == 1
     assert call(eos=1000) == 1
     assert call(target=None) == 1
-    assert call(top_k=10) == 4                 # filters: unsupported in this build
+    assert call(top_k=10, ws_bytes=16) == 2    # filtered path: workspace too small
+    assert call(top_k=129) == 4                # top_k above the candidate-select limit
+    assert call(top_k=0, top_p=0.9) == 4       # top-p without top-k
     assert call(ws_bytes=16) == 2              # workspace too small
 
 
 def test_stage_names(lib):
-    lib.specv_stage_name.argtypes = [ctypes.c_int]
+    lib.specv_stage_name.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.specv_stage_name.restype = ctypes.c_char_p
-    n = lib.specv_num_stages()
-    names = [lib.specv_stage_name(i) for i in range(n)]
-    assert n >= 1 and names[0] == b"row_stats" and all(names)
-    assert lib.specv_stage_name(n) is None and lib.specv_stage_name(-1) is None
+    lib.specv_num_stages.argtypes = [ctypes.c_int]
+    for filtered, first in ((0, b"row_stats"), (1, b"filter_cand")):
+        n = lib.specv_num_stages(filtered)
+        names = [lib.specv_stage_name(filtered, i) for i in range(n)]
+        assert n >= 1 and names[0] == first and all(names)
+        assert lib.specv_stage_name(filtered, n) is None
+        assert lib.specv_stage_name(filtered, -1) is None
 
 
 def test_status_strings(lib):
