@@ -9,6 +9,8 @@ scan and the float64 residual / bonus draw for every request.
 Output: exactly one JSON line on stdout (progress goes to stderr):
   value            verified draft positions per second (sum of draft lengths / step time)
   ms_per_step      mean step time over the timed region (HIP events on the call's stream)
+  host_us_per_call host time to enqueue one call from Python (below ms_per_step: the
+                   timed steps are GPU-bound, not launch-bound)
   roofline         the dominant kernel (row statistics): algorithmic bytes per launch
                    over its mean duration, against the 8 TB/s HBM peak
   cpu_baseline     the fp64 oracle on this host, on a bounded sample of the same workload
@@ -142,7 +144,7 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    # Timed region: the plain entry point, K steps bracketed by synchronisation.
+    # Timed region: K steps bracketed by synchronisation.
     ev = HipEvents(2)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -156,6 +158,17 @@ def main():
     ev.close()
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step "
         f"(host wall {wall / args.steps * 1e6:.2f} us/step)")
+
+    # Host enqueue cost alone: a short burst right after a sync, timed on the
+    # host before the GPU could back-pressure the launches.
+    torch.cuda.synchronize()
+    n_burst = 8
+    h0 = time.perf_counter()
+    for i in range(n_burst):
+        step(i)
+    host_us = (time.perf_counter() - h0) / n_burst * 1e6
+    torch.cuda.synchronize()
+    log(f"host enqueue {host_us:.2f} us/call")
 
     # Per-kernel durations: the same steps through the timing entry point.
     names = binding.stage_names()
@@ -207,6 +220,7 @@ def main():
                    "logits": "bf16", "temperature": w0.T, "top_k": 0, "top_p": 1.0,
                    "input_sets": args.sets, "positions_per_step": positions,
                    "algorithmic_bytes_per_step": alg_bytes},
+        "host_us_per_call": host_us,
         "hbm_gbps_whole_step": step_gbps,
         "hbm_frac_whole_step": step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,

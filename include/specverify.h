@@ -144,10 +144,11 @@ SPECV_API specv_status_t specv_verify_debug(const void *target_logits, const voi
 /*
  * Timing variant of specv_verify, for benchmarks: identical work, plus
  * hipEventRecord on `stream` of events[0] before the first kernel launch and
- * of events[i+1] after kernel stage i.  `events` holds specv_num_stages() + 1
- * caller-created HIP events (SPECV_EINVAL if NULL or any entry is NULL); the
- * caller reads stage durations with hipEventElapsedTime after synchronising.
- * The stages differ with and without filters (specv_stage_name).
+ * of events[i+1] after kernel stage i.  `events` holds specv_num_stages(f) + 1
+ * caller-created HIP events, f being whether this call's top-k / top-p is
+ * active (SPECV_EINVAL if NULL or any of those entries is NULL); the caller
+ * reads stage durations with hipEventElapsedTime after synchronising.  The
+ * stages differ with and without filters (specv_stage_name).
  */
 SPECV_API specv_status_t specv_verify_timed(const void *target_logits, const void *draft_logits,
                                             specv_dtype_t dtype, const int32_t *draft_tokens,

@@ -1,15 +1,19 @@
 // Table-driven float64 exp for the sampler (P. T. P. Tang, "Table-driven
 // implementation of the exponential function in IEEE floating-point
-// arithmetic", ACM TOMS 15(2), 1989), with N = 256 table entries.
+// arithmetic", ACM TOMS 15(2), 1989), with N = 512 table entries.
 //
-//   x = (k / N) ln2 + r,  k = rint(x N / ln2),  |r| <= ln2 / (2N) ~ 1.35e-3
-//   exp(x) = 2^(k >> 8) * 2^((k & 255) / 256) * (1 + p(r)),
-//   p(r) = r + r^2/2 + r^3/6 + r^4/24   (truncation < r^5/120 < 4e-17)
+//   x = (k / N) ln2 + r,  k = rint(x N / ln2),  |r| <= ln2 / (2N) ~ 6.8e-4
+//   (k comes from adding 1.5 * 2^52, which rounds to an integer in one FMA)
+//   exp(x) = 2^(k >> 9) * 2^((k & 511) / 512) * (1 + p(r)),
+//   p(r) = r + r^2/2 + r^3/6   (truncation r^4/24 < 8.8e-15)
 //
-// ln2/N is split into a 32-bit head (k * head is exact for |k| < 2^21) and a
-// tail, so r carries full float64 accuracy.  Error: about 1 ulp over the
-// whole range.  Valid for x <= 709; x below about -745.1 (including -inf)
-// returns 0.  The constants come from gen_exp64_table.py.
+// r = x - k * (ln2/N) is one FMA with ln2/N rounded to float64, which adds a
+// relative error of at most |x| * 2^-53.  Relative error in total: below
+// 1e-14 + |x| * 1.2e-16 (below 1.5e-14 where x >= -40, the only range whose
+// weights reach a sum's last bits), four orders of magnitude inside what the
+// sampler needs (its draws are resolved to 1e-10 of the total mass).
+// Valid for x <= 709; x below about -745.1 (including -inf) returns 0.  The
+// constants come from gen_exp64_table.py.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,7 +24,7 @@ namespace specv {
 
 static __device__ const double kExp64Table[SPECV_EXP64_N] = SPECV_EXP64_TABLE;
 
-// Stage the 2 KB table in LDS; every thread of the block must call this,
+// Stage the 4 KB table in LDS; every thread of the block must call this,
 // followed by __syncthreads() before the first exp64.
 __device__ __forceinline__ void exp64_stage_table(double* lds) {
   for (int i = threadIdx.x; i < SPECV_EXP64_N; i += blockDim.x) lds[i] = kExp64Table[i];
@@ -28,16 +32,23 @@ __device__ __forceinline__ void exp64_stage_table(double* lds) {
 
 __device__ __forceinline__ double exp64(double x, const double* __restrict__ tbl) {
   x = fmax(x, -746.0);                              // -inf and deep underflow -> 0 below
-  const double kd = rint(x * SPECV_EXP64_INV_L);
-  double r = fma(-kd, SPECV_EXP64_L_HI, x);
-  r = fma(-kd, SPECV_EXP64_L_LO, r);
-  const int k = (int)kd;
-  double q = fma(r, SPECV_EXP64_C4, SPECV_EXP64_C3);
-  q = fma(r, q, 0.5);
+  // t = 1.5 * 2^52 + rint(x * N / ln2): its low 32 bits are k as an integer.
+  const double t = fma(x, SPECV_EXP64_INV_L, SPECV_EXP64_SHIFT);
+  const double kd = t - SPECV_EXP64_SHIFT;
+  const int k = (int)(unsigned)__double_as_longlong(t);
+  const double r = fma(-kd, SPECV_EXP64_L, x);
+  double q = fma(r, SPECV_EXP64_C3, 0.5);
   q = fma(r, q, 1.0);
   const double p = r * q;                           // exp(r) - 1
-  const double t = tbl[k & (SPECV_EXP64_N - 1)];
-  return ldexp(fma(t, p, t), k >> 8);               // k >> 8 is floor(k / 256)
+  const double tj = tbl[k & (SPECV_EXP64_N - 1)];
+  return ldexp(fma(tj, p, tj), k >> SPECV_EXP64_LOG2N);   // floor(k / N)
+}
+
+// exp((z - m) / T) for a logit z, with mi = m / T precomputed: the argument
+// is z / T - m / T formed with one rounding.
+__device__ __forceinline__ double exp64_logit(float z, double invT, double mi,
+                                              const double* __restrict__ tbl) {
+  return exp64(fma((double)z, invT, -mi), tbl);
 }
 
 }  // namespace specv

@@ -6,6 +6,9 @@
 // "4. 实现逻辑": softmax of logits over temperature; nickwang.xyz
 // "推测解码：草稿、验证与实际加速", section "接受与拒绝怎样保住分布").
 //
+// The workgroup whose chunk holds a row's drafted token also records that
+// token's logit, so the accept scan needs no gather of its own.
+//
 // This pass reads every needed row once and carries nearly all of the call's
 // HBM traffic.  Each workgroup streams one chunk with coalesced 16-byte loads
 // issued up front, reduces with wave64 shuffles and combines its four waves
@@ -19,7 +22,8 @@ namespace specv {
 template <typename T, int VECS>
 __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
-    int K, int V, int nchunk, float c, float2* __restrict__ part) {
+    const int* __restrict__ tokens, int K, int V, int nchunk, float c,
+    float2* __restrict__ part, float* __restrict__ zx) {
   constexpr int N = Elem<T>::kPerVec;
   constexpr int kChunk = kRowThreads * VECS * N;
   const int R = 2 * K + 1;
@@ -49,6 +53,19 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
 #pragma unroll
     for (int j = 0; j < VECS; ++j)
       load_vec_checked(row, e_wave + (long)j * kWave * N, V, aligned, v[j]);
+  }
+
+  // Drafted token of this row (draft position k < K): its logit, read after
+  // the stream is in flight and stored at the end.  zx[b][k] is the target
+  // row's, zx[b][K + k] the draft row's.
+  int gx = -1;
+  float gz = 0.f;
+  if (k < K) {
+    const int x = tokens[(size_t)b * K + k];
+    if (x >= 0 && x < V && x >= e_base && x < e_base + kChunk) {
+      gx = x;
+      gz = to_f32(row[x]);
+    }
   }
 
   float m = -INFINITY;
@@ -84,6 +101,7 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
           S += red[w].y * __builtin_amdgcn_exp2f(__fmul_rn(red[w].x, c) - Mc);
     }
     part[(size_t)rr * nchunk + chunk] = make_float2(M, S);
+    if (gx >= 0) zx[(size_t)b * 2 * K + (is_target ? k : K + k)] = gz;
   }
 }
 
@@ -92,19 +110,19 @@ int row_stats_chunk(bool bf16) {
 }
 
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
-                            int B, int K, int V, int nchunk, float c, float2* part,
-                            hipStream_t stream) {
+                            const int* tokens, int B, int K, int V, int nchunk, float c,
+                            float2* part, float* zx, hipStream_t stream) {
   const size_t blocks = (size_t)B * (2 * K + 1) * nchunk;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   if (bf16)
     row_stats_kernel<bf16_t, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
-        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V, nchunk,
-        c, part);
+        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, tokens, K, V,
+        nchunk, c, part, zx);
   else
     row_stats_kernel<float, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
-        static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, nchunk,
-        c, part);
+        static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, tokens, K, V,
+        nchunk, c, part, zx);
   return hipGetLastError();
 }
 

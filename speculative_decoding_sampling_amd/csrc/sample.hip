@@ -58,7 +58,7 @@ __device__ __forceinline__ void load8(const T* __restrict__ row, long c0, int V,
 }
 
 constexpr int kSampWaves = kSampThreads / kWave;
-constexpr int kPassChunks = 1;   // chunks per pass workgroup
+constexpr int kTiePre = 2;       // near-tie slots per chunk the finish reads up front
 
 // Sum of one double per thread over the block, in a fixed order (every
 // thread gets the result).
@@ -115,17 +115,18 @@ __device__ __forceinline__ int block_min(int v, int* lds) {
 
 __device__ __forceinline__ int block_max(int v, int* lds) { return -block_min(-v, lds); }
 
-// e = exp((z - m) / T), the unnormalised float64 weight of one logit.
-__device__ __forceinline__ double weight_e(float z, double m, double invT, const double* tbl) {
-  return exp64(((double)z - m) * invT, tbl);
+// e = exp((z - m) / T), the unnormalised float64 weight of one logit, with
+// mi = m / T of the row precomputed.
+__device__ __forceinline__ double weight_e(float z, double mi, double invT, const double* tbl) {
+  return exp64_logit(z, invT, mi, tbl);
 }
 
 // Residual weights max(e_t/S_t - e_d/S_d, 0) (resid) or target weights e_t of
-// one thread's 8 tokens.
+// one thread's 8 tokens; rSt = 1/S_t and rSd = 1/S_d.
 template <typename T>
 __device__ __forceinline__ void chunk_weights(const T* trow, const T* drow, long c0, int V,
-                                              bool resid, double mt, double md, double invT,
-                                              double St, double Sd, const double* tbl,
+                                              bool resid, double mti, double mdi, double invT,
+                                              double rSt, double rSd, const double* tbl,
                                               double* w) {
   float zt[kSampPerThread];
   load8(trow, c0, V, zt);
@@ -134,75 +135,178 @@ __device__ __forceinline__ void chunk_weights(const T* trow, const T* drow, long
     load8(drow, c0, V, zd);
 #pragma unroll
     for (int i = 0; i < kSampPerThread; ++i) {
-      const double r = weight_e(zt[i], mt, invT, tbl) / St - weight_e(zd[i], md, invT, tbl) / Sd;
+      const double r = fma(weight_e(zt[i], mti, invT, tbl), rSt,
+                           -weight_e(zd[i], mdi, invT, tbl) * rSd);
       w[i] = r > 0.0 ? r : 0.0;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kSampPerThread; ++i) w[i] = weight_e(zt[i], mt, invT, tbl);
+    for (int i = 0; i < kSampPerThread; ++i) w[i] = weight_e(zt[i], mti, invT, tbl);
   }
+}
+
+// Inclusive prefix sum over the wave, in lane order.
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Raw logits of one thread's 8 tokens, kept packed until used.
+template <typename T> struct Raw8 {
+  uint4 w[kSampPerThread / Elem<T>::kPerVec];
+};
+
+// Packed bit pattern of -inf, for elements past the end of the row.
+__device__ __forceinline__ uint32_t neg_inf_bits(float) { return 0xff800000u; }
+__device__ __forceinline__ uint32_t neg_inf_bits(bf16_t) { return 0xff80u; }
+__device__ __forceinline__ uint32_t elem_bits(const float* row, long e) {
+  return __float_as_uint(row[e]);
+}
+__device__ __forceinline__ uint32_t elem_bits(const bf16_t* row, long e) { return row[e]; }
+
+// This thread's 8 logits of the chunk starting at element c0, as raw words;
+// elements at or past V read as -inf.  The interior test is uniform per chunk.
+template <typename T>
+__device__ __forceinline__ void load_raw8(const T* __restrict__ row, long c0, int V,
+                                          Raw8<T>& r) {
+  constexpr int N = Elem<T>::kPerVec, NV = kSampPerThread / N;
+  const long e0 = c0 + (long)threadIdx.x * kSampPerThread;
+  const bool aligned = aligned16(row);
+  if (aligned && c0 + kSampChunk <= V) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) r.w[j] = *reinterpret_cast<const uint4*>(row + e0 + j * N);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const long ej = e0 + j * N;
+      if (aligned && ej + N <= V) {
+        r.w[j] = *reinterpret_cast<const uint4*>(row + ej);
+      } else {
+        uint32_t e[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) e[i] = ej + i < V ? elem_bits(row, ej + i) : neg_inf_bits(T{});
+        if constexpr (N == 4) {
+          r.w[j] = make_uint4(e[0], e[1], e[2], e[3]);
+        } else {
+          r.w[j] = make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16,
+                              e[6] | e[7] << 16);
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack8(const Raw8<T>& r, float* z) {
+  constexpr int N = Elem<T>::kPerVec;
+#pragma unroll
+  for (int j = 0; j < kSampPerThread / N; ++j) unpack(r.w[j], z + j * N, T{});
+}
+
+// Lane exchanges for the wave reductions, without per-lane index registers:
+// DPP moves within a row of 16 lanes, a swizzle across the two rows of each
+// half wave, and one permute across the halves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double swizzle_xor16(double v) {   // lane ^ 16 within 32 lanes
+  const int lo = __builtin_amdgcn_ds_swizzle(__double2loint(v), 0x401f);
+  const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(v), 0x401f);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double permute_xor32(double v, int addr) {   // addr = (lane ^ 32) * 4
+  const int lo = __builtin_amdgcn_ds_bpermute(addr, __double2loint(v));
+  const int hi = __builtin_amdgcn_ds_bpermute(addr, __double2hiint(v));
+  return __hiloint2double(hi, lo);
+}
+
+// Sums of four doubles over the wave.  The first two steps exchange halves
+// of the set (lane ^ 32, then lane ^ 16), so each 16-lane row keeps one
+// quantity; four DPP steps then sum within the row (quad swaps, then the
+// half-row and row mirrors, which pair each lane with one in the other half
+// once the halves are uniform).  Lane L ends with the full sum of quantity
+// 2 * bit5(L) + bit4(L) of (a, b, c, d), summed in one fixed tree order.
+__device__ __forceinline__ double wave_sum4(double a, double b, double c, double d) {
+  const int lane = threadIdx.x % kWave;
+  const bool h5 = lane & 32, h4 = lane & 16;
+  const int addr32 = (lane ^ 32) << 2;
+  double k0 = h5 ? c : a, k1 = h5 ? d : b;
+  k0 += permute_xor32(h5 ? a : c, addr32);
+  k1 += permute_xor32(h5 ? b : d, addr32);
+  double k = h4 ? k1 : k0;
+  k += swizzle_xor16(h4 ? k0 : k1);
+  k += dpp_mov<0xb1>(k);     // quad_perm [1,0,3,2]: lane ^ 1
+  k += dpp_mov<0x4e>(k);     // quad_perm [2,3,0,1]: lane ^ 2
+  k += dpp_mov<0x141>(k);    // row_half_mirror
+  k += dpp_mov<0x140>(k);    // row_mirror
+  return k;
 }
 
 // Sums and near ties of one 2048-token chunk whose logits this thread holds
 // (8 per thread, token order = thread order), written to the chunk's record.
+//
+// With d = e_t - e_d g and band = e_d g w: d > band means p > q for certain,
+// d < -band means p <= q for certain (the finish checks g against the exact
+// ratio to a quarter of w), anything else is a near tie.  Tokens with
+// e_t = 0 are never ties (their residual is 0).  Near ties are appended to an
+// LDS list as they are found and stored in token order (rank by id), so the
+// stored slots do not depend on scheduling.  tcnt counts this chunk's ties;
+// tcnt_next (the counter of a following chunk, if the caller loops) is
+// cleared between the two barriers, after its last reader.
 __device__ __forceinline__ void pass_chunk(const float* zt, const float* zd, bool rej, long e0,
-                                           double mt, double md, double invT, double g,
-                                           const double* tbl, double* dl, int* il,
-                                           ChunkRec* __restrict__ rec, Tie* __restrict__ slot) {
+                                           double mti, double mdi, double invT, double g,
+                                           const double* tbl, double* dl, Tie* tl, int* tcnt,
+                                           int* tcnt_next, ChunkRec* __restrict__ rec,
+                                           Tie* __restrict__ slot) {
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  double et[kSampPerThread], ed[kSampPerThread];
   double st = 0.0, sd = 0.0, at = 0.0, ad = 0.0;
+  const double gw = g * kTieWindow;
 #pragma unroll
   for (int i = 0; i < kSampPerThread; ++i) {
-    et[i] = weight_e(zt[i], mt, invT, tbl);
-    st += et[i];
-  }
-  unsigned tiemask = 0;
-  if (rej) {
-    const double ghi = g * (1.0 + kTieWindow), glo = g * (1.0 - kTieWindow);
-#pragma unroll
-    for (int i = 0; i < kSampPerThread; ++i) {
-      ed[i] = weight_e(zd[i], md, invT, tbl);
-      sd += ed[i];
-      if (et[i] > ed[i] * ghi) {
-        at += et[i];
-        ad += ed[i];
-      } else if (et[i] > 0.0 && et[i] >= ed[i] * glo) {
-        tiemask |= 1u << i;
-      }
-    }
-  }
-  st = wave_sum(st);
-  sd = wave_sum(sd);
-  at = wave_sum(at);
-  ad = wave_sum(ad);
-  __syncthreads();                                   // dl / il free from any earlier use
-  if (lane == 0) {
-    dl[wid * 4 + 0] = st;
-    dl[wid * 4 + 1] = sd;
-    dl[wid * 4 + 2] = at;
-    dl[wid * 4 + 3] = ad;
-  }
-  int ntie_all = 0;
-  if (rej) {
-    // near ties go to the chunk's slots in token order (block prefix of counts)
-    int off = block_exclusive_scan<int>(__popc(tiemask), il, ntie_all);
-#pragma unroll
-    for (int i = 0; i < kSampPerThread; ++i) {
-      if ((tiemask >> i) & 1u) {
-        if (off < kTieCap) {
+    const double et = weight_e(zt[i], mti, invT, tbl);
+    st += et;
+    if (rej) {
+      const double ed = weight_e(zd[i], mdi, invT, tbl);
+      sd += ed;
+      const double dlt = fma(-ed, g, et);
+      const double band = ed * gw;
+      const bool sure = dlt > band;
+      at += sure ? et : 0.0;
+      ad += sure ? ed : 0.0;
+      if (!sure && dlt >= -band && et > 0.0) {
+        const int s = atomicAdd(tcnt, 1);
+        if (s < kTieCap) {
           Tie tv;
-          tv.et = et[i];
-          tv.ed = ed[i];
+          tv.et = et;
+          tv.ed = ed;
           tv.v = (int)(e0 + i);
           tv.pad = 0;
-          slot[off] = tv;
+          tl[s] = tv;
         }
-        ++off;
       }
     }
   }
+  const double red = wave_sum4(st, sd, at, ad);
+  __syncthreads();                                   // ties recorded; dl free from the last chunk
+  if ((lane & 15) == 0) dl[wid * 4 + (lane >> 4)] = red;
+  if (threadIdx.x == 0) *tcnt_next = 0;              // its last reader ran before the barrier
   __syncthreads();
+  const int ntie = *tcnt;
+  const int nst = min(ntie, kTieCap);
+  if ((int)threadIdx.x < nst) {                      // store in token order
+    const Tie tv = tl[threadIdx.x];
+    int rank = 0;
+    for (int j = 0; j < nst; ++j) rank += tl[j].v < tv.v;
+    slot[rank] = tv;
+  }
   if (threadIdx.x == 0) {
     ChunkRec r;
     r.et = r.ed = r.at = r.ad = 0.0;
@@ -213,55 +317,52 @@ __device__ __forceinline__ void pass_chunk(const float* zt, const float* zd, boo
       r.at += dl[w * 4 + 2];
       r.ad += dl[w * 4 + 3];
     }
-    r.ntie = ntie_all;
+    r.ntie = ntie;
 #pragma unroll
     for (int i = 0; i < 7; ++i) r.pad[i] = 0;
     *rec = r;
   }
 }
 
-// (a) chunk pass: float64 sums and near ties, kPassChunks chunks per
-// workgroup with every logit load issued before the first exp.
+// (a) chunk pass: one workgroup per (request, chunk).  The plan load and the
+// exp table staging overlap; every logit load is issued before the first
+// exp.  Many small workgroups keep the chip busy while others wait on memory.
 template <typename T>
 __global__ __launch_bounds__(kSampThreads) void sample_pass_kernel(
-    const T* __restrict__ tgt, const T* __restrict__ dft, int K, int V, int nch, int ngrp,
+    const T* __restrict__ tgt, const T* __restrict__ dft, int K, int V, int nch,
     double invT, const Plan* __restrict__ plan, ChunkRec* __restrict__ recs,
     Tie* __restrict__ ties) {
   __shared__ double tbl[SPECV_EXP64_N];
   __shared__ double dl[kSampWaves * 4];
-  __shared__ int il[kSampWaves];
+  __shared__ Tie tl[kTieCap];
+  __shared__ int tcnt[2];
 
-  const int grp = blockIdx.x % ngrp, b = blockIdx.x / ngrp;
-  exp64_stage_table(tbl);                            // independent of the plan: overlaps it
+  const int c = blockIdx.x % nch, b = blockIdx.x / nch;
+  exp64_stage_table(tbl);
   const Plan pl = plan[b];
   if (pl.path != kPathReject && pl.path != kPathBonus) return;   // uniform per block
   const bool rej = pl.path == kPathReject;
   const T* trow = tgt + target_row_off(b, pl.trow, K, V);
   const T* drow = rej ? dft + draft_row_off(b, pl.drow, K, V) : nullptr;
-  const int c0 = grp * kPassChunks;
-  const int nc = min(kPassChunks, nch - c0);
-  float zt[kPassChunks][kSampPerThread], zd[kPassChunks][kSampPerThread];
-#pragma unroll
-  for (int s = 0; s < kPassChunks; ++s) {
-    if (s < nc) {
-      const long cs = (long)(c0 + s) * kSampChunk;
-      load8(trow, cs, V, zt[s]);
-      if (rej) load8(drow, cs, V, zd[s]);
-    }
-  }
-  __syncthreads();                                   // table staged
-#pragma unroll
-  for (int s = 0; s < kPassChunks; ++s) {
-    if (s < nc) {
-      const int c = c0 + s;
-      const long e0 = (long)c * kSampChunk + (long)threadIdx.x * kSampPerThread;
-      pass_chunk(zt[s], zd[s], rej, e0, (double)pl.mt, (double)pl.md, invT, pl.g, tbl, dl, il,
-                 recs + (size_t)b * nch + c, ties + ((size_t)b * nch + c) * kTieCap);
-    }
-  }
+  const double mti = (double)pl.mt * invT, mdi = (double)pl.md * invT;   // m / T
+
+  Raw8<T> rt, rd;
+  load_raw8(trow, (long)c * kSampChunk, V, rt);
+  if (rej) load_raw8(drow, (long)c * kSampChunk, V, rd);
+  if (threadIdx.x == 0) tcnt[0] = 0;
+  __syncthreads();                                   // table staged, tie counter clear
+  float zt[kSampPerThread], zd[kSampPerThread];
+  unpack8(rt, zt);
+  if (rej) unpack8(rd, zd);
+  const long e0 = (long)c * kSampChunk + (long)threadIdx.x * kSampPerThread;
+  pass_chunk(zt, zd, rej, e0, mti, mdi, invT, pl.g, tbl, dl, tl, &tcnt[0], &tcnt[1],
+             recs + (size_t)b * nch + c, ties + ((size_t)b * nch + c) * kTieCap);
 }
 
 // (b) the draw: one workgroup per request, after every chunk record exists.
+// Barriers are few: the chunk holding t is found by every wave on its own
+// (a wave-wide blocked prefix over the chunk masses), and only the in-chunk
+// scan combines the four waves.
 template <typename T>
 __global__ __launch_bounds__(kSampThreads) void sample_finish_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const float* __restrict__ u_final,
@@ -270,155 +371,205 @@ __global__ __launch_bounds__(kSampThreads) void sample_finish_kernel(
     double* __restrict__ rmass_out) {
   __shared__ double tbl[SPECV_EXP64_N];
   __shared__ double dl[kSampWaves * 4];
-  __shared__ int il[kSampWaves];
+  __shared__ int il[kSampWaves * 2];
   __shared__ double wts[kMaxSampChunks];
-  __shared__ int s_fb;
-  __shared__ double s_St, s_Sd, s_cpre;
+  __shared__ int s_nredo;
+  __shared__ int redo[kMaxSampChunks];
 
   const int b = blockIdx.x;
-  exp64_stage_table(tbl);                            // independent of the plan: overlaps it
+  const int tid = threadIdx.x, lane = tid % kWave, wid = tid / kWave;
+  // Everything that does not depend on the plan is requested with it: the
+  // exp table, this thread's first chunk record and that chunk's first
+  // kTiePre near-tie slots (read whether used or not; the slots exist).
+  exp64_stage_table(tbl);
   const Plan pl = plan[b];
+  const ChunkRec* rb = recs + (size_t)b * nch;
+  const Tie* tb = ties + (size_t)b * nch * kTieCap;
+  const bool have0 = tid < nch;
+  ChunkRec r0;
+  Tie t0[kTiePre];
+  if (have0) {
+    r0 = rb[tid];
+#pragma unroll
+    for (int i = 0; i < kTiePre; ++i) t0[i] = tb[(size_t)tid * kTieCap + i];
+  }
   if (pl.path != kPathReject && pl.path != kPathBonus) return;   // uniform per block
   const bool rej = pl.path == kPathReject;
-  __syncthreads();
   const T* trow = tgt + target_row_off(b, pl.trow, K, V);
   const T* drow = rej ? dft + draft_row_off(b, pl.drow, K, V) : nullptr;
-  const double mt = pl.mt, md = pl.md;
-  const int lane = threadIdx.x % kWave;
+  const double mti = (double)pl.mt * invT, mdi = (double)pl.md * invT;   // m / T
 
-  // ---------------- finish (one workgroup per request) ----------------
-  const ChunkRec* rb = recs + (size_t)b * nch;
-  if (threadIdx.x < kWave) {
-    double a = 0.0, d = 0.0;
-    int ovf = 0;
-    for (int i = lane; i < nch; i += kWave) {
-      a += rb[i].et;
-      d += rb[i].ed;
-      ovf |= rb[i].ntie > kTieCap;
-    }
-    a = wave_sum(a);
-    d = wave_sum(d);
-    const bool any_ovf = __ballot(ovf) != 0;
-    if (lane == 0) {
-      s_St = a;
-      s_Sd = d;
-      s_fb = any_ovf;
-    }
+  // exact normalisers: chunk sums added in a fixed order (thread-strided,
+  // then the wave tree, then the four waves), and whether any chunk
+  // overflowed its tie slots
+  double a = 0.0, d = 0.0;
+  int ovf = 0;
+  if (have0) {
+    a = r0.et;
+    d = r0.ed;
+    ovf = r0.ntie > kTieCap;
   }
-  __syncthreads();
-  const double St = s_St, Sd = s_Sd;
-  bool fb = s_fb != 0;
+  for (int cc = tid + kSampThreads; cc < nch; cc += kSampThreads) {
+    const ChunkRec r = rb[cc];
+    a += r.et;
+    d += r.ed;
+    ovf |= r.ntie > kTieCap;
+  }
+  const double red = wave_sum4(a, d, 0.0, 0.0);
+  const bool wovf = __ballot(ovf) != 0;
+  if (tid == 0) s_nredo = 0;
+  if (lane == 0 || lane == 16) dl[wid * 2 + (lane >> 4)] = red;
+  if (lane == 0) il[wid] = wovf;
+  __syncthreads();                                   // table staged; wave sums
+  double St = 0.0, Sd = 0.0;
+  bool fb = false;
+#pragma unroll
+  for (int w = 0; w < kSampWaves; ++w) {
+    St += dl[w * 2];
+    Sd += dl[w * 2 + 1];
+    fb |= il[w] != 0;
+  }
   if (rej && !fb) fb = !(fabs(pl.g * Sd / St - 1.0) <= 0.25 * kTieWindow);
+  const double rSt = 1.0 / St, rSd = 1.0 / Sd;
 
   // chunk masses: A_t/S_t - A_d/S_d plus the chunk's near ties resolved exactly;
   // a chunk with more ties than slots (or every chunk, if the estimate check
   // failed) gets its mass recomputed exactly from the logits.
-  __shared__ int s_nredo;
-  __shared__ int redo[kMaxSampChunks];
-  if (threadIdx.x == 0) s_nredo = 0;
-  __syncthreads();
   if (rej) {
-    for (int cc = threadIdx.x; cc < nch; cc += kSampThreads) {
-      const ChunkRec r = rb[cc];
+    for (int cc = tid; cc < nch; cc += kSampThreads) {
+      const bool first = cc == tid;
+      const ChunkRec r = first ? r0 : rb[cc];
       if (fb || r.ntie > kTieCap) {
         redo[atomicAdd(&s_nredo, 1)] = cc;
         continue;
       }
-      double w = r.at / St - r.ad / Sd;
-      const Tie* ts = ties + ((size_t)b * nch + cc) * kTieCap;
+      double w = fma(r.at, rSt, -r.ad * rSd);
+      const Tie* ts = tb + (size_t)cc * kTieCap;
       for (int i = 0; i < r.ntie; ++i) {
-        const double x = ts[i].et / St - ts[i].ed / Sd;
+        Tie tv;
+        if (first && i < kTiePre) {
+#pragma unroll
+          for (int j = 0; j < kTiePre; ++j)
+            if (j == i) tv = t0[j];
+        } else {
+          tv = ts[i];
+        }
+        const double x = fma(tv.et, rSt, -tv.ed * rSd);
         if (x > 0.0) w += x;
       }
       wts[cc] = w > 0.0 ? w : 0.0;
     }
   } else {
-    for (int cc = threadIdx.x; cc < nch; cc += kSampThreads) wts[cc] = rb[cc].et;
+    for (int cc = tid; cc < nch; cc += kSampThreads) wts[cc] = cc == tid ? r0.et : rb[cc].et;
   }
-  __syncthreads();
+  __syncthreads();                                   // wts, redo list
   const int nredo = s_nredo;
   for (int i = 0; i < nredo; ++i) {                  // each chunk's mass is order-independent
     const int cc = redo[i];
     double w[kSampPerThread];
-    chunk_weights(trow, drow, (long)cc * kSampChunk, V, true, mt, md, invT, St, Sd, tbl, w);
+    chunk_weights(trow, drow, (long)cc * kSampChunk, V, true, mti, mdi, invT, rSt, rSd, tbl, w);
     double sum = 0.0;
 #pragma unroll
     for (int k = 0; k < kSampPerThread; ++k) sum += w[k];
     sum = block_sum(sum, dl);
-    if (threadIdx.x == 0) wts[cc] = sum;
+    if (tid == 0) wts[cc] = sum;
   }
-  __syncthreads();
+  if (nredo > 0) __syncthreads();                    // uniform
 
-  // blocked prefix over chunk masses: thread t owns chunks [c_lo, c_hi)
-  const int q = (nch + kSampThreads - 1) / kSampThreads;
-  const int c_lo = min(nch, (int)threadIdx.x * q), c_hi = min(nch, c_lo + q);
+  // Blocked prefix over the chunk masses, per wave: lane l owns chunks
+  // [l q, l q + q).  If the residual rounded to zero everywhere (unreachable
+  // in exact arithmetic) the draw is from p_j: the target sums instead.
+  const int q = (nch + kWave - 1) / kWave;
+  const int c_lo = min(nch, lane * q), c_hi = min(nch, c_lo + q);
   bool resid = rej;
   double mine = 0.0;
   for (int cc = c_lo; cc < c_hi; ++cc) mine += wts[cc];
-  double total;
-  double excl = block_exclusive_scan<double>(mine, dl, total);
+  double incl = wave_incl_scan(mine);
+  double total = __shfl(incl, kWave - 1, kWave);
   if (resid && !(total > 0.0)) {
-    // residual rounded to zero everywhere (unreachable in exact arithmetic): draw from p_j
     resid = false;
-    __syncthreads();
-    for (int cc = threadIdx.x; cc < nch; cc += kSampThreads) wts[cc] = rb[cc].et;
-    __syncthreads();
     mine = 0.0;
-    for (int cc = c_lo; cc < c_hi; ++cc) mine += wts[cc];
-    excl = block_exclusive_scan<double>(mine, dl, total);
+    for (int cc = c_lo; cc < c_hi; ++cc) mine += rb[cc].et;
+    incl = wave_incl_scan(mine);
+    total = __shfl(incl, kWave - 1, kWave);
   }
   const double rmass = (rej && resid) ? total : 0.0;
   const double t = (double)u_final[b] * total;
-  int cand = INT_MAX, last_pos = -1;
-  double run = excl;
+  double excl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) excl = 0.0;
+  int cand = -1, last_pos = -1;
+  double run = excl, pre = 0.0;
   for (int cc = c_lo; cc < c_hi; ++cc) {
-    run += wts[cc];
-    if (cand == INT_MAX && t < run) cand = cc;
-    if (wts[cc] > 0.0) last_pos = cc;
+    const double m = (rej && !resid) ? rb[cc].et : wts[cc];
+    const double before = run;
+    run += m;
+    if (cand < 0 && t < run) {
+      cand = cc;
+      pre = before;
+    }
+    if (m > 0.0) last_pos = cc;
   }
-  int cstar = block_min(cand, il);
+  const uint64_t hit = __ballot(cand >= 0);
+  int cstar;
   double tprime;
-  if (cstar == INT_MAX) {            // rounding fall-through: last chunk with mass
-    cstar = block_max(last_pos, il);
-    tprime = INFINITY;
-    if (cstar < 0) {                 // no positive mass at all (non-finite input)
-      if (threadIdx.x == 0) {
+  if (hit) {
+    const int L = __ffsll((unsigned long long)hit) - 1;
+    cstar = __shfl(cand, L, kWave);
+    tprime = t - __shfl(pre, L, kWave);
+  } else {                           // rounding fall-through: last chunk with mass
+    const uint64_t pos = __ballot(last_pos >= 0);
+    if (!pos) {                      // no positive mass at all (non-finite input)
+      if (tid == 0) {
         out_tokens[(size_t)b * (K + 1) + pl.stop] = -1;
         if (rmass_out) rmass_out[b] = rmass;
       }
-      return;
+      return;                        // uniform: every wave saw the same masses
     }
-  } else {
-    __syncthreads();
-    if (cand == cstar) {             // the one thread owning chunk cstar
-      double pre = excl;
-      for (int cc = c_lo; cc < cstar; ++cc) pre += wts[cc];
-      s_cpre = pre;
-    }
-    __syncthreads();
-    tprime = t - s_cpre;
+    cstar = __shfl(last_pos, 63 - __clzll((long long)pos), kWave);
+    tprime = INFINITY;
   }
 
   // in-chunk scan of chunk cstar
-  const long e0 = (long)cstar * kSampChunk + (long)threadIdx.x * kSampPerThread;
+  const long e0 = (long)cstar * kSampChunk + (long)tid * kSampPerThread;
   double w[kSampPerThread];
-  chunk_weights(trow, drow, (long)cstar * kSampChunk, V, resid, mt, md, invT, St, Sd, tbl, w);
+  chunk_weights(trow, drow, (long)cstar * kSampChunk, V, resid, mti, mdi, invT, rSt, rSd, tbl, w);
   double mysum = 0.0;
 #pragma unroll
   for (int i = 0; i < kSampPerThread; ++i) mysum += w[i];
-  double ctot;
-  const double ex = block_exclusive_scan<double>(mysum, dl, ctot);
+  const double wincl = wave_incl_scan(mysum);
+  double wex = __shfl_up(wincl, 1, kWave);
+  if (lane == 0) wex = 0.0;
+  if (lane == kWave - 1) dl[wid] = wincl;            // dl's last readers passed a barrier
+  __syncthreads();
+  double off = 0.0;
+#pragma unroll
+  for (int wv = 0; wv < kSampWaves; ++wv)
+    if (wv < wid) off += dl[wv];
   int vc = INT_MAX, vlast = -1;
-  run = ex;
+  run = off + wex;
 #pragma unroll
   for (int i = 0; i < kSampPerThread; ++i) {
     run += w[i];
     if (vc == INT_MAX && tprime < run) vc = (int)(e0 + i);
     if (w[i] > 0.0) vlast = (int)(e0 + i);
   }
-  int y = block_min(vc, il);
-  if (y == INT_MAX) y = block_max(vlast, il);   // rounding fall-through inside the chunk
-  if (threadIdx.x == 0) {
+  // token order is thread order: the wave's first hit is its smallest
+  const uint64_t h1 = __ballot(vc != INT_MAX), h2 = __ballot(vlast >= 0);
+  const int wvc = h1 ? __shfl(vc, __ffsll((unsigned long long)h1) - 1, kWave) : INT_MAX;
+  const int wvl = h2 ? __shfl(vlast, 63 - __clzll((long long)h2), kWave) : -1;
+  if (lane == 0) {
+    il[wid] = wvc;
+    il[kSampWaves + wid] = wvl;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int y = INT_MAX, yl = -1;
+#pragma unroll
+    for (int wv = 0; wv < kSampWaves; ++wv) {
+      y = min(y, il[wv]);
+      yl = max(yl, il[kSampWaves + wv]);
+    }
+    if (y == INT_MAX) y = yl;        // rounding fall-through inside the chunk
     out_tokens[(size_t)b * (K + 1) + pl.stop] = y;
     if (rmass_out) rmass_out[b] = rmass;
   }
@@ -428,11 +579,10 @@ template <typename T>
 static hipError_t sample_pass_t(const void* tgt, const void* dft, int B, int K, int V, int nch,
                                 double invT, const Plan* plan, ChunkRec* recs, Tie* ties,
                                 hipStream_t stream) {
-  const int ngrp = (nch + kPassChunks - 1) / kPassChunks;
-  const size_t blocks = (size_t)B * ngrp;
+  const size_t blocks = (size_t)B * nch;
   if (blocks > 0x7fffffffu || nch > kMaxSampChunks) return hipErrorInvalidConfiguration;
   sample_pass_kernel<T><<<dim3((unsigned)blocks), dim3(kSampThreads), 0, stream>>>(
-      static_cast<const T*>(tgt), static_cast<const T*>(dft), K, V, nch, ngrp, invT, plan, recs,
+      static_cast<const T*>(tgt), static_cast<const T*>(dft), K, V, nch, invT, plan, recs,
       ties);
   return hipGetLastError();
 }

@@ -7,19 +7,19 @@
 #include <cmath>
 #include <cstdint>
 
+#include "accept_core.h"
 #include "common.h"
 
 namespace specv {
 int row_stats_chunk(bool bf16);
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
-                            int B, int K, int V, int nchunk, float c, float2* part,
-                            hipStream_t stream);
+                            const int* tokens, int B, int K, int V, int nchunk, float c,
+                            float2* part, float* zx, hipStream_t stream);
 hipError_t launch_accept(bool bf16, bool filt, const void* tgt, const void* dft, const int* tokens,
                          const int* draft_len, const float* u, const float* u_final, int B,
-                         int K, int V, int nchunk, float c, double invT, int eos_id,
-                         const float2* part, const FiltRow* frows, Plan* plan, int* out_tokens,
-                         int* n_emitted, float* alpha_out, double* rmass_out, int* stop_out,
-                         int* path_out, hipStream_t stream);
+                         int K, int V, int nch_row, float c, double invT, int eos_id,
+                         const float2* part, const float* zx, const FiltRow* frows,
+                         const AcceptOut& out, hipStream_t stream);
 int filter_cap(int top_k);
 int filter_row_stride(int nch, int top_k);
 hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int* draft_len, int B,
@@ -43,7 +43,7 @@ hipError_t launch_exp64_selftest(const double* x, double* y, int n, hipStream_t 
 const char* const kStageNames[2][4] = {
     {"row_stats", "accept", "sample_pass", "sample_finish"},
     {"filter_cand", "filter_merge", "accept", "sample_list"}};
-constexpr int kNumStages = 4;
+constexpr int kNumStages[2] = {4, 4};
 
 namespace {
 
@@ -54,6 +54,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Workspace regions, each 256-byte aligned.
 // Without filters:
 //   row partials   float2   [B][2K+1][nch_row]        (max, partial normaliser)
+//   drafted logits float    [B][2K]                   (target rows, then draft rows)
 //   plans          Plan     [B]
 //   chunk records  ChunkRec [B][nch_samp]             (fp64 sums per sampler chunk)
 //   near ties      Tie      [B][nch_samp][kTieCap]
@@ -66,7 +67,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   bool filt = false;
   int nch_row = 0, nch_samp = 0, nch_filt = 0, cap = 0;
-  size_t off_row = 0, off_plan = 0, off_recs = 0, off_ties = 0;
+  size_t off_row = 0, off_zx = 0, off_plan = 0, off_recs = 0, off_ties = 0;
   size_t off_cand = 0, off_counts = 0, off_frows = 0, off_kept = 0, total = 0;
 };
 
@@ -83,6 +84,8 @@ Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p) {
     L.nch_samp = (V + kSampChunk - 1) / kSampChunk;
     L.off_row = off;
     off = align_up(off + (size_t)B * R * L.nch_row * sizeof(float2));
+    L.off_zx = off;
+    off = align_up(off + (size_t)B * 2 * K * sizeof(float));
     L.off_plan = off;
     off = align_up(off + (size_t)B * sizeof(Plan));
     L.off_recs = off;
@@ -168,15 +171,24 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
   };
   if (!mark(0)) return SPECV_EHIP;
   hipError_t e;
+  AcceptOut out;
+  out.plan = plan;
+  out.out_tokens = out_tokens;
+  out.n_emitted = n_emitted;
+  out.alpha_out = alpha_out;
+  out.rmass_out = rmass_out;
+  out.stop_out = stop_out;
+  out.path_out = path_out;
   if (!L.filt) {
     float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
+    float* zx = reinterpret_cast<float*>(ws + L.off_zx);
     ChunkRec* recs = reinterpret_cast<ChunkRec*>(ws + L.off_recs);
     Tie* ties = reinterpret_cast<Tie*>(ws + L.off_ties);
-    e = launch_row_stats(bf16, target, draft, draft_len, B, K, V, L.nch_row, c, row_part, stream);
+    e = launch_row_stats(bf16, target, draft, draft_len, tokens, B, K, V, L.nch_row, c, row_part,
+                         zx, stream);
     if (e != hipSuccess || !mark(1)) return SPECV_EHIP;
     e = launch_accept(bf16, false, target, draft, tokens, draft_len, u, u_final, B, K, V,
-                      L.nch_row, c, invT, eos_id, row_part, nullptr, plan, out_tokens, n_emitted,
-                      alpha_out, rmass_out, stop_out, path_out, stream);
+                      L.nch_row, c, invT, eos_id, row_part, zx, nullptr, out, stream);
     if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
     e = launch_sample_pass(bf16, target, draft, B, K, V, L.nch_samp, invT, plan, recs, ties,
                            stream);
@@ -193,8 +205,7 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
                       cand, counts, frows, kept, stream, events ? events[1] : nullptr);
     if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
     e = launch_accept(bf16, true, target, draft, tokens, draft_len, u, u_final, B, K, V, 0, c,
-                      invT, eos_id, nullptr, frows, plan, out_tokens, n_emitted, alpha_out,
-                      rmass_out, stop_out, path_out, stream);
+                      invT, eos_id, nullptr, nullptr, frows, out, stream);
     if (e != hipSuccess || !mark(3)) return SPECV_EHIP;
     e = launch_sample_list(bf16, draft, u_final, B, K, V, invT, plan, frows, kept, out_tokens,
                            rmass_out, stream);
@@ -246,17 +257,15 @@ specv_status_t specv_verify_timed(const void* target_logits, const void* draft_l
                                   int32_t* n_emitted, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream, hipEvent_t* events) {
   if (!events) return SPECV_EINVAL;
-  for (int i = 0; i <= specv::kNumStages; ++i)
+  const int nst = specv::kNumStages[specv::filters_on(V, top_k, top_p) ? 1 : 0];
+  for (int i = 0; i <= nst; ++i)
     if (!events[i]) return SPECV_EINVAL;
   return specv::run(target_logits, draft_logits, dtype, draft_tokens, draft_len, u, u_final, B,
                     K, V, temperature, top_k, top_p, eos_id, out_tokens, n_emitted, workspace,
                     workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr, events);
 }
 
-int specv_num_stages(int filtered) {
-  (void)filtered;
-  return specv::kNumStages;
-}
+int specv_num_stages(int filtered) { return specv::kNumStages[filtered ? 1 : 0]; }
 
 specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream_t stream) {
   if (n < 0 || (n > 0 && (!x || !y))) return SPECV_EINVAL;
@@ -264,7 +273,8 @@ specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream
 }
 
 const char* specv_stage_name(int filtered, int i) {
-  return (i >= 0 && i < specv::kNumStages) ? specv::kStageNames[filtered ? 1 : 0][i] : nullptr;
+  const int f = filtered ? 1 : 0;
+  return (i >= 0 && i < specv::kNumStages[f]) ? specv::kStageNames[f][i] : nullptr;
 }
 
 const char* specv_status_string(specv_status_t status) {

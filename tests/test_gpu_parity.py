@@ -193,8 +193,10 @@ def test_host_argument_errors():
 
 
 def test_exp64_against_numpy():
-    # The sampler's float64 exp (table-driven, Tang 1989) within 2 ulp of
-    # numpy's exp over the range the sampler uses, and 0 at and below -745.2.
+    # The sampler's float64 exp (table-driven, Tang 1989; N = 512, cubic, one
+    # FMA argument reduction) against numpy's exp: relative error below
+    # 1e-14 + |x| * 1.2e-16 (its stated bound, plus 2 ulp for numpy's own
+    # rounding), and 0 at and below -745.2.
     rng = np.random.default_rng(5)
     x = np.concatenate([-rng.random(400000) * 745.0, -rng.random(200000) * 40.0,
                         -rng.random(50000) * 1e-3, rng.random(50000) * 700.0,
@@ -202,11 +204,15 @@ def test_exp64_against_numpy():
     y = binding.selftest_exp64(torch.from_numpy(x).to(DEV)).cpu().numpy()
     ref = np.exp(x)
     normal = ref > 2.3e-308
-    ulp = np.abs(y[normal] - ref[normal]) / np.spacing(ref[normal])
-    print(f"  exp64: max {ulp.max():.2f} ulp, mean {ulp.mean():.3f} ulp over {normal.sum()} values")
-    assert ulp.max() <= 2.0
+    rel = np.abs(y[normal] - ref[normal]) / ref[normal]
+    bound = 1e-14 + np.abs(x[normal]) * 1.2e-16 + 4.5e-16
+    near = x[normal] >= -40.0
+    print(f"  exp64: max rel {rel.max():.3g}; over x >= -40: {rel[near].max():.3g}; "
+          f"max rel/bound {(rel / bound).max():.3f} over {normal.sum()} values")
+    assert np.all(rel <= bound)
     sub = ~normal
-    assert np.all(np.abs(y[sub] - ref[sub]) <= 2 * 5e-324)
+    sub_bound = (1e-14 + np.abs(x[sub]) * 1.2e-16) * ref[sub] + 2 * 5e-324   # subnormal grid
+    assert np.all(np.abs(y[sub] - ref[sub]) <= sub_bound)
     z = binding.selftest_exp64(torch.tensor([-np.inf, -746.0, -1e6], dtype=torch.float64,
                                             device=DEV)).cpu().numpy()
     assert np.all(z == 0.0)
@@ -285,3 +291,37 @@ def test_many_draws_large_vocabulary_non_unit_temperature():
     w = make_workload(2, B=1024)
     rep, g, o = assert_parity(w, label="1024 draws")
     assert rep["requests"] == 1024
+
+
+@pytest.mark.parametrize("cfg,B", [(3, 8), (4, 6)])
+def test_graph_replay_matches_eager(cfg, B):
+    # One call captured in a HIP graph and replayed several times, with eager
+    # calls on other inputs and synchronisations in between: every replay
+    # gives the eager result on its inputs (the call records no memset, so
+    # replays after the first are as good as the first).
+    w = make_workload(cfg, B=B, draft_sampler=oracle_sampler if cfg == 4 else None)
+    other = make_workload(cfg, B=B, seed=77, draft_sampler=oracle_sampler if cfg == 4 else None)
+    a = upload(w, DEV)
+    b = upload(other, DEV)
+    ws = torch.empty(binding.workspace_bytes(w.B, w.K, w.V,
+                                             torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                                             w.top_k, f32(w.top_p)), dtype=torch.uint8, device=DEV)
+    ref = {k: v.clone() for k, v in binding.verify(**a, workspace=ws).items()}
+    ref_b = {k: v.clone() for k, v in binding.verify(**b, workspace=ws).items()}
+    torch.cuda.synchronize()
+    out_t = torch.full_like(ref["out_tokens"], -7)
+    out_n = torch.full_like(ref["n_emitted"], -7)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.verify(**a, workspace=ws, out_tokens=out_t, n_emitted=out_n)
+    for rep in range(4):
+        out_t.fill_(-7)
+        out_n.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_t, ref["out_tokens"]), rep
+        assert torch.equal(out_n, ref["n_emitted"]), rep
+        # eager work on other inputs, sharing the workspace, between replays
+        r = binding.verify(**b, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(r["out_tokens"], ref_b["out_tokens"])
