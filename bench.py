@@ -12,7 +12,8 @@ Output: exactly one JSON line on stdout (progress goes to stderr):
   host_us_per_call host time to enqueue one call from Python (below ms_per_step: the
                    timed steps are GPU-bound, not launch-bound)
   roofline         the dominant kernel (row statistics): algorithmic bytes per launch
-                   over its mean duration, against the 8 TB/s HBM peak
+                   over its mean duration (a burst of launches between two HIP events),
+                   against the 8 TB/s HBM peak
   cpu_baseline     the fp64 oracle on this host, on a bounded sample of the same workload
 Inputs rotate over several independent sets whose total exceeds twice the
 256 MB last-level cache, so reads come from HBM.
@@ -32,6 +33,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# HBM bytes of one row-statistics launch on this workload, from rocprofv3
+# FETCH_SIZE and WRITE_SIZE runs scaled by a plain-copy calibration (see the
+# profiles directory); valid only for the sources they were taken with.
+ROW_STATS_TRAFFIC = {"sources_sha256_16": "57ff51f6d13b4659", "bytes": 148166594}
 WORKLOAD = 3
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,K=4,V=128k"
 
@@ -66,6 +71,15 @@ class HipEvents:
     def close(self):
         for h in self.arr:
             self.lib.hipEventDestroy(h)
+
+
+def row_stats_sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("row_stats.hip", "common.h"):
+        with open(os.path.join(ROOT, "speculative_decoding_sampling_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(w, budget_s):
@@ -199,8 +213,19 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 5 copies of {args.copy_calibration_mib} MiB")
 
+    # The dominant kernel alone, for the roofline: a burst of row-statistics
+    # launches cycling over the input sets between two events on the stream.
+    reps = max(40, args.steps)
+    evb = HipEvents(2)
+    torch.cuda.synchronize()
+    binding.bench_row_stats(sets, ws, reps, w0.T, stream, evb.arr[0], evb.arr[1])
+    torch.cuda.synchronize()
     dominant = "row_stats"
-    k1_us = stage_us[dominant]
+    k1_us = evb.elapsed_ms(0, 1) / reps * 1e3
+    traffic = (ROW_STATS_TRAFFIC["bytes"]
+               if row_stats_sources_hash() == ROW_STATS_TRAFFIC["sources_sha256_16"] else None)
+    evb.close()
+    log(f"row_stats alone: {k1_us:.2f} us/launch over {reps} launches")
     achieved = alg_bytes / (k1_us * 1e-6) / 1e9
     step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -214,7 +239,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32+f64",
         "data": "synthetic",
         "config": {"workload": WORKLOADS[WORKLOAD]["name"], "B": w0.B, "K": w0.K, "V": w0.V,
                    "logits": "bf16", "temperature": w0.T, "top_k": 0, "top_p": 1.0,
@@ -225,7 +250,7 @@ def main():
         "hbm_frac_whole_step": step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "launch_us": k1_us,
+                     "traffic": traffic, "launch_us": k1_us,
                      "bytes_per_launch": alg_bytes},
         "stages_us": stage_us,
     }

@@ -1,8 +1,9 @@
 /*
- * libspecverify self-test hooks (not part of the verification API).
+ * libspecverify self-test and benchmark hooks (not part of the verification
+ * API).
  *
  * These expose internal device routines so tests can check them directly
- * against a float64 reference.
+ * against a float64 reference, and let a benchmark time one kernel alone.
  */
 #ifndef SPECVERIFY_SELFTEST_H
 #define SPECVERIFY_SELFTEST_H
@@ -22,6 +23,30 @@ extern "C" {
  */
 SPECV_API specv_status_t specv_selftest_exp64(const double *x, double *y, int n,
                                               hipStream_t stream);
+
+/*
+ * The row-statistics kernel alone (the first kernel of an unfiltered
+ * specv_verify call), `reps` times back to back on `stream`, cycling through
+ * `nsets` input sets, with `start` recorded before the first launch and
+ * `stop` after the last, so (stop - start) / reps is the kernel's mean
+ * duration (plus the short gap between consecutive launches).  Set i is
+ * targets[i], drafts[i], draft_tokens[i], draft_lens[i]: device arrays laid
+ * out as for specv_verify, all with the same dtype, B, K and V; the arrays of
+ * pointers themselves are host arrays of nsets entries.  The workspace is
+ * one valid for specv_verify with these sizes and no filters; its contents
+ * are overwritten.  Returns SPECV_EINVAL for bad sizes, counts, temperature,
+ * null or misaligned pointers or null events, SPECV_EWORKSPACE for a short
+ * workspace, SPECV_EHIP if a launch or event record fails.  Asynchronous.
+ */
+SPECV_API specv_status_t specv_bench_row_stats(const void *const *targets,
+                                               const void *const *drafts,
+                                               const int32_t *const *draft_tokens,
+                                               const int32_t *const *draft_lens, int nsets,
+                                               specv_dtype_t dtype, int B, int K, int V,
+                                               float temperature, void *workspace,
+                                               size_t workspace_bytes, int reps,
+                                               hipStream_t stream, hipEvent_t start,
+                                               hipEvent_t stop);
 
 #ifdef __cplusplus
 }

@@ -65,6 +65,10 @@ def load_library():
         lib.specv_status_string.restype = ctypes.c_char_p
         lib.specv_selftest_exp64.argtypes = [c_vp, c_vp, c_int, c_vp]
         lib.specv_selftest_exp64.restype = c_int
+        lib.specv_bench_row_stats.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                              c_int, c_float, c_vp, c_size, c_int, c_vp, c_vp,
+                                              c_vp]
+        lib.specv_bench_row_stats.restype = c_int
         lib.specv_version.argtypes = []
         lib.specv_version.restype = c_int
         _lib = lib
@@ -93,6 +97,30 @@ def selftest_exp64(x):
     if st != SPECV_OK:
         raise SpecVerifyError(st, status_string(st))
     return y
+
+
+def bench_row_stats(sets, workspace, reps, temperature=1.0, stream=None, start=None, stop=None):
+    """Benchmark hook: the row-statistics kernel alone, ``reps`` launches
+    cycling through ``sets`` (dicts as ``verify`` takes, same sizes), between
+    the HIP events ``start`` and ``stop`` (raw handles) recorded on ``stream``."""
+    lib = load_library()
+    t0 = sets[0]["target_logits"]
+    B, K1, V = t0.shape
+    n = len(sets)
+    arr = lambda key: (ctypes.c_void_p * n)(*[s[key].data_ptr() if s[key].numel() else 0
+                                               for s in sets])
+    for s in sets:
+        if s["target_logits"].shape != t0.shape or s["target_logits"].dtype != t0.dtype:
+            raise ValueError("all sets must share shape and dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(t0.device)
+    st = lib.specv_bench_row_stats(arr("target_logits"), arr("draft_logits"), arr("draft_tokens"),
+                                   arr("draft_len"), n, _dtype_code(t0), B, K1 - 1, V,
+                                   float(temperature), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), int(reps),
+                                   ctypes.c_void_p(stream.cuda_stream), start, stop)
+    if st != SPECV_OK:
+        raise SpecVerifyError(st, status_string(st))
 
 
 def _dtype_code(t):

@@ -267,6 +267,44 @@ specv_status_t specv_verify_timed(const void* target_logits, const void* draft_l
 
 int specv_num_stages(int filtered) { return specv::kNumStages[filtered ? 1 : 0]; }
 
+specv_status_t specv_bench_row_stats(const void* const* targets, const void* const* drafts,
+                                     const int32_t* const* draft_tokens,
+                                     const int32_t* const* draft_lens, int nsets,
+                                     specv_dtype_t dtype, int B, int K, int V, float temperature,
+                                     void* workspace, size_t workspace_bytes, int reps,
+                                     hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  using namespace specv;
+  if (check_sizes(B, K, V, dtype, 0, 1.0f) != SPECV_OK) return SPECV_EINVAL;
+  if (!targets || !drafts || !draft_tokens || !draft_lens || nsets < 1 || reps < 1 || !start ||
+      !stop)
+    return SPECV_EINVAL;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SPECV_EINVAL;
+  const size_t esz = dtype == SPECV_BF16 ? 2 : 4;
+  for (int i = 0; i < nsets; ++i) {
+    if (!targets[i] || !draft_lens[i] || misaligned(targets[i], esz) ||
+        misaligned(draft_lens[i], 4))
+      return SPECV_EINVAL;
+    if (K > 0 && (!drafts[i] || !draft_tokens[i] || misaligned(drafts[i], esz) ||
+                  misaligned(draft_tokens[i], 4)))
+      return SPECV_EINVAL;
+  }
+  const bool bf16 = dtype == SPECV_BF16;
+  const Layout L = make_layout(B, K, V, bf16, 0, 1.0f);
+  if (!workspace || misaligned(workspace, 16) || workspace_bytes < L.total) return SPECV_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
+  float* zx = reinterpret_cast<float*>(ws + L.off_zx);
+  const float c = (float)(1.4426950408889634 / (double)temperature);
+  if (hipEventRecord(start, stream) != hipSuccess) return SPECV_EHIP;
+  for (int r = 0; r < reps; ++r) {
+    const int i = r % nsets;
+    if (launch_row_stats(bf16, targets[i], drafts[i], draft_lens[i], draft_tokens[i], B, K, V,
+                         L.nch_row, c, row_part, zx, stream) != hipSuccess)
+      return SPECV_EHIP;
+  }
+  return hipEventRecord(stop, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
+}
+
 specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream_t stream) {
   if (n < 0 || (n > 0 && (!x || !y))) return SPECV_EINVAL;
   return specv::launch_exp64_selftest(x, y, n, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;

@@ -325,3 +325,27 @@ def test_graph_replay_matches_eager(cfg, B):
         r = binding.verify(**b, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(r["out_tokens"], ref_b["out_tokens"])
+
+
+def test_bench_row_stats_hook_runs():
+    # The benchmark hook launches the row-statistics kernel alone; afterwards a
+    # full call on the same workspace still matches the oracle.
+    import ctypes
+    w = make_workload(3, B=4)
+    a = upload(w, DEV)
+    ws = torch.empty(binding.workspace_bytes(w.B, w.K, w.V, torch.bfloat16), dtype=torch.uint8,
+                     device=DEV)
+    lib = ctypes.CDLL("libamdhip64.so")
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert lib.hipEventCreate(ctypes.byref(e)) == 0
+    binding.bench_row_stats([a, a], ws, 5, w.T, None, ev[0].value, ev[1].value)
+    torch.cuda.synchronize()
+    ms = ctypes.c_float()
+    assert lib.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0 and ms.value > 0
+    for e in ev:
+        lib.hipEventDestroy(e)
+    g = to_numpy(binding.verify(**a, workspace=ws, debug=True))
+    torch.cuda.synchronize()
+    rep = compare(g, run_oracle(w), w.K)
+    assert not rep["mismatches"], rep["mismatches"][:5]

@@ -35,7 +35,8 @@ def test_header_declares_the_api():
     names = declared_functions()
     assert set(names) == {"specv_workspace_bytes", "specv_verify", "specv_verify_debug",
                           "specv_verify_timed", "specv_num_stages", "specv_stage_name",
-                          "specv_status_string", "specv_version", "specv_selftest_exp64"}, names
+                          "specv_status_string", "specv_version", "specv_selftest_exp64",
+                          "specv_bench_row_stats"}, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -119,3 +120,27 @@ def test_status_strings(lib):
     s.restype = ctypes.c_char_p
     assert s(0) == b"ok" and s(1) == b"invalid argument"
     assert lib.specv_version() == 100
+
+
+def test_bench_hook_rejects_bad_arguments(lib):
+    f = lib.specv_bench_row_stats
+    vp, i, fl, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    f.argtypes = [vp, vp, vp, vp, i, i, i, i, i, fl, vp, sz, i, vp, vp, vp]
+    f.restype = i
+    one = (vp * 1)(16)
+    ok = dict(targets=one, drafts=one, toks=one, lens=one, nsets=1, dtype=1, B=2, K=3, V=4096,
+              T=1.0, ws=16, wsb=1 << 20, reps=4, start=16, stop=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["targets"], a["drafts"], a["toks"], a["lens"], a["nsets"], a["dtype"], a["B"],
+                 a["K"], a["V"], a["T"], a["ws"], a["wsb"], a["reps"], None, a["start"],
+                 a["stop"])
+
+    assert call(nsets=0) == 1
+    assert call(reps=0) == 1
+    assert call(start=None) == 1
+    assert call(T=0.0) == 1
+    assert call(targets=(vp * 1)(0)) == 1
+    assert call(wsb=16) == 2
