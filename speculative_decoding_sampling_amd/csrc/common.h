@@ -140,18 +140,33 @@ __device__ __forceinline__ bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 }
 
-// Butterfly reductions: every lane ends with the same, bit-identical value
-// (each step adds the same two operands, and IEEE addition is commutative).
+// Wave reductions of a float: four DPP steps reduce each 16-lane row (quad
+// swaps, then the half-row and row mirrors, which pair each lane with one in
+// the other half once the halves are uniform), then the four row results are
+// read as scalars and combined in a fixed order.  No LDS traffic and no lane
+// index arithmetic; every lane gets the same, bit-identical value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f32<0xb1>(v));      // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4e>(v));      // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));     // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));     // row_mirror
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f32<0xb1>(v);
+  v += dpp_f32<0x4e>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
+// Butterfly sum of a double over the wave (every lane gets the same value).
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

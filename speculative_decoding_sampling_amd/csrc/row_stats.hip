@@ -26,6 +26,12 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
     float2* __restrict__ part, float* __restrict__ zx) {
   constexpr int N = Elem<T>::kPerVec;
   constexpr int kChunk = kRowThreads * VECS * N;
+  // Arrival counter of the end-of-workgroup combine, cleared as the
+  // workgroup starts (its waves start together, so the barrier is cheap).
+  __shared__ float2 red[kRowThreads / kWave];
+  __shared__ int arrived;
+  if (threadIdx.x == 0) arrived = 0;
+  __syncthreads();
   const int R = 2 * K + 1;
   const int chunk = blockIdx.x % nchunk;
   const int rr = blockIdx.x / nchunk;
@@ -85,10 +91,16 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   }
   s = wave_sum(s);
 
-  __shared__ float2 red[kRowThreads / kWave];
-  if (lane == 0) red[wid] = make_float2(m, s);
-  __syncthreads();
-  if (threadIdx.x == 0) {
+  // The last wave to finish combines the four wave partials; the others
+  // exit at once instead of waiting at a barrier.  The arrival increment is
+  // a workgroup-scope acquire-release: each wave's partial is written before
+  // it arrives, and the last arriver reads them after.
+  if (lane == 0) {
+    red[wid] = make_float2(m, s);
+    const int before = __hip_atomic_fetch_add(&arrived, 1, __ATOMIC_ACQ_REL,
+                                              __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (before != kRowThreads / kWave - 1) return;
+
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kRowThreads / kWave; ++w) M = fmaxf(M, red[w].x);
