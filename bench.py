@@ -100,6 +100,65 @@ def cpu_baseline(w, budget_s):
             "seconds_per_call": t_total / reps}
 
 
+def bench_sample(args):
+    """The draft model's sampling step on the headline workload: one draw from
+    the processed distribution of each of the 256 draft rows (B=64 x K=4,
+    V=128256, bf16, T=1), through specv_sample."""
+    import torch
+    from speculative_decoding_sampling_amd import binding
+    from speculative_decoding_sampling_amd.build import LIB
+    from speculative_decoding_sampling_amd.workloads import WORKLOADS, make_workload, uniforms
+
+    if not os.path.exists(LIB):
+        from speculative_decoding_sampling_amd.build import build
+        build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sets = []
+    for i in range(args.sets):
+        w = make_workload(WORKLOAD, seed=1000 + WORKLOAD + 100 * i)
+        rows = np.ascontiguousarray(w.draft.reshape(-1, w.V))
+        u = uniforms(np.random.default_rng(5000 + i), rows.shape[0])
+        sets.append(dict(
+            logits=torch.from_numpy(rows.view(np.int16)).to(dev).view(torch.bfloat16),
+            u=torch.from_numpy(u).to(dev),
+            out=torch.empty(rows.shape[0], dtype=torch.int32, device=dev)))
+    R, V, T = rows.shape[0], w.V, w.T
+    alg_bytes = R * V * 2
+    stream = torch.cuda.current_stream(dev)
+    ws = torch.empty(binding.workspace_bytes(R, 0, V, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        st = sets[i % len(sets)]
+        binding.sample(st["logits"], st["u"], T, out_tokens=st["out"], workspace=ws,
+                       stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    ev.lib.hipEventRecord(ev.arr[0], stream.cuda_stream)
+    for i in range(args.steps):
+        step(i)
+    ev.lib.hipEventRecord(ev.arr[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / args.steps
+    ev.close()
+    y = sets[0]["out"].cpu().numpy()
+    assert np.all((y >= 0) & (y < V)), y
+    log(f"sample: {ms * 1e3:.2f} us/step for {R} rows")
+    print(json.dumps({
+        "metric": "draft tokens drawn/sec (processed-distribution sampler)", "value": R / (ms * 1e-3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32+f64", "data": "synthetic",
+        "config": {"workload": WORKLOADS[WORKLOAD]["name"] + " draft rows", "rows": R, "V": V,
+                   "logits": "bf16", "temperature": T, "top_k": 0, "top_p": 1.0,
+                   "algorithmic_bytes_per_step": alg_bytes},
+        "hbm_gbps_whole_step": alg_bytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +167,10 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=["verify", "sample"], default="verify",
+                    help="verify: the verification step (default, the headline); sample: the "
+                         "draft-side draw of the same workload (256 draft rows), reported for "
+                         "reference")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -118,6 +181,9 @@ def main():
         log("multi-GPU runs are not part of this build: the path would shard over requests "
             "with no communication (see the design notes); run with --gpus 1")
         sys.exit(2)
+
+    if args.op == "sample":
+        return bench_sample(args)
 
     import torch
     from speculative_decoding_sampling_amd import binding

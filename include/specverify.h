@@ -142,6 +142,34 @@ SPECV_API specv_status_t specv_verify_debug(const void *target_logits, const voi
                                   int32_t *stop_pos, int32_t *path);
 
 /*
+ * Batched draws from processed distributions: for each row r of
+ * logits[R][V], out_tokens[r] is the token at u[r] of the inverse CDF of
+ * F(logits[r]), F being the temperature / top-k / top-p processing that
+ * specv_verify applies, with token ids in ascending order and a strict
+ * comparison (nickwang.xyz, "推测解码：草稿、验证与实际加速", section
+ * "算完三个 token 的全部概率", function sample()).  Its main use is the draft
+ * model's own step: a drafted token x_k is a draw from q_k (same page,
+ * section "接受与拒绝怎样保住分布"), so tokens drawn here from the draft
+ * logits, with their own uniforms, are the draft_tokens that specv_verify
+ * then checks.
+ *
+ *  logits      [R][V] dtype, row-major, device; rows 16-B aligned take the vector path
+ *  u           [R] float32 in [0, 1), device
+ *  out_tokens  [R] int32, device: the drawn ids; -1 for a row with no finite
+ *              logit or u outside [0, 1) (other rows unaffected)
+ *  workspace   device, 16-B aligned, at least specv_workspace_bytes(R, 0, V,
+ *              dtype, top_k, top_p) bytes
+ *
+ * Same conventions, limits and status codes as specv_verify (it is that call
+ * with K = 0 and draft_len = 0 for every row); 1 <= R.  Asynchronous on
+ * `stream`.
+ */
+SPECV_API specv_status_t specv_sample(const void *logits, specv_dtype_t dtype, const float *u,
+                                      int R, int V, float temperature, int top_k, float top_p,
+                                      int32_t *out_tokens, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Timing variant of specv_verify, for benchmarks: identical work, plus
  * hipEventRecord on `stream` of events[0] before the first kernel launch and
  * of events[i+1] after kernel stage i.  `events` holds specv_num_stages(f) + 1

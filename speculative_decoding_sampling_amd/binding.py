@@ -57,6 +57,9 @@ def load_library():
         lib.specv_verify_debug.restype = c_int
         lib.specv_verify_timed.argtypes = common + [c_vp]
         lib.specv_verify_timed.restype = c_int
+        lib.specv_sample.argtypes = [c_vp, c_int, c_vp, c_int, c_int, c_float, c_int, c_float, c_vp,
+                                     c_vp, c_size, c_vp]
+        lib.specv_sample.restype = c_int
         lib.specv_num_stages.argtypes = [c_int]
         lib.specv_num_stages.restype = c_int
         lib.specv_stage_name.argtypes = [c_int, c_int]
@@ -97,6 +100,38 @@ def selftest_exp64(x):
     if st != SPECV_OK:
         raise SpecVerifyError(st, status_string(st))
     return y
+
+
+def sample(logits, u, temperature=1.0, top_k=0, top_p=1.0, *, out_tokens=None, workspace=None,
+           stream=None):
+    """Draw one token per row of ``logits`` [R, V] (bf16 or fp32) from its
+    processed distribution (temperature, top-k, top-p) at the uniforms ``u``
+    [R] (fp32), by inverse CDF over ascending token ids.  Returns
+    ``out_tokens`` [R] int32 (-1 for a row with no finite logit or a uniform
+    outside [0, 1)).  Asynchronous on ``stream``."""
+    lib = load_library()
+    dev = logits.device
+    if dev.type != "cuda" or logits.dim() != 2:
+        raise ValueError("logits must be a [R, V] GPU tensor")
+    R, V = logits.shape
+    code = _dtype_code(logits)
+    _check(logits, "logits", None, (R, V), dev)
+    _check(u, "u", torch.float32, (R,), dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((R,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", torch.int32, (R,), dev)
+    nbytes = int(lib.specv_workspace_bytes(R, 0, V, code, int(top_k), float(top_p)))
+    if workspace is None:
+        workspace = _workspace(dev, nbytes)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib.specv_sample(_ptr(logits), code, _ptr(u), R, V, float(temperature), int(top_k),
+                          float(top_p), _ptr(out_tokens), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(),
+                          ctypes.c_void_p(stream.cuda_stream))
+    if st != SPECV_OK:
+        raise SpecVerifyError(st, status_string(st))
+    return out_tokens
 
 
 def bench_row_stats(sets, workspace, reps, temperature=1.0, stream=None, start=None, stop=None):

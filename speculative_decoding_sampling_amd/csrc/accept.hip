@@ -23,7 +23,7 @@ __global__ __launch_bounds__(kWave) void accept_kernel(
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const int R = 2 * K + 1;
-  const int nb_raw = draft_len[b];
+  const int nb_raw = draft_len ? draft_len[b] : 0;   // null: no drafts (sampling)
   const float uf = u_final[b];
   int x = -1;
   float uk = 0.f, zt = -INFINITY, zd = -INFINITY;

@@ -78,7 +78,7 @@ struct LaneRows {
 struct AcceptOut {
   Plan* plan;          // [B] the plan, for the sampler kernels
   int* out_tokens;     // [B][K+1]
-  int* n_emitted;      // [B]
+  int* n_emitted;      // [B], or null (sampling calls)
   float* alpha_out;    // [B][K] or null
   double* rmass_out;   // [B] or null (written 0 here; the sampler sets it)
   int* stop_out;       // [B] or null
@@ -133,7 +133,7 @@ __device__ __forceinline__ void accept_scan(int b, int lane, int K, float c, dou
       pl.path = kPathError;
       pl.stop = -1;
       out.plan[b] = pl;
-      out.n_emitted[b] = -1;
+      if (out.n_emitted) out.n_emitted[b] = -1;
       if (out.rmass_out) out.rmass_out[b] = 0.0;
       if (out.stop_out) out.stop_out[b] = -1;
       if (out.path_out) out.path_out[b] = kPathError;
@@ -173,7 +173,7 @@ __device__ __forceinline__ void accept_scan(int b, int lane, int K, float c, dou
     }
     pl.pad2 = 0.0;
     out.plan[b] = pl;
-    out.n_emitted[b] = stop + 1;
+    if (out.n_emitted) out.n_emitted[b] = stop + 1;
     if (out.rmass_out) out.rmass_out[b] = 0.0;
     if (out.stop_out) out.stop_out[b] = stop;
     if (out.path_out) out.path_out[b] = path;

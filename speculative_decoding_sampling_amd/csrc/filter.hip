@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
   const int chunk = blockIdx.x % nch;
   const int rr = blockIdx.x / nch;
   const int r = rr % R, b = rr / R;
-  const int nb = draft_len[b];
+  const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
   if (nb < 0 || nb > K) return;
   bool is_target;
   int k;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   const int rr = blockIdx.x;
   const int r = rr % R, b = rr / R;
   exp64_stage_table(tbl);
-  const int nb = draft_len[b];
+  const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
   if (nb < 0 || nb > K) return;
   bool is_target;
   int k;

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   const int rr = blockIdx.x / nchunk;
   const int r = rr % R;
   const int b = rr / R;
-  const int nb = draft_len[b];
+  const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
   if (nb < 0 || nb > K) return;                      // the accept scan reports the error
   const bool is_target = r <= K;
   const int k = is_target ? r : r - (K + 1);

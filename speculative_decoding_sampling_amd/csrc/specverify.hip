@@ -138,13 +138,17 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
                    float top_p, int eos_id, int32_t* out_tokens, int32_t* n_emitted,
                    void* workspace, size_t workspace_bytes, hipStream_t stream,
                    float* alpha_out, double* rmass_out, int32_t* stop_out, int32_t* path_out,
-                   hipEvent_t* events) {
+                   hipEvent_t* events, bool sampling = false) {
   specv_status_t st = check_sizes(B, K, V, dtype, top_k, top_p);
   if (st != SPECV_OK) return st;
   if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SPECV_EINVAL;
   if (eos_id < -1 || eos_id >= V) return SPECV_EINVAL;
   const size_t esz = dtype == SPECV_BF16 ? 2 : 4;
-  if (!target || !draft_len || !u_final || !out_tokens || !n_emitted) return SPECV_EINVAL;
+  // A sampling call is a verification with no drafts: draft_len and
+  // n_emitted may then be null (every request draws its bonus token).
+  if (sampling && K != 0) return SPECV_EINVAL;
+  if (!target || !u_final || !out_tokens) return SPECV_EINVAL;
+  if (!sampling && (!draft_len || !n_emitted)) return SPECV_EINVAL;
   if (K > 0 && (!draft || !tokens || !u)) return SPECV_EINVAL;
   if (misaligned(target, esz) || (draft && misaligned(draft, esz))) return SPECV_EINVAL;
   if (misaligned(draft_len, 4) || misaligned(u_final, 4) || misaligned(out_tokens, 4) ||
@@ -305,6 +309,14 @@ specv_status_t specv_bench_row_stats(const void* const* targets, const void* con
   return hipEventRecord(stop, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }
 
+specv_status_t specv_sample(const void* logits, specv_dtype_t dtype, const float* u, int R, int V,
+                            float temperature, int top_k, float top_p, int32_t* out_tokens,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return specv::run(logits, nullptr, dtype, nullptr, nullptr, nullptr, u, R, 0, V, temperature,
+                    top_k, top_p, -1, out_tokens, nullptr, workspace, workspace_bytes, stream,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, true);
+}
+
 specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream_t stream) {
   if (n < 0 || (n > 0 && (!x || !y))) return SPECV_EINVAL;
   return specv::launch_exp64_selftest(x, y, n, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
@@ -326,6 +338,6 @@ const char* specv_status_string(specv_status_t status) {
   return "unknown status";
 }
 
-int specv_version(void) { return 100; }
+int specv_version(void) { return 101; }
 
 }  // extern "C"

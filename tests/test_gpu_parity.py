@@ -349,3 +349,85 @@ def test_bench_row_stats_hook_runs():
     torch.cuda.synchronize()
     rep = compare(g, run_oracle(w), w.K)
     assert not rep["mismatches"], rep["mismatches"][:5]
+
+
+# ---------------------------------------------------------------------------
+# Processed-distribution sampler (draft-side draws): specv_sample.
+
+def oracle_sample(logits, u, T, top_k, top_p, dtype):
+    """The oracle's draws: a verification with no drafts draws each row's bonus
+    token from F(row) at u (same inverse CDF, same flags)."""
+    R, V = logits.shape
+    t = logits[:, None, :]
+    o = O.verify(t, t[:, :0, :], np.zeros((R, 0), np.int32),
+                 np.zeros(R, np.int32), np.zeros((R, 0), np.float32), u, f32(T), top_k,
+                 f32(top_p), -1, dtype)
+    return o["out_tokens"][:, 0], o["flag_kind"]
+
+
+def upload_logits(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def assert_sample_parity(logits, u, T, top_k, top_p, dtype, label=""):
+    y = binding.sample(upload_logits(logits, dtype), torch.from_numpy(u).to(DEV), T, top_k, top_p)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    yo, flags = oracle_sample(logits, u, T, top_k, top_p, dtype)
+    certain = flags == O.FLAG_NONE
+    bad = np.flatnonzero(certain & (y != yo))
+    print(f"[sample] {label} R={len(u)} V={logits.shape[1]} {dtype} T={T} k={top_k} p={top_p}: "
+          f"flagged {int((~certain).sum())}, mismatches {len(bad)}", flush=True)
+    assert len(bad) == 0, [(int(r), int(y[r]), int(yo[r])) for r in bad[:5]]
+    return y, yo
+
+
+@pytest.mark.parametrize("cfg,R", [(1, 32), (2, None), (3, 48), (5, 32)])
+def test_sample_matches_oracle_unfiltered(cfg, R):
+    w = make_workload(cfg, B=R if cfg != 2 else None)
+    rows = w.draft.reshape(-1, w.V)
+    rng = np.random.default_rng(700 + cfg)
+    from speculative_decoding_sampling_amd.workloads import uniforms
+    u = uniforms(rng, rows.shape[0])
+    assert_sample_parity(rows, u, w.T, 0, 1.0, w.dtype, label=f"cfg{cfg}")
+
+
+@pytest.mark.parametrize("top_k,top_p", [(50, 0.9), (1, 1.0), (100, 0.95)])
+def test_sample_matches_oracle_filtered(top_k, top_p):
+    w = make_workload(4, B=4, draft_sampler=oracle_sampler)
+    rows = w.draft.reshape(-1, w.V)[:24]
+    from speculative_decoding_sampling_amd.workloads import uniforms
+    u = uniforms(np.random.default_rng(800 + top_k), rows.shape[0])
+    assert_sample_parity(rows, u, w.T, top_k, top_p, w.dtype, label="cfg4 rows")
+
+
+def test_sample_edge_cases():
+    # u = 0 and the largest uniform below 1; a row with one finite logit; rows
+    # with no finite logit or a uniform outside [0, 1) give -1, alone.
+    rng = np.random.default_rng(11)
+    V = 5000
+    z = rng.normal(0, 2, size=(6, V)).astype(np.float32)
+    z[2, :] = -np.inf
+    z[2, 1234] = 0.5
+    z[3, :] = -np.inf
+    u = np.array([0.0, 1.0 - 2.0 ** -24, 0.5, 0.5, 1.0, -0.25], dtype=np.float32)
+    y = binding.sample(upload_logits(z, "f32"), torch.from_numpy(u).to(DEV), 1.0).cpu().numpy()
+    yo, _ = oracle_sample(z[:3], u[:3], 1.0, 0, 1.0, "f32")
+    assert np.array_equal(y[:3], yo) and y[2] == 1234
+    assert np.all(y[3:] == -1)
+
+
+def test_full_round_with_gpu_drawn_drafts():
+    # One whole synthetic round on the GPU: the draft tokens are drawn from the
+    # draft logits by specv_sample with their own uniforms, then verified.  The
+    # oracle draws the same tokens (except where it flags the draw) and the
+    # verification matches it.
+    w = make_workload(3, B=16)
+    from speculative_decoding_sampling_amd.workloads import uniforms
+    ud = uniforms(np.random.default_rng(913), (w.B, w.K))
+    rows = w.draft.reshape(-1, w.V)
+    y, yo = assert_sample_parity(rows, ud.reshape(-1), w.T, 0, 1.0, w.dtype, label="round drafts")
+    w.draft_tokens = y.reshape(w.B, w.K).astype(np.int32)
+    assert_parity(w, label="verify GPU-drawn drafts")

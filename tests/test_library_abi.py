@@ -36,7 +36,7 @@ def test_header_declares_the_api():
     assert set(names) == {"specv_workspace_bytes", "specv_verify", "specv_verify_debug",
                           "specv_verify_timed", "specv_num_stages", "specv_stage_name",
                           "specv_status_string", "specv_version", "specv_selftest_exp64",
-                          "specv_bench_row_stats"}, names
+                          "specv_bench_row_stats", "specv_sample"}, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -119,7 +119,7 @@ def test_status_strings(lib):
     s.argtypes = [ctypes.c_int]
     s.restype = ctypes.c_char_p
     assert s(0) == b"ok" and s(1) == b"invalid argument"
-    assert lib.specv_version() == 100
+    assert lib.specv_version() == 101
 
 
 def test_bench_hook_rejects_bad_arguments(lib):
@@ -143,4 +143,28 @@ def test_bench_hook_rejects_bad_arguments(lib):
     assert call(start=None) == 1
     assert call(T=0.0) == 1
     assert call(targets=(vp * 1)(0)) == 1
+    assert call(wsb=16) == 2
+
+
+def test_sample_rejects_bad_arguments(lib):
+    f = lib.specv_sample
+    vp, i, fl, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    f.argtypes = [vp, i, vp, i, i, fl, i, fl, vp, vp, sz, vp]
+    f.restype = i
+    ok = dict(logits=16, dtype=1, u=16, R=4, V=1000, T=1.0, k=0, p=1.0, out=16, ws=16,
+              wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["logits"], a["dtype"], a["u"], a["R"], a["V"], a["T"], a["k"], a["p"],
+                 a["out"], a["ws"], a["wsb"], None)
+
+    assert call(R=0) == 1
+    assert call(logits=None) == 1
+    assert call(u=None) == 1
+    assert call(out=None) == 1
+    assert call(T=-1.0) == 1
+    assert call(p=0.0) == 1
+    assert call(k=10, p=0.5, wsb=16) == 2            # filtered workspace too small
     assert call(wsb=16) == 2
