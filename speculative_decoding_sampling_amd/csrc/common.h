@@ -136,6 +136,40 @@ __device__ __forceinline__ void load_vec_checked(const T* __restrict__ row, long
   }
 }
 
+// Raw-word loads: the same elements as load_vec_*, left packed so a caller
+// can issue them and unpack later.  Elements at or beyond V read as -inf.
+__device__ __forceinline__ uint32_t neg_inf_bits(float) { return 0xff800000u; }
+__device__ __forceinline__ uint32_t neg_inf_bits(bf16_t) { return 0xff80u; }
+__device__ __forceinline__ uint32_t elem_bits(const float* row, long e) {
+  return __float_as_uint(row[e]);
+}
+__device__ __forceinline__ uint32_t elem_bits(const bf16_t* row, long e) { return row[e]; }
+
+template <typename T>
+__device__ __forceinline__ uint4 load_raw_stream(const T* __restrict__ row, long e0) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(row + e0);
+  uint4 w;
+  w.x = __builtin_nontemporal_load(p);
+  w.y = __builtin_nontemporal_load(p + 1);
+  w.z = __builtin_nontemporal_load(p + 2);
+  w.w = __builtin_nontemporal_load(p + 3);
+  return w;
+}
+template <typename T>
+__device__ __forceinline__ uint4 load_raw_checked(const T* __restrict__ row, long e0, int V,
+                                                  bool aligned) {
+  constexpr int N = Elem<T>::kPerVec;
+  if (aligned && e0 + N <= V) return *reinterpret_cast<const uint4*>(row + e0);
+  uint32_t e[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) e[i] = e0 + i < V ? elem_bits(row, e0 + i) : neg_inf_bits(T{});
+  if constexpr (N == 4) {
+    return make_uint4(e[0], e[1], e[2], e[3]);
+  } else {
+    return make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16);
+  }
+}
+
 __device__ __forceinline__ bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 }

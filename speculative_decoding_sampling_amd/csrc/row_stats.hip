@@ -26,12 +26,6 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
     float2* __restrict__ part, float* __restrict__ zx) {
   constexpr int N = Elem<T>::kPerVec;
   constexpr int kChunk = kRowThreads * VECS * N;
-  // Arrival counter of the end-of-workgroup combine, cleared as the
-  // workgroup starts (its waves start together, so the barrier is cheap).
-  __shared__ float2 red[kRowThreads / kWave];
-  __shared__ int arrived;
-  if (threadIdx.x == 0) arrived = 0;
-  __syncthreads();
   const int R = 2 * K + 1;
   const int chunk = blockIdx.x % nchunk;
   const int rr = blockIdx.x / nchunk;
@@ -47,19 +41,29 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   // Each wave reads one contiguous segment of VECS * 1 KB: its loads are
   // 1 KB apart, so concurrent loads spread over the HBM channels instead of
   // striding by the workgroup width.
-  float v[VECS][N];
+  uint4 w[VECS];
   const long e_base = (long)chunk * kChunk;
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   const long e_wave = e_base + (long)wid * VECS * kWave * N + (long)lane * N;
   const bool aligned = aligned16(row);
   if (aligned && e_base + kChunk <= V) {              // uniform: interior chunk
 #pragma unroll
-    for (int j = 0; j < VECS; ++j) load_vec_stream(row, e_wave + (long)j * kWave * N, v[j]);
+    for (int j = 0; j < VECS; ++j) w[j] = load_raw_stream(row, e_wave + (long)j * kWave * N);
   } else {
 #pragma unroll
     for (int j = 0; j < VECS; ++j)
-      load_vec_checked(row, e_wave + (long)j * kWave * N, V, aligned, v[j]);
+      w[j] = load_raw_checked(row, e_wave + (long)j * kWave * N, V, aligned);
   }
+
+  // Arrival counter of the end-of-workgroup combine, cleared while the loads
+  // are in flight: every wave waits on memory here anyway.
+  __shared__ float2 red[kRowThreads / kWave];
+  __shared__ int arrived;
+  if (threadIdx.x == 0) arrived = 0;
+  __syncthreads();
+  float v[VECS][N];
+#pragma unroll
+  for (int j = 0; j < VECS; ++j) unpack(w[j], v[j], T{});
 
   // Drafted token of this row (draft position k < K): its logit, read after
   // the stream is in flight and stored at the end.  zx[b][k] is the target

@@ -161,14 +161,6 @@ template <typename T> struct Raw8 {
   uint4 w[kSampPerThread / Elem<T>::kPerVec];
 };
 
-// Packed bit pattern of -inf, for elements past the end of the row.
-__device__ __forceinline__ uint32_t neg_inf_bits(float) { return 0xff800000u; }
-__device__ __forceinline__ uint32_t neg_inf_bits(bf16_t) { return 0xff80u; }
-__device__ __forceinline__ uint32_t elem_bits(const float* row, long e) {
-  return __float_as_uint(row[e]);
-}
-__device__ __forceinline__ uint32_t elem_bits(const bf16_t* row, long e) { return row[e]; }
-
 // This thread's 8 logits of the chunk starting at element c0, as raw words;
 // elements at or past V read as -inf.  The interior test is uniform per chunk.
 template <typename T>
@@ -182,22 +174,7 @@ __device__ __forceinline__ void load_raw8(const T* __restrict__ row, long c0, in
     for (int j = 0; j < NV; ++j) r.w[j] = *reinterpret_cast<const uint4*>(row + e0 + j * N);
   } else {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const long ej = e0 + j * N;
-      if (aligned && ej + N <= V) {
-        r.w[j] = *reinterpret_cast<const uint4*>(row + ej);
-      } else {
-        uint32_t e[N];
-#pragma unroll
-        for (int i = 0; i < N; ++i) e[i] = ej + i < V ? elem_bits(row, ej + i) : neg_inf_bits(T{});
-        if constexpr (N == 4) {
-          r.w[j] = make_uint4(e[0], e[1], e[2], e[3]);
-        } else {
-          r.w[j] = make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16,
-                              e[6] | e[7] << 16);
-        }
-      }
-    }
+    for (int j = 0; j < NV; ++j) r.w[j] = load_raw_checked(row, e0 + j * N, V, aligned);
   }
 }
 
