@@ -233,11 +233,12 @@ __device__ __forceinline__ double wave_sum4(double a, double b, double c, double
 // With d = e_t - e_d g and band = e_d g w: d > band means p > q for certain,
 // d < -band means p <= q for certain (the finish checks g against the exact
 // ratio to a quarter of w), anything else is a near tie.  Tokens with
-// e_t = 0 are never ties (their residual is 0).  Near ties are appended to an
-// LDS list as they are found and stored in token order (rank by id), so the
-// stored slots do not depend on scheduling.  tcnt counts this chunk's ties;
-// tcnt_next (the counter of a following chunk, if the caller loops) is
-// cleared between the two barriers, after its last reader.
+// e_t = 0 are never ties (their residual is 0).  The common path keeps only a
+// per-lane "some near tie" flag; a wave that has one recomputes its weights
+// and appends each near tie to an LDS list, stored in token order (rank by
+// id) so that the stored slots do not depend on scheduling.  tcnt counts
+// this chunk's ties; tcnt_next (the counter of a following chunk, if the
+// caller loops) is cleared between the two barriers, after its last reader.
 __device__ __forceinline__ void pass_chunk(const float* zt, const float* zd, bool rej, long e0,
                                            double mti, double mdi, double invT, double g,
                                            const double* tbl, double* dl, Tie* tl, int* tcnt,
@@ -246,6 +247,7 @@ __device__ __forceinline__ void pass_chunk(const float* zt, const float* zd, boo
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   double st = 0.0, sd = 0.0, at = 0.0, ad = 0.0;
   const double gw = g * kTieWindow;
+  bool anytie = false;
 #pragma unroll
   for (int i = 0; i < kSampPerThread; ++i) {
     const double et = weight_e(zt[i], mti, invT, tbl);
@@ -256,9 +258,22 @@ __device__ __forceinline__ void pass_chunk(const float* zt, const float* zd, boo
       const double dlt = fma(-ed, g, et);
       const double band = ed * gw;
       const bool sure = dlt > band;
-      at += sure ? et : 0.0;
-      ad += sure ? ed : 0.0;
-      if (!sure && dlt >= -band && et > 0.0) {
+      const double s01 = sure ? 1.0 : 0.0;           // weights are finite: fma adds or keeps
+      at = fma(et, s01, at);
+      ad = fma(ed, s01, ad);
+      anytie |= !sure && dlt >= -band && et > 0.0;
+    }
+  }
+  if (__ballot(anytie) != 0) {                       // rare: this wave has near ties
+    // Recompute the weights (the same arithmetic, so the same classification)
+    // and append each near tie to the chunk's list.
+#pragma unroll
+    for (int i = 0; i < kSampPerThread; ++i) {
+      const double et = weight_e(zt[i], mti, invT, tbl);
+      const double ed = weight_e(zd[i], mdi, invT, tbl);
+      const double dlt = fma(-ed, g, et);
+      const double band = ed * gw;
+      if (!(dlt > band) && dlt >= -band && et > 0.0) {
         const int s = atomicAdd(tcnt, 1);
         if (s < kTieCap) {
           Tie tv;
