@@ -43,4 +43,6 @@ from .specverify_oracle import (  # noqa: F401
     icdf,
     verify,
     expected_tokens_per_round,
+    acceptance_rate,
+    acceptance_rates,
 )

@@ -162,6 +162,45 @@ def icdf(w, u):
     return y, float(margin)
 
 
+def acceptance_rate(P, Q):
+    """beta = sum_x min(p(x), q(x)), the probability that a token drawn from
+    q is accepted for a fixed prefix.
+
+    [NW] "好草稿也要算得便宜" (the acceptance rate of a fixed prefix); the same
+    page's worked example sums the directly accepted mass to 0.8.  Works on
+    float arrays and on arrays of Fractions.
+    """
+    return np.minimum(P, Q).sum()
+
+
+def acceptance_rates(target, draft, draft_len, temperature, top_k=0, top_p=1.0, dtype="f32"):
+    """beta[b][k] = acceptance_rate(p_k, q_k) of every drafted position.
+
+    p_k and q_k are the processed distributions of target row k and draft
+    row k (the same ones verify() uses).  Positions at or after draft_len[b],
+    requests whose draft_len lies outside [0, K], and positions whose target
+    or draft row has no finite logit read -1.
+    """
+    B, K1, V = target.shape
+    K = K1 - 1
+    beta = np.full((B, K), -1.0)
+    for b in range(B):
+        nb = int(draft_len[b])
+        if not 0 <= nb <= K:
+            continue
+        for k in range(nb):
+            zt = widen_row(target[b, k], dtype)
+            zd = widen_row(draft[b, k], dtype)
+            if not (np.isfinite(zt).any() and np.isfinite(zd).any()):
+                continue
+            P, _ = processed_distribution(zt, temperature, top_k, top_p)
+            Q, _ = processed_distribution(zd, temperature, top_k, top_p)
+            if P is None or Q is None:
+                continue
+            beta[b, k] = float(acceptance_rate(P, Q))
+    return beta
+
+
 def expected_tokens_per_round(alpha, gamma):
     """E[N] = 1 + alpha + ... + alpha^gamma under i.i.d. acceptance.
 

@@ -21,13 +21,17 @@ MUTANTS = {
     "accept_not_strict": ("if u[b, k] < alphas[k]:", "if u[b, k] <= alphas[k]:"),
     "cdf_not_strict": ("hit = t < C", "hit = t <= C"),
     "bonus_from_last_row": ("y, margin = icdf(P[nb], uf)", "y, margin = icdf(P[-1] if False else P[0], uf)"),
-    "draft_row_shift": ("widen_row(draft[b, k], dtype)", "widen_row(draft[b, (k + 1) % draft.shape[1]], dtype)"),
+    "draft_row_shift": ("processed_distribution(widen_row(draft[b, k], dtype)",
+                        "processed_distribution(widen_row(draft[b, (k + 1) % draft.shape[1]], dtype)"),
     "temperature_multiplies": ("np.exp((z[kept] - m) / temperature)", "np.exp((z[kept] - m) * temperature)"),
     "topk_off_by_one": ("np.partition(z, V - k)[V - k]", "np.partition(z, V - k - 1)[V - k - 1]"),
     "residual_from_next_row": ("r = residual(P[stop], Q[stop])", "r = residual(P[stop + 1], Q[stop])"),
     "scan_does_not_stop": ("            stop, path = k, PATH_REJECT\n            break",
                            "            stop, path = k, PATH_REJECT"),
     "eos_ignored": ("            if x == eos_id:", "            if x == eos_id and False:"),
+    "beta_uses_max": ("return np.minimum(P, Q).sum()", "return np.maximum(P, Q).sum()"),
+    "beta_rows_swapped": ("zd = widen_row(draft[b, k], dtype)\n            if not",
+                          "zd = widen_row(draft[b, (k + 1) % draft.shape[1]], dtype)\n            if not"),
 }
 
 CHECKS = [
@@ -41,6 +45,8 @@ CHECKS = [
     "test_exhaustive_round_law_ragged_bonus_row",
     "test_strict_accept_never_takes_a_zero_probability_token",
     "test_eos_truncation_invariant",
+    "test_acceptance_rate_worked_example",
+    "test_acceptance_rates_equal_expected_acceptance_per_position",
 ]
 
 
@@ -57,6 +63,8 @@ def _run_check(name):
     fn = getattr(pins, name)
     if name == "test_worked_example_replay":
         fn("f64", 1e-12)
+    elif name == "test_acceptance_rates_equal_expected_acceptance_per_position":
+        fn(0, 1.0)
     else:
         fn()
 

@@ -485,3 +485,62 @@ def test_strict_accept_never_takes_a_zero_probability_token():
                  np.array([[0.0]], np.float32), np.array([0.1], np.float32), 1.0, dtype="f64")
     assert r["alpha"][0, 0] == 0.0 and r["path"][0] == O.PATH_REJECT
     assert r["out_tokens"][0, 0] in (0, 1)
+
+
+# ---------------------------------------------------------------------------
+# nickwang.xyz "推测解码：草稿、验证与实际加速", section "好草稿也要算得便宜":
+# the acceptance rate of a fixed prefix
+# ---------------------------------------------------------------------------
+
+def test_acceptance_rate_worked_example():
+    # The three-token example of "算完三个 token 的全部概率" prints a total
+    # acceptance rate of 0.8 (accepted mass 0.5 + 0.1 + 0.2).
+    g = _golden("nw_worked_example.json")
+    p, q = _fr(g["p"]), _fr(g["q"])
+    assert O.acceptance_rate(p, q) == F(g["acceptance_printed"]).limit_denominator(1000)
+    pf = np.array([float(x) for x in p]); qf = np.array([float(x) for x in q])
+    assert abs(O.acceptance_rate(pf, qf) - g["acceptance_printed"]) < 1e-15
+
+
+def test_acceptance_rate_is_one_minus_total_variation():
+    # Closed form: for distributions p, q, sum min(p, q) = 1 - (1/2) sum |p - q|
+    # (min(a, b) = (a + b - |a - b|) / 2 summed over x); hence symmetric, 1 for
+    # p = q and 0 for disjoint supports.
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        V = int(rng.integers(2, 8))
+        p, q = _rand_dist(rng, V, 0.3), _rand_dist(rng, V, 0.3)
+        tv = sum(abs(a - b) for a, b in zip(p, q)) / 2
+        assert O.acceptance_rate(p, q) == 1 - tv
+        assert O.acceptance_rate(q, p) == O.acceptance_rate(p, q)
+        assert O.acceptance_rate(p, p) == 1
+    a = _fr(["1/2", "1/2", "0", "0"])
+    b = _fr(["0", "0", "1/4", "3/4"])
+    assert O.acceptance_rate(a, b) == 0
+
+
+@pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (3, 1.0), (4, 0.8)])
+def test_acceptance_rates_equal_expected_acceptance_per_position(top_k, top_p):
+    # For every drafted position of a batch, beta equals the probability that
+    # the verification accepts a token drawn from q there: sum_x q(x) alpha(x)
+    # with the oracle's alpha on the same processed rows.  Positions at or
+    # after draft_len, an out-of-range draft_len and a row with no finite
+    # logit read -1.
+    rng = np.random.default_rng(31 + top_k)
+    B, K, V = 5, 3, 7
+    target = rng.normal(0, 1.5, size=(B, K + 1, V)).astype(np.float32)
+    draft = (target[:, :K] + rng.normal(0, 0.8, size=(B, K, V))).astype(np.float32)
+    draft_len = np.array([3, 1, 0, 2, 9], dtype=np.int32)
+    draft[3, 1, :] = -np.inf
+    T = 0.9
+    beta = O.acceptance_rates(target, draft, draft_len, T, top_k, top_p, "f32")
+    for b in range(B):
+        for k in range(K):
+            nb = int(draft_len[b])
+            if not 0 <= nb <= K or k >= nb or (b, k) == (3, 1):
+                assert beta[b, k] == -1.0
+                continue
+            P, _ = O.processed_distribution(target[b, k].astype(np.float64), T, top_k, top_p)
+            Q, _ = O.processed_distribution(draft[b, k].astype(np.float64), T, top_k, top_p)
+            expect = sum(Q[x] * O.accept_prob(P, Q, x) for x in range(V) if Q[x] > 0)
+            assert abs(beta[b, k] - expect) < 1e-12
