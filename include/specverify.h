@@ -170,6 +170,31 @@ SPECV_API specv_status_t specv_sample(const void *logits, specv_dtype_t dtype, c
                                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Per-position acceptance rates, a diagnostic: beta[b][k] =
+ * sum_x min(p_k(x), q_k(x)) for every drafted position k < draft_len[b], the
+ * probability that a token drawn from q_k is accepted at that position
+ * (nickwang.xyz, "推测解码：草稿、验证与实际加速", section "好草稿也要算得便宜").
+ * p_k, q_k are the same processed distributions as in specv_verify.  It
+ * reads both rows of every drafted position (a second pass over them when
+ * run next to specv_verify); draft tokens and uniforms are not needed.
+ *
+ *  target_logits, draft_logits, draft_len: as for specv_verify
+ *  beta        [B][K] float32, device: the rates; -1 where k >= draft_len[b],
+ *              draft_len[b] is outside [0, K] or a row has no finite logit
+ *              (or, with filters, exceeds the kept-list capacity)
+ *  workspace   at least specv_workspace_bytes(B, K, V, dtype, top_k, top_p)
+ *
+ * Float32 without filters (relative error ~1e-7), float64 with them.  Same
+ * conventions, limits and status codes as specv_verify.  Asynchronous.
+ */
+SPECV_API specv_status_t specv_acceptance_rates(const void *target_logits,
+                                                const void *draft_logits, specv_dtype_t dtype,
+                                                const int32_t *draft_len, int B, int K, int V,
+                                                float temperature, int top_k, float top_p,
+                                                float *beta, void *workspace,
+                                                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Timing variant of specv_verify, for benchmarks: identical work, plus
  * hipEventRecord on `stream` of events[0] before the first kernel launch and
  * of events[i+1] after kernel stage i.  `events` holds specv_num_stages(f) + 1

@@ -60,6 +60,9 @@ def load_library():
         lib.specv_sample.argtypes = [c_vp, c_int, c_vp, c_int, c_int, c_float, c_int, c_float, c_vp,
                                      c_vp, c_size, c_vp]
         lib.specv_sample.restype = c_int
+        lib.specv_acceptance_rates.argtypes = [c_vp, c_vp, c_int, c_vp, c_int, c_int, c_int,
+                                               c_float, c_int, c_float, c_vp, c_vp, c_size, c_vp]
+        lib.specv_acceptance_rates.restype = c_int
         lib.specv_num_stages.argtypes = [c_int]
         lib.specv_num_stages.restype = c_int
         lib.specv_stage_name.argtypes = [c_int, c_int]
@@ -132,6 +135,40 @@ def sample(logits, u, temperature=1.0, top_k=0, top_p=1.0, *, out_tokens=None, w
     if st != SPECV_OK:
         raise SpecVerifyError(st, status_string(st))
     return out_tokens
+
+
+def acceptance_rates(target_logits, draft_logits, draft_len, temperature=1.0, top_k=0, top_p=1.0,
+                     *, beta=None, workspace=None, stream=None):
+    """Per-position acceptance rates sum_x min(p_k(x), q_k(x)) of a batch
+    (target [B, K+1, V], draft [B, K, V], draft_len [B] int32), as a [B, K]
+    float32 tensor; -1 where a position was not drafted or a row has no
+    finite logit.  Asynchronous on ``stream``."""
+    lib = load_library()
+    dev = target_logits.device
+    if dev.type != "cuda" or target_logits.dim() != 3:
+        raise ValueError("target_logits must be a [B, K+1, V] GPU tensor")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits", None, (B, K + 1, V), dev)
+    _check(draft_logits, "draft_logits", target_logits.dtype, (B, K, V), dev)
+    _check(draft_len, "draft_len", torch.int32, (B,), dev)
+    if beta is None:
+        beta = torch.empty((B, K), dtype=torch.float32, device=dev)
+    _check(beta, "beta", torch.float32, (B, K), dev)
+    nbytes = int(lib.specv_workspace_bytes(B, K, V, code, int(top_k), float(top_p)))
+    if workspace is None:
+        workspace = _workspace(dev, nbytes)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib.specv_acceptance_rates(_ptr(target_logits), _ptr(draft_logits), code,
+                                    _ptr(draft_len), B, K, V, float(temperature), int(top_k),
+                                    float(top_p), _ptr(beta), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    ctypes.c_void_p(stream.cuda_stream))
+    if st != SPECV_OK:
+        raise SpecVerifyError(st, status_string(st))
+    return beta
 
 
 def bench_row_stats(sets, workspace, reps, temperature=1.0, stream=None, start=None, stop=None):

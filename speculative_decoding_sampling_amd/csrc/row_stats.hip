@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   // row's, zx[b][K + k] the draft row's.
   int gx = -1;
   float gz = 0.f;
-  if (k < K) {
+  if (tokens && k < K) {
     const int x = tokens[(size_t)b * K + k];
     if (x >= 0 && x < V && x >= e_base && x < e_base + kChunk) {
       gx = x;

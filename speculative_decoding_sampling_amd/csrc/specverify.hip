@@ -37,6 +37,10 @@ hipError_t launch_sample_finish(bool bf16, const void* tgt, const void* dft, con
                                 const ChunkRec* recs, const Tie* ties, int* out_tokens,
                                 double* rmass_out, hipStream_t stream);
 hipError_t launch_exp64_selftest(const double* x, double* y, int n, hipStream_t stream);
+hipError_t launch_beta(bool bf16, bool filt, const void* tgt, const void* dft,
+                       const int* draft_len, int B, int K, int V, int nch_row, float c,
+                       double invT, const float2* part, const FiltRow* frows, const Kept* kept,
+                       float* beta_part, float* beta, hipStream_t stream);
 
 // Kernel stages of one call, in launch order (specv_verify_timed records an
 // event after each): without filters, and with top-k / top-p.
@@ -55,6 +59,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Without filters:
 //   row partials   float2   [B][2K+1][nch_row]        (max, partial normaliser)
 //   drafted logits float    [B][2K]                   (target rows, then draft rows)
+//   beta partials  float    [B][K][nch_row]           (acceptance-rate chunk sums)
 //   plans          Plan     [B]
 //   chunk records  ChunkRec [B][nch_samp]             (fp64 sums per sampler chunk)
 //   near ties      Tie      [B][nch_samp][kTieCap]
@@ -67,7 +72,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   bool filt = false;
   int nch_row = 0, nch_samp = 0, nch_filt = 0, cap = 0;
-  size_t off_row = 0, off_zx = 0, off_plan = 0, off_recs = 0, off_ties = 0;
+  size_t off_row = 0, off_zx = 0, off_beta = 0, off_plan = 0, off_recs = 0, off_ties = 0;
   size_t off_cand = 0, off_counts = 0, off_frows = 0, off_kept = 0, total = 0;
 };
 
@@ -86,6 +91,8 @@ Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p) {
     off = align_up(off + (size_t)B * R * L.nch_row * sizeof(float2));
     L.off_zx = off;
     off = align_up(off + (size_t)B * 2 * K * sizeof(float));
+    L.off_beta = off;
+    off = align_up(off + (size_t)B * K * L.nch_row * sizeof(float));
     L.off_plan = off;
     off = align_up(off + (size_t)B * sizeof(Plan));
     L.off_recs = off;
@@ -315,6 +322,50 @@ specv_status_t specv_sample(const void* logits, specv_dtype_t dtype, const float
   return specv::run(logits, nullptr, dtype, nullptr, nullptr, nullptr, u, R, 0, V, temperature,
                     top_k, top_p, -1, out_tokens, nullptr, workspace, workspace_bytes, stream,
                     nullptr, nullptr, nullptr, nullptr, nullptr, true);
+}
+
+specv_status_t specv_acceptance_rates(const void* target_logits, const void* draft_logits,
+                                      specv_dtype_t dtype, const int32_t* draft_len, int B,
+                                      int K, int V, float temperature, int top_k, float top_p,
+                                      float* beta, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  using namespace specv;
+  specv_status_t st = check_sizes(B, K, V, dtype, top_k, top_p);
+  if (st != SPECV_OK) return st;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SPECV_EINVAL;
+  const size_t esz = dtype == SPECV_BF16 ? 2 : 4;
+  if (!target_logits || !draft_len || !beta || (K > 0 && !draft_logits)) return SPECV_EINVAL;
+  if (misaligned(target_logits, esz) || (draft_logits && misaligned(draft_logits, esz)) ||
+      misaligned(draft_len, 4) || misaligned(beta, 4))
+    return SPECV_EINVAL;
+  const bool bf16 = dtype == SPECV_BF16;
+  const Layout L = make_layout(B, K, V, bf16, top_k, top_p);
+  if (!workspace || misaligned(workspace, 16) || workspace_bytes < L.total) return SPECV_EWORKSPACE;
+  if (K == 0) return SPECV_OK;
+  char* ws = static_cast<char*>(workspace);
+  const float c = (float)(1.4426950408889634 / (double)temperature);
+  const double invT = 1.0 / (double)temperature;
+  hipError_t e;
+  if (!L.filt) {
+    float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
+    e = launch_row_stats(bf16, target_logits, draft_logits, draft_len, nullptr, B, K, V,
+                         L.nch_row, c, row_part, nullptr, stream);
+    if (e == hipSuccess)
+      e = launch_beta(bf16, false, target_logits, draft_logits, draft_len, B, K, V, L.nch_row,
+                      c, invT, row_part, nullptr, nullptr,
+                      reinterpret_cast<float*>(ws + L.off_beta), beta, stream);
+  } else {
+    uint64_t* cand = reinterpret_cast<uint64_t*>(ws + L.off_cand);
+    int* counts = reinterpret_cast<int*>(ws + L.off_counts);
+    FiltRow* frows = reinterpret_cast<FiltRow*>(ws + L.off_frows);
+    Kept* kept = reinterpret_cast<Kept*>(ws + L.off_kept);
+    e = launch_filter(bf16, target_logits, draft_logits, draft_len, B, K, V, L.nch_filt, top_k,
+                      top_p, invT, cand, counts, frows, kept, stream, nullptr);
+    if (e == hipSuccess)
+      e = launch_beta(bf16, true, target_logits, draft_logits, draft_len, B, K, V, 0, c, invT,
+                      nullptr, frows, kept, nullptr, beta, stream);
+  }
+  return e == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }
 
 specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream_t stream) {

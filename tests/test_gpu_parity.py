@@ -431,3 +431,54 @@ def test_full_round_with_gpu_drawn_drafts():
     y, yo = assert_sample_parity(rows, ud.reshape(-1), w.T, 0, 1.0, w.dtype, label="round drafts")
     w.draft_tokens = y.reshape(w.B, w.K).astype(np.int32)
     assert_parity(w, label="verify GPU-drawn drafts")
+
+
+# ---------------------------------------------------------------------------
+# Per-position acceptance rates: specv_acceptance_rates.
+
+def assert_beta_parity(w, tol, label=""):
+    a = upload(w, DEV)
+    beta = binding.acceptance_rates(a["target_logits"], a["draft_logits"], a["draft_len"], w.T,
+                                    w.top_k, w.top_p)
+    torch.cuda.synchronize()
+    g = beta.cpu().numpy().astype(np.float64)
+    o = O.acceptance_rates(w.target, w.draft, w.draft_len, f32(w.T), w.top_k, f32(w.top_p),
+                           w.dtype)
+    drafted = o >= 0
+    assert np.array_equal(g < 0, ~drafted), "undrafted / error positions differ"
+    err = np.abs(g[drafted] - o[drafted])
+    bad = []
+    for b, k in zip(*np.nonzero(drafted & (np.abs(g - o) > tol))):
+        # with top-p, a cut within 1e-10 of top_p may keep a different set
+        marg = [O.processed_distribution(O.widen_row(r, w.dtype), f32(w.T), w.top_k,
+                                         f32(w.top_p))[1]["topp_margin"]
+                for r in (w.target[b, k], w.draft[b, k])]
+        if min(marg) > O.TOPP_FLAG_ABS:
+            bad.append((int(b), int(k), float(g[b, k]), float(o[b, k])))
+    print(f"[beta] {label} cfg={w.cfg} B={w.B} K={w.K} V={w.V} {w.dtype}: "
+          f"{int(drafted.sum())} positions, max err {err.max() if err.size else 0:.2e}, "
+          f"mean beta {o[drafted].mean() if drafted.any() else 0:.4f}", flush=True)
+    assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("cfg,B", [(1, None), (2, None), (3, 8), (5, 16)])
+def test_acceptance_rates_unfiltered(cfg, B):
+    assert_beta_parity(make_workload(cfg, B=B), 1e-5)
+
+
+def test_acceptance_rates_filtered():
+    # float64 inside; the float32 result is within half an ulp (6e-8 at <= 1).
+    assert_beta_parity(make_workload(4, B=6, draft_sampler=oracle_sampler), 1e-7)
+
+
+def test_acceptance_rates_identical_rows_and_ragged():
+    # draft == target gives beta = 1; positions past draft_len give -1.
+    w = make_workload(5, B=16)
+    w.draft = np.ascontiguousarray(w.target[:, :w.K])
+    assert_beta_parity(w, 1e-5, label="draft == target")
+    a = upload(w, DEV)
+    g = binding.acceptance_rates(a["target_logits"], a["draft_logits"], a["draft_len"],
+                                 w.T).cpu().numpy()
+    for b in range(w.B):
+        nb = int(w.draft_len[b])
+        assert np.all(np.abs(g[b, :nb] - 1.0) < 1e-5) and np.all(g[b, nb:] == -1.0)

@@ -36,7 +36,8 @@ def test_header_declares_the_api():
     assert set(names) == {"specv_workspace_bytes", "specv_verify", "specv_verify_debug",
                           "specv_verify_timed", "specv_num_stages", "specv_stage_name",
                           "specv_status_string", "specv_version", "specv_selftest_exp64",
-                          "specv_bench_row_stats", "specv_sample"}, names
+                          "specv_bench_row_stats", "specv_sample",
+                          "specv_acceptance_rates"}, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -168,3 +169,27 @@ def test_sample_rejects_bad_arguments(lib):
     assert call(p=0.0) == 1
     assert call(k=10, p=0.5, wsb=16) == 2            # filtered workspace too small
     assert call(wsb=16) == 2
+
+
+def test_acceptance_rates_reject_bad_arguments(lib):
+    f = lib.specv_acceptance_rates
+    vp, i, fl, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    f.argtypes = [vp, vp, i, vp, i, i, i, fl, i, fl, vp, vp, sz, vp]
+    f.restype = i
+    ok = dict(t=16, d=16, dtype=1, dl=16, B=2, K=3, V=1000, T=1.0, k=0, p=1.0, beta=16, ws=16,
+              wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["t"], a["d"], a["dtype"], a["dl"], a["B"], a["K"], a["V"], a["T"], a["k"],
+                 a["p"], a["beta"], a["ws"], a["wsb"], None)
+
+    assert call(B=0) == 1
+    assert call(dl=None) == 1
+    assert call(beta=None) == 1
+    assert call(d=None) == 1
+    assert call(T=0.0) == 1
+    assert call(k=0, p=0.5) == 4                     # top-p without top-k
+    assert call(wsb=16) == 2
+    assert call(K=0, d=None, wsb=1 << 20) == 0       # nothing to compute, nothing launched
