@@ -259,12 +259,13 @@ def test_bf16_widening():
 # Whole-round law, exhaustively: every decision interval of every uniform
 # ---------------------------------------------------------------------------
 
-def _exhaustive_round(p_rows, q_rows, draft_len, T=1.0):
+def _exhaustive_round(p_rows, q_rows, draft_len, T=1.0, with_drafts=False):
     """Exact output law of one request, found by running ``O.verify`` once per
     cell of the uniforms' decision partition, weighted by the cell's size.
 
     p_rows: K+1 target distributions, q_rows: K draft distributions (float64).
-    Returns a list of (weight, out_tokens, n_emitted).
+    Returns a list of (weight, out_tokens, n_emitted), with the drafted
+    tokens appended to each tuple when ``with_drafts``.
     """
     K = len(q_rows)
     V = len(p_rows[0])
@@ -310,6 +311,9 @@ def _exhaustive_round(p_rows, q_rows, draft_len, T=1.0):
     uf = np.array([r[3] for r in rows], dtype=np.float32)
     dl = np.full(B, draft_len, dtype=np.int32)
     res = O.verify(tgt, dft, toks, dl, uu, uf, T, dtype="f64")
+    if with_drafts:
+        return [(rows[i][0], res["out_tokens"][i], int(res["n_emitted"][i]), toks[i])
+                for i in range(B)]
     return [(rows[i][0], res["out_tokens"][i], int(res["n_emitted"][i])) for i in range(B)]
 
 
