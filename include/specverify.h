@@ -195,6 +195,92 @@ SPECV_API specv_status_t specv_acceptance_rates(const void *target_logits,
                                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Statistics of one verified round (nickwang.xyz, "推测解码：草稿、验证与实际加速",
+ * section "好草稿也要算得便宜": count the tokens a round really commits; its
+ * measurement table under "在相同负载和质量下比较" keeps the draft acceptance
+ * apart from the useful output).  The inputs are one specv_verify call's
+ * inputs and outputs, unchanged.
+ *
+ *  draft_tokens, draft_len   [B][K], [B] int32, device: as passed to specv_verify
+ *                            (draft_tokens may be NULL when K == 0)
+ *  out_tokens, n_emitted     [B][K+1], [B] int32, device: as specv_verify wrote them
+ *  beta        [B][K] float32, device, or NULL: rates from specv_acceptance_rates
+ *  accepted    [B] int32, device, or NULL: accepted drafts of each request, i.e.
+ *              the emitted tokens that are drafts the verifier accepted (all
+ *              but the last, or all when an accepted EOS stopped the round);
+ *              -1 for a failed round (n_emitted < 1 or inconsistent with
+ *              draft_len).  When the verifier had to fall back from an empty
+ *              residual (a flagged case, impossible in exact arithmetic) and
+ *              redrew the rejected token, that round reads as an EOS stop.
+ *  expected    [B] float32, device, or NULL (needs beta): E[N] of the
+ *              request's round if its drafted positions accepted independently
+ *              with rates beta[b][0..draft_len-1]: 1 + b0 + b0 b1 + ...;
+ *              -1 when draft_len is outside [0, K] or a rate is negative
+ *  totals      [SPECV_NUM_TOTALS] int64, device, or NULL: batch sums indexed by
+ *              specv_total_t (failed rounds count only as errors)
+ *
+ * B >= 1, 0 <= K <= SPECV_MAX_K; arrays element-aligned.  SPECV_EINVAL for
+ * bad sizes, NULL required pointers or expected without beta.
+ * Asynchronous on `stream`; allocates nothing.
+ */
+typedef enum {
+  SPECV_TOTAL_REQUESTS = 0,     /* rounds that verified */
+  SPECV_TOTAL_ERRORS = 1,       /* failed rounds */
+  SPECV_TOTAL_DRAFTED = 2,      /* sum of draft_len */
+  SPECV_TOTAL_ACCEPTED = 3,     /* sum of accepted drafts */
+  SPECV_TOTAL_EMITTED = 4,      /* sum of n_emitted */
+  SPECV_TOTAL_EOS_STOPS = 5,    /* rounds stopped by an accepted EOS */
+  SPECV_TOTAL_FULL_ACCEPTS = 6, /* rounds that accepted every draft (a bonus was drawn) */
+  SPECV_TOTAL_REJECTIONS = 7,   /* rounds that ended on a rejection (a correction) */
+  SPECV_NUM_TOTALS = 8
+} specv_total_t;
+
+SPECV_API specv_status_t specv_round_stats(const int32_t *draft_tokens, const int32_t *draft_len,
+                                           const int32_t *out_tokens, const int32_t *n_emitted,
+                                           const float *beta, int B, int K, int32_t *accepted,
+                                           float *expected, int64_t *totals, hipStream_t stream);
+
+/* Largest monitor window, in rounds. */
+#define SPECV_MAX_WINDOW 4096
+
+/*
+ * Adaptive draft length (tbxsx.cn, "推测解码采样验证优化策略 —— 深度调研报告",
+ * section "4. 实现逻辑": an acceptance-rate monitor over a window of rounds, and
+ * a draft length that moves one step up when the rate is above 0.85, at most
+ * to the maximum draft length, and one step down when it is below 0.60, at
+ * least to 1).  Every request has its own window in `state`: the ratio of its
+ * accepted drafts (as specv_round_stats counts them) to its drafted positions
+ * over its last `window` verified rounds.  The thresholds are applied exactly
+ * as 17/20 and 3/5, strictly.
+ *
+ * specv_monitor_state_bytes(B, window): bytes of state for B requests (0 when
+ *   B < 1 or window is outside [1, SPECV_MAX_WINDOW]).  The caller owns it:
+ *   device memory, 16-byte aligned.
+ * specv_monitor_reset: empties every window; needed before the first update
+ *   and when window changes.  A fill kernel, so it may be captured in a graph.
+ * specv_monitor_update, after a specv_verify call with the same B and K:
+ *   draft_tokens, draft_len, out_tokens, n_emitted  as for specv_round_stats
+ *   next_draft_len [B] int32, device: the draft length of each request's next
+ *                 round, in [1, max_k]: draft_len[b] moved by the rule (kept
+ *                 as it is while the window has no drafted position).  It may
+ *                 be the draft_len array itself (updated in place).
+ *   rate          [B] float64, device, or NULL: the window's rate after this
+ *                 round, the correctly rounded quotient; -1 when undefined
+ *   1 <= max_k <= SPECV_MAX_K.  A failed round adds nothing to its window.
+ *   A state header that no reset wrote restarts that request's window.
+ * Both asynchronous on `stream`; they allocate nothing.  Updates of one state
+ * must not overlap (use one stream).
+ */
+SPECV_API size_t specv_monitor_state_bytes(int B, int window);
+SPECV_API specv_status_t specv_monitor_reset(void *state, int B, int window, hipStream_t stream);
+SPECV_API specv_status_t specv_monitor_update(const int32_t *draft_tokens,
+                                              const int32_t *draft_len,
+                                              const int32_t *out_tokens,
+                                              const int32_t *n_emitted, int B, int K, int max_k,
+                                              int window, void *state, int32_t *next_draft_len,
+                                              double *rate, hipStream_t stream);
+
+/*
  * Timing variant of specv_verify, for benchmarks: identical work, plus
  * hipEventRecord on `stream` of events[0] before the first kernel launch and
  * of events[i+1] after kernel stage i.  `events` holds specv_num_stages(f) + 1

@@ -18,6 +18,9 @@ Sources the oracle follows (cited by page title and section):
 * [BZ] bowenzhou.top, "投机采样" (notes): sections "机制：起草-验证-接受",
   "收益账" and "深入推导" (distribution-preservation identity).
 
+``oracle.round_policy`` holds the round statistics and the adaptive draft
+length ([TB] "4. 实现逻辑"; [NW] "好草稿也要算得便宜").
+
 Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, exact rational arithmetic or brute force.
 """

@@ -113,6 +113,23 @@ def expected_tokens_given_rates(rates):
     return total
 
 
+def expected_tokens_per_request(beta, draft_len):
+    """E[N] of every request of a batch from its rates beta [B][K] (float32,
+    -1 where undefined) over its drafted positions, as float32; -1 where
+    draft_len is outside [0, K] or a drafted position has no rate."""
+    beta = np.asarray(beta, dtype=np.float32)
+    B, K = beta.shape
+    out = np.full(B, -1.0, dtype=np.float32)
+    for b in range(B):
+        nb = int(draft_len[b])
+        if nb < 0 or nb > K:
+            continue
+        rates = beta[b, :nb].astype(np.float64)
+        if np.all(rates >= 0.0):
+            out[b] = np.float32(expected_tokens_given_rates(rates))
+    return out
+
+
 def adjust_k(rate, k, max_k):
     """[TB] "4. 实现逻辑", _adjust_K: one step up above 0.85 (at most max_k),
     one step down below 0.60 (at least 1); rate None keeps k.  The result is

@@ -18,6 +18,9 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecver
 SPECV_F32, SPECV_BF16 = 0, 1
 SPECV_OK, SPECV_EINVAL, SPECV_EWORKSPACE, SPECV_EHIP, SPECV_EUNSUPPORTED = 0, 1, 2, 3, 4
 MAX_K = 63
+MAX_WINDOW = 4096
+TOTAL_FIELDS = ("requests", "errors", "drafted", "accepted", "emitted", "eos_stops",
+                "full_accepts", "rejections")
 
 PATH_ERROR, PATH_REJECT, PATH_BONUS, PATH_EOS = -1, 0, 1, 2
 
@@ -63,6 +66,16 @@ def load_library():
         lib.specv_acceptance_rates.argtypes = [c_vp, c_vp, c_int, c_vp, c_int, c_int, c_int,
                                                c_float, c_int, c_float, c_vp, c_vp, c_size, c_vp]
         lib.specv_acceptance_rates.restype = c_int
+        lib.specv_round_stats.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_vp, c_vp,
+                                          c_vp, c_vp]
+        lib.specv_round_stats.restype = c_int
+        lib.specv_monitor_state_bytes.argtypes = [c_int, c_int]
+        lib.specv_monitor_state_bytes.restype = c_size
+        lib.specv_monitor_reset.argtypes = [c_vp, c_int, c_int, c_vp]
+        lib.specv_monitor_reset.restype = c_int
+        lib.specv_monitor_update.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                             c_vp, c_vp, c_vp, c_vp]
+        lib.specv_monitor_update.restype = c_int
         lib.specv_num_stages.argtypes = [c_int]
         lib.specv_num_stages.restype = c_int
         lib.specv_stage_name.argtypes = [c_int, c_int]
@@ -169,6 +182,96 @@ def acceptance_rates(target_logits, draft_logits, draft_len, temperature=1.0, to
     if st != SPECV_OK:
         raise SpecVerifyError(st, status_string(st))
     return beta
+
+
+def _round_args(draft_tokens, draft_len, out_tokens, n_emitted):
+    dev = out_tokens.device
+    if dev.type != "cuda" or out_tokens.dim() != 2:
+        raise ValueError("out_tokens must be a [B, K+1] GPU tensor")
+    B, K1 = out_tokens.shape
+    K = K1 - 1
+    _check(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(draft_len, "draft_len", torch.int32, (B,), dev)
+    _check(n_emitted, "n_emitted", torch.int32, (B,), dev)
+    return dev, B, K
+
+
+def round_stats(draft_tokens, draft_len, out_tokens, n_emitted, beta=None, *, accepted=None,
+                expected=None, totals=None, stream=None):
+    """Statistics of one verified round from a ``verify`` call's inputs and
+    outputs.  Returns (accepted [B] int32, expected [B] float32 or None,
+    totals [8] int64 in ``TOTAL_FIELDS`` order); ``expected`` (E[N] from the
+    per-position rates) needs ``beta`` from ``acceptance_rates``.
+    Asynchronous on ``stream``."""
+    lib = load_library()
+    dev, B, K = _round_args(draft_tokens, draft_len, out_tokens, n_emitted)
+    if accepted is None:
+        accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(accepted, "accepted", torch.int32, (B,), dev)
+    if beta is not None:
+        _check(beta, "beta", torch.float32, (B, K), dev)
+        if expected is None:
+            expected = torch.empty(B, dtype=torch.float32, device=dev)
+    if expected is not None:
+        _check(expected, "expected", torch.float32, (B,), dev)
+    if totals is None:
+        totals = torch.empty(len(TOTAL_FIELDS), dtype=torch.int64, device=dev)
+    _check(totals, "totals", torch.int64, (len(TOTAL_FIELDS),), dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib.specv_round_stats(_ptr(draft_tokens), _ptr(draft_len), _ptr(out_tokens),
+                               _ptr(n_emitted), _ptr(beta), B, K, _ptr(accepted), _ptr(expected),
+                               _ptr(totals), ctypes.c_void_p(stream.cuda_stream))
+    if st != SPECV_OK:
+        raise SpecVerifyError(st, status_string(st))
+    return accepted, expected, totals
+
+
+class AcceptRateMonitor:
+    """Per-request acceptance-rate windows and the adaptive draft length, held
+    in device memory (``specv_monitor_*``).  ``update`` takes one verified
+    round and returns the next round's draft lengths, without a host sync."""
+
+    def __init__(self, batch, window, max_k, device, stream=None):
+        self.lib = load_library()
+        self.B, self.window, self.max_k = int(batch), int(window), int(max_k)
+        self.device = torch.device(device)
+        nbytes = int(self.lib.specv_monitor_state_bytes(self.B, self.window))
+        if nbytes == 0 or not 1 <= self.max_k <= MAX_K:
+            raise ValueError(f"bad monitor sizes: batch={batch} window={window} max_k={max_k}")
+        self.state = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=self.device)
+        self.reset(stream)
+
+    def _stream(self, stream):
+        return torch.cuda.current_stream(self.device) if stream is None else stream
+
+    def reset(self, stream=None):
+        st = self.lib.specv_monitor_reset(_ptr(self.state), self.B, self.window,
+                                          ctypes.c_void_p(self._stream(stream).cuda_stream))
+        if st != SPECV_OK:
+            raise SpecVerifyError(st, status_string(st))
+
+    def update(self, draft_tokens, draft_len, out_tokens, n_emitted, *, next_draft_len=None,
+               rate=None, stream=None):
+        """Returns (next_draft_len [B] int32, rate [B] float64); pass
+        ``next_draft_len=draft_len`` to update the draft lengths in place."""
+        dev, B, K = _round_args(draft_tokens, draft_len, out_tokens, n_emitted)
+        if B != self.B or dev != self.device:
+            raise ValueError(f"monitor holds {self.B} requests on {self.device}")
+        if next_draft_len is None:
+            next_draft_len = torch.empty(B, dtype=torch.int32, device=dev)
+        _check(next_draft_len, "next_draft_len", torch.int32, (B,), dev)
+        if rate is None:
+            rate = torch.empty(B, dtype=torch.float64, device=dev)
+        _check(rate, "rate", torch.float64, (B,), dev)
+        st = self.lib.specv_monitor_update(_ptr(draft_tokens), _ptr(draft_len), _ptr(out_tokens),
+                                           _ptr(n_emitted), B, K, self.max_k, self.window,
+                                           _ptr(self.state), _ptr(next_draft_len), _ptr(rate),
+                                           ctypes.c_void_p(self._stream(stream).cuda_stream))
+        if st != SPECV_OK:
+            raise SpecVerifyError(st, status_string(st))
+        return next_draft_len, rate
 
 
 def bench_row_stats(sets, workspace, reps, temperature=1.0, stream=None, start=None, stop=None):

@@ -41,6 +41,16 @@ hipError_t launch_beta(bool bf16, bool filt, const void* tgt, const void* dft,
                        const int* draft_len, int B, int K, int V, int nch_row, float c,
                        double invT, const float2* part, const FiltRow* frows, const Kept* kept,
                        float* beta_part, float* beta, hipStream_t stream);
+hipError_t launch_round_stats(const int32_t* draft_tokens, const int32_t* draft_len,
+                              const int32_t* out_tokens, const int32_t* n_emitted,
+                              const float* beta, int B, int K, int32_t* accepted, float* expected,
+                              long long* totals, hipStream_t stream);
+size_t monitor_state_bytes(int B, int window);
+hipError_t launch_monitor_reset(void* state, int B, int window, hipStream_t stream);
+hipError_t launch_monitor_update(const int32_t* draft_tokens, const int32_t* draft_len,
+                                 const int32_t* out_tokens, const int32_t* n_emitted, int B,
+                                 int K, int max_k, int window, void* state,
+                                 int32_t* next_draft_len, double* rate, hipStream_t stream);
 
 // Kernel stages of one call, in launch order (specv_verify_timed records an
 // event after each): without filters, and with top-k / top-p.
@@ -368,6 +378,56 @@ specv_status_t specv_acceptance_rates(const void* target_logits, const void* dra
   return e == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }
 
+specv_status_t specv_round_stats(const int32_t* draft_tokens, const int32_t* draft_len,
+                                 const int32_t* out_tokens, const int32_t* n_emitted,
+                                 const float* beta, int B, int K, int32_t* accepted,
+                                 float* expected, int64_t* totals, hipStream_t stream) {
+  using namespace specv;
+  if (B < 1 || K < 0 || K > SPECV_MAX_K) return SPECV_EINVAL;
+  if ((K > 0 && !draft_tokens) || !draft_len || !out_tokens || !n_emitted) return SPECV_EINVAL;
+  if (expected && !beta) return SPECV_EINVAL;
+  if ((draft_tokens && misaligned(draft_tokens, 4)) || misaligned(draft_len, 4) ||
+      misaligned(out_tokens, 4) || misaligned(n_emitted, 4) || (beta && misaligned(beta, 4)) ||
+      (accepted && misaligned(accepted, 4)) || (expected && misaligned(expected, 4)) ||
+      (totals && misaligned(totals, 8)))
+    return SPECV_EINVAL;
+  const hipError_t e =
+      launch_round_stats(draft_tokens, draft_len, out_tokens, n_emitted, beta, B, K, accepted,
+                         expected, reinterpret_cast<long long*>(totals), stream);
+  return e == hipSuccess ? SPECV_OK : SPECV_EHIP;
+}
+
+size_t specv_monitor_state_bytes(int B, int window) {
+  if (B < 1 || window < 1 || window > SPECV_MAX_WINDOW) return 0;
+  return specv::monitor_state_bytes(B, window);
+}
+
+specv_status_t specv_monitor_reset(void* state, int B, int window, hipStream_t stream) {
+  using namespace specv;
+  if (B < 1 || window < 1 || window > SPECV_MAX_WINDOW) return SPECV_EINVAL;
+  if (!state || misaligned(state, 16)) return SPECV_EINVAL;
+  return launch_monitor_reset(state, B, window, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
+}
+
+specv_status_t specv_monitor_update(const int32_t* draft_tokens, const int32_t* draft_len,
+                                    const int32_t* out_tokens, const int32_t* n_emitted, int B,
+                                    int K, int max_k, int window, void* state,
+                                    int32_t* next_draft_len, double* rate, hipStream_t stream) {
+  using namespace specv;
+  if (B < 1 || K < 0 || K > SPECV_MAX_K || max_k < 1 || max_k > SPECV_MAX_K) return SPECV_EINVAL;
+  if (window < 1 || window > SPECV_MAX_WINDOW) return SPECV_EINVAL;
+  if ((K > 0 && !draft_tokens) || !draft_len || !out_tokens || !n_emitted || !state ||
+      !next_draft_len)
+    return SPECV_EINVAL;
+  if ((draft_tokens && misaligned(draft_tokens, 4)) || misaligned(draft_len, 4) ||
+      misaligned(out_tokens, 4) || misaligned(n_emitted, 4) || misaligned(state, 16) ||
+      misaligned(next_draft_len, 4) || (rate && misaligned(rate, 8)))
+    return SPECV_EINVAL;
+  const hipError_t e = launch_monitor_update(draft_tokens, draft_len, out_tokens, n_emitted, B, K,
+                                             max_k, window, state, next_draft_len, rate, stream);
+  return e == hipSuccess ? SPECV_OK : SPECV_EHIP;
+}
+
 specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream_t stream) {
   if (n < 0 || (n > 0 && (!x || !y))) return SPECV_EINVAL;
   return specv::launch_exp64_selftest(x, y, n, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
@@ -389,6 +449,6 @@ const char* specv_status_string(specv_status_t status) {
   return "unknown status";
 }
 
-int specv_version(void) { return 101; }
+int specv_version(void) { return 102; }
 
 }  // extern "C"

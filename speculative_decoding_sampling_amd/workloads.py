@@ -230,3 +230,39 @@ def upload(w, device="cuda"):
         top_p=w.top_p,
         eos_id=w.eos_id,
     )
+
+
+def make_round_outcomes(B, K, seed, draft_len=None, fail_frac=0.05, eos_frac=0.1, V=1000):
+    """Random outcomes of one verified round, shaped as a verification call's
+    inputs and outputs: (draft_tokens [B][K], draft_len [B], out_tokens
+    [B][K+1], n_emitted [B]), all int32.
+
+    Only random draws: draft_len (if not given) uniform in [0, K]; n_emitted
+    uniform in [1, draft_len + 1]; the emitted tokens before the last repeat
+    the drafts; the last one repeats the draft at its position for an
+    ``eos_frac`` share of the rounds that stop inside the drafts and differs
+    from it otherwise; a ``fail_frac`` share of rounds are failed ones
+    (n_emitted = -1, out_tokens all -1).  Stream order of SeedSequence(seed)
+    .spawn(4): draft tokens, draft lengths, stop positions, round kinds.
+    """
+    rs = [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(4)]
+    toks = rs[0].integers(0, V, size=(B, K), dtype=np.int64).astype(np.int32)
+    if draft_len is None:
+        draft_len = rs[1].integers(0, K + 1, size=B)
+    dl = np.asarray(draft_len, dtype=np.int32).copy()
+    out = np.full((B, K + 1), -1, dtype=np.int32)
+    n = np.full(B, -1, dtype=np.int32)
+    stop = rs[2].random(B)
+    kind = rs[3].random(B)
+    for b in range(B):
+        nb = int(dl[b])
+        if kind[b] < fail_frac or nb < 0 or nb > K:
+            continue
+        last = min(int(stop[b] * (nb + 1)), nb)
+        out[b, :last] = toks[b, :last]
+        if last < nb and kind[b] < fail_frac + eos_frac:
+            out[b, last] = toks[b, last]
+        else:
+            out[b, last] = (toks[b, last] + 1) % V if last < nb else V - 1 - b % V
+        n[b] = last + 1
+    return toks, dl, out, n

@@ -1,0 +1,191 @@
+"""Round statistics and the adaptive draft length on the GPU against the
+oracle, through the C ABI (GPU only).
+
+Every input is either drawn by the seeded generators or produced by the
+oracle's own verification; integer results and the float64 rates are
+compared bit for bit, and so are the float32 E[N] values, which both sides
+form from the same float32 rates by the same rounded steps.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import oracle.round_policy as RP  # noqa: E402
+from speculative_decoding_sampling_amd import binding  # noqa: E402
+from speculative_decoding_sampling_amd.workloads import (  # noqa: E402
+    f32, make_round_outcomes, make_workload, upload)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def gpu_stats(toks, dl, out, n, beta=None):
+    acc, exp, tot = binding.round_stats(dev(toks), dev(dl), dev(out), dev(n),
+                                        None if beta is None else dev(beta))
+    torch.cuda.synchronize()
+    return (acc.cpu().numpy(), None if exp is None else exp.cpu().numpy(),
+            dict(zip(binding.TOTAL_FIELDS, tot.cpu().tolist())))
+
+
+def assert_stats(toks, dl, out, n, label):
+    acc, _, tot = gpu_stats(toks, dl, out, n)
+    acc_o, tot_o = RP.round_stats(toks, dl, out, n)
+    print(f"[round_stats] {label}: {tot_o}", flush=True)
+    assert np.array_equal(acc, acc_o), np.nonzero(acc != acc_o)[0][:10]
+    assert tot == tot_o
+
+
+@pytest.mark.parametrize("B,K,seed", [(1, 0, 1), (7, 1, 2), (64, 4, 3), (1000, 8, 4),
+                                      (3000, 63, 5)])
+def test_round_stats_synthetic(B, K, seed):
+    toks, dl, out, n = make_round_outcomes(B, K, seed)
+    assert_stats(toks, dl, out, n, f"synthetic B={B} K={K} seed={seed}")
+
+
+def test_round_stats_invalid_draft_len():
+    toks, dl, out, n = make_round_outcomes(40, 6, 9)
+    dl[::5] = -3
+    dl[1::7] = 7                                    # above K: a failed round
+    assert_stats(toks, dl, out, n, "invalid draft_len")
+
+
+def oracle_verify(w):
+    return O.verify(w.target, w.draft, w.draft_tokens, w.draft_len, w.u, w.u_final, f32(w.T),
+                    w.top_k, f32(w.top_p), w.eos_id, w.dtype)
+
+
+def test_round_stats_of_a_verified_round_with_eos():
+    # Ragged drafts with EOS stops: the oracle's verify outputs go to both.
+    w = make_workload(5, B=16)
+    o = oracle_verify(w)
+    assert (o["path"] == O.PATH_EOS).any() and (o["path"] == O.PATH_REJECT).any()
+    assert_stats(w.draft_tokens, w.draft_len, o["out_tokens"], o["n_emitted"], "cfg 5 B=16")
+    # The GPU chain (verify, then round statistics) reaches the same counts.
+    a = upload(w, DEV)
+    res = binding.verify(**a)
+    acc, _, tot = binding.round_stats(a["draft_tokens"], a["draft_len"], res["out_tokens"],
+                                      res["n_emitted"])
+    torch.cuda.synchronize()
+    acc_o, tot_o = RP.round_stats(w.draft_tokens, w.draft_len, o["out_tokens"], o["n_emitted"])
+    sure = o["flag_kind"] == O.FLAG_NONE
+    assert np.array_equal(acc.cpu().numpy()[sure], acc_o[sure])
+    if sure.all():
+        assert dict(zip(binding.TOTAL_FIELDS, tot.cpu().tolist())) == tot_o
+
+
+def test_expected_tokens_from_rates():
+    w = make_workload(5, B=16)
+    beta = O.acceptance_rates(w.target, w.draft, w.draft_len, f32(w.T), w.top_k, f32(w.top_p),
+                              w.dtype).astype(np.float32)
+    drafted = np.nonzero(w.draft_len >= 1)[0]
+    nr, bad = int(drafted[0]), int(drafted[1])
+    beta[nr, 0] = -1.0                              # a drafted position without a rate
+    dl = w.draft_len.copy()
+    dl[bad] = -1
+    o = oracle_verify(w)
+    _, exp, _ = gpu_stats(w.draft_tokens, dl, o["out_tokens"], o["n_emitted"], beta)
+    want = RP.expected_tokens_per_request(beta, dl)
+    print(f"[expected] E[N] per request: {np.round(want, 3).tolist()}", flush=True)
+    assert exp[nr] == -1.0 and exp[bad] == -1.0
+    assert np.array_equal(exp.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("B,max_k,window,rounds,seed", [(64, 8, 5, 40, 1), (300, 63, 64, 30, 2),
+                                                        (5, 4, 1, 20, 3), (17, 6, 4096, 12, 4)])
+def test_monitor_sequence(B, max_k, window, rounds, seed):
+    K = max_k
+    mons = [RP.AcceptRateMonitor(window) for _ in range(B)]
+    gm = binding.AcceptRateMonitor(B, window, max_k, DEV)
+    rng = np.random.default_rng(seed)
+    dl = rng.integers(1, max_k + 1, size=B).astype(np.int32)
+    changes = 0
+    for r in range(rounds):
+        dl_r = dl.copy()
+        if r == rounds // 2:
+            dl_r[::9] = -1                          # failed rounds keep their window
+        toks, dl_r, out, n = make_round_outcomes(B, K, 1000 * seed + r, draft_len=dl_r)
+        nxt_o, rate_o = RP.monitor_round(mons, toks, dl_r, out, n, max_k)
+        nxt_g, rate_g = gm.update(dev(toks), dev(dl_r), dev(out), dev(n))
+        torch.cuda.synchronize()
+        assert np.array_equal(nxt_g.cpu().numpy(), nxt_o), r
+        assert np.array_equal(rate_g.cpu().numpy(), rate_o), r
+        changes += int((nxt_o != dl_r).sum())
+        dl = nxt_o.astype(np.int32)
+    print(f"[monitor] B={B} max_k={max_k} window={window}: {changes} draft-length changes over "
+          f"{rounds} rounds", flush=True)
+    assert changes > 0
+
+
+def test_monitor_in_place_and_reset():
+    B, K, W = 33, 8, 3
+    mons = [RP.AcceptRateMonitor(W) for _ in range(B)]
+    gm = binding.AcceptRateMonitor(B, W, K, DEV)
+    dl = np.full(B, 4, dtype=np.int32)
+    for r in range(4):
+        if r == 3:                                  # a reset empties every window
+            gm.reset()
+            mons = [RP.AcceptRateMonitor(W) for _ in range(B)]
+        toks, dl_r, out, n = make_round_outcomes(B, K, 77 + r, draft_len=dl)
+        nxt_o, rate_o = RP.monitor_round(mons, toks, dl_r, out, n, K)
+        dl_dev = dev(dl_r)
+        gm.update(dev(toks), dl_dev, dev(out), dev(n), next_draft_len=dl_dev)
+        torch.cuda.synchronize()
+        assert np.array_equal(dl_dev.cpu().numpy(), nxt_o), r
+        dl = nxt_o.astype(np.int32)
+
+
+def oracle_sample(logits, u, T, dtype):
+    # K = 0 verification draws the bonus token from each row: a plain draw.
+    R = logits.shape[0]
+    t = logits[:, None, :]
+    res = O.verify(t, t[:, :0, :], np.zeros((R, 0), np.int32), np.zeros(R, np.int32),
+                   np.zeros((R, 0), np.float32), u, f32(T), dtype=dtype)
+    return res["out_tokens"][:, 0]
+
+
+def test_device_resident_decode_loop():
+    # Draft draws, verification and the monitor chained on the GPU for several
+    # rounds with no host copy in between, against the same chain in the
+    # oracle.  Each round's logits and uniforms are drawn up front.
+    B, K, V, W, rounds = 8, 4, 4096, 2, 6
+    ws = [make_workload(1, seed=500 + r) for r in range(rounds)]
+    rng = np.random.default_rng(5)
+    u_draft = [(rng.integers(0, 1 << 24, size=(B, K)) * 2.0 ** -24).astype(np.float32)
+               for _ in range(rounds)]
+    # GPU chain
+    gm = binding.AcceptRateMonitor(B, W, K, DEV)
+    dl_dev = dev(np.full(B, 2, dtype=np.int32))
+    gpu_out = []
+    for r, w in enumerate(ws):
+        a = upload(w, DEV)
+        toks = binding.sample(a["draft_logits"].reshape(B * K, V), dev(u_draft[r].reshape(-1)),
+                              w.T).reshape(B, K)
+        res = binding.verify(a["target_logits"], a["draft_logits"], toks, dl_dev, a["u"],
+                             a["u_final"], w.T)
+        gm.update(toks, dl_dev, res["out_tokens"], res["n_emitted"], next_draft_len=dl_dev)
+        gpu_out.append((toks, res["out_tokens"], res["n_emitted"], dl_dev.clone()))
+    torch.cuda.synchronize()
+    # Oracle chain
+    mons = [RP.AcceptRateMonitor(W) for _ in range(B)]
+    dl = np.full(B, 2, dtype=np.int32)
+    for r, w in enumerate(ws):
+        toks = oracle_sample(w.draft.reshape(B * K, V), u_draft[r].reshape(-1), w.T,
+                             w.dtype).reshape(B, K).astype(np.int32)
+        o = O.verify(w.target, w.draft, toks, dl, w.u, w.u_final, f32(w.T), dtype=w.dtype)
+        assert (o["flag_kind"] == O.FLAG_NONE).all(), "pick seeds without near-ties"
+        nxt, _ = RP.monitor_round(mons, toks, dl, o["out_tokens"], o["n_emitted"], K)
+        g_toks, g_out, g_n, g_dl = (t.cpu().numpy() for t in gpu_out[r])
+        for b in range(B):                          # drafts past draft_len are never read
+            assert np.array_equal(g_toks[b, :dl[b]], toks[b, :dl[b]]), (r, b)
+        assert np.array_equal(g_out, o["out_tokens"]) and np.array_equal(g_n, o["n_emitted"]), r
+        assert np.array_equal(g_dl, nxt), r
+        dl = nxt.astype(np.int32)
+    print(f"[loop] final draft lengths {dl.tolist()}", flush=True)

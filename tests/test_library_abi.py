@@ -37,7 +37,9 @@ def test_header_declares_the_api():
                           "specv_verify_timed", "specv_num_stages", "specv_stage_name",
                           "specv_status_string", "specv_version", "specv_selftest_exp64",
                           "specv_bench_row_stats", "specv_sample",
-                          "specv_acceptance_rates"}, names
+                          "specv_acceptance_rates", "specv_round_stats",
+                          "specv_monitor_state_bytes", "specv_monitor_reset",
+                          "specv_monitor_update"}, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -120,7 +122,7 @@ def test_status_strings(lib):
     s.argtypes = [ctypes.c_int]
     s.restype = ctypes.c_char_p
     assert s(0) == b"ok" and s(1) == b"invalid argument"
-    assert lib.specv_version() == 101
+    assert lib.specv_version() == 102
 
 
 def test_bench_hook_rejects_bad_arguments(lib):
@@ -193,3 +195,55 @@ def test_acceptance_rates_reject_bad_arguments(lib):
     assert call(k=0, p=0.5) == 4                     # top-p without top-k
     assert call(wsb=16) == 2
     assert call(K=0, d=None, wsb=1 << 20) == 0       # nothing to compute, nothing launched
+
+
+def test_round_stats_reject_bad_arguments(lib):
+    f = lib.specv_round_stats
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [vp, vp, vp, vp, vp, i, i, vp, vp, vp, vp]
+    f.restype = i
+    ok = dict(dt=16, dl=16, out=16, n=16, beta=None, B=4, K=3, acc=16, exp=None, tot=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["dt"], a["dl"], a["out"], a["n"], a["beta"], a["B"], a["K"], a["acc"],
+                 a["exp"], a["tot"], None)
+
+    assert call(B=0) == 1
+    assert call(K=64) == 1 and call(K=-1) == 1
+    assert call(dt=None) == 1
+    assert call(out=None) == 1 and call(n=None) == 1 and call(dl=None) == 1
+    assert call(exp=16) == 1                         # expected tokens need beta
+    assert call(dl=18) == 1                          # misaligned
+    assert call(tot=20) == 1                         # int64 totals must be 8-aligned
+
+
+def test_monitor_sizes_and_bad_arguments(lib):
+    sb = lib.specv_monitor_state_bytes
+    sb.argtypes = [ctypes.c_int, ctypes.c_int]
+    sb.restype = ctypes.c_size_t
+    assert sb(1, 1) == 32 and sb(3, 4) == 3 * 32 and sb(2, 5) == 2 * 48
+    assert sb(0, 4) == 0 and sb(4, 0) == 0 and sb(4, 4097) == 0 and sb(1, 4096) == 4100 * 4
+    rs = lib.specv_monitor_reset
+    rs.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    rs.restype = ctypes.c_int
+    assert rs(None, 4, 8, None) == 1 and rs(16, 0, 8, None) == 1 and rs(16, 4, 0, None) == 1
+    assert rs(24, 4, 8, None) == 1                   # state must be 16-aligned
+    f = lib.specv_monitor_update
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp]
+    f.restype = i
+    ok = dict(dt=16, dl=16, out=16, n=16, B=4, K=3, mk=6, W=8, st=16, nxt=16, rate=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["dt"], a["dl"], a["out"], a["n"], a["B"], a["K"], a["mk"], a["W"], a["st"],
+                 a["nxt"], a["rate"], None)
+
+    assert call(B=0) == 1 and call(K=64) == 1
+    assert call(mk=0) == 1 and call(mk=64) == 1
+    assert call(W=0) == 1 and call(W=4097) == 1
+    assert call(st=None) == 1 and call(nxt=None) == 1 and call(dt=None) == 1
+    assert call(st=20) == 1 and call(rate=20) == 1

@@ -126,6 +126,17 @@ def test_expected_tokens_brute_force_patterns():
         assert abs(RP.expected_tokens_given_rates(rates) - e) < 1e-12
 
 
+def test_expected_tokens_per_request():
+    beta = np.array([[0.5, 0.25, -1.0], [0.5, -1.0, -1.0], [1.0, 1.0, 1.0], [0.1, 0.2, 0.3]],
+                    dtype=np.float32)
+    got = RP.expected_tokens_per_request(beta, [2, 2, 3, -1])
+    assert got.dtype == np.float32
+    assert list(got) == [1 + 0.5 + 0.125, -1.0, 4.0, -1.0]
+    assert list(RP.expected_tokens_per_request(beta, [0, 1, 4, 3])) == [1.0, 1.5, -1.0,
+                                                                       np.float32(1 + 0.1 + 0.02
+                                                                                  + 0.006)]
+
+
 # ---------------------------------------------------------------------------
 # The adaptive draft length of tbxsx.cn "4. 实现逻辑"
 # ---------------------------------------------------------------------------
