@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kFiltThreads) void beta_list_kernel(
   const int bk = blockIdx.x;
   const int k = bk % K, b = bk / K;
   const int nb = draft_len[b];
-  exp64_stage_table(tbl);
+  exp64_stage_table<kFiltThreads>(tbl);
   const int R = 2 * K + 1;
   const bool drafted = nb >= 0 && nb <= K && k < nb;
   FiltRow tr, dr;

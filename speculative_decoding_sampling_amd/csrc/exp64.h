@@ -24,10 +24,32 @@ namespace specv {
 
 static __device__ const double kExp64Table[SPECV_EXP64_N] = SPECV_EXP64_TABLE;
 
-// Stage the 4 KB table in LDS; every thread of the block must call this,
-// followed by __syncthreads() before the first exp64.
+// The 4 KB table staged in LDS by a block of NT threads, in two steps so a
+// kernel can request its entries together with its other independent loads
+// and write them to LDS once those are in flight: fetch() issues this
+// thread's global loads (no wait in between), store() writes them.  Every
+// thread of the block calls both, then __syncthreads() before the first exp64.
+template <int NT>
+struct Exp64Stage {
+  static_assert(SPECV_EXP64_N % NT == 0, "block size must divide the table");
+  static constexpr int kPer = SPECV_EXP64_N / NT;
+  double v[kPer];
+  __device__ __forceinline__ void fetch() {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = kExp64Table[threadIdx.x + i * NT];
+  }
+  __device__ __forceinline__ void store(double* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) lds[threadIdx.x + i * NT] = v[i];
+  }
+};
+
+// Both steps at once, for a block of NT threads.
+template <int NT>
 __device__ __forceinline__ void exp64_stage_table(double* lds) {
-  for (int i = threadIdx.x; i < SPECV_EXP64_N; i += blockDim.x) lds[i] = kExp64Table[i];
+  Exp64Stage<NT> st;
+  st.fetch();
+  st.store(lds);
 }
 
 __device__ __forceinline__ double exp64(double x, const double* __restrict__ tbl) {

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   const int R = 2 * K + 1;
   const int rr = blockIdx.x;
   const int r = rr % R, b = rr / R;
-  exp64_stage_table(tbl);
+  exp64_stage_table<kFiltThreads>(tbl);
   const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
   if (nb < 0 || nb > K) return;
   bool is_target;
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kFiltThreads) void sample_list_kernel(
   __shared__ double dl[kFiltThreads / kWave];
   __shared__ int il[kFiltThreads / kWave];
   const int b = blockIdx.x;
-  exp64_stage_table(tbl);
+  exp64_stage_table<kFiltThreads>(tbl);
   const Plan pl = plan[b];
   if (pl.path != kPathReject && pl.path != kPathBonus) return;   // uniform per block
   const int R = 2 * K + 1;

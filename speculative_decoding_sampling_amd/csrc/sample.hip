@@ -330,17 +330,27 @@ __global__ __launch_bounds__(kSampThreads) void sample_pass_kernel(
   __shared__ int tcnt[2];
 
   const int c = blockIdx.x % nch, b = blockIdx.x / nch;
-  exp64_stage_table(tbl);
+  // One round trip before the logits: the plan and this thread's exp-table
+  // entries are requested together, the logit loads as soon as the plan
+  // names the rows, and the table reaches LDS while those are in flight.  A
+  // request with no draw (EOS, error) loads from target row 0, which every
+  // request has, and leaves before using it.
   const Plan pl = plan[b];
-  if (pl.path != kPathReject && pl.path != kPathBonus) return;   // uniform per block
+  Exp64Stage<kSampThreads> xs;
+  xs.fetch();
+  const bool live = pl.path == kPathReject || pl.path == kPathBonus;
   const bool rej = pl.path == kPathReject;
-  const T* trow = tgt + target_row_off(b, pl.trow, K, V);
-  const T* drow = rej ? dft + draft_row_off(b, pl.drow, K, V) : nullptr;
-  const double mti = (double)pl.mt * invT, mdi = (double)pl.md * invT;   // m / T
+  // Row indices are selected, not branched on, so the plan arrives in one
+  // round trip; the draft row is dereferenced only after a rejection.
+  const T* trow = tgt + target_row_off(b, live ? pl.trow : 0, K, V);
+  const T* drow = dft + draft_row_off(b, rej ? pl.drow : 0, K, V);
 
   Raw8<T> rt, rd;
   load_raw8(trow, (long)c * kSampChunk, V, rt);
   if (rej) load_raw8(drow, (long)c * kSampChunk, V, rd);
+  if (!live) return;                                 // uniform per block
+  const double mti = (double)pl.mt * invT, mdi = (double)pl.md * invT;   // m / T
+  xs.store(tbl);
   if (threadIdx.x == 0) tcnt[0] = 0;
   __syncthreads();                                   // table staged, tie counter clear
   float zt[kSampPerThread], zd[kSampPerThread];
@@ -372,8 +382,10 @@ __global__ __launch_bounds__(kSampThreads) void sample_finish_kernel(
   const int tid = threadIdx.x, lane = tid % kWave, wid = tid / kWave;
   // Everything that does not depend on the plan is requested with it: the
   // exp table, this thread's first chunk record and that chunk's first
-  // kTiePre near-tie slots (read whether used or not; the slots exist).
-  exp64_stage_table(tbl);
+  // kTiePre near-tie slots (read whether used or not; the slots exist).  The
+  // table reaches LDS just before the first barrier.
+  Exp64Stage<kSampThreads> xs;
+  xs.fetch();
   const Plan pl = plan[b];
   const ChunkRec* rb = recs + (size_t)b * nch;
   const Tie* tb = ties + (size_t)b * nch * kTieCap;
@@ -412,6 +424,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_finish_kernel(
   if (tid == 0) s_nredo = 0;
   if (lane == 0 || lane == 16) dl[wid * 2 + (lane >> 4)] = red;
   if (lane == 0) il[wid] = wovf;
+  xs.store(tbl);
   __syncthreads();                                   // table staged; wave sums
   double St = 0.0, Sd = 0.0;
   bool fb = false;
@@ -612,7 +625,7 @@ hipError_t launch_sample_finish(bool bf16, const void* tgt, const void* dft, con
 __global__ __launch_bounds__(256) void exp64_selftest_kernel(const double* __restrict__ x,
                                                              double* __restrict__ y, int n) {
   __shared__ double tbl[SPECV_EXP64_N];
-  exp64_stage_table(tbl);
+  exp64_stage_table<256>(tbl);
   __syncthreads();
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
     y[i] = exp64(x[i], tbl);
