@@ -19,7 +19,9 @@ Sources the oracle follows (cited by page title and section):
   "收益账" and "深入推导" (distribution-preservation identity).
 
 ``oracle.round_policy`` holds the round statistics and the adaptive draft
-length ([TB] "4. 实现逻辑"; [NW] "好草稿也要算得便宜").
+length ([TB] "4. 实现逻辑"; [NW] "好草稿也要算得便宜").  ``oracle.lm_head``
+holds the target logits of the verification fused with the LM head ([TB]
+"6. 扩展性与安全性").
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, exact rational arithmetic or brute force.

@@ -209,6 +209,121 @@ def make_workload(cfg, seed=None, B=None, draft_sampler=None):
                     draft_len=draft_len, u=u, u_final=u_final, classes=classes)
 
 
+@dataclass
+class LmHeadWorkload:
+    """Inputs of the verification fused with the target LM head."""
+    seed: int
+    B: int
+    K: int
+    V: int
+    D: int
+    T: float
+    eos_id: int
+    exact: bool                 # small-integer values: every float32 sum is exact
+    hidden: np.ndarray          # [B, K+1, D] bf16 bit patterns (uint16)
+    weight: np.ndarray          # [V, D] bf16 bit patterns (uint16)
+    draft: np.ndarray           # [B, K, V] bf16 bit patterns (uint16)
+    draft_tokens: np.ndarray    # [B, K] int32
+    draft_len: np.ndarray       # [B] int32
+    u: np.ndarray               # [B, K] float32
+    u_final: np.ndarray         # [B] float32
+
+    @property
+    def positions(self):
+        return int(np.clip(self.draft_len, 0, self.K).sum())
+
+    @property
+    def dtype(self):
+        return "bf16"
+
+
+# Exact LM-head inputs: hidden = i / 16, weight = j / 32 with i, j uniform on
+# -8..8, so a logit is an integer multiple of 2**-9 whose partial sums stay
+# below 2**24 in magnitude for D <= 4096 (exact in float32 in any order), with
+# standard deviation sqrt(D) * 24 / 512 (3.0 at D = 4096).
+_HID_SCALE, _W_SCALE = 16.0, 32.0
+
+
+def _small_int_bf16(rng, shape, scale):
+    i = rng.integers(-8, 9, size=shape, dtype=np.int8)
+    return i, to_bf16_bits(i.astype(np.float32) / np.float32(scale))
+
+
+def make_lm_head_workload(B, K, V, D, seed=2000, exact=True, T=1.0, draft_sigma=0.7,
+                          ragged=False, eos_id=-1):
+    """Seeded inputs of the fused call at batch B, K drafts, vocabulary V and
+    hidden size D.
+
+    ``exact`` draws small-integer hidden states and weights (see above);
+    otherwise hidden ~ N(0, 1) and weight ~ N(0, (3 / sqrt(D))**2) in bf16
+    (logits ~ N(0, 3**2), float32 sums rounded).  The draft logits are the
+    target logits plus N(0, draft_sigma**2) noise, rounded to bf16 -- the
+    target logits here are an exact float32 product of the integer draws
+    (inputs to the draft only; the verification consumes its own); with
+    ``exact`` false they come from the float32 product of the bf16 values.
+    Draft tokens are drawn from the draft rows by Gumbel-max on z / T; draft
+    lengths are K, or uniform on 0..K with ``ragged``.  Stream order of
+    SeedSequence(seed).spawn(7): hidden, weight, draft noise, draft tokens,
+    u, u_final, draft lengths.
+    """
+    if exact and D > 4096:
+        raise ValueError("exact LM-head inputs need D <= 4096")
+    rs = [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(7)]
+    r_h, r_w, r_dn, r_tok, r_u, r_uf, r_len = rs
+    M = B * (K + 1)
+    if exact:
+        hi, h_bits = _small_int_bf16(r_h, (M, D), _HID_SCALE)
+        wi, w_bits = _small_int_bf16(r_w, (V, D), _W_SCALE)
+        t = (hi.astype(np.float32) @ wi.astype(np.float32).T) / np.float32(_HID_SCALE * _W_SCALE)
+        del wi
+    else:
+        h_bits = to_bf16_bits(r_h.standard_normal((M, D), dtype=np.float32))
+        w_bits = to_bf16_bits(r_w.standard_normal((V, D), dtype=np.float32)
+                              * np.float32(3.0 / np.sqrt(D)))
+        t = from_bf16_bits(h_bits) @ from_bf16_bits(w_bits).T
+    t = t.reshape(B, K + 1, V)
+    T = f32(T)
+    d = t[:, :K, :] + np.float32(draft_sigma) * r_dn.standard_normal((B, K, V), dtype=np.float32)
+    d_bits = to_bf16_bits(d)
+    d = from_bf16_bits(d_bits)
+    del t
+    tokens = np.zeros((B, K), dtype=np.int32)
+    for b in range(B):
+        for k in range(K):
+            tokens[b, k] = gumbel_max_token(d[b, k].astype(np.float64), T, r_tok)
+    u = uniforms(r_u, (B, K))
+    u_final = uniforms(r_uf, (B,))
+    if ragged:
+        draft_len = r_len.integers(0, K + 1, size=B).astype(np.int32)
+    else:
+        draft_len = np.full(B, K, dtype=np.int32)
+    return LmHeadWorkload(seed=seed, B=B, K=K, V=V, D=D, T=T, eos_id=eos_id, exact=exact,
+                          hidden=np.ascontiguousarray(h_bits.reshape(B, K + 1, D)),
+                          weight=np.ascontiguousarray(w_bits),
+                          draft=np.ascontiguousarray(d_bits), draft_tokens=tokens,
+                          draft_len=draft_len, u=u, u_final=u_final)
+
+
+def upload_lm_head(w, device="cuda"):
+    """Copy an LM-head workload to the GPU as ``binding.verify_lm_head`` takes it."""
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+
+    return dict(
+        hidden=bf(w.hidden),
+        lm_head_weight=bf(w.weight),
+        draft_logits=bf(w.draft),
+        draft_tokens=torch.from_numpy(w.draft_tokens).to(device),
+        draft_len=torch.from_numpy(w.draft_len).to(device),
+        u=torch.from_numpy(w.u).to(device),
+        u_final=torch.from_numpy(w.u_final).to(device),
+        temperature=w.T,
+        eos_id=w.eos_id,
+    )
+
+
 def upload(w, device="cuda"):
     """Copy a workload's arrays to the GPU as the tensors ``binding.verify`` takes."""
     import torch
