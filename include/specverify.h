@@ -69,6 +69,8 @@ typedef enum {
 #define SPECV_MAX_V 4194304
 /* Largest top_k the filter path accepts (candidates per row are held on chip). */
 #define SPECV_MAX_TOPK 128
+/* Largest hidden size the fused LM-head call accepts. */
+#define SPECV_MAX_D 65536
 
 /*
  * Bytes of device workspace specv_verify needs for these sizes.  Returns 0
@@ -279,6 +281,47 @@ SPECV_API specv_status_t specv_monitor_update(const int32_t *draft_tokens,
                                               const int32_t *n_emitted, int B, int K, int max_k,
                                               int window, void *state, int32_t *next_draft_len,
                                               double *rate, hipStream_t stream);
+
+/*
+ * The verification step fused with the target model's LM head (tbxsx.cn,
+ * "推测解码采样验证优化策略 —— 深度调研报告", section "6. 扩展性与安全性": fuse the
+ * verification-stage forward pass of the target model with the sampling
+ * step).  The target logits are computed on the matrix cores from the target
+ * model's final hidden states, logits[b][k][v] = sum_d hidden[b][k][d] *
+ * lm_head_weight[v][d] (bf16 products, float32 accumulation, rounded to bf16
+ * nearest-even), and the softmax statistics of each target row are taken in
+ * the same kernel, from the rounded values, before the logits leave the chip;
+ * the rest is specv_verify on those logits (no top-k / top-p).
+ *
+ *  hidden          [B][K+1][D] bf16, device, 16-byte aligned: the hidden state
+ *                  that produces target row k of request b.
+ *  lm_head_weight  [V][D] bf16, device, 16-byte aligned.
+ *  D               > 0, a multiple of 64, <= SPECV_MAX_D.
+ *  target_logits   [B][K+1][V] bf16, device output: the LM head's logits
+ *                  (every row, whatever draft_len is); the draws read it.
+ *  draft_logits, draft_tokens, draft_len, u, u_final, B, K, V, temperature,
+ *  eos_id, out_tokens, n_emitted: as for specv_verify (bf16 draft logits).
+ *  workspace       at least specv_lm_head_workspace_bytes(B, K, V, D) bytes,
+ *                  16-byte aligned; no initialisation needed.
+ *  accept_prob, residual_mass, stop_pos, path: nullable diagnostics, as for
+ *                  specv_verify_debug.
+ *
+ * Status codes as specv_verify; SPECV_EINVAL also for D not a multiple of
+ * 64 or misaligned hidden / weight.  Per-request errors as specv_verify.
+ * Asynchronous on `stream`; allocates nothing.
+ */
+SPECV_API size_t specv_lm_head_workspace_bytes(int B, int K, int V, int D);
+SPECV_API specv_status_t specv_verify_lm_head(const void *hidden, const void *lm_head_weight,
+                                              const void *draft_logits,
+                                              const int32_t *draft_tokens,
+                                              const int32_t *draft_len, const float *u,
+                                              const float *u_final, int B, int K, int V, int D,
+                                              float temperature, int eos_id, void *target_logits,
+                                              int32_t *out_tokens, int32_t *n_emitted,
+                                              void *workspace, size_t workspace_bytes,
+                                              hipStream_t stream, float *accept_prob,
+                                              double *residual_mass, int32_t *stop_pos,
+                                              int32_t *path);
 
 /*
  * Timing variant of specv_verify, for benchmarks: identical work, plus

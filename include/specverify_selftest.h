@@ -48,6 +48,27 @@ SPECV_API specv_status_t specv_bench_row_stats(const void *const *targets,
                                                hipStream_t stream, hipEvent_t start,
                                                hipEvent_t stop);
 
+/*
+ * Benchmark hook: the LM-head kernel of specv_verify_lm_head alone (logits
+ * and their per-256-id tile statistics), `reps` launches on `stream` between
+ * hipEventRecord(start) and hipEventRecord(stop), for the roofline.
+ *
+ *  hidden [M][D] bf16, lm_head_weight [V][D] bf16 (device, 16-byte aligned),
+ *  logits [M][V] bf16 device output; D a multiple of 64, <= SPECV_MAX_D.
+ *  workspace  at least M * ceil(V / 256) * 8 bytes, 16-byte aligned (the
+ *             tile statistics are written there).
+ *
+ * SPECV_EINVAL for bad sizes, temperature, reps, null or misaligned pointers
+ * or null events; SPECV_EWORKSPACE for a short workspace; SPECV_EHIP if a
+ * launch or event record fails.  Asynchronous.
+ */
+SPECV_API specv_status_t specv_bench_lm_head(const void *hidden, const void *lm_head_weight,
+                                             int M, int D, int V, float temperature,
+                                             void *logits, void *workspace,
+                                             size_t workspace_bytes, int reps,
+                                             hipStream_t stream, hipEvent_t start,
+                                             hipEvent_t stop);
+
 #ifdef __cplusplus
 }
 #endif

@@ -88,6 +88,15 @@ def load_library():
                                               c_int, c_float, c_vp, c_size, c_int, c_vp, c_vp,
                                               c_vp]
         lib.specv_bench_row_stats.restype = c_int
+        lib.specv_lm_head_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+        lib.specv_lm_head_workspace_bytes.restype = c_size
+        lib.specv_verify_lm_head.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
+                                             c_int, c_int, c_float, c_int, c_vp, c_vp, c_vp, c_vp,
+                                             c_size, c_vp, c_vp, c_vp, c_vp, c_vp]
+        lib.specv_verify_lm_head.restype = c_int
+        lib.specv_bench_lm_head.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_float, c_vp, c_vp,
+                                            c_size, c_int, c_vp, c_vp, c_vp]
+        lib.specv_bench_lm_head.restype = c_int
         lib.specv_version.argtypes = []
         lib.specv_version.restype = c_int
         _lib = lib
@@ -400,3 +409,85 @@ def verify(target_logits, draft_logits, draft_tokens, draft_len, u, u_final, tem
     if status != SPECV_OK:
         raise SpecVerifyError(status, status_string(status))
     return res
+
+
+def lm_head_workspace_bytes(B, K, V, D):
+    return int(load_library().specv_lm_head_workspace_bytes(int(B), int(K), int(V), int(D)))
+
+
+def verify_lm_head(hidden, lm_head_weight, draft_logits, draft_tokens, draft_len, u, u_final,
+                   temperature=1.0, eos_id=-1, *, target_logits=None, out_tokens=None,
+                   n_emitted=None, workspace=None, debug=False, stream=None):
+    """The verification step fused with the target model's LM head.
+
+    Shapes: hidden [B, K+1, D] bf16 (the target model's final hidden states),
+    lm_head_weight [V, D] bf16, draft_logits [B, K, V] bf16, draft_tokens
+    [B, K] int32, draft_len [B] int32, u [B, K] fp32, u_final [B] fp32; D a
+    multiple of 64.  Returns a dict with ``target_logits`` [B, K+1, V] bf16
+    (the LM head's output), ``out_tokens`` and ``n_emitted``, plus the
+    ``verify`` diagnostics when ``debug`` is true.  Asynchronous on
+    ``stream``."""
+    lib = load_library()
+    dev = hidden.device
+    if dev.type != "cuda" or hidden.dim() != 3 or lm_head_weight.dim() != 2:
+        raise ValueError("hidden must be a [B, K+1, D] and lm_head_weight a [V, D] GPU tensor")
+    B, K1, D = hidden.shape
+    K = K1 - 1
+    V = lm_head_weight.shape[0]
+    bf = torch.bfloat16
+    _check(hidden, "hidden", bf, (B, K + 1, D), dev)
+    _check(lm_head_weight, "lm_head_weight", bf, (V, D), dev)
+    _check(draft_logits, "draft_logits", bf, (B, K, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(draft_len, "draft_len", torch.int32, (B,), dev)
+    _check(u, "u", torch.float32, (B, K), dev)
+    _check(u_final, "u_final", torch.float32, (B,), dev)
+    if target_logits is None:
+        target_logits = torch.empty((B, K + 1, V), dtype=bf, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if n_emitted is None:
+        n_emitted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(target_logits, "target_logits", bf, (B, K + 1, V), dev)
+    _check(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+    _check(n_emitted, "n_emitted", torch.int32, (B,), dev)
+    nbytes = lm_head_workspace_bytes(B, K, V, D)
+    if workspace is None:
+        workspace = _workspace(dev, nbytes)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    res = {"target_logits": target_logits, "out_tokens": out_tokens, "n_emitted": n_emitted}
+    diag = [None, None, None, None]
+    if debug:
+        res["accept_prob"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+        res["residual_mass"] = torch.empty((B,), dtype=torch.float64, device=dev)
+        res["stop_pos"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        res["path"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        diag = [res["accept_prob"], res["residual_mass"], res["stop_pos"], res["path"]]
+    st = lib.specv_verify_lm_head(_ptr(hidden), _ptr(lm_head_weight), _ptr(draft_logits),
+                                  _ptr(draft_tokens), _ptr(draft_len), _ptr(u), _ptr(u_final), B,
+                                  K, V, D, float(temperature), int(eos_id), _ptr(target_logits),
+                                  _ptr(out_tokens), _ptr(n_emitted), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  ctypes.c_void_p(stream.cuda_stream), *[_ptr(t) for t in diag])
+    if st != SPECV_OK:
+        raise SpecVerifyError(st, status_string(st))
+    return res
+
+
+def bench_lm_head(hidden, lm_head_weight, logits, workspace, reps, temperature=1.0, stream=None,
+                  start=None, stop=None):
+    """Benchmark hook: the LM-head kernel alone (hidden [M, D], weight [V, D],
+    logits [M, V], all bf16), ``reps`` launches between the HIP events
+    ``start`` and ``stop`` (raw handles) recorded on ``stream``."""
+    lib = load_library()
+    M, D = hidden.shape
+    V = lm_head_weight.shape[0]
+    if stream is None:
+        stream = torch.cuda.current_stream(hidden.device)
+    st = lib.specv_bench_lm_head(_ptr(hidden), _ptr(lm_head_weight), M, D, V, float(temperature),
+                                 _ptr(logits), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), int(reps),
+                                 ctypes.c_void_p(stream.cuda_stream), start, stop)
+    if st != SPECV_OK:
+        raise SpecVerifyError(st, status_string(st))

@@ -22,15 +22,18 @@ namespace specv {
 template <typename T, int VECS>
 __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
-    const int* __restrict__ tokens, int K, int V, int nchunk, float c,
+    const int* __restrict__ tokens, int K, int V, int nchunk, int row_lo, float c,
     float2* __restrict__ part, float* __restrict__ zx) {
   constexpr int N = Elem<T>::kPerVec;
   constexpr int kChunk = kRowThreads * VECS * N;
   const int R = 2 * K + 1;
+  // The grid covers rows row_lo .. 2K of every request (row_lo = K + 1: draft
+  // rows only, when the target rows' statistics come from elsewhere).
   const int chunk = blockIdx.x % nchunk;
-  const int rr = blockIdx.x / nchunk;
-  const int r = rr % R;
-  const int b = rr / R;
+  const int rq = blockIdx.x / nchunk;
+  const int r = row_lo + rq % (R - row_lo);
+  const int b = rq / (R - row_lo);
+  const size_t rr = (size_t)b * R + r;
   const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
   if (nb < 0 || nb > K) return;                      // the accept scan reports the error
   const bool is_target = r <= K;
@@ -127,18 +130,19 @@ int row_stats_chunk(bool bf16) {
 
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                             const int* tokens, int B, int K, int V, int nchunk, float c,
-                            float2* part, float* zx, hipStream_t stream) {
-  const size_t blocks = (size_t)B * (2 * K + 1) * nchunk;
+                            float2* part, float* zx, hipStream_t stream, int row_lo) {
+  if (row_lo < 0 || row_lo > 2 * K) return hipErrorInvalidValue;
+  const size_t blocks = (size_t)B * (2 * K + 1 - row_lo) * nchunk;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   if (bf16)
     row_stats_kernel<bf16_t, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
         static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, tokens, K, V,
-        nchunk, c, part, zx);
+        nchunk, row_lo, c, part, zx);
   else
     row_stats_kernel<float, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
         static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, tokens, K, V,
-        nchunk, c, part, zx);
+        nchunk, row_lo, c, part, zx);
   return hipGetLastError();
 }
 

@@ -14,7 +14,15 @@ namespace specv {
 int row_stats_chunk(bool bf16);
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                             const int* tokens, int B, int K, int V, int nchunk, float c,
-                            float2* part, float* zx, hipStream_t stream);
+                            float2* part, float* zx, hipStream_t stream, int row_lo = 0);
+int lm_head_tiles(int V);
+int lm_head_rows_per_block();
+int lm_head_kblock();
+hipError_t launch_lm_head(const void* hidden, const void* weight, int M, int D, int V, float c,
+                          void* logits, float2* tpart, hipStream_t stream);
+hipError_t launch_fold_tile_stats(const float2* tpart, const void* logits, const int* tokens,
+                                  int B, int K, int V, int nch, float c, float2* part, float* zx,
+                                  hipStream_t stream);
 hipError_t launch_accept(bool bf16, bool filt, const void* tgt, const void* dft, const int* tokens,
                          const int* draft_len, const float* u, const float* u_final, int B,
                          int K, int V, int nch_row, float c, double invT, int eos_id,
@@ -235,6 +243,102 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
   return SPECV_OK;
 }
 
+// Target LM head fused with verification: the layout of an unfiltered bf16
+// call plus the LM head's tile statistics [B (K+1)][ntile] (float2).
+struct LmLayout {
+  Layout base;
+  size_t off_tpart = 0, total = 0;
+};
+
+LmLayout make_lm_layout(int B, int K, int V) {
+  LmLayout L;
+  L.base = make_layout(B, K, V, true, 0, 1.0f);
+  L.off_tpart = L.base.total;
+  L.total = align_up(L.off_tpart +
+                     (size_t)B * (K + 1) * lm_head_tiles(V) * sizeof(float2));
+  return L;
+}
+
+specv_status_t check_lm_sizes(int B, int K, int V, int D) {
+  const specv_status_t st = check_sizes(B, K, V, SPECV_BF16, 0, 1.0f);
+  if (st != SPECV_OK) return st;
+  if (D < 1 || D % lm_head_kblock() != 0) return SPECV_EINVAL;
+  if (D > SPECV_MAX_D) return SPECV_EUNSUPPORTED;
+  // the LM head's grid: vocabulary tiles x row blocks
+  const size_t rows = (size_t)B * (K + 1);
+  const size_t blocks = (size_t)lm_head_tiles(V) *
+                        ((rows + lm_head_rows_per_block() - 1) / lm_head_rows_per_block());
+  if (blocks > 0x7fffffffu || rows * (size_t)V > ((size_t)1 << 62)) return SPECV_EUNSUPPORTED;
+  return SPECV_OK;
+}
+
+specv_status_t run_lm_head(const void* hidden, const void* weight, const void* draft,
+                           const int32_t* tokens, const int32_t* draft_len, const float* u,
+                           const float* u_final, int B, int K, int V, int D, float temperature,
+                           int eos_id, void* target_out, int32_t* out_tokens,
+                           int32_t* n_emitted, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, float* alpha_out, double* rmass_out,
+                           int32_t* stop_out, int32_t* path_out) {
+  specv_status_t st = check_lm_sizes(B, K, V, D);
+  if (st != SPECV_OK) return st;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SPECV_EINVAL;
+  if (eos_id < -1 || eos_id >= V) return SPECV_EINVAL;
+  if (!hidden || !weight || !target_out || !draft_len || !u_final || !out_tokens || !n_emitted)
+    return SPECV_EINVAL;
+  if (K > 0 && (!draft || !tokens || !u)) return SPECV_EINVAL;
+  // 16-byte loads of hidden-state and weight rows (D is a multiple of 64)
+  if (misaligned(hidden, 16) || misaligned(weight, 16) || misaligned(target_out, 2) ||
+      (draft && misaligned(draft, 2)))
+    return SPECV_EINVAL;
+  if (misaligned(draft_len, 4) || misaligned(u_final, 4) || misaligned(out_tokens, 4) ||
+      misaligned(n_emitted, 4) || (tokens && misaligned(tokens, 4)) || (u && misaligned(u, 4)))
+    return SPECV_EINVAL;
+  if ((alpha_out && misaligned(alpha_out, 4)) || (rmass_out && misaligned(rmass_out, 8)) ||
+      (stop_out && misaligned(stop_out, 4)) || (path_out && misaligned(path_out, 4)))
+    return SPECV_EINVAL;
+  const LmLayout LL = make_lm_layout(B, K, V);
+  const Layout& L = LL.base;
+  if (!workspace || misaligned(workspace, 16) || workspace_bytes < LL.total)
+    return SPECV_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  Plan* plan = reinterpret_cast<Plan*>(ws + L.off_plan);
+  float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
+  float* zx = reinterpret_cast<float*>(ws + L.off_zx);
+  ChunkRec* recs = reinterpret_cast<ChunkRec*>(ws + L.off_recs);
+  Tie* ties = reinterpret_cast<Tie*>(ws + L.off_ties);
+  float2* tpart = reinterpret_cast<float2*>(ws + LL.off_tpart);
+  const float c = (float)(1.4426950408889634 / (double)temperature);
+  const double invT = 1.0 / (double)temperature;
+  AcceptOut out = {};
+  out.plan = plan;
+  out.out_tokens = out_tokens;
+  out.n_emitted = n_emitted;
+  out.alpha_out = alpha_out;
+  out.rmass_out = rmass_out;
+  out.stop_out = stop_out;
+  out.path_out = path_out;
+
+  // target logits and their statistics, then the draft rows' statistics; from
+  // there on the call is the unfiltered verification
+  hipError_t e = launch_lm_head(hidden, weight, B * (K + 1), D, V, c, target_out, tpart, stream);
+  if (e == hipSuccess)
+    e = launch_fold_tile_stats(tpart, target_out, tokens, B, K, V, L.nch_row, c, row_part, zx,
+                               stream);
+  if (e == hipSuccess && K > 0)
+    e = launch_row_stats(true, target_out, draft, draft_len, tokens, B, K, V, L.nch_row, c,
+                         row_part, zx, stream, K + 1);
+  if (e == hipSuccess)
+    e = launch_accept(true, false, target_out, draft, tokens, draft_len, u, u_final, B, K, V,
+                      L.nch_row, c, invT, eos_id, row_part, zx, nullptr, out, stream);
+  if (e == hipSuccess)
+    e = launch_sample_pass(true, target_out, draft, B, K, V, L.nch_samp, invT, plan, recs, ties,
+                           stream);
+  if (e == hipSuccess)
+    e = launch_sample_finish(true, target_out, draft, u_final, B, K, V, L.nch_samp, invT, plan,
+                             recs, ties, out_tokens, rmass_out, stream);
+  return e == hipSuccess ? SPECV_OK : SPECV_EHIP;
+}
+
 }  // namespace
 }  // namespace specv
 
@@ -323,6 +427,49 @@ specv_status_t specv_bench_row_stats(const void* const* targets, const void* con
                          L.nch_row, c, row_part, zx, stream) != hipSuccess)
       return SPECV_EHIP;
   }
+  return hipEventRecord(stop, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
+}
+
+size_t specv_lm_head_workspace_bytes(int B, int K, int V, int D) {
+  if (specv::check_lm_sizes(B, K, V, D) != SPECV_OK) return 0;
+  return specv::make_lm_layout(B, K, V).total;
+}
+
+specv_status_t specv_verify_lm_head(const void* hidden, const void* lm_head_weight,
+                                    const void* draft_logits, const int32_t* draft_tokens,
+                                    const int32_t* draft_len, const float* u,
+                                    const float* u_final, int B, int K, int V, int D,
+                                    float temperature, int eos_id, void* target_logits,
+                                    int32_t* out_tokens, int32_t* n_emitted, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream,
+                                    float* accept_prob, double* residual_mass,
+                                    int32_t* stop_pos, int32_t* path) {
+  return specv::run_lm_head(hidden, lm_head_weight, draft_logits, draft_tokens, draft_len, u,
+                            u_final, B, K, V, D, temperature, eos_id, target_logits, out_tokens,
+                            n_emitted, workspace, workspace_bytes, stream, accept_prob,
+                            residual_mass, stop_pos, path);
+}
+
+specv_status_t specv_bench_lm_head(const void* hidden, const void* lm_head_weight, int M, int D,
+                                   int V, float temperature, void* logits, void* workspace,
+                                   size_t workspace_bytes, int reps, hipStream_t stream,
+                                   hipEvent_t start, hipEvent_t stop) {
+  using namespace specv;
+  if (M < 1 || V < 1 || V > SPECV_MAX_V || D < 1 || D % lm_head_kblock() != 0 ||
+      D > SPECV_MAX_D || reps < 1 || !start || !stop)
+    return SPECV_EINVAL;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SPECV_EINVAL;
+  if (!hidden || !lm_head_weight || !logits || misaligned(hidden, 16) ||
+      misaligned(lm_head_weight, 16) || misaligned(logits, 2))
+    return SPECV_EINVAL;
+  const size_t need = (size_t)M * lm_head_tiles(V) * sizeof(float2);
+  if (!workspace || misaligned(workspace, 16) || workspace_bytes < need) return SPECV_EWORKSPACE;
+  const float c = (float)(1.4426950408889634 / (double)temperature);
+  if (hipEventRecord(start, stream) != hipSuccess) return SPECV_EHIP;
+  for (int i = 0; i < reps; ++i)
+    if (launch_lm_head(hidden, lm_head_weight, M, D, V, c, logits,
+                       static_cast<float2*>(workspace), stream) != hipSuccess)
+      return SPECV_EHIP;
   return hipEventRecord(stop, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }
 

@@ -1,0 +1,145 @@
+"""The verification fused with the target LM head, against the oracle (GPU only).
+
+On small-integer inputs every float32 sum of the LM head is exact, so the
+target logits must equal the oracle's bfloat16-rounded exact product bit for
+bit, and the verification on them must match the oracle's as in the unfused
+parity tests (tokens bit-exact except flagged decisions, accept
+probabilities and residual masses within 1e-5).  On general inputs the
+logits are checked against the float64 product within the float32
+accumulation bound 2 D 2^-24 sum |h w|: between the roundings of the
+product minus and plus the bound, equal to the rounded product where those
+agree, and equal to it for all but a small fraction overall.  Shapes cover a partial row tile, several row blocks, a
+ragged vocabulary tail and V not a multiple of 4.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+from oracle import lm_head as OL  # noqa: E402
+from speculative_decoding_sampling_amd import binding  # noqa: E402
+from speculative_decoding_sampling_amd.workloads import (  # noqa: E402
+    make_lm_head_workload, upload_lm_head)
+from tests.parity import compare, to_numpy  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run_fused(w, **kw):
+    args = upload_lm_head(w, DEV)
+    args.update(kw)
+    res = binding.verify_lm_head(**args, debug=True)
+    torch.cuda.synchronize()
+    out = to_numpy({k: v for k, v in res.items() if k != "target_logits"})
+    out["target_bits"] = res["target_logits"].view(torch.int16).cpu().numpy().view(np.uint16)
+    return out
+
+
+@pytest.mark.parametrize("B,K,V,D,ragged,seed", [
+    (4, 3, 5000, 256, False, 1),       # M = 16: one partial row tile; V tail
+    (8, 4, 20000, 512, True, 2),       # M = 40: a full and a partial row tile; ragged drafts
+    (70, 4, 3000, 128, False, 3),      # M = 350: two row blocks
+    (2, 0, 4100, 64, False, 4),        # no drafts: bonus draws only
+    (1, 5, 32000, 1024, False, 5),     # single request, low-latency shape
+    (3, 2, 4097, 192, True, 6),        # V odd: element stores; D = 3 k blocks
+])
+def test_fused_exact_parity(B, K, V, D, ragged, seed):
+    print(f"[lm_head] B={B} K={K} V={V} D={D} ragged={ragged} seed={seed}", flush=True)
+    w = make_lm_head_workload(B, K, V, D, seed=seed, ragged=ragged)
+    g = run_fused(w)
+    t_bits = OL.lm_head_target_bits(w.hidden, w.weight)
+    assert np.array_equal(g["target_bits"], t_bits), int(np.sum(g["target_bits"] != t_bits))
+    o = O.verify(t_bits, w.draft, w.draft_tokens, w.draft_len, w.u, w.u_final, w.T, 0, 1.0,
+                 w.eos_id, "bf16")
+    rep = compare(g, o, w.K)
+    print(f"  requests={rep['requests']} positions={rep['positions']} flagged={rep['flagged']} "
+          f"max_alpha_err={rep['max_alpha_err']:.2e} max_mass_err={rep['max_mass_err']:.2e}",
+          flush=True)
+    assert not rep["mismatches"], rep["mismatches"][:5]
+
+
+def test_fused_general_inputs_logits_within_accumulation_bound():
+    B, K, V, D = 3, 3, 3001, 1024
+    w = make_lm_head_workload(B, K, V, D, seed=21, exact=False)
+    print(f"[lm_head] general inputs B={B} K={K} V={V} D={D}", flush=True)
+    g = run_fused(w)
+    exact = OL.lm_head_logits(w.hidden, w.weight)
+    absprod = np.abs(OL.widen_bf16(w.hidden)).reshape(-1, D) @ np.abs(OL.widen_bf16(w.weight)).T
+    bound = 2 * D * 2.0 ** -24 * absprod.reshape(exact.shape)   # any fp32 order, truncation too
+    want = OL.round_bf16(exact)
+    got = OL.widen_bf16(g["target_bits"])
+    # rounding is monotone: a float32 sum within the bound of the exact value
+    # rounds to a bfloat16 between these two, and to want where they agree
+    lo, hi = OL.round_bf16(exact - bound), OL.round_bf16(exact + bound)
+    assert np.all((lo <= got) & (got <= hi))
+    certain = lo == hi
+    assert np.array_equal(got[certain], want[certain])
+    # typical float32 rounding is far inside the worst-case bound: nearly
+    # every logit is the nearest bfloat16 of the exact product
+    agree = float(np.mean(got == want))
+    print(f"  certain {certain.mean():.4f}, equal to the rounded exact product {agree:.5f}",
+          flush=True)
+    assert agree > 0.99
+
+
+def test_fused_deterministic():
+    w = make_lm_head_workload(6, 4, 9000, 256, seed=31)
+    a, b = run_fused(w), run_fused(w)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_fused_host_argument_errors():
+    lib = binding.load_library()
+    w = make_lm_head_workload(2, 2, 1000, 128, seed=41)
+    args = upload_lm_head(w, DEV)
+    B, K, V, D = w.B, w.K, w.V, w.D
+    tl = torch.empty((B, K + 1, V), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=DEV)
+    n = torch.empty((B,), dtype=torch.int32, device=DEV)
+    ws = torch.empty(binding.lm_head_workspace_bytes(B, K, V, D), dtype=torch.uint8, device=DEV)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = binding._ptr
+
+    def call(D_=D, ws_bytes=None, hidden=None, T=1.0):
+        h = args["hidden"] if hidden is None else hidden
+        return lib.specv_verify_lm_head(
+            p(h), p(args["lm_head_weight"]), p(args["draft_logits"]), p(args["draft_tokens"]),
+            p(args["draft_len"]), p(args["u"]), p(args["u_final"]), B, K, V, D_, T, -1, p(tl),
+            p(out), p(n), p(ws), ws.numel() if ws_bytes is None else ws_bytes, s, None, None,
+            None, None)
+
+    assert call() == 0
+    assert call(D_=100) == 1                     # not a multiple of 64
+    assert call(D_=0) == 1
+    assert call(T=0.0) == 1
+    assert call(ws_bytes=16) == 2
+    assert binding.lm_head_workspace_bytes(B, K, V, 100) == 0
+    mis = torch.empty(B * (K + 1) * D + 8, dtype=torch.bfloat16, device=DEV)[1:]
+    assert call(hidden=mis) == 1                 # hidden not 16-byte aligned
+    torch.cuda.synchronize()
+
+
+def test_bench_lm_head_hook_runs():
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    w = make_lm_head_workload(2, 1, 2000, 128, seed=51)
+    a = upload_lm_head(w, DEV)
+    M = w.B * (w.K + 1)
+    hid = a["hidden"].reshape(M, w.D)
+    logits = torch.empty((M, w.V), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(M * ((w.V + 255) // 256) * 8, dtype=torch.uint8, device=DEV)
+    binding.bench_lm_head(hid, a["lm_head_weight"], logits, ws, 3, start=ev[0], stop=ev[1])
+    torch.cuda.synchronize()
+    t_bits = OL.lm_head_target_bits(w.hidden, w.weight).reshape(M, w.V)
+    got = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, t_bits)
