@@ -16,13 +16,15 @@
 // holds one hidden row per lane and 16 vocabulary ids per register set, so
 // the per-row statistics are mostly an in-register reduction.
 //
-// Work split.  A workgroup of 8 waves owns 256 vocabulary ids (32 per wave)
-// and 320 hidden rows (10 tiles of 32; larger M runs more row blocks).  Per
+// Work split.  A workgroup of 4 waves owns 128 vocabulary ids (32 per wave)
+// and 320 hidden rows (10 tiles of 32; larger M runs more row blocks); two
+// workgroups share a CU, so one computes while the other waits.  Per
 // 64-wide k block each lane reads 64 contiguous bytes of its weight row
-// straight into registers (the weights are streamed from HBM exactly once
-// per row block), while the block's 320 x 64 hidden states are staged in LDS
-// (double-buffered; rows padded to 144 bytes so the 16-byte fragment reads of
-// 8 consecutive lanes cover all banks).  The k values of one MFMA step are
+// straight into registers, two blocks ahead of its use (the weights are
+// streamed from HBM exactly once per row block), while the block's 320 x 64
+// hidden states are loaded straight into LDS (double-buffered; 16-byte pieces
+// XOR-swizzled by row so the fragment reads of 8 consecutive lanes cover all
+// banks).  The k values of one MFMA step are
 // {k0 + 32 h + 8 s + i : h = lane / 32, i < 8} for step s = 0..3: any
 // permutation of k shared by both operands leaves the dot product unchanged,
 // and this one makes each lane's weight bytes contiguous.
@@ -30,9 +32,9 @@
 // Epilogue.  Each accumulator is rounded to bfloat16 (nearest even) and
 // written; the statistics are taken over the rounded values, the logits every
 // later stage reads.  Per row: the max and sum over the lane's 16 ids, the
-// lane pair holding the other 16, then the 8 waves through LDS in a fixed
-// order, giving one (max, normaliser) per 256-id tile.  fold_tile_stats then
-// combines 32 tiles into the 8192-id chunk partials of the row-statistics
+// lane pair holding the other 16, then the 4 waves through LDS in a fixed
+// order, giving one (max, normaliser) per 128-id tile.  fold_tile_stats then
+// combines 64 tiles into the 8192-id chunk partials of the row-statistics
 // layout, and records the logit of each row's drafted token.
 #include "common.h"
 
@@ -41,18 +43,17 @@ namespace specv {
 typedef __bf16 lm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float lm_f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kLmThreads = 512;
-constexpr int kLmWaves = kLmThreads / kWave;        // 8
-constexpr int kLmVocab = kLmWaves * 32;             // 256 vocabulary ids per workgroup
+constexpr int kLmThreads = 256;
+constexpr int kLmWaves = kLmThreads / kWave;        // 4
+constexpr int kLmVocab = kLmWaves * 32;             // 128 vocabulary ids per workgroup
 constexpr int kLmMTiles = 10;
 constexpr int kLmRows = kLmMTiles * 32;             // 320 hidden rows per row block
 constexpr int kLmKB = 64;                           // k per block
-constexpr int kLmLdsRow = kLmKB + 8;                // bf16 per LDS row (144 bytes)
 constexpr int kLmHPieces = kLmRows * kLmKB / 8;     // 16-byte pieces of one hidden block
-constexpr int kLmHPer = kLmHPieces / kLmThreads;    // 5 per thread
+constexpr int kLmHPer = kLmHPieces / kLmThreads;    // 10 per thread
 static_assert(kLmHPieces % kLmThreads == 0, "hidden block pieces per thread");
 static_assert(kRowThreads * kRowVecs * 8 % kLmVocab == 0, "a statistics chunk is whole tiles");
-constexpr int kLmTilesPerChunk = kRowThreads * kRowVecs * 8 / kLmVocab;   // 32
+constexpr int kLmTilesPerChunk = kRowThreads * kRowVecs * 8 / kLmVocab;   // 64
 
 __device__ __forceinline__ lm_bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(lm_bf16x8, w); }
 
@@ -62,46 +63,54 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-__global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
+// s_waitcnt immediates (vector-memory count only; LDS / export counts untouched)
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm4 = 0x0F74;
+static_assert(kLmKB == 64, "wait immediates assume 4 weight loads per block");
+static_assert(kLmTilesPerChunk <= kWave, "one chunk's tiles fold in one wave");
+
+__global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
     const bf16_t* __restrict__ H, const bf16_t* __restrict__ W, int M, int D, int V, int ntile,
     float c, bf16_t* __restrict__ out, float2* __restrict__ tpart) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][kLmRows * kLmLdsRow];
+  // Hidden-state blocks, unpadded: row r's 16-byte piece p sits at slot
+  // p ^ (r & 7) of the row, so the fragment reads of 8 consecutive lanes
+  // (8 consecutive rows, one piece) fall in 8 different bank groups.
+  __shared__ __attribute__((aligned(16))) bf16_t lds0[kLmRows * kLmKB];
+  __shared__ __attribute__((aligned(16))) bf16_t lds1[kLmRows * kLmKB];
 
   const int tile = blockIdx.x % ntile;
   const int m0 = (blockIdx.x / ntile) * kLmRows;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int h = lane / 32, l32 = lane % 32;
 
   // This lane's weight row (rows past V read row V - 1; their sums are dropped).
   const int v_lane = tile * kLmVocab + wave * 32 + l32;
   const bf16_t* wrow = W + (size_t)min(v_lane, V - 1) * D + 32 * h;
 
-  // Hidden-state staging: piece q = threadIdx.x + kLmThreads * j is row q / 8,
-  // 16-byte piece q % 8 of the block; rows past M are staged as zeros.
+  // Hidden-state staging goes straight to LDS: instruction j of wave w fills
+  // slots [(10 w + j) 64, +64), rows 8 (10 w + j) .. +8; lane i fills slot i
+  // of those, i.e. row 8 (10 w + j) + i / 8 at position i % 8, which holds piece
+  // (i % 8) ^ (row & 7).  Rows past M repeat row M - 1 (their sums are dropped).
   const bf16_t* hsrc[kLmHPer];
-  int hdst[kLmHPer];
-  bool hok[kLmHPer];
 #pragma unroll
   for (int j = 0; j < kLmHPer; ++j) {
-    const int q = threadIdx.x + kLmThreads * j;
-    const int r = q / 8, p = q % 8;
-    hok[j] = m0 + r < M;
-    hsrc[j] = H + (size_t)(hok[j] ? m0 + r : 0) * D + p * 8;
-    hdst[j] = r * kLmLdsRow + p * 8;
+    const int r = 8 * (kLmHPer * wave + j) + lane / 8;
+    const int pc = (lane % 8) ^ (r & 7);
+    hsrc[j] = H + (size_t)min(m0 + r, M - 1) * D + pc * 8;
   }
+  auto stage_h = [&](int k0, bf16_t* buf) {
+#pragma unroll
+    for (int j = 0; j < kLmHPer; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(hsrc[j] + k0),
+          (__attribute__((address_space(3))) void*)(buf + (kLmHPer * wave + j) * 64 * 8), 16, 0,
+          0);
+  };
   auto load_w = [&](int k0, uint4* w) {
     const uint4* src = reinterpret_cast<const uint4*>(wrow + k0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) w[s] = src[s];
-  };
-  auto load_h = [&](int k0, uint4* hv) {
-#pragma unroll
-    for (int j = 0; j < kLmHPer; ++j)
-      hv[j] = hok[j] ? *reinterpret_cast<const uint4*>(hsrc[j] + k0) : make_uint4(0, 0, 0, 0);
-  };
-  auto store_h = [&](int buf, const uint4* hv) {
-#pragma unroll
-    for (int j = 0; j < kLmHPer; ++j) *reinterpret_cast<uint4*>(&lds[buf][hdst[j]]) = hv[j];
   };
 
   lm_f32x16 acc[kLmMTiles];
@@ -110,40 +119,77 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 
+  // B fragment of tile t, step s: row 32 t + l32, piece 4 h + s
+  int boff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) boff[s] = (((4 * h + s) ^ (l32 & 7)) * 8);
+
   const int nkb = D / kLmKB;
-  uint4 wa[4], wn[4], hn[kLmHPer];
-  load_w(0, wa);
-  load_h(0, hn);
-  store_h(0, hn);
+  uint4 wr0[4], wr1[4], wr2[4];                      // weight ring: blocks kb, kb+1, kb+2
+  stage_h(0, lds0);
+  load_w(0, wr0);
+  if (nkb > 1) load_w(kLmKB, wr1);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    if (more) {                                      // next block in flight during this one
-      load_w((kb + 1) * kLmKB, wn);
-      load_h((kb + 1) * kLmKB, hn);
-    }
-    const bf16_t* hb = lds[kb & 1] + l32 * kLmLdsRow + 32 * h;
+  // One k block: stage the next hidden block, request the weights two blocks
+  // ahead, multiply, then wait for the staged block only and meet.
+  // The prefetches are unconditional (past the last block they repeat it:
+  // valid addresses, unused data), so the count of loads in flight is the
+  // same at every block boundary and the compiler's waits stay exact.
+  const int klast = (nkb - 1) * kLmKB;
+  auto block = [&](int kb, const uint4* wa, uint4* w2, const bf16_t* cur, bf16_t* next) {
+    stage_h(min((kb + 1) * kLmKB, klast), next);
+    asm volatile("" ::: "memory");                   // keep the staging loads first in the count
+    load_w(min((kb + 2) * kLmKB, klast), w2);
+    asm volatile("" ::: "memory");
+    // The fragment reads are issued as inline ds_read_b128 with explicit LDS
+    // waits: the compiler cannot tell them from the staging DMA into the
+    // other buffer and would otherwise wait for every load, weights included,
+    // before the first read.  The block's own staging completed before the
+    // last barrier.
+    const uint32_t hbase = (uint32_t)(uintptr_t)(cur + l32 * kLmKB);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const lm_bf16x8 a = as_bf16x8(wa[s]);
+      const uint32_t addr = hbase + 2 * boff[s];
 #pragma unroll
-      for (int t = 0; t < kLmMTiles; ++t) {
-        const lm_bf16x8 b =
-            as_bf16x8(*reinterpret_cast<const uint4*>(hb + t * 32 * kLmLdsRow + 8 * s));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+      for (int t = 0; t < kLmMTiles; t += 2) {
+        uint4 b0, b1;
+        asm volatile("ds_read_b128 %0, %2 offset:%3\n\t"
+                     "ds_read_b128 %1, %2 offset:%4\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(b0), "=&v"(b1)
+                     : "v"(addr), "i"(t * 32 * kLmKB * 2), "i"((t + 1) * 32 * kLmKB * 2));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(b0), acc[t], 0, 0, 0);
+        acc[t + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(b1), acc[t + 1], 0, 0, 0);
       }
     }
-    if (more) {
-      store_h((kb + 1) & 1, hn);                     // that buffer's readers passed the last barrier
-#pragma unroll
-      for (int s = 0; s < 4; ++s) wa[s] = wn[s];
-    }
-    __syncthreads();
+    // Meet: the staged block is in LDS (its loads are older than the 4 weight
+    // loads, which stay in flight), and every wave's reads of this block's
+    // buffer have returned (its MFMAs consumed them), so the next staging may
+    // overwrite it.  A bare barrier: the workgroup fences of __syncthreads
+    // would also wait for the weight loads.
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    __builtin_amdgcn_s_barrier();
+  };
+  // six blocks per trip: the weight ring (3) and the LDS buffers (2) both
+  // index statically, so the compiler sees which buffer each access touches
+  for (int kb = 0; kb < nkb; kb += 6) {
+    block(kb, wr0, wr2, lds0, lds1);
+    if (kb + 1 < nkb) block(kb + 1, wr1, wr0, lds1, lds0);
+    if (kb + 2 < nkb) block(kb + 2, wr2, wr1, lds0, lds1);
+    if (kb + 3 < nkb) block(kb + 3, wr0, wr2, lds1, lds0);
+    if (kb + 4 < nkb) block(kb + 4, wr1, wr0, lds0, lds1);
+    if (kb + 5 < nkb) block(kb + 5, wr2, wr1, lds1, lds0);
   }
+  // the last blocks' repeated prefetches are still landing: drain them before
+  // the epilogue reuses LDS
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_barrier();
 
   // Epilogue.  acc[t][r] is logit (row m0 + 32 t + l32, id vbase + vof(r)).
-  float2* red = reinterpret_cast<float2*>(&lds[0][0]);   // [kLmWaves][kLmRows]; LDS is free now
+  float2* red = reinterpret_cast<float2*>(lds0);   // [kLmWaves][kLmRows]; LDS is free now
   const int vbase = tile * kLmVocab + wave * 32 + 4 * h;
   // 8-byte stores need every row to start 8-byte aligned
   const bool vec_ok = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0;
