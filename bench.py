@@ -159,6 +159,104 @@ def bench_sample(args):
         "hbm_gbps_whole_step": alg_bytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def bench_lm_head(args):
+    """The verification fused with the target LM head (specv_verify_lm_head)
+    at B=64, K=4, V=128256 with a D=4096 LM head: the target logits are
+    produced on the matrix cores from synthetic hidden states and weights
+    (small-integer values, so the float32 sums are exact) and reduced to row
+    statistics in the same kernel.  Reported for reference next to the
+    headline verification."""
+    import torch
+    import oracle as O
+    from oracle import lm_head as OL
+    from speculative_decoding_sampling_amd import binding
+    from speculative_decoding_sampling_amd.build import LIB
+    from speculative_decoding_sampling_amd.workloads import make_lm_head_workload, upload_lm_head
+
+    if not os.path.exists(LIB):
+        from speculative_decoding_sampling_amd.build import build
+        build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, K, V, D = 64, 4, 128256, 4096
+    t0 = time.perf_counter()
+    w = make_lm_head_workload(B, K, V, D, seed=3003)
+    log(f"LM-head workload B={B} K={K} V={V} D={D}: {time.perf_counter() - t0:.1f} s to generate")
+    a = upload_lm_head(w, dev)
+    M = B * (K + 1)
+    tl = torch.empty((B, K + 1, V), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    n = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = torch.empty(binding.lm_head_workspace_bytes(B, K, V, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.verify_lm_head(**a, target_logits=tl, out_tokens=out, n_emitted=n, workspace=ws,
+                               stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    ev.lib.hipEventRecord(ev.arr[0], stream.cuda_stream)
+    for _ in range(args.steps):
+        step()
+    ev.lib.hipEventRecord(ev.arr[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / args.steps
+    nn = n.cpu().numpy()
+    assert np.all((nn >= 1) & (nn <= w.draft_len + 1)), nn
+    # the LM-head kernel alone, for the roofline
+    reps = max(10, args.steps // 4)
+    logits = tl.view(M, V)
+    tws = torch.empty(M * ((V + 127) // 128) * 8, dtype=torch.uint8, device=dev)
+    ev.lib.hipEventRecord(ev.arr[0], stream.cuda_stream)
+    binding.bench_lm_head(a["hidden"].view(M, D), a["lm_head_weight"], logits, tws, reps,
+                          temperature=w.T, stream=stream, start=ev.arr[0], stop=ev.arr[1])
+    torch.cuda.synchronize()
+    k_us = ev.elapsed_ms(0, 1) / reps * 1e3
+    ev.close()
+    flops = 2.0 * M * V * D
+    hbm_bytes = V * D * 2 + M * D * 2 + M * V * 2       # weights and hidden read once, logits written
+    log(f"lm_head fused step {ms * 1e3:.1f} us; LM-head kernel {k_us:.1f} us "
+        f"({flops / k_us / 1e6:.0f} TFLOP/s, {hbm_bytes / k_us / 1e3:.0f} GB/s)")
+    result = {
+        "metric": "verified draft positions/sec, verification fused with the target LM head",
+        "value": w.positions / (ms * 1e-3), "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 MFMA (fp32 accumulate) + f32/f64 verification", "data": "synthetic",
+        "config": {"workload": f"B{B}_K{K}_V{V}_D{D}_lm_head_bf16", "B": B, "K": K, "V": V,
+                   "D": D, "temperature": w.T, "positions_per_step": w.positions,
+                   "input_sets": 1},
+        "roofline": {"bound": "mfma", "kernel": "lm_head", "achieved": flops / k_us / 1e6,
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": flops / k_us / 1e6 / 2500.0,
+                     "traffic": None, "launch_us": k_us, "flops_per_launch": flops,
+                     "hbm_gbps": hbm_bytes / k_us / 1e3, "hbm_bytes_per_launch": hbm_bytes},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on whole requests: its LM-head rows in float64, then verify
+        log(f"timing the oracle for about {args.cpu_seconds:.0f} s")
+        t_total, positions, reqs = 0.0, 0, 0
+        b = 0
+        while t_total < args.cpu_seconds and b < B:
+            t1 = time.perf_counter()
+            tb = OL.lm_head_target_bits(w.hidden[b:b + 1], w.weight)
+            O.verify(tb, w.draft[b:b + 1], w.draft_tokens[b:b + 1], w.draft_len[b:b + 1],
+                     w.u[b:b + 1], w.u_final[b:b + 1], w.T, 0, 1.0, w.eos_id, "bf16")
+            t_total += time.perf_counter() - t1
+            positions += int(w.draft_len[b])
+            reqs += 1
+            b += 1
+        result["cpu_baseline"] = {
+            "value": positions / t_total, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reqs} requests of the same workload (LM-head rows in float64 numpy, "
+                      f"then the verification), {t_total:.1f} s"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,10 +265,11 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["verify", "sample"], default="verify",
+    ap.add_argument("--op", choices=["verify", "sample", "lm_head"], default="verify",
                     help="verify: the verification step (default, the headline); sample: the "
-                         "draft-side draw of the same workload (256 draft rows), reported for "
-                         "reference")
+                         "draft-side draw of the same workload (256 draft rows); lm_head: the "
+                         "verification fused with a D=4096 target LM head; the last two are "
+                         "reported for reference")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -184,6 +283,8 @@ def main():
 
     if args.op == "sample":
         return bench_sample(args)
+    if args.op == "lm_head":
+        return bench_lm_head(args)
 
     import torch
     from speculative_decoding_sampling_amd import binding
