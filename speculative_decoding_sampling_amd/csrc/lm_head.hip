@@ -23,8 +23,8 @@
 // straight into registers, two blocks ahead of its use (the weights are
 // streamed from HBM exactly once per row block), while the block's 320 x 64
 // hidden states are loaded straight into LDS (double-buffered; 16-byte pieces
-// XOR-swizzled by row so the fragment reads of 8 consecutive lanes cover all
-// banks).  The k values of one MFMA step are
+// XOR-swizzled by row pair so each 16-lane pass of a fragment read covers all
+// 64 banks once).  The k values of one MFMA step are
 // {k0 + 32 h + 8 s + i : h = lane / 32, i < 8} for step s = 0..3: any
 // permutation of k shared by both operands leaves the dot product unchanged,
 // and this one makes each lane's weight bytes contiguous.
@@ -42,6 +42,7 @@ namespace specv {
 
 typedef __bf16 lm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float lm_f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t lm_u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLmThreads = 256;
 constexpr int kLmWaves = kLmThreads / kWave;        // 4
@@ -56,6 +57,7 @@ static_assert(kRowThreads * kRowVecs * 8 % kLmVocab == 0, "a statistics chunk is
 constexpr int kLmTilesPerChunk = kRowThreads * kRowVecs * 8 / kLmVocab;   // 64
 
 __device__ __forceinline__ lm_bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(lm_bf16x8, w); }
+__device__ __forceinline__ lm_bf16x8 as_bf16x8(lm_u32x4 w) { return __builtin_bit_cast(lm_bf16x8, w); }
 
 // float -> bfloat16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -67,14 +69,17 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm4 = 0x0F74;
 static_assert(kLmKB == 64, "wait immediates assume 4 weight loads per block");
+static_assert(kLmMTiles == 10, "the fragment pipeline is written out for 20 pairs");
 static_assert(kLmTilesPerChunk <= kWave, "one chunk's tiles fold in one wave");
 
 __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
     const bf16_t* __restrict__ H, const bf16_t* __restrict__ W, int M, int D, int V, int ntile,
     float c, bf16_t* __restrict__ out, float2* __restrict__ tpart) {
   // Hidden-state blocks, unpadded: row r's 16-byte piece p sits at slot
-  // p ^ (r & 7) of the row, so the fragment reads of 8 consecutive lanes
-  // (8 consecutive rows, one piece) fall in 8 different bank groups.
+  // p ^ ((r >> 1) & 7) of the row.  A 128-byte row covers half of the 64
+  // banks (even rows one half, odd rows the other), and one 16-lane pass of a
+  // fragment read (16 consecutive rows, one piece) then touches every bank
+  // once: 8 distinct slots among the even rows and 8 among the odd.
   __shared__ __attribute__((aligned(16))) bf16_t lds0[kLmRows * kLmKB];
   __shared__ __attribute__((aligned(16))) bf16_t lds1[kLmRows * kLmKB];
 
@@ -91,21 +96,22 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
   // Hidden-state staging goes straight to LDS: instruction j of wave w fills
   // slots [(10 w + j) 64, +64), rows 8 (10 w + j) .. +8; lane i fills slot i
   // of those, i.e. row 8 (10 w + j) + i / 8 at position i % 8, which holds piece
-  // (i % 8) ^ (row & 7).  Rows past M repeat row M - 1 (their sums are dropped).
-  const bf16_t* hsrc[kLmHPer];
-#pragma unroll
-  for (int j = 0; j < kLmHPer; ++j) {
-    const int r = 8 * (kLmHPer * wave + j) + lane / 8;
-    const int pc = (lane % 8) ^ (r & 7);
-    hsrc[j] = H + (size_t)min(m0 + r, M - 1) * D + pc * 8;
-  }
+  // (i % 8) ^ ((row >> 1) & 7).  Rows past M repeat row M - 1 (their sums are
+  // dropped).
+  // Row r_j = r0 + 8 j of instruction j has ((r_j >> 1) & 7) equal to
+  // ((r0 >> 1) & 7) ^ 4 (j & 1), so each source is formed on the fly from r0.
+  const int r0 = 8 * kLmHPer * wave + lane / 8;
+  const int pc0 = (lane % 8) ^ ((r0 >> 1) & 7);
   auto stage_h = [&](int k0, bf16_t* buf) {
 #pragma unroll
-    for (int j = 0; j < kLmHPer; ++j)
+    for (int j = 0; j < kLmHPer; ++j) {
+      const int row = min(m0 + r0 + 8 * j, M - 1);
+      const bf16_t* src = H + (size_t)row * D + (pc0 ^ (4 * (j & 1))) * 8 + k0;
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(hsrc[j] + k0),
+          (const __attribute__((address_space(1))) void*)src,
           (__attribute__((address_space(3))) void*)(buf + (kLmHPer * wave + j) * 64 * 8), 16, 0,
           0);
+    }
   };
   auto load_w = [&](int k0, uint4* w) {
     const uint4* src = reinterpret_cast<const uint4*>(wrow + k0);
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
   // B fragment of tile t, step s: row 32 t + l32, piece 4 h + s
   int boff[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) boff[s] = (((4 * h + s) ^ (l32 & 7)) * 8);
+  for (int s = 0; s < 4; ++s) boff[s] = (((4 * h + s) ^ ((l32 >> 1) & 7)) * 8);   // 32 t: no effect
 
   const int nkb = D / kLmKB;
   uint4 wr0[4], wr1[4], wr2[4];                      // weight ring: blocks kb, kb+1, kb+2
@@ -143,28 +149,44 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
     asm volatile("" ::: "memory");                   // keep the staging loads first in the count
     load_w(min((kb + 2) * kLmKB, klast), w2);
     asm volatile("" ::: "memory");
-    // The fragment reads are issued as inline ds_read_b128 with explicit LDS
-    // waits: the compiler cannot tell them from the staging DMA into the
-    // other buffer and would otherwise wait for every load, weights included,
-    // before the first read.  The block's own staging completed before the
-    // last barrier.
+    // The fragment reads are inline ds_read_b128 with explicit LDS waits: the
+    // compiler cannot tell them from the staging DMA into the other buffer
+    // and would otherwise wait for every load, weights included, before the
+    // first read.  They are software-pipelined: the next pair of fragments is
+    // requested before the current pair's MFMAs, and the wait that releases a
+    // pair takes its registers as in-out operands, so no MFMA can move ahead
+    // of it.  The block's own staging completed before the last barrier.
     const uint32_t hbase = (uint32_t)(uintptr_t)(cur + l32 * kLmKB);
+    uint32_t addr[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const lm_bf16x8 a = as_bf16x8(wa[s]);
-      const uint32_t addr = hbase + 2 * boff[s];
-#pragma unroll
-      for (int t = 0; t < kLmMTiles; t += 2) {
-        uint4 b0, b1;
-        asm volatile("ds_read_b128 %0, %2 offset:%3\n\t"
-                     "ds_read_b128 %1, %2 offset:%4\n\t"
-                     "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(b0), "=&v"(b1)
-                     : "v"(addr), "i"(t * 32 * kLmKB * 2), "i"((t + 1) * 32 * kLmKB * 2));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(b0), acc[t], 0, 0, 0);
-        acc[t + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(b1), acc[t + 1], 0, 0, 0);
-      }
-    }
+    for (int s = 0; s < 4; ++s) addr[s] = hbase + 2 * boff[s];
+    lm_u32x4 f0[2], f1[2];                           // the two pair buffers
+    constexpr int kTP = kLmMTiles / 2;               // tile pairs per step
+#define SPECV_LDS_READ2(dst, q)                                                              \
+  asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4"             \
+               : "=&v"(dst[0]), "=&v"(dst[1])                                                  \
+               : "v"(addr[(q) / kTP]), "i"(((q) % kTP) * 2 * 32 * kLmKB * 2),                  \
+                 "i"((((q) % kTP) * 2 + 1) * 32 * kLmKB * 2))
+#define SPECV_PAIR(q, cf, nf, WAITN)                                                         \
+  {                                                                                          \
+    if ((q) + 1 < 4 * kTP) SPECV_LDS_READ2(nf, (q) + 1 < 4 * kTP ? (q) + 1 : 0);              \
+    asm volatile("s_waitcnt lgkmcnt(" #WAITN ")" : "+v"(cf[0]), "+v"(cf[1]));               \
+    const lm_bf16x8 a_ = as_bf16x8(wa[(q) / kTP]);                                          \
+    const int t_ = ((q) % kTP) * 2;                                                          \
+    acc[t_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, as_bf16x8(cf[0]), acc[t_], 0, 0, 0); \
+    acc[t_ + 1] =                                                                            \
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, as_bf16x8(cf[1]), acc[t_ + 1], 0, 0, 0);  \
+  }
+    SPECV_LDS_READ2(f0, 0);
+    SPECV_PAIR(0, f0, f1, 2) SPECV_PAIR(1, f1, f0, 2) SPECV_PAIR(2, f0, f1, 2)
+    SPECV_PAIR(3, f1, f0, 2) SPECV_PAIR(4, f0, f1, 2) SPECV_PAIR(5, f1, f0, 2)
+    SPECV_PAIR(6, f0, f1, 2) SPECV_PAIR(7, f1, f0, 2) SPECV_PAIR(8, f0, f1, 2)
+    SPECV_PAIR(9, f1, f0, 2) SPECV_PAIR(10, f0, f1, 2) SPECV_PAIR(11, f1, f0, 2)
+    SPECV_PAIR(12, f0, f1, 2) SPECV_PAIR(13, f1, f0, 2) SPECV_PAIR(14, f0, f1, 2)
+    SPECV_PAIR(15, f1, f0, 2) SPECV_PAIR(16, f0, f1, 2) SPECV_PAIR(17, f1, f0, 2)
+    SPECV_PAIR(18, f0, f1, 2) SPECV_PAIR(19, f1, f0, 0)
+#undef SPECV_PAIR
+#undef SPECV_LDS_READ2
     // Meet: the staged block is in LDS (its loads are older than the 4 weight
     // loads, which stay in flight), and every wave's reads of this block's
     // buffer have returned (its MFMAs consumed them), so the next staging may
