@@ -36,7 +36,7 @@ HBM_PEAK_GBPS = 8000.0
 # HBM bytes of one row-statistics launch on this workload, from rocprofv3
 # FETCH_SIZE and WRITE_SIZE runs scaled by a plain-copy calibration (see the
 # profiles directory); valid only for the sources they were taken with.
-ROW_STATS_TRAFFIC = {"sources_sha256_16": "955f8a5a9d95818f", "bytes": 148137301}
+ROW_STATS_TRAFFIC = {"sources_sha256_16": "f0804ab9644a5c5b", "bytes": 148139654}
 WORKLOAD = 3
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,K=4,V=128k"
 
