@@ -39,7 +39,8 @@ def test_header_declares_the_api():
                           "specv_bench_row_stats", "specv_sample",
                           "specv_acceptance_rates", "specv_round_stats",
                           "specv_monitor_state_bytes", "specv_monitor_reset",
-                          "specv_monitor_update"}, names
+                          "specv_monitor_update", "specv_lm_head_workspace_bytes",
+                          "specv_verify_lm_head", "specv_bench_lm_head"}, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -247,3 +248,54 @@ def test_monitor_sizes_and_bad_arguments(lib):
     assert call(W=0) == 1 and call(W=4097) == 1
     assert call(st=None) == 1 and call(nxt=None) == 1 and call(dt=None) == 1
     assert call(st=20) == 1 and call(rate=20) == 1
+
+
+def test_lm_head_workspace_sizes(lib):
+    f = lib.specv_lm_head_workspace_bytes
+    f.argtypes = [ctypes.c_int] * 4
+    f.restype = ctypes.c_size_t
+    g = lib.specv_workspace_bytes
+    g.argtypes = [ctypes.c_int] * 5 + [ctypes.c_float]
+    g.restype = ctypes.c_size_t
+    n = f(64, 4, 128256, 4096)
+    # the unfiltered bf16 layout plus the LM head's tile statistics
+    assert n >= g(64, 4, 128256, 1, 0, 1.0) + 64 * 5 * ((128256 + 127) // 128) * 8
+    assert n % 256 == 0
+    assert f(64, 4, 128256, 4096) == f(64, 4, 128256, 64)        # D only validated
+    assert f(64, 4, 128256, 100) == 0                             # D not a multiple of 64
+    assert f(64, 4, 128256, 0) == 0
+    assert f(64, 4, 128256, 65536 + 64) == 0                      # above SPECV_MAX_D
+    assert f(0, 4, 100, 64) == 0 and f(1, 64, 100, 64) == 0 and f(1, 4, 0, 64) == 0
+
+
+def test_lm_head_validation_returns_before_any_gpu_work(lib):
+    v = lib.specv_verify_lm_head
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    v.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, vp, vp,
+                  ctypes.c_size_t, vp, vp, vp, vp, vp]
+    v.restype = ci
+    d = ctypes.c_void_p(4096)
+    base = [d, d, d, d, d, d, d, 4, 4, 1000, 64, 1.0, -1, d, d, d, d, 1 << 30, None,
+            None, None, None, None]
+    idx = {"hidden": 0, "weight": 1, "B": 7, "K": 8, "V": 9, "D": 10, "T": 11, "eos": 12,
+           "out": 13, "ws": 16, "ws_bytes": 17}
+
+    def call(**kw):
+        args = list(base)
+        for k, val in kw.items():
+            args[idx[k]] = val
+        return v(*args)
+
+    assert call(D=100) == 1
+    assert call(D=0) == 1
+    assert call(B=0) == 1
+    assert call(K=64) == 1
+    assert call(T=0.0) == 1
+    assert call(eos=1000) == 1
+    assert call(hidden=None) == 1
+    assert call(hidden=ctypes.c_void_p(4104)) == 1               # not 16-byte aligned
+    assert call(weight=ctypes.c_void_p(4098)) == 1
+    assert call(out=None) == 1
+    assert call(ws_bytes=16) == 2
+    assert call(ws=None) == 2
+    assert call(D=65536 + 64) == 4                                # SPECV_EUNSUPPORTED
