@@ -64,6 +64,26 @@ def test_fused_exact_parity(B, K, V, D, ragged, seed):
     assert not rep["mismatches"], rep["mismatches"][:5]
 
 
+@pytest.mark.parametrize("T,eos_id,seed", [(0.7, -1, 61), (1.3, 17, 62)])
+def test_fused_exact_parity_temperature_and_eos(T, eos_id, seed):
+    B, K, V, D = 16, 4, 6000, 256
+    print(f"[lm_head] T={T} eos={eos_id} B={B} K={K} V={V} D={D} seed={seed}", flush=True)
+    w = make_lm_head_workload(B, K, V, D, seed=seed, T=T, ragged=True, eos_id=eos_id)
+    if eos_id >= 0:
+        # make EOS occur: some drafted tokens are the EOS id (their acceptance
+        # still follows p and q at that id)
+        w.draft_tokens[::3, 0] = eos_id
+    g = run_fused(w)
+    t_bits = OL.lm_head_target_bits(w.hidden, w.weight)
+    assert np.array_equal(g["target_bits"], t_bits)
+    o = O.verify(t_bits, w.draft, w.draft_tokens, w.draft_len, w.u, w.u_final, w.T, 0, 1.0,
+                 w.eos_id, "bf16")
+    rep = compare(g, o, w.K)
+    print(f"  requests={rep['requests']} positions={rep['positions']} flagged={rep['flagged']} "
+          f"paths={np.bincount(o['path'] + 1, minlength=4).tolist()}", flush=True)
+    assert not rep["mismatches"], rep["mismatches"][:5]
+
+
 def test_fused_general_inputs_logits_within_accumulation_bound():
     B, K, V, D = 3, 3, 3001, 1024
     w = make_lm_head_workload(B, K, V, D, seed=21, exact=False)
