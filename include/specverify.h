@@ -283,19 +283,49 @@ SPECV_API specv_status_t specv_monitor_update(const int32_t *draft_tokens,
                                               double *rate, hipStream_t stream);
 
 /*
+ * LM-head weights in the order the fused call reads them.  The weights are a
+ * model constant: pack them once, when the model is loaded, and pass the
+ * packed copy to every specv_verify_lm_head call.
+ *
+ * The packed matrix is [ceil(V/128)][D/64][4][4][64] 16-byte pieces of bf16;
+ * piece (t, kb, w, s, l) holds lm_head_weight[128 t + 32 w + l % 32][64 kb +
+ * 32 (l / 32) + 8 s .. + 7], and zeros for vocabulary ids >= V.  Each load
+ * instruction of the LM-head kernel then reads 1 KB of consecutive bytes and
+ * each workgroup streams one contiguous range, instead of 128 rows D * 2
+ * bytes apart.
+ *
+ * specv_lm_head_packed_weight_bytes: ceil(V/128) * 128 * D * 2, or 0 for
+ * invalid sizes (V outside [1, SPECV_MAX_V], D not a positive multiple of 64
+ * or above SPECV_MAX_D).
+ *
+ * specv_lm_head_pack_weight:
+ *  lm_head_weight  [V][D] bf16 row-major, device, 16-byte aligned (read only).
+ *  packed_weight   device output of specv_lm_head_packed_weight_bytes(V, D)
+ *                  bytes, 16-byte aligned, not overlapping lm_head_weight.
+ * SPECV_EINVAL for invalid sizes, null, misaligned or overlapping pointers;
+ * SPECV_EHIP if the launch fails.  Asynchronous on `stream`; allocates
+ * nothing.
+ */
+SPECV_API size_t specv_lm_head_packed_weight_bytes(int V, int D);
+SPECV_API specv_status_t specv_lm_head_pack_weight(const void *lm_head_weight,
+                                                   void *packed_weight, int V, int D,
+                                                   hipStream_t stream);
+
+/*
  * The verification step fused with the target model's LM head (tbxsx.cn,
  * "推测解码采样验证优化策略 —— 深度调研报告", section "6. 扩展性与安全性": fuse the
  * verification-stage forward pass of the target model with the sampling
  * step).  The target logits are computed on the matrix cores from the target
  * model's final hidden states, logits[b][k][v] = sum_d hidden[b][k][d] *
- * lm_head_weight[v][d] (bf16 products, float32 accumulation, rounded to bf16
+ * weight[v][d] (bf16 products, float32 accumulation, rounded to bf16
  * nearest-even), and the softmax statistics of each target row are taken in
  * the same kernel, from the rounded values, before the logits leave the chip;
  * the rest is specv_verify on those logits (no top-k / top-p).
  *
  *  hidden          [B][K+1][D] bf16, device, 16-byte aligned: the hidden state
  *                  that produces target row k of request b.
- *  lm_head_weight  [V][D] bf16, device, 16-byte aligned.
+ *  packed_weight   the LM-head weight [V][D] bf16 as specv_lm_head_pack_weight
+ *                  writes it for this V and D; device, 16-byte aligned.
  *  D               > 0, a multiple of 64, <= SPECV_MAX_D.
  *  target_logits   [B][K+1][V] bf16, device output: the LM head's logits
  *                  (every row, whatever draft_len is); the draws read it.
@@ -307,11 +337,11 @@ SPECV_API specv_status_t specv_monitor_update(const int32_t *draft_tokens,
  *                  specv_verify_debug.
  *
  * Status codes as specv_verify; SPECV_EINVAL also for D not a multiple of
- * 64 or misaligned hidden / weight.  Per-request errors as specv_verify.
+ * 64 or misaligned hidden / packed weight.  Per-request errors as specv_verify.
  * Asynchronous on `stream`; allocates nothing.
  */
 SPECV_API size_t specv_lm_head_workspace_bytes(int B, int K, int V, int D);
-SPECV_API specv_status_t specv_verify_lm_head(const void *hidden, const void *lm_head_weight,
+SPECV_API specv_status_t specv_verify_lm_head(const void *hidden, const void *packed_weight,
                                               const void *draft_logits,
                                               const int32_t *draft_tokens,
                                               const int32_t *draft_len, const float *u,

@@ -53,7 +53,8 @@ SPECV_API specv_status_t specv_bench_row_stats(const void *const *targets,
  * and their per-128-id tile statistics), `reps` launches on `stream` between
  * hipEventRecord(start) and hipEventRecord(stop), for the roofline.
  *
- *  hidden [M][D] bf16, lm_head_weight [V][D] bf16 (device, 16-byte aligned),
+ *  hidden [M][D] bf16, packed_weight as specv_lm_head_pack_weight writes it for
+ *  this V and D (device, 16-byte aligned),
  *  logits [M][V] bf16 device output; D a multiple of 64, <= SPECV_MAX_D.
  *  workspace  at least M * ceil(V / 128) * 8 bytes, 16-byte aligned (the
  *             tile statistics are written there).
@@ -62,7 +63,7 @@ SPECV_API specv_status_t specv_bench_row_stats(const void *const *targets,
  * or null events; SPECV_EWORKSPACE for a short workspace; SPECV_EHIP if a
  * launch or event record fails.  Asynchronous.
  */
-SPECV_API specv_status_t specv_bench_lm_head(const void *hidden, const void *lm_head_weight,
+SPECV_API specv_status_t specv_bench_lm_head(const void *hidden, const void *packed_weight,
                                              int M, int D, int V, float temperature,
                                              void *logits, void *workspace,
                                              size_t workspace_bytes, int reps,

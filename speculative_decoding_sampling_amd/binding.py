@@ -88,6 +88,10 @@ def load_library():
                                               c_int, c_float, c_vp, c_size, c_int, c_vp, c_vp,
                                               c_vp]
         lib.specv_bench_row_stats.restype = c_int
+        lib.specv_lm_head_packed_weight_bytes.argtypes = [c_int, c_int]
+        lib.specv_lm_head_packed_weight_bytes.restype = c_size
+        lib.specv_lm_head_pack_weight.argtypes = [c_vp, c_vp, c_int, c_int, c_vp]
+        lib.specv_lm_head_pack_weight.restype = c_int
         lib.specv_lm_head_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
         lib.specv_lm_head_workspace_bytes.restype = c_size
         lib.specv_verify_lm_head.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
@@ -411,17 +415,51 @@ def verify(target_logits, draft_logits, draft_tokens, draft_len, u, u_final, tem
     return res
 
 
+class PackedLmHeadWeight:
+    """An LM-head weight [V, D] bf16 in the layout the fused call reads
+    (``specv_lm_head_pack_weight``): ``data`` is the packed device buffer."""
+
+    def __init__(self, data, V, D):
+        self.data, self.V, self.D = data, int(V), int(D)
+
+
+def lm_head_packed_weight_bytes(V, D):
+    return int(load_library().specv_lm_head_packed_weight_bytes(int(V), int(D)))
+
+
+def pack_lm_head_weight(weight, stream=None):
+    """Repack an LM-head weight [V, D] bf16 (GPU) once for ``verify_lm_head``;
+    asynchronous on ``stream``."""
+    lib = load_library()
+    if weight.device.type != "cuda" or weight.dim() != 2:
+        raise ValueError("weight must be a [V, D] GPU tensor")
+    V, D = weight.shape
+    _check(weight, "weight", torch.bfloat16, (V, D), weight.device)
+    nbytes = lm_head_packed_weight_bytes(V, D)
+    if nbytes == 0:
+        raise SpecVerifyError(SPECV_EINVAL, f"unsupported LM-head shape V={V} D={D}")
+    data = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=weight.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(weight.device)
+    st = lib.specv_lm_head_pack_weight(_ptr(weight), _ptr(data), V, D,
+                                       ctypes.c_void_p(stream.cuda_stream))
+    if st != SPECV_OK:
+        raise SpecVerifyError(st, status_string(st))
+    return PackedLmHeadWeight(data, V, D)
+
+
 def lm_head_workspace_bytes(B, K, V, D):
     return int(load_library().specv_lm_head_workspace_bytes(int(B), int(K), int(V), int(D)))
 
 
-def verify_lm_head(hidden, lm_head_weight, draft_logits, draft_tokens, draft_len, u, u_final,
+def verify_lm_head(hidden, packed_weight, draft_logits, draft_tokens, draft_len, u, u_final,
                    temperature=1.0, eos_id=-1, *, target_logits=None, out_tokens=None,
                    n_emitted=None, workspace=None, debug=False, stream=None):
     """The verification step fused with the target model's LM head.
 
     Shapes: hidden [B, K+1, D] bf16 (the target model's final hidden states),
-    lm_head_weight [V, D] bf16, draft_logits [B, K, V] bf16, draft_tokens
+    packed_weight a ``PackedLmHeadWeight`` (``pack_lm_head_weight`` of the
+    [V, D] bf16 weight), draft_logits [B, K, V] bf16, draft_tokens
     [B, K] int32, draft_len [B] int32, u [B, K] fp32, u_final [B] fp32; D a
     multiple of 64.  Returns a dict with ``target_logits`` [B, K+1, V] bf16
     (the LM head's output), ``out_tokens`` and ``n_emitted``, plus the
@@ -429,14 +467,17 @@ def verify_lm_head(hidden, lm_head_weight, draft_logits, draft_tokens, draft_len
     ``stream``."""
     lib = load_library()
     dev = hidden.device
-    if dev.type != "cuda" or hidden.dim() != 3 or lm_head_weight.dim() != 2:
-        raise ValueError("hidden must be a [B, K+1, D] and lm_head_weight a [V, D] GPU tensor")
+    if dev.type != "cuda" or hidden.dim() != 3 or not isinstance(packed_weight, PackedLmHeadWeight):
+        raise ValueError("hidden must be a [B, K+1, D] GPU tensor and packed_weight a "
+                         "PackedLmHeadWeight")
     B, K1, D = hidden.shape
     K = K1 - 1
-    V = lm_head_weight.shape[0]
+    V = packed_weight.V
+    if packed_weight.D != D:
+        raise ValueError(f"packed weight has D={packed_weight.D}, hidden D={D}")
     bf = torch.bfloat16
     _check(hidden, "hidden", bf, (B, K + 1, D), dev)
-    _check(lm_head_weight, "lm_head_weight", bf, (V, D), dev)
+    _check(packed_weight.data, "packed_weight", bf, (lm_head_packed_weight_bytes(V, D) // 2,), dev)
     _check(draft_logits, "draft_logits", bf, (B, K, V), dev)
     _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
     _check(draft_len, "draft_len", torch.int32, (B,), dev)
@@ -464,7 +505,7 @@ def verify_lm_head(hidden, lm_head_weight, draft_logits, draft_tokens, draft_len
         res["stop_pos"] = torch.empty((B,), dtype=torch.int32, device=dev)
         res["path"] = torch.empty((B,), dtype=torch.int32, device=dev)
         diag = [res["accept_prob"], res["residual_mass"], res["stop_pos"], res["path"]]
-    st = lib.specv_verify_lm_head(_ptr(hidden), _ptr(lm_head_weight), _ptr(draft_logits),
+    st = lib.specv_verify_lm_head(_ptr(hidden), _ptr(packed_weight.data), _ptr(draft_logits),
                                   _ptr(draft_tokens), _ptr(draft_len), _ptr(u), _ptr(u_final), B,
                                   K, V, D, float(temperature), int(eos_id), _ptr(target_logits),
                                   _ptr(out_tokens), _ptr(n_emitted), _ptr(workspace),
@@ -475,17 +516,19 @@ def verify_lm_head(hidden, lm_head_weight, draft_logits, draft_tokens, draft_len
     return res
 
 
-def bench_lm_head(hidden, lm_head_weight, logits, workspace, reps, temperature=1.0, stream=None,
+def bench_lm_head(hidden, packed_weight, logits, workspace, reps, temperature=1.0, stream=None,
                   start=None, stop=None):
-    """Benchmark hook: the LM-head kernel alone (hidden [M, D], weight [V, D],
-    logits [M, V], all bf16), ``reps`` launches between the HIP events
-    ``start`` and ``stop`` (raw handles) recorded on ``stream``."""
+    """Benchmark hook: the LM-head kernel alone (hidden [M, D] and logits
+    [M, V] bf16, a ``PackedLmHeadWeight``), ``reps`` launches between the HIP
+    events ``start`` and ``stop`` (raw handles) recorded on ``stream``."""
     lib = load_library()
     M, D = hidden.shape
-    V = lm_head_weight.shape[0]
+    V = packed_weight.V
+    if packed_weight.D != D:
+        raise ValueError(f"packed weight has D={packed_weight.D}, hidden D={D}")
     if stream is None:
         stream = torch.cuda.current_stream(hidden.device)
-    st = lib.specv_bench_lm_head(_ptr(hidden), _ptr(lm_head_weight), M, D, V, float(temperature),
+    st = lib.specv_bench_lm_head(_ptr(hidden), _ptr(packed_weight.data), M, D, V, float(temperature),
                                  _ptr(logits), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), int(reps),
                                  ctypes.c_void_p(stream.cuda_stream), start, stop)

@@ -19,15 +19,23 @@
 // Work split.  A workgroup of 4 waves owns 128 vocabulary ids (32 per wave)
 // and 320 hidden rows (10 tiles of 32; larger M runs more row blocks); two
 // workgroups share a CU, so one computes while the other waits.  Per
-// 64-wide k block each lane reads 64 contiguous bytes of its weight row
-// straight into registers, two blocks ahead of its use (the weights are
-// streamed from HBM exactly once per row block), while the block's 320 x 64
-// hidden states are loaded straight into LDS (double-buffered; 16-byte pieces
-// XOR-swizzled by row pair so each 16-lane pass of a fragment read covers all
-// 64 banks once).  The k values of one MFMA step are
-// {k0 + 32 h + 8 s + i : h = lane / 32, i < 8} for step s = 0..3: any
-// permutation of k shared by both operands leaves the dot product unchanged,
-// and this one makes each lane's weight bytes contiguous.
+// 64-wide k block each wave reads its 32 x 64 weights straight into
+// registers, two blocks ahead of their use (the weights are streamed from HBM
+// exactly once per row block), while the block's 320 x 64 hidden states are
+// loaded straight into LDS (double-buffered; 16-byte pieces XOR-swizzled by
+// row pair so each 16-lane pass of a fragment read covers all 64 banks once).
+// The k values of one MFMA step are {k0 + 32 h + 8 s + i : h = lane / 32,
+// i < 8} for step s = 0..3: any permutation of k shared by both operands
+// leaves the dot product unchanged.
+//
+// Weight layout.  The weights are repacked once, when the model is loaded,
+// into the order the kernel reads them: [tile][k block][wave][step s][lane]
+// 16-byte pieces, piece (t, kb, w, s, l) holding
+// W[128 t + 32 w + l % 32][64 kb + 32 (l / 32) + 8 s .. + 7], zero past V.
+// One load instruction then reads 1 KB of consecutive bytes and a workgroup
+// streams one contiguous 1 MB range, where the row-major matrix costs it 128
+// rows 8 KB apart per block (measured 379 vs 326 us per launch at M = 320,
+// D = 4096, V = 128256).
 //
 // Epilogue.  Each accumulator is rounded to bfloat16 (nearest even) and
 // written; the statistics are taken over the rounded values, the logits every
@@ -55,6 +63,8 @@ constexpr int kLmHPer = kLmHPieces / kLmThreads;    // 10 per thread
 static_assert(kLmHPieces % kLmThreads == 0, "hidden block pieces per thread");
 static_assert(kRowThreads * kRowVecs * 8 % kLmVocab == 0, "a statistics chunk is whole tiles");
 constexpr int kLmTilesPerChunk = kRowThreads * kRowVecs * 8 / kLmVocab;   // 64
+constexpr int kLmPackWave = 4 * kWave * 8;             // packed elements of one wave's block
+constexpr int kLmPackBlock = kLmWaves * kLmPackWave;   // of one workgroup's block (16 KB)
 
 __device__ __forceinline__ lm_bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(lm_bf16x8, w); }
 __device__ __forceinline__ lm_bf16x8 as_bf16x8(lm_u32x4 w) { return __builtin_bit_cast(lm_bf16x8, w); }
@@ -89,9 +99,10 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int h = lane / 32, l32 = lane % 32;
 
-  // This lane's weight row (rows past V read row V - 1; their sums are dropped).
-  const int v_lane = tile * kLmVocab + wave * 32 + l32;
-  const bf16_t* wrow = W + (size_t)min(v_lane, V - 1) * D + 32 * h;
+  // This wave's packed weights: block kb at wbase + kb * kLmPackBlock, step s
+  // of this lane at + s * 512 + lane * 8 elements (ids past V are zeros;
+  // their sums are dropped).
+  const bf16_t* wbase = W + ((size_t)tile * (D / kLmKB) * kLmWaves + wave) * kLmPackWave + lane * 8;
 
   // Hidden-state staging goes straight to LDS: instruction j of wave w fills
   // slots [(10 w + j) 64, +64), rows 8 (10 w + j) .. +8; lane i fills slot i
@@ -114,9 +125,9 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
     }
   };
   auto load_w = [&](int k0, uint4* w) {
-    const uint4* src = reinterpret_cast<const uint4*>(wrow + k0);
+    const bf16_t* src = wbase + (size_t)(k0 / kLmKB) * kLmPackBlock;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) w[s] = src[s];
+    for (int s = 0; s < 4; ++s) w[s] = *reinterpret_cast<const uint4*>(src + s * kWave * 8);
   };
 
   lm_f32x16 acc[kLmMTiles];
@@ -311,7 +322,43 @@ __global__ __launch_bounds__(kWave) void fold_tile_stats_kernel(
   }
 }
 
+// Weight repack, one thread per 16-byte piece of the packed matrix (the
+// layout described at the top of this file).
+__global__ __launch_bounds__(256) void lm_head_pack_kernel(const bf16_t* __restrict__ W,
+                                                           bf16_t* __restrict__ P, int V, int D,
+                                                           size_t pieces) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= pieces) return;
+  const int nkb = D / kLmKB;
+  const int lane = (int)(i % kWave);
+  size_t r = i / kWave;
+  const int s = (int)(r % 4);
+  r /= 4;
+  const int wave = (int)(r % kLmWaves);
+  r /= kLmWaves;
+  const int kb = (int)(r % nkb);
+  const size_t tile = r / nkb;
+  const size_t v = tile * kLmVocab + wave * 32 + lane % 32;
+  const int k = kb * kLmKB + 32 * (lane / 32) + 8 * s;
+  uint4 val = make_uint4(0u, 0u, 0u, 0u);
+  if (v < (size_t)V) val = *reinterpret_cast<const uint4*>(W + v * D + k);
+  *reinterpret_cast<uint4*>(P + i * 8) = val;
+}
+
 int lm_head_tiles(int V) { return (V + kLmVocab - 1) / kLmVocab; }
+size_t lm_head_packed_elems(int V, int D) { return (size_t)lm_head_tiles(V) * kLmVocab * D; }
+
+hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int D,
+                               hipStream_t stream) {
+  if (D % kLmKB != 0) return hipErrorInvalidConfiguration;
+  const size_t pieces = lm_head_packed_elems(V, D) / 8;
+  const size_t blocks = (pieces + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  lm_head_pack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      static_cast<const bf16_t*>(weight), static_cast<bf16_t*>(packed), V, D, pieces);
+  return hipGetLastError();
+}
 int lm_head_rows_per_block() { return kLmRows; }
 int lm_head_kblock() { return kLmKB; }
 

@@ -16,6 +16,9 @@ hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const i
                             const int* tokens, int B, int K, int V, int nchunk, float c,
                             float2* part, float* zx, hipStream_t stream, int row_lo = 0);
 int lm_head_tiles(int V);
+size_t lm_head_packed_elems(int V, int D);
+hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int D,
+                               hipStream_t stream);
 int lm_head_rows_per_block();
 int lm_head_kblock();
 hipError_t launch_lm_head(const void* hidden, const void* weight, int M, int D, int V, float c,
@@ -286,7 +289,7 @@ specv_status_t run_lm_head(const void* hidden, const void* weight, const void* d
   if (!hidden || !weight || !target_out || !draft_len || !u_final || !out_tokens || !n_emitted)
     return SPECV_EINVAL;
   if (K > 0 && (!draft || !tokens || !u)) return SPECV_EINVAL;
-  // 16-byte loads of hidden-state and weight rows (D is a multiple of 64)
+  // 16-byte loads of hidden-state rows and packed weights (D is a multiple of 64)
   if (misaligned(hidden, 16) || misaligned(weight, 16) || misaligned(target_out, 2) ||
       (draft && misaligned(draft, 2)))
     return SPECV_EINVAL;
@@ -430,12 +433,37 @@ specv_status_t specv_bench_row_stats(const void* const* targets, const void* con
   return hipEventRecord(stop, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }
 
+size_t specv_lm_head_packed_weight_bytes(int V, int D) {
+  if (V < 1 || V > SPECV_MAX_V || D < 1 || D % specv::lm_head_kblock() != 0 || D > SPECV_MAX_D)
+    return 0;
+  return specv::lm_head_packed_elems(V, D) * sizeof(uint16_t);
+}
+
+specv_status_t specv_lm_head_pack_weight(const void* lm_head_weight, void* packed_weight, int V,
+                                         int D, hipStream_t stream) {
+  using namespace specv;
+  if (V < 1 || V > SPECV_MAX_V || D < 1 || D % lm_head_kblock() != 0 || D > SPECV_MAX_D)
+    return SPECV_EINVAL;
+  if (!lm_head_weight || !packed_weight || misaligned(lm_head_weight, 16) ||
+      misaligned(packed_weight, 16))
+    return SPECV_EINVAL;
+  // the packed copy must not overlap the source
+  const char* a = static_cast<const char*>(lm_head_weight);
+  const char* p = static_cast<const char*>(packed_weight);
+  const size_t na = (size_t)V * D * sizeof(uint16_t);
+  const size_t np = lm_head_packed_elems(V, D) * sizeof(uint16_t);
+  if (a < p + np && p < a + na) return SPECV_EINVAL;
+  return launch_lm_head_pack(lm_head_weight, packed_weight, V, D, stream) == hipSuccess
+             ? SPECV_OK
+             : SPECV_EHIP;
+}
+
 size_t specv_lm_head_workspace_bytes(int B, int K, int V, int D) {
   if (specv::check_lm_sizes(B, K, V, D) != SPECV_OK) return 0;
   return specv::make_lm_layout(B, K, V).total;
 }
 
-specv_status_t specv_verify_lm_head(const void* hidden, const void* lm_head_weight,
+specv_status_t specv_verify_lm_head(const void* hidden, const void* packed_weight,
                                     const void* draft_logits, const int32_t* draft_tokens,
                                     const int32_t* draft_len, const float* u,
                                     const float* u_final, int B, int K, int V, int D,
@@ -444,13 +472,13 @@ specv_status_t specv_verify_lm_head(const void* hidden, const void* lm_head_weig
                                     size_t workspace_bytes, hipStream_t stream,
                                     float* accept_prob, double* residual_mass,
                                     int32_t* stop_pos, int32_t* path) {
-  return specv::run_lm_head(hidden, lm_head_weight, draft_logits, draft_tokens, draft_len, u,
+  return specv::run_lm_head(hidden, packed_weight, draft_logits, draft_tokens, draft_len, u,
                             u_final, B, K, V, D, temperature, eos_id, target_logits, out_tokens,
                             n_emitted, workspace, workspace_bytes, stream, accept_prob,
                             residual_mass, stop_pos, path);
 }
 
-specv_status_t specv_bench_lm_head(const void* hidden, const void* lm_head_weight, int M, int D,
+specv_status_t specv_bench_lm_head(const void* hidden, const void* packed_weight, int M, int D,
                                    int V, float temperature, void* logits, void* workspace,
                                    size_t workspace_bytes, int reps, hipStream_t stream,
                                    hipEvent_t start, hipEvent_t stop) {
@@ -459,15 +487,15 @@ specv_status_t specv_bench_lm_head(const void* hidden, const void* lm_head_weigh
       D > SPECV_MAX_D || reps < 1 || !start || !stop)
     return SPECV_EINVAL;
   if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SPECV_EINVAL;
-  if (!hidden || !lm_head_weight || !logits || misaligned(hidden, 16) ||
-      misaligned(lm_head_weight, 16) || misaligned(logits, 2))
+  if (!hidden || !packed_weight || !logits || misaligned(hidden, 16) ||
+      misaligned(packed_weight, 16) || misaligned(logits, 2))
     return SPECV_EINVAL;
   const size_t need = (size_t)M * lm_head_tiles(V) * sizeof(float2);
   if (!workspace || misaligned(workspace, 16) || workspace_bytes < need) return SPECV_EWORKSPACE;
   const float c = (float)(1.4426950408889634 / (double)temperature);
   if (hipEventRecord(start, stream) != hipSuccess) return SPECV_EHIP;
   for (int i = 0; i < reps; ++i)
-    if (launch_lm_head(hidden, lm_head_weight, M, D, V, c, logits,
+    if (launch_lm_head(hidden, packed_weight, M, D, V, c, logits,
                        static_cast<float2*>(workspace), stream) != hipSuccess)
       return SPECV_EHIP;
   return hipEventRecord(stop, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;

@@ -305,15 +305,18 @@ def make_lm_head_workload(B, K, V, D, seed=2000, exact=True, T=1.0, draft_sigma=
 
 
 def upload_lm_head(w, device="cuda"):
-    """Copy an LM-head workload to the GPU as ``binding.verify_lm_head`` takes it."""
+    """Copy an LM-head workload to the GPU as ``binding.verify_lm_head`` takes it
+    (the weight repacked once by the library, as at model load)."""
     import torch
+
+    from speculative_decoding_sampling_amd import binding
 
     def bf(a):
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
 
     return dict(
         hidden=bf(w.hidden),
-        lm_head_weight=bf(w.weight),
+        packed_weight=binding.pack_lm_head_weight(bf(w.weight)),
         draft_logits=bf(w.draft),
         draft_tokens=torch.from_numpy(w.draft_tokens).to(device),
         draft_len=torch.from_numpy(w.draft_len).to(device),

@@ -130,7 +130,7 @@ def test_fused_host_argument_errors():
     def call(D_=D, ws_bytes=None, hidden=None, T=1.0):
         h = args["hidden"] if hidden is None else hidden
         return lib.specv_verify_lm_head(
-            p(h), p(args["lm_head_weight"]), p(args["draft_logits"]), p(args["draft_tokens"]),
+            p(h), p(args["packed_weight"].data), p(args["draft_logits"]), p(args["draft_tokens"]),
             p(args["draft_len"]), p(args["u"]), p(args["u_final"]), B, K, V, D_, T, -1, p(tl),
             p(out), p(n), p(ws), ws.numel() if ws_bytes is None else ws_bytes, s, None, None,
             None, None)
@@ -158,8 +158,51 @@ def test_bench_lm_head_hook_runs():
     hid = a["hidden"].reshape(M, w.D)
     logits = torch.empty((M, w.V), dtype=torch.bfloat16, device=DEV)
     ws = torch.empty(M * ((w.V + 127) // 128) * 8, dtype=torch.uint8, device=DEV)
-    binding.bench_lm_head(hid, a["lm_head_weight"], logits, ws, 3, start=ev[0], stop=ev[1])
+    binding.bench_lm_head(hid, a["packed_weight"], logits, ws, 3, start=ev[0], stop=ev[1])
     torch.cuda.synchronize()
     t_bits = OL.lm_head_target_bits(w.hidden, w.weight).reshape(M, w.V)
     got = logits.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, t_bits)
+
+
+@pytest.mark.parametrize("V,D", [(300, 128), (128, 64), (1, 192)])
+def test_packed_weight_layout(V, D):
+    # the documented layout: piece (t, kb, w, s, l) of 8 values holds
+    # weight[128 t + 32 w + l % 32][64 kb + 32 (l / 32) + 8 s + i], zeros past V
+    print(f"[lm_head] pack V={V} D={D}", flush=True)
+    rng = np.random.default_rng(V + D)
+    wbits = rng.integers(0, 0x7F7F, size=(V, D), dtype=np.uint16)
+    wt = torch.from_numpy(wbits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    pk = binding.pack_lm_head_weight(wt)
+    torch.cuda.synchronize()
+    got = pk.data.view(torch.int16).cpu().numpy().view(np.uint16)
+    ntile, nkb = (V + 127) // 128, D // 64
+    assert got.size == ntile * 128 * D
+    want = np.zeros(got.size, dtype=np.uint16)
+    for t in range(ntile):
+        for kb in range(nkb):
+            for w in range(4):
+                for s in range(4):
+                    for l in range(64):
+                        v = 128 * t + 32 * w + l % 32
+                        piece = (((t * nkb + kb) * 4 + w) * 4 + s) * 64 + l
+                        if v < V:
+                            k = 64 * kb + 32 * (l // 32) + 8 * s
+                            want[8 * piece:8 * piece + 8] = wbits[v, k:k + 8]
+    assert np.array_equal(got, want)
+
+
+def test_pack_argument_errors():
+    lib = binding.load_library()
+    wt = torch.zeros((256, 128), dtype=torch.bfloat16, device=DEV)
+    n = binding.lm_head_packed_weight_bytes(256, 128)
+    buf = torch.empty(n // 2 + 16, dtype=torch.bfloat16, device=DEV)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = binding._ptr
+    assert lib.specv_lm_head_pack_weight(p(wt), p(buf), 256, 128, s) == 0
+    assert lib.specv_lm_head_pack_weight(p(wt), p(buf[1:]), 256, 128, s) == 1   # misaligned
+    assert lib.specv_lm_head_pack_weight(p(wt), p(wt), 256, 128, s) == 1        # in place
+    assert lib.specv_lm_head_pack_weight(p(wt), p(buf), 256, 100, s) == 1
+    with pytest.raises(TypeError):
+        binding.pack_lm_head_weight(wt.float())
+    torch.cuda.synchronize()

@@ -40,7 +40,9 @@ def test_header_declares_the_api():
                           "specv_acceptance_rates", "specv_round_stats",
                           "specv_monitor_state_bytes", "specv_monitor_reset",
                           "specv_monitor_update", "specv_lm_head_workspace_bytes",
-                          "specv_verify_lm_head", "specv_bench_lm_head"}, names
+                          "specv_verify_lm_head", "specv_bench_lm_head",
+                          "specv_lm_head_packed_weight_bytes",
+                          "specv_lm_head_pack_weight"}, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -266,6 +268,31 @@ def test_lm_head_workspace_sizes(lib):
     assert f(64, 4, 128256, 0) == 0
     assert f(64, 4, 128256, 65536 + 64) == 0                      # above SPECV_MAX_D
     assert f(0, 4, 100, 64) == 0 and f(1, 64, 100, 64) == 0 and f(1, 4, 0, 64) == 0
+
+
+def test_lm_head_packed_weight_sizes_and_validation(lib):
+    f = lib.specv_lm_head_packed_weight_bytes
+    f.argtypes = [ctypes.c_int] * 2
+    f.restype = ctypes.c_size_t
+    # whole 128-id tiles of D bf16 values each
+    assert f(128256, 4096) == 1002 * 128 * 4096 * 2
+    assert f(128, 64) == 128 * 64 * 2
+    assert f(129, 64) == 256 * 64 * 2
+    assert f(1, 64) == 128 * 64 * 2
+    assert f(0, 64) == 0 and f(100, 0) == 0 and f(100, 96) == 0 and f(100, 65536 + 64) == 0
+    p = lib.specv_lm_head_pack_weight
+    vp = ctypes.c_void_p
+    p.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    p.restype = ctypes.c_int
+    src, dst = vp(1 << 20), vp(1 << 30)
+    assert p(None, dst, 100, 64, None) == 1
+    assert p(src, None, 100, 64, None) == 1
+    assert p(vp((1 << 20) + 8), dst, 100, 64, None) == 1         # not 16-byte aligned
+    assert p(src, vp((1 << 30) + 4), 100, 64, None) == 1
+    assert p(src, dst, 100, 96, None) == 1                       # D not a multiple of 64
+    assert p(src, dst, 0, 64, None) == 1
+    assert p(src, vp((1 << 20) + 4096), 100, 64, None) == 1      # overlaps the source
+    assert p(vp((1 << 20) + 4096), src, 100, 64, None) == 1
 
 
 def test_lm_head_validation_returns_before_any_gpu_work(lib):
