@@ -210,7 +210,7 @@ def bench_lm_head(args):
     # the LM-head kernel alone, for the roofline
     reps = max(10, args.steps // 4)
     logits = tl.view(M, V)
-    tws = torch.empty(M * ((V + 127) // 128) * 8, dtype=torch.uint8, device=dev)
+    tws = torch.empty(M * ((V + 255) // 256) * 8, dtype=torch.uint8, device=dev)
     ev.lib.hipEventRecord(ev.arr[0], stream.cuda_stream)
     binding.bench_lm_head(a["hidden"].view(M, D), a["packed_weight"], logits, tws, reps,
                           temperature=w.T, stream=stream, start=ev.arr[0], stop=ev.arr[1])

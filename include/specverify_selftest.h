@@ -50,13 +50,13 @@ SPECV_API specv_status_t specv_bench_row_stats(const void *const *targets,
 
 /*
  * Benchmark hook: the LM-head kernel of specv_verify_lm_head alone (logits
- * and their per-128-id tile statistics), `reps` launches on `stream` between
+ * and their per-256-id tile statistics), `reps` launches on `stream` between
  * hipEventRecord(start) and hipEventRecord(stop), for the roofline.
  *
  *  hidden [M][D] bf16, packed_weight as specv_lm_head_pack_weight writes it for
  *  this V and D (device, 16-byte aligned),
  *  logits [M][V] bf16 device output; D a multiple of 64, <= SPECV_MAX_D.
- *  workspace  at least M * ceil(V / 128) * 8 bytes, 16-byte aligned (the
+ *  workspace  at least M * ceil(V / 256) * 8 bytes, 16-byte aligned (the
  *             tile statistics are written there).
  *
  * SPECV_EINVAL for bad sizes, temperature, reps, null or misaligned pointers

@@ -16,33 +16,36 @@
 // holds one hidden row per lane and 16 vocabulary ids per register set, so
 // the per-row statistics are mostly an in-register reduction.
 //
-// Work split.  A workgroup of 4 waves owns 128 vocabulary ids (32 per wave)
-// and 320 hidden rows (10 tiles of 32; larger M runs more row blocks); two
-// workgroups share a CU, so one computes while the other waits.  Per
-// 64-wide k block each wave reads its 32 x 64 weights straight into
-// registers, two blocks ahead of their use (the weights are streamed from HBM
-// exactly once per row block), while the block's 320 x 64 hidden states are
-// loaded straight into LDS (double-buffered; 16-byte pieces XOR-swizzled by
-// row pair so each 16-lane pass of a fragment read covers all 64 banks once).
+// Work split.  A workgroup of 8 waves (one per CU, two per SIMD) owns 256
+// vocabulary ids (32 per wave) and 320 hidden rows (10 tiles of 32; larger M
+// runs more row blocks).  Per 64-wide k block each wave reads its 32 x 64
+// weights straight into registers, two blocks ahead of their use (the
+// weights are streamed from HBM exactly once per row block), while the
+// block's 320 x 64 hidden states are loaded straight into LDS, also two
+// blocks ahead (three buffers; 16-byte pieces XOR-swizzled by row pair so
+// each 16-lane pass of a fragment read covers all 64 banks once).  One
+// 8-wave workgroup stages each hidden block once per CU; two 4-wave
+// workgroups per CU each staged it (330 vs 308 us per launch at M = 320,
+// D = 4096, V = 128256).
 // The k values of one MFMA step are {k0 + 32 h + 8 s + i : h = lane / 32,
 // i < 8} for step s = 0..3: any permutation of k shared by both operands
 // leaves the dot product unchanged.
 //
 // Weight layout.  The weights are repacked once, when the model is loaded,
-// into the order the kernel reads them: [tile][k block][wave][step s][lane]
-// 16-byte pieces, piece (t, kb, w, s, l) holding
+// into the order the kernel reads them: [128-id tile][k block][32-id group]
+// [step s][lane] 16-byte pieces, piece (t, kb, w, s, l) holding
 // W[128 t + 32 w + l % 32][64 kb + 32 (l / 32) + 8 s .. + 7], zero past V.
 // One load instruction then reads 1 KB of consecutive bytes and a workgroup
-// streams one contiguous 1 MB range, where the row-major matrix costs it 128
-// rows 8 KB apart per block (measured 379 vs 326 us per launch at M = 320,
-// D = 4096, V = 128256).
+// streams two contiguous ranges, where the row-major matrix costs it rows
+// 8 KB apart per block (measured 379 vs 326 us per launch with 4-wave
+// workgroups at M = 320, D = 4096, V = 128256).
 //
 // Epilogue.  Each accumulator is rounded to bfloat16 (nearest even) and
 // written; the statistics are taken over the rounded values, the logits every
 // later stage reads.  Per row: the max and sum over the lane's 16 ids, the
-// lane pair holding the other 16, then the 4 waves through LDS in a fixed
-// order, giving one (max, normaliser) per 128-id tile.  fold_tile_stats then
-// combines 64 tiles into the 8192-id chunk partials of the row-statistics
+// lane pair holding the other 16, then the 8 waves through LDS in a fixed
+// order, giving one (max, normaliser) per 256-id tile.  fold_tile_stats then
+// combines 32 tiles into the 8192-id chunk partials of the row-statistics
 // layout, and records the logit of each row's drafted token.
 #include "common.h"
 
@@ -52,19 +55,22 @@ typedef __bf16 lm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float lm_f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t lm_u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kLmThreads = 256;
-constexpr int kLmWaves = kLmThreads / kWave;        // 4
-constexpr int kLmVocab = kLmWaves * 32;             // 128 vocabulary ids per workgroup
+constexpr int kLmThreads = 512;
+constexpr int kLmWaves = kLmThreads / kWave;        // 8
+constexpr int kLmVocab = kLmWaves * 32;             // 256 vocabulary ids per workgroup
 constexpr int kLmMTiles = 10;
 constexpr int kLmRows = kLmMTiles * 32;             // 320 hidden rows per row block
 constexpr int kLmKB = 64;                           // k per block
 constexpr int kLmHPieces = kLmRows * kLmKB / 8;     // 16-byte pieces of one hidden block
-constexpr int kLmHPer = kLmHPieces / kLmThreads;    // 10 per thread
+constexpr int kLmHPer = kLmHPieces / kLmThreads;    // 5 per thread
 static_assert(kLmHPieces % kLmThreads == 0, "hidden block pieces per thread");
 static_assert(kRowThreads * kRowVecs * 8 % kLmVocab == 0, "a statistics chunk is whole tiles");
-constexpr int kLmTilesPerChunk = kRowThreads * kRowVecs * 8 / kLmVocab;   // 64
-constexpr int kLmPackWave = 4 * kWave * 8;             // packed elements of one wave's block
-constexpr int kLmPackBlock = kLmWaves * kLmPackWave;   // of one workgroup's block (16 KB)
+constexpr int kLmTilesPerChunk = kRowThreads * kRowVecs * 8 / kLmVocab;   // 32
+constexpr int kLmPackVocab = 128;                      // vocabulary ids per packed tile
+constexpr int kLmPackGroups = kLmPackVocab / 32;       // 32-id groups (one wave each) per tile
+constexpr int kLmPackWave = 4 * kWave * 8;             // packed elements of one group's block
+constexpr int kLmPackBlock = kLmPackGroups * kLmPackWave;   // of one tile's block (16 KB)
+static_assert(kLmVocab % kLmPackVocab == 0, "a workgroup covers whole packed tiles");
 
 __device__ __forceinline__ lm_bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(lm_bf16x8, w); }
 __device__ __forceinline__ lm_bf16x8 as_bf16x8(lm_u32x4 w) { return __builtin_bit_cast(lm_bf16x8, w); }
@@ -77,12 +83,13 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 
 // s_waitcnt immediates (vector-memory count only; LDS / export counts untouched)
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm4 = 0x0F74;
-static_assert(kLmKB == 64, "wait immediates assume 4 weight loads per block");
+constexpr int kWaitVm13 = 0x0F7D;
+static_assert(kLmKB == 64 && kLmHPer == 5,
+              "wait immediates assume 5 staging and 4 weight loads per block");
 static_assert(kLmMTiles == 10, "the fragment pipeline is written out for 20 pairs");
 static_assert(kLmTilesPerChunk <= kWave, "one chunk's tiles fold in one wave");
 
-__global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
+__global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
     const bf16_t* __restrict__ H, const bf16_t* __restrict__ W, int M, int D, int V, int ntile,
     float c, bf16_t* __restrict__ out, float2* __restrict__ tpart) {
   // Hidden-state blocks, unpadded: row r's 16-byte piece p sits at slot
@@ -92,6 +99,7 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
   // once: 8 distinct slots among the even rows and 8 among the odd.
   __shared__ __attribute__((aligned(16))) bf16_t lds0[kLmRows * kLmKB];
   __shared__ __attribute__((aligned(16))) bf16_t lds1[kLmRows * kLmKB];
+  __shared__ __attribute__((aligned(16))) bf16_t lds2[kLmRows * kLmKB];
 
   const int tile = blockIdx.x % ntile;
   const int m0 = (blockIdx.x / ntile) * kLmRows;
@@ -99,14 +107,19 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int h = lane / 32, l32 = lane % 32;
 
-  // This wave's packed weights: block kb at wbase + kb * kLmPackBlock, step s
-  // of this lane at + s * 512 + lane * 8 elements (ids past V are zeros;
-  // their sums are dropped).
-  const bf16_t* wbase = W + ((size_t)tile * (D / kLmKB) * kLmWaves + wave) * kLmPackWave + lane * 8;
+  // This wave's packed weights (packed tile ptile, group wave % 4): block kb
+  // at wbase + kb * kLmPackBlock, step s of this lane at + s * 512 + lane * 8
+  // elements.  Ids past V are zeros, and a packed tile wholly past V (the
+  // second half of a last, half-used workgroup tile) repeats the last one:
+  // their sums are dropped.
+  const int ptiles = (V + kLmPackVocab - 1) / kLmPackVocab;
+  const int ptile = min(tile * (kLmVocab / kLmPackVocab) + wave / kLmPackGroups, ptiles - 1);
+  const bf16_t* wbase = W + ((size_t)ptile * (D / kLmKB) * kLmPackGroups + wave % kLmPackGroups) *
+                                kLmPackWave + lane * 8;
 
   // Hidden-state staging goes straight to LDS: instruction j of wave w fills
-  // slots [(10 w + j) 64, +64), rows 8 (10 w + j) .. +8; lane i fills slot i
-  // of those, i.e. row 8 (10 w + j) + i / 8 at position i % 8, which holds piece
+  // slots [(5 w + j) 64, +64), rows 8 (5 w + j) .. +8; lane i fills slot i
+  // of those, i.e. row 8 (5 w + j) + i / 8 at position i % 8, which holds piece
   // (i % 8) ^ ((row >> 1) & 7).  Rows past M repeat row M - 1 (their sums are
   // dropped).
   // Row r_j = r0 + 8 j of instruction j has ((r_j >> 1) & 7) equal to
@@ -143,20 +156,21 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
 
   const int nkb = D / kLmKB;
   uint4 wr0[4], wr1[4], wr2[4];                      // weight ring: blocks kb, kb+1, kb+2
+  const int klast = (nkb - 1) * kLmKB;
   stage_h(0, lds0);
   load_w(0, wr0);
-  if (nkb > 1) load_w(kLmKB, wr1);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
+  stage_h(min(kLmKB, klast), lds1);
+  load_w(min(kLmKB, klast), wr1);
+  __builtin_amdgcn_s_waitcnt(kWaitVm13);             // block 0 staged: 13 younger loads may fly
+  __builtin_amdgcn_s_barrier();
 
-  // One k block: stage the next hidden block, request the weights two blocks
-  // ahead, multiply, then wait for the staged block only and meet.
+  // One k block: stage the hidden block and request the weights two blocks
+  // ahead, multiply, then wait for the next block's staging only and meet.
   // The prefetches are unconditional (past the last block they repeat it:
   // valid addresses, unused data), so the count of loads in flight is the
   // same at every block boundary and the compiler's waits stay exact.
-  const int klast = (nkb - 1) * kLmKB;
   auto block = [&](int kb, const uint4* wa, uint4* w2, const bf16_t* cur, bf16_t* next) {
-    stage_h(min((kb + 1) * kLmKB, klast), next);
+    stage_h(min((kb + 2) * kLmKB, klast), next);
     asm volatile("" ::: "memory");                   // keep the staging loads first in the count
     load_w(min((kb + 2) * kLmKB, klast), w2);
     asm volatile("" ::: "memory");
@@ -198,23 +212,21 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_kernel(
     SPECV_PAIR(18, f0, f1, 2) SPECV_PAIR(19, f1, f0, 0)
 #undef SPECV_PAIR
 #undef SPECV_LDS_READ2
-    // Meet: the staged block is in LDS (its loads are older than the 4 weight
-    // loads, which stay in flight), and every wave's reads of this block's
-    // buffer have returned (its MFMAs consumed them), so the next staging may
+    // Meet: block kb + 1 is in LDS (its 5 staging loads are older than the
+    // 13 issued since: weights kb + 1, staging and weights kb + 2, which stay
+    // in flight), and every wave's reads of this block's buffer have returned
+    // (its MFMAs consumed them), so the staging issued in the next block may
     // overwrite it.  A bare barrier: the workgroup fences of __syncthreads
     // would also wait for the weight loads.
-    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    __builtin_amdgcn_s_waitcnt(kWaitVm13);
     __builtin_amdgcn_s_barrier();
   };
-  // six blocks per trip: the weight ring (3) and the LDS buffers (2) both
+  // three blocks per trip: the weight ring and the LDS buffers (three each)
   // index statically, so the compiler sees which buffer each access touches
-  for (int kb = 0; kb < nkb; kb += 6) {
-    block(kb, wr0, wr2, lds0, lds1);
+  for (int kb = 0; kb < nkb; kb += 3) {
+    block(kb, wr0, wr2, lds0, lds2);
     if (kb + 1 < nkb) block(kb + 1, wr1, wr0, lds1, lds0);
-    if (kb + 2 < nkb) block(kb + 2, wr2, wr1, lds0, lds1);
-    if (kb + 3 < nkb) block(kb + 3, wr0, wr2, lds1, lds0);
-    if (kb + 4 < nkb) block(kb + 4, wr1, wr0, lds0, lds1);
-    if (kb + 5 < nkb) block(kb + 5, wr2, wr1, lds1, lds0);
+    if (kb + 2 < nkb) block(kb + 2, wr2, wr1, lds2, lds1);
   }
   // the last blocks' repeated prefetches are still landing: drain them before
   // the epilogue reuses LDS
@@ -334,11 +346,11 @@ __global__ __launch_bounds__(256) void lm_head_pack_kernel(const bf16_t* __restr
   size_t r = i / kWave;
   const int s = (int)(r % 4);
   r /= 4;
-  const int wave = (int)(r % kLmWaves);
-  r /= kLmWaves;
+  const int group = (int)(r % kLmPackGroups);
+  r /= kLmPackGroups;
   const int kb = (int)(r % nkb);
   const size_t tile = r / nkb;
-  const size_t v = tile * kLmVocab + wave * 32 + lane % 32;
+  const size_t v = tile * kLmPackVocab + group * 32 + lane % 32;
   const int k = kb * kLmKB + 32 * (lane / 32) + 8 * s;
   uint4 val = make_uint4(0u, 0u, 0u, 0u);
   if (v < (size_t)V) val = *reinterpret_cast<const uint4*>(W + v * D + k);
@@ -346,7 +358,9 @@ __global__ __launch_bounds__(256) void lm_head_pack_kernel(const bf16_t* __restr
 }
 
 int lm_head_tiles(int V) { return (V + kLmVocab - 1) / kLmVocab; }
-size_t lm_head_packed_elems(int V, int D) { return (size_t)lm_head_tiles(V) * kLmVocab * D; }
+size_t lm_head_packed_elems(int V, int D) {
+  return (size_t)((V + kLmPackVocab - 1) / kLmPackVocab) * kLmPackVocab * D;
+}
 
 hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int D,
                                hipStream_t stream) {

@@ -157,7 +157,7 @@ def test_bench_lm_head_hook_runs():
     M = w.B * (w.K + 1)
     hid = a["hidden"].reshape(M, w.D)
     logits = torch.empty((M, w.V), dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(M * ((w.V + 127) // 128) * 8, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(M * ((w.V + 255) // 256) * 8, dtype=torch.uint8, device=DEV)
     binding.bench_lm_head(hid, a["packed_weight"], logits, ws, 3, start=ev[0], stop=ev[1])
     torch.cuda.synchronize()
     t_bits = OL.lm_head_target_bits(w.hidden, w.weight).reshape(M, w.V)
