@@ -206,3 +206,30 @@ def test_pack_argument_errors():
     with pytest.raises(TypeError):
         binding.pack_lm_head_weight(wt.float())
     torch.cuda.synchronize()
+
+
+def test_fused_full_size_sampled():
+    # the benchmarked launch: B=64, K=4, V=128256, D=4096; the oracle checks a
+    # sample of requests (their 5 target rows bit for bit, then their
+    # verification); every request's counts and padding are checked
+    B, K, V, D = 64, 4, 128256, 4096
+    print(f"[lm_head] full size B={B} K={K} V={V} D={D}", flush=True)
+    w = make_lm_head_workload(B, K, V, D, seed=3003)
+    g = run_fused(w)
+    n, out = g["n_emitted"], g["out_tokens"]
+    assert np.all((n >= 1) & (n <= w.draft_len + 1))
+    for b in range(B):
+        assert np.all(out[b, :n[b]] >= 0) and np.all(out[b, :n[b]] < V)
+        assert np.all(out[b, n[b]:] == -1)
+    sample = np.array([0, 7, 19, 26, 33, 41, 50, 63])
+    t_bits = OL.lm_head_target_bits(w.hidden[sample], w.weight)
+    got = g["target_bits"].reshape(B, K + 1, V)[sample]
+    assert np.array_equal(got, t_bits), int(np.sum(got != t_bits))
+    o = O.verify(t_bits, w.draft[sample], w.draft_tokens[sample], w.draft_len[sample],
+                 w.u[sample], w.u_final[sample], w.T, 0, 1.0, w.eos_id, "bf16")
+    gs = {k: v[sample] for k, v in g.items() if k != "target_bits"}
+    rep = compare(gs, o, K)
+    print(f"  sampled requests={rep['requests']} positions={rep['positions']} "
+          f"flagged={rep['flagged']} paths={np.bincount(o['path'] + 1, minlength=4).tolist()}",
+          flush=True)
+    assert not rep["mismatches"], rep["mismatches"][:5]
