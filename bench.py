@@ -14,9 +14,17 @@ Output: exactly one JSON line on stdout (progress goes to stderr):
   roofline         the dominant kernel (row statistics): algorithmic bytes per launch
                    over its mean duration (a burst of launches between two HIP events),
                    against the 8 TB/s HBM peak
+  us_per_call      median, p10 and p90 of single calls (a pass with one event per call)
   cpu_baseline     the fp64 oracle on this host, on a bounded sample of the same workload
 Inputs rotate over several independent sets whose total exceeds twice the
 256 MB last-level cache, so reads come from HBM.
+
+--workload N runs the same measurement on the other synthetic workloads (1: B=8,
+K=4, V=4096 fp32; 2: B=1, K=5, V=32000 bf16, T=0.8; 4: B=256, K=8, V=152064 fp32,
+T=0.7, top-k 50 then top-p 0.9; 5: B=64, ragged drafts up to 8, V=129280 bf16,
+EOS), for reference next to the headline.  On workload 4 the draft tokens are
+drawn from the processed draft rows by the library's own sampler (specv_sample),
+and the dominant kernel is the top-k candidate pass, timed per call.
 """
 
 import argparse
@@ -82,22 +90,30 @@ def row_stats_sources_hash():
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, budget_s):
-    """Time the fp64 oracle on whole calls of the same workload, single core."""
+def cpu_baseline(w, budget_s, group=None):
+    """Time the fp64 oracle on the same workload, single core: whole calls, or
+    groups of ``group`` requests in turn where a whole call is too long for
+    the budget."""
     import oracle as O
     reps, t_total, positions = 0, 0.0, 0
-    reqs = list(range(w.B))
+    groups = ([list(range(w.B))] if group is None else
+              [list(range(i, min(i + group, w.B))) for i in range(0, w.B, group)])
     while t_total < budget_s:
+        reqs = groups[reps % len(groups)]
         t0 = time.perf_counter()
         O.verify(w.target, w.draft, w.draft_tokens, w.draft_len, w.u, w.u_final, w.T, w.top_k,
                  w.top_p, w.eos_id, w.dtype, requests=reqs)
         t_total += time.perf_counter() - t0
-        positions += w.positions
+        positions += int(np.sum(w.draft_len[reqs]))
         reps += 1
+    if group is None:
+        what = f"{reps} whole calls of the same workload (B={w.B}, K={w.K}, V={w.V})"
+    else:
+        what = (f"{reps} groups of {group} requests of the same workload (B={w.B}, K={w.K}, "
+                f"V={w.V})")
     return {"value": positions / t_total, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} whole calls of the same workload (B={w.B}, K={w.K}, V={w.V}), "
-                      f"{t_total:.1f} s of single-threaded numpy fp64",
-            "seconds_per_call": t_total / reps}
+            "sample": f"{what}, {t_total:.1f} s of single-threaded numpy fp64",
+            "seconds_per_call": t_total / reps * (1 if group is None else w.B / group)}
 
 
 def bench_sample(args):
@@ -263,7 +279,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sets", type=int, default=4, help="input sets rotated through")
+    ap.add_argument("--sets", type=int, default=None,
+                    help="input sets rotated through (default 4; 1 for workload 4, 2.6 GB each)")
+    ap.add_argument("--workload", type=int, choices=[1, 2, 3, 4, 5], default=WORKLOAD,
+                    help="synthetic workload of the verify op (3, the default, is the headline)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--op", choices=["verify", "sample", "lm_head"], default="verify",
@@ -282,6 +301,11 @@ def main():
             "with no communication (see the design notes); run with --gpus 1")
         sys.exit(2)
 
+    if args.sets is None:
+        args.sets = 1 if args.workload == 4 else 4
+    if args.op != "verify" and args.workload != WORKLOAD:
+        log("--workload applies to the verify op only")
+        sys.exit(2)
     if args.op == "sample":
         return bench_sample(args)
     if args.op == "lm_head":
@@ -290,7 +314,8 @@ def main():
     import torch
     from speculative_decoding_sampling_amd import binding
     from speculative_decoding_sampling_amd.build import LIB
-    from speculative_decoding_sampling_amd.workloads import WORKLOADS, make_workload, upload
+    from speculative_decoding_sampling_amd.workloads import (WORKLOADS, make_workload, upload,
+                                                             uniforms)
 
     if not os.path.exists(LIB):
         from speculative_decoding_sampling_amd.build import build
@@ -298,25 +323,46 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    wl = args.workload
+    spec = WORKLOADS[wl]
+    filtered = 0 < spec["top_k"] < spec["V"] or spec["top_p"] < 1.0
     sets, hosts = [], []
     for i in range(args.sets):
         t0 = time.perf_counter()
-        w = make_workload(WORKLOAD, seed=1000 + WORKLOAD + 100 * i)
+        seed = 1000 + wl + 100 * i
+        if filtered:
+            # placeholder drafts, replaced below by draws from the processed
+            # draft rows made on the GPU by specv_sample
+            w = make_workload(wl, seed=seed, draft_sampler=lambda z, T, k, p, x: 0)
+        else:
+            w = make_workload(wl, seed=seed)
         hosts.append(w)
         a = upload(w, dev)
+        if filtered:
+            R = w.B * w.K
+            ud = torch.from_numpy(uniforms(np.random.default_rng(seed + 7), R)).to(dev)
+            tok = binding.sample(a["draft_logits"].reshape(R, w.V), ud, w.T, w.top_k, w.top_p)
+            a["draft_tokens"] = tok.reshape(w.B, w.K).contiguous()
+            w.draft_tokens = a["draft_tokens"].cpu().numpy()
+            assert np.all((w.draft_tokens >= 0) & (w.draft_tokens < w.V))
         a["out_tokens"] = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
         a["n_emitted"] = torch.empty((w.B,), dtype=torch.int32, device=dev)
         sets.append(a)
         log(f"input set {i}: {w.algorithmic_bytes / 1e6:.1f} MB needed rows, "
             f"{w.positions} positions ({time.perf_counter() - t0:.1f} s to generate)")
     w0 = hosts[0]
-    positions = w0.positions
-    alg_bytes = w0.algorithmic_bytes
-    assert all(h.positions == positions and h.algorithmic_bytes == alg_bytes for h in hosts)
+    # per-step means over the sets the timed steps cycle through (the sets
+    # differ only where draft lengths are ragged)
+    positions = float(np.mean([hosts[i % len(hosts)].positions for i in range(args.steps)]))
+    alg_bytes = float(np.mean([hosts[i % len(hosts)].algorithmic_bytes
+                               for i in range(args.steps)]))
+    if positions.is_integer() and alg_bytes.is_integer():
+        positions, alg_bytes = int(positions), int(alg_bytes)
 
     stream = torch.cuda.current_stream(dev)
-    ws = torch.empty(binding.workspace_bytes(w0.B, w0.K, w0.V, torch.bfloat16), dtype=torch.uint8,
-                     device=dev)
+    ldt = sets[0]["target_logits"].dtype
+    ws = torch.empty(binding.workspace_bytes(w0.B, w0.K, w0.V, ldt, w0.top_k, w0.top_p),
+                     dtype=torch.uint8, device=dev)
 
     def step(i, events=None):
         binding.verify(**sets[i % len(sets)], workspace=ws, stream=stream, events=events)
@@ -352,8 +398,21 @@ def main():
     torch.cuda.synchronize()
     log(f"host enqueue {host_us:.2f} us/call")
 
+    # Single-call durations: one event before each call and one after the last.
+    evc = HipEvents(args.steps + 1)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evc.lib.hipEventRecord(evc.arr[i], stream.cuda_stream)
+        step(i)
+    evc.lib.hipEventRecord(evc.arr[args.steps], stream.cuda_stream)
+    torch.cuda.synchronize()
+    call_us = np.array([evc.elapsed_ms(i, i + 1) for i in range(args.steps)]) * 1e3
+    evc.close()
+    p10, med, p90 = (float(x) for x in np.percentile(call_us, [10, 50, 90]))
+    log(f"single calls: median {med:.2f} us, p10 {p10:.2f}, p90 {p90:.2f}")
+
     # Per-kernel durations: the same steps through the timing entry point.
-    names = binding.stage_names()
+    names = binding.stage_names(filtered)
     nst = len(names)
     evs = [HipEvents(nst + 1) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -381,23 +440,39 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 5 copies of {args.copy_calibration_mib} MiB")
 
-    # The dominant kernel alone, for the roofline: a burst of row-statistics
-    # launches cycling over the input sets between two events on the stream.
-    reps = max(40, args.steps)
-    evb = HipEvents(2)
-    torch.cuda.synchronize()
-    binding.bench_row_stats(sets, ws, reps, w0.T, stream, evb.arr[0], evb.arr[1])
-    torch.cuda.synchronize()
-    dominant = "row_stats"
-    k1_us = evb.elapsed_ms(0, 1) / reps * 1e3
-    traffic = (ROW_STATS_TRAFFIC["bytes"]
-               if row_stats_sources_hash() == ROW_STATS_TRAFFIC["sources_sha256_16"] else None)
-    evb.close()
-    log(f"row_stats alone: {k1_us:.2f} us/launch over {reps} launches")
-    achieved = alg_bytes / (k1_us * 1e-6) / 1e9
+    if filtered:
+        # The dominant kernel is the top-k candidate pass (one read of every
+        # needed row); its duration is the per-call stage mean above.
+        dominant = "filter_cand"
+        k1_us = stage_us[dominant]
+        traffic = None
+        log(f"filter_cand: {k1_us:.2f} us/launch (stage mean)")
+    else:
+        # The dominant kernel alone, for the roofline: a burst of row-statistics
+        # launches cycling over the input sets between two events on the stream.
+        reps = max(40, args.steps)
+        evb = HipEvents(2)
+        torch.cuda.synchronize()
+        binding.bench_row_stats(sets, ws, reps, w0.T, stream, evb.arr[0], evb.arr[1])
+        torch.cuda.synchronize()
+        dominant = "row_stats"
+        k1_us = evb.elapsed_ms(0, 1) / reps * 1e3
+        burst_bytes = float(np.mean([hosts[i % len(hosts)].algorithmic_bytes
+                                     for i in range(reps)]))
+        # the counters were taken on the headline workload's launch
+        traffic = (ROW_STATS_TRAFFIC["bytes"]
+                   if wl == WORKLOAD and
+                   row_stats_sources_hash() == ROW_STATS_TRAFFIC["sources_sha256_16"] else None)
+        evb.close()
+        log(f"row_stats alone: {k1_us:.2f} us/launch over {reps} launches")
+    if filtered:
+        burst_bytes = alg_bytes
+    achieved = burst_bytes / (k1_us * 1e-6) / 1e9
     step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    metric = METRIC if wl == WORKLOAD else (
+        f"verified draft positions/sec and achieved HBM GB/s (% of peak), {spec['name']}")
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": positions / (ms_per_step * 1e-3),
         "unit": "positions/s",
         "n_gpus": 1,
@@ -409,22 +484,24 @@ def main():
         "vs_baseline": None,
         "dtype": "f32+f64",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[WORKLOAD]["name"], "B": w0.B, "K": w0.K, "V": w0.V,
-                   "logits": "bf16", "temperature": w0.T, "top_k": 0, "top_p": 1.0,
-                   "input_sets": args.sets, "positions_per_step": positions,
-                   "algorithmic_bytes_per_step": alg_bytes},
+        "config": {"workload": spec["name"], "B": w0.B, "K": w0.K, "V": w0.V,
+                   "logits": w0.dtype, "temperature": float(w0.T), "top_k": int(w0.top_k),
+                   "top_p": float(w0.top_p), "input_sets": args.sets,
+                   "positions_per_step": positions, "algorithmic_bytes_per_step": alg_bytes},
+        "us_per_call": {"median": med, "p10": p10, "p90": p90},
         "host_us_per_call": host_us,
         "hbm_gbps_whole_step": step_gbps,
         "hbm_frac_whole_step": step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "launch_us": k1_us,
-                     "bytes_per_launch": alg_bytes},
+                     "bytes_per_launch": burst_bytes},
         "stages_us": stage_us,
     }
     if not args.no_cpu_baseline:
         log(f"timing the oracle for about {args.cpu_seconds:.0f} s")
-        result["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds,
+                                              group=8 if wl == 4 else None)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

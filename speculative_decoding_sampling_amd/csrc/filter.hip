@@ -13,10 +13,11 @@
 // max of its 32 logits and T_c is the k-th largest of the 256 thread maxima,
 // so the chunk has >= k logits >= T_c; the chunk's k-th largest logit is
 // >= T_c, and the row's k-th largest is at least the chunk's, so every logit
-// the row keeps is a candidate.  The candidates (~1.1 k per chunk on random
-// data) go to a per-chunk slot.  filter_merge
-// sorts a row's candidates in LDS by (logit desc, id asc), reads tau_k at
-// rank k, runs top-p in float64 over the sorted prefix, and writes the row
+// the row keeps is a candidate.  The candidates (~60 per chunk, ~1.1 k per
+// 152k-token row on random data) go to a per-chunk slot.  filter_merge
+// selects tau_k, the k-th largest candidate, by radix select, sorts the
+// candidates >= tau_k in LDS by (logit desc, id asc), runs top-p in float64
+// over that sorted prefix, and writes the row
 // maximum, the final threshold, the float64 normaliser over the kept set and
 // the kept tokens sorted by id.  Nothing downstream reads the full rows
 // again: acceptance needs two gathers per position, and the residual or
@@ -28,15 +29,22 @@
 
 namespace specv {
 
-// Order-preserving 32-bit key of a float (larger float -> larger key).
+// Order-preserving 32-bit key of a float (larger float -> larger key): the
+// sign bit set for a positive float, every bit flipped for a negative one.
+// Written as one XOR with a sign-derived mask, no select, so a key costs one
+// register where it is kept.
 __device__ __forceinline__ uint32_t fkey(float f) {
   const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float unkey(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 constexpr uint32_t kNegInfKey = 0x007fffffu;   // fkey(-inf)
+static_assert(kFiltSortMax % kFiltThreads == 0, "the merge gather gives each thread whole steps");
+static_assert(kFiltMaxChunks <= kWave, "one wave scans a row's chunk counts");
+constexpr int kRadixBins = 2048;               // the merge's radix select: 11-bit digits
+static_assert(kFiltSortMax / kFiltThreads <= 16, "a thread's block of the list stays small");
 
 // Descending sort of one key per lane across a wave (bitonic network).
 __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t key) {
@@ -100,12 +108,17 @@ __device__ __forceinline__ bool row_needed(int r, int K, int nb, bool& is_target
 }
 
 // ---------------------------------------------------------------------------
-// filter_cand: per (request, needed row, 8192-token chunk).  Thread t holds
-// tokens e_base + 256 j + t, j = 0..31: loads are coalesced, issued
-// back-to-back (the address is clamped instead of branched on), and any
-// chunk with 256 or more valid tokens gives every thread data, so every
-// wave's threshold is a real logit.  A chunk with at most `slot` valid tokens
-// (only a row's last chunk can have so few) keeps all of them.
+// filter_cand: per (request, needed row, 8192-token chunk).  In a full chunk
+// of a 16-byte aligned row, thread t holds the 16-byte vectors j = 0..NV-1 at
+// elements e_base + (256 j + t) N .. + N - 1 (N logits per vector): every
+// load instruction of a wave reads 1 KB of consecutive bytes.  Any other
+// chunk uses element loads, thread t holding tokens e_base + 256 j + t,
+// j = 0..31, issued back-to-back (the address is clamped instead of branched
+// on); a chunk with 256 or more valid tokens then gives every thread data, so
+// every wave's threshold is a real logit.  Which 32 logits a thread holds
+// does not matter to the threshold argument below, only that each thread's
+// maximum is one of the chunk's logits.  A chunk with at most `slot` valid
+// tokens (only a row's last chunk can have so few) keeps all of them.
 template <typename T>
 __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
@@ -128,18 +141,49 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
   const long e_base = (long)chunk * kFiltChunk;
   const int n_valid = (int)min((long)kFiltChunk, (long)V - e_base);
   const int slot = chunk == nch - 1 ? row_stride - (nch - 1) * cap : cap;
+  constexpr int N = Elem<T>::kPerVec;
+  const bool vec = n_valid == kFiltChunk && aligned16(row);   // uniform per block
+  // token id of v[j], formed where a candidate is stored (the empty asm keeps
+  // the compiler from computing all 32 ahead and holding them)
+  const uint32_t id_base = (uint32_t)(vec ? e_base + threadIdx.x * N : e_base + threadIdx.x);
+  auto id_of = [&](int j) -> uint32_t {
+    uint32_t ib = id_base;
+    asm volatile("" : "+v"(ib));
+    return ib + (vec ? (uint32_t)((j / N) * kFiltThreads * N + j % N) : (uint32_t)(j * kFiltThreads));
+  };
+  // Addressing keeps registers for the logits: each vector load adds this
+  // lane's one offset to a per-vector base that is uniform (scalar
+  // registers), and each element load's clamped offset is formed right
+  // before its load (the empty asm pins it there) instead of all 32 first.
+  const T* cb = row + e_base;
   float v[kFiltPerThread];
-  if (n_valid == kFiltChunk) {
+  if (vec) {
+    const uint32_t lo = threadIdx.x * N;
 #pragma unroll
-    for (int j = 0; j < kFiltPerThread; ++j)
-      v[j] = to_f32(row[e_base + (long)j * kFiltThreads + threadIdx.x]);
+    for (int j = 0; j < kFiltPerThread / N; ++j)
+      load_vec_stream(cb + (size_t)j * kFiltThreads * N, lo, v + j * N);
   } else {
+    // offsets past the row are clamped to its last token and read as -inf
+    const uint32_t last = (uint32_t)(n_valid - 1);
 #pragma unroll
     for (int j = 0; j < kFiltPerThread; ++j) {
-      const long e = e_base + (long)j * kFiltThreads + threadIdx.x;
-      const float x = to_f32(row[e < V ? e : (long)V - 1]);
-      v[j] = e < V ? x : -INFINITY;
+      // a 32-bit byte offset from the uniform base: one address register
+      uint32_t ob = min((uint32_t)(j * kFiltThreads) + threadIdx.x, last) * (uint32_t)sizeof(T);
+      asm volatile("" : "+v"(ob));
+      v[j] = to_f32(*reinterpret_cast<const T*>(reinterpret_cast<const char*>(cb) + ob));
     }
+#pragma unroll
+    for (int j = 0; j < kFiltPerThread; ++j)
+      if ((uint32_t)(j * kFiltThreads) + threadIdx.x > last) v[j] = -INFINITY;
+  }
+  // order-preserving keys, formed once (the logits are not needed again);
+  // the empty asm makes each key exist here, so the compiler cannot sink
+  // half of its computation into the later uses and hold both halves
+  uint32_t kx[kFiltPerThread];
+#pragma unroll
+  for (int j = 0; j < kFiltPerThread; ++j) {
+    kx[j] = fkey(v[j]);
+    asm volatile("" : "+v"(kx[j]));
   }
   uint32_t tc = kNegInfKey;                          // keep every valid logit ...
   if (n_valid > slot) {                              // ... unless the chunk is larger than its slot
@@ -148,7 +192,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
     // thread ranks its own maximum against the four sorted lists.
     uint32_t tmax = kNegInfKey;
 #pragma unroll
-    for (int j = 0; j < kFiltPerThread; ++j) tmax = max(tmax, fkey(v[j]));
+    for (int j = 0; j < kFiltPerThread; ++j) tmax = max(tmax, kx[j]);
     lists[threadIdx.x] = wave_sort_desc(tmax);        // wave w's list at [64w, 64w + 64)
     __syncthreads();
     int rank = 0;                                    // thread maxima >= tmax
@@ -171,25 +215,29 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
 #pragma unroll
     for (int w = 1; w < kFiltThreads / kWave; ++w) tc = max(tc, tw[w]);
   }
-  // candidates: finite logits with key >= tc, written in thread order
-  int mine = 0;
+  // candidates: finite logits with key >= tc, written in thread order.  They
+  // are rare (~60 of 8192 on random data), so each thread keeps a bit mask
+  // of its own, and a position no lane of the wave has is skipped whole.
+  static_assert(kFiltPerThread <= 32, "one 32-bit mask per thread");
+  uint32_t cm = 0u;
 #pragma unroll
-  for (int j = 0; j < kFiltPerThread; ++j) {
-    const uint32_t kk = fkey(v[j]);
-    mine += (kk >= tc && kk > kNegInfKey) ? 1 : 0;
-  }
+  for (int j = 0; j < kFiltPerThread; ++j)
+    cm |= (uint32_t)(kx[j] >= tc && kx[j] > kNegInfKey) << j;
   int total;
-  int off = block_scan_excl<int>(mine, il, total);
+  int off = block_scan_excl<int>(__popc(cm), il, total);
   uint64_t* dst = cand + (size_t)rr * row_stride + (size_t)chunk * cap;
 #pragma unroll
   for (int j = 0; j < kFiltPerThread; ++j) {
-    const uint32_t kk = fkey(v[j]);
-    if (kk >= tc && kk > kNegInfKey) {
-      if (off < slot) {
-        const uint32_t id = (uint32_t)(e_base + (long)j * kFiltThreads + threadIdx.x);
-        dst[off] = ((uint64_t)kk << 32) | (uint64_t)(0xffffffffu - id);
+    const bool c = (cm >> j) & 1u;
+    if (__ballot(c) != 0ull) {
+      if (c) {
+        // a fresh copy of the key for the 64-bit word: otherwise the register
+        // allocator places every key in the high half of a register pair
+        uint32_t hi = kx[j];
+        asm volatile("" : "+v"(hi));
+        if (off < slot) dst[off] = ((uint64_t)hi << 32) | (uint64_t)(0xffffffffu - id_of(j));
+        ++off;
       }
-      ++off;
     }
   }
   if (threadIdx.x == 0) counts[(size_t)rr * nch + chunk] = total;
@@ -226,6 +274,8 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   __shared__ int il[kFiltThreads / kWave];
   __shared__ int s_off[kFiltMaxChunks + 1];
   __shared__ int s_status;
+  __shared__ int s_digit, s_need;
+  __shared__ int hist[kRadixBins];
   const int R = 2 * K + 1;
   const int rr = blockIdx.x;
   const int r = rr % R, b = rr / R;
@@ -236,43 +286,135 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   int k;
   if (!row_needed(r, K, nb, is_target, k)) return;
 
-  // gather the row's candidates into LDS
-  if (threadIdx.x == 0) {
-    int acc = 0, st = 0;
-    for (int c = 0; c < nch; ++c) {
-      const int n = counts[(size_t)rr * nch + c];
+  // the chunks' candidate counts, clipped to their slots, and their offsets
+  // in the row's list: one wave, lane c = chunk c (nch <= kFiltMaxChunks)
+  if (threadIdx.x < kWave) {
+    const int c = threadIdx.x;
+    int n = 0, over = 0;
+    if (c < nch) {
+      const int cnt = counts[(size_t)rr * nch + c];
       const int slot = c == nch - 1 ? row_stride - (nch - 1) * cap : cap;
-      if (n > slot) st = 1;
-      s_off[c] = acc;
-      acc += min(n, slot);
+      over = cnt > slot;
+      n = min(cnt, slot);
     }
-    s_off[nch] = acc;
-    s_status = st;
+    int x = n;                                       // inclusive scan over the lanes
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x, o, kWave);
+      if (c >= o) x += y;
+    }
+    if (c < nch) s_off[c + 1] = x;
+    const bool any_over = __ballot(over) != 0;
+    if (c == 0) {
+      s_off[0] = 0;
+      s_status = any_over ? 1 : 0;
+    }
   }
   __syncthreads();
   const int n_all = s_off[nch];
-  int P = 2;
-  while (P < n_all) P <<= 1;
-  for (int c = 0; c < nch; ++c) {
-    const int base = s_off[c], n = s_off[c + 1] - base;
-    for (int i = threadIdx.x; i < n; i += kFiltThreads)
-      keys[base + i] = cand[(size_t)rr * row_stride + (size_t)c * cap + i];
+  // gather: every load of this thread first (flat index f, its chunk found
+  // by binary search over the offsets), then the stores to LDS
+  constexpr int kGather = kFiltSortMax / kFiltThreads;
+  uint64_t gv[kGather];
+#pragma unroll
+  for (int j = 0; j < kGather; ++j) {
+    const int f = (int)threadIdx.x + j * kFiltThreads;
+    gv[j] = 0ull;
+    if (f < n_all) {
+      int lo = 0, hi = nch;                          // s_off[lo] <= f < s_off[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= f) lo = mid;
+        else hi = mid;
+      }
+      gv[j] = cand[(size_t)rr * row_stride + (size_t)lo * cap + (f - s_off[lo])];
+    }
   }
-  for (int i = n_all + threadIdx.x; i < P; i += kFiltThreads) keys[i] = 0ull;   // sorts last
+#pragma unroll
+  for (int j = 0; j < kGather; ++j) {
+    const int f = (int)threadIdx.x + j * kFiltThreads;
+    if (f < n_all) keys[f] = gv[j];
+  }
+  __syncthreads();
+
+  // tau_k = the kk-th largest candidate key, kk = min(top_k, n_all) (top_k <
+  // V here; ties are kept), by radix select: three passes over 11-, 11- and
+  // 10-bit digits, each a histogram in LDS of the keys that match the digits
+  // chosen so far, then the bin where the count from the top reaches the
+  // remaining rank.  Only the keys >= tau_k (the top-k and its ties) are
+  // sorted afterwards; the other candidates never need an order.
+  const int kk = min(top_k, n_all);
+  uint32_t tau_k = 0u;
+  if (n_all > 0) {
+    constexpr int kPer = kRadixBins / kFiltThreads;
+    uint32_t prefix = 0u, pmask = 0u;
+    int need = kk;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int bits = pass < 2 ? 11 : 10, shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int nbins = 1 << bits;
+      for (int i = threadIdx.x; i < kRadixBins; i += kFiltThreads) hist[i] = 0;
+      __syncthreads();
+      for (int f = threadIdx.x; f < n_all; f += kFiltThreads) {
+        const uint32_t k32 = (uint32_t)(keys[f] >> 32);
+        if ((k32 & pmask) == prefix) atomicAdd(&hist[(k32 >> shift) & (uint32_t)(nbins - 1)], 1);
+      }
+      __syncthreads();
+      // thread t takes bins nbins-1-(kPer t + i), i < kPer: digits from the top
+      int c[kPer], csum = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int d = nbins - 1 - (kPer * (int)threadIdx.x + i);
+        c[i] = d >= 0 ? hist[d] : 0;
+        csum += c[i];
+      }
+      int tot;
+      int above = block_scan_excl<int>(csum, il, tot);   // matching keys in higher bins
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (above < need && need <= above + c[i]) {      // exactly one bin of the block
+          s_digit = nbins - 1 - (kPer * (int)threadIdx.x + i);
+          s_need = need - above;
+        }
+        above += c[i];
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      pmask |= (uint32_t)(nbins - 1) << shift;
+      need = s_need;
+      __syncthreads();                               // s_digit read before it is rewritten
+    }
+    tau_k = prefix;
+  }
+  // the keys >= tau_k, moved to the front of keys in their current order (L
+  // of them; each thread takes a contiguous block of the list, so a key
+  // never moves past a slot not yet read) and sorted descending
+  const int qa = (n_all + kFiltThreads - 1) / kFiltThreads;
+  const int a_lo = min(n_all, (int)threadIdx.x * qa), a_hi = min(n_all, a_lo + qa);
+  int mine_n = 0;
+  for (int f = a_lo; f < a_hi; ++f) mine_n += (uint32_t)(keys[f] >> 32) >= tau_k ? 1 : 0;
+  int L;
+  int pos = block_scan_excl<int>(mine_n, il, L);
+  uint64_t kept_keys[kGather];
+  int nk = 0;
+#pragma unroll
+  for (int j = 0; j < kGather; ++j) {
+    const int f = a_lo + j;
+    kept_keys[j] = f < a_hi ? keys[f] : 0ull;
+  }
+  __syncthreads();                                   // every read of the list is done
+#pragma unroll
+  for (int j = 0; j < kGather; ++j) {
+    if (a_lo + j < a_hi && (uint32_t)(kept_keys[j] >> 32) >= tau_k) keys[pos + nk++] = kept_keys[j];
+  }
+  int P = 2;
+  while (P < L) P <<= 1;
+  for (int i = L + (int)threadIdx.x; i < P; i += kFiltThreads) keys[i] = 0ull;   // sorts last
   lds_bitonic_desc(keys, P);
 
   FiltRow out;
   out.status = s_status;
   if (n_all == 0) out.status = 2;                    // no finite logit in the row
-  // tau_k: the top_k-th largest logit (top_k < V here), ties kept
-  const int kk = min(top_k, n_all);
-  const uint32_t tau_k = n_all > 0 ? (uint32_t)(keys[max(kk, 1) - 1] >> 32) : 0u;
-  // L = number of candidates with key >= tau_k: first index below it
-  int cand_i = INT_MAX;
-  for (int i = threadIdx.x; i < n_all; i += kFiltThreads)
-    if ((uint32_t)(keys[i] >> 32) < tau_k) cand_i = min(cand_i, i);
-  int L = block_min_i(cand_i, il);
-  if (L == INT_MAX) L = n_all;
   const float m = n_all > 0 ? unkey((uint32_t)(keys[0] >> 32)) : -INFINITY;
   const double md = (double)m;
 
