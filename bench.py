@@ -175,6 +175,126 @@ def bench_sample(args):
         "hbm_gbps_whole_step": alg_bytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def bench_rates(args):
+    """Acceptance diagnostics on the headline workload (B=64, K=4, V=128256,
+    bf16, T=1): specv_acceptance_rates (the row statistics, then a second
+    pass over each drafted row pair for sum_x min(p(x), q(x))), and on one
+    verified round's outcome specv_round_stats and the device-resident
+    AcceptRateMonitor update.  Reported for reference next to the headline."""
+    import torch
+    from speculative_decoding_sampling_amd import binding
+    from speculative_decoding_sampling_amd.build import LIB
+    from speculative_decoding_sampling_amd.workloads import WORKLOADS, make_workload, upload
+
+    if not os.path.exists(LIB):
+        from speculative_decoding_sampling_amd.build import build
+        build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sets, hosts = [], []
+    for i in range(args.sets):
+        w = make_workload(WORKLOAD, seed=1000 + WORKLOAD + 100 * i)
+        hosts.append(w)
+        a = upload(w, dev)
+        a["beta"] = torch.empty((w.B, w.K), dtype=torch.float32, device=dev)
+        sets.append(a)
+    w0 = hosts[0]
+    B, K, V = w0.B, w0.K, w0.V
+    positions = w0.positions
+    # one read of every needed row for the statistics, then one of each
+    # drafted (target, draft) row pair for the sums of min(p, q)
+    drafted = int(np.sum(w0.draft_len))
+    alg_bytes = w0.algorithmic_bytes + 2 * drafted * V * 2
+    stream = torch.cuda.current_stream(dev)
+    ws = torch.empty(binding.workspace_bytes(B, K, V, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+
+    def rates(i):
+        st = sets[i % len(sets)]
+        binding.acceptance_rates(st["target_logits"], st["draft_logits"], st["draft_len"], w0.T,
+                                 beta=st["beta"], workspace=ws, stream=stream)
+
+    ev = HipEvents(args.steps + 1)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev.lib.hipEventRecord(ev.arr[i], stream.cuda_stream)
+            fn(i)
+        ev.lib.hipEventRecord(ev.arr[args.steps], stream.cuda_stream)
+        torch.cuda.synchronize()
+        us = np.array([ev.elapsed_ms(i, i + 1) for i in range(args.steps)]) * 1e3
+        return float(ev.elapsed_ms(0, args.steps) / args.steps * 1e3), us
+
+    rates_us, rates_calls = timed(rates)
+    b = sets[0]["beta"].cpu().numpy()
+    assert np.all((b > 0) & (b <= 1)), "every position is drafted in this workload"
+    # one verified round per set, then its statistics and the monitor update
+    outs = []
+    for st in sets:
+        r = binding.verify(**{k: v for k, v in st.items() if k != "beta"}, workspace=ws,
+                           stream=stream)
+        outs.append((st, r["out_tokens"], r["n_emitted"]))
+    mon = binding.AcceptRateMonitor(B, 16, 8, dev, stream=stream)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    rate = torch.empty(B, dtype=torch.float64, device=dev)
+
+    def round_stats(i):
+        st, out, n = outs[i % len(outs)]
+        binding.round_stats(st["draft_tokens"], st["draft_len"], out, n, st["beta"], stream=stream)
+
+    def monitor(i):
+        st, out, n = outs[i % len(outs)]
+        mon.update(st["draft_tokens"], st["draft_len"], out, n, next_draft_len=nxt, rate=rate,
+                   stream=stream)
+
+    stats_us, _ = timed(round_stats)
+    mon_us, _ = timed(monitor)
+    ev.close()
+    p10, med, p90 = (float(x) for x in np.percentile(rates_calls, [10, 50, 90]))
+    gbps = alg_bytes / (rates_us * 1e-6) / 1e9
+    log(f"acceptance rates: {rates_us:.2f} us/call (median {med:.2f}), {gbps:.0f} GB/s; "
+        f"round stats {stats_us:.2f} us; monitor update {mon_us:.2f} us")
+    result = {
+        "metric": "per-position acceptance rates sum_x min(p, q): drafted positions/sec",
+        "value": positions / (rates_us * 1e-6), "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rates_us * 1e-3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[WORKLOAD]["name"] + " acceptance rates", "B": B, "K": K,
+                   "V": V, "logits": "bf16", "temperature": float(w0.T),
+                   "input_sets": args.sets, "positions_per_step": positions,
+                   "algorithmic_bytes_per_step": alg_bytes},
+        "us_per_call": {"median": med, "p10": p10, "p90": p90},
+        "roofline": {"bound": "hbm", "kernel": "row_stats + beta_pass (whole call)",
+                     "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "launch_us": rates_us,
+                     "bytes_per_launch": alg_bytes},
+        # both are a few-microsecond kernel behind a Python call: these per-call
+        # times are the host's enqueue rate, not the GPU's
+        "round_stats_host_bound_us_per_call": stats_us,
+        "monitor_update_host_bound_us_per_call": mon_us,
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        log(f"timing the oracle for about {args.cpu_seconds:.0f} s")
+        t_total, reps = 0.0, 0
+        while t_total < args.cpu_seconds:
+            t1 = time.perf_counter()
+            O.acceptance_rates(w0.target, w0.draft, w0.draft_len, w0.T, dtype=w0.dtype)
+            t_total += time.perf_counter() - t1
+            reps += 1
+        result["cpu_baseline"] = {
+            "value": positions * reps / t_total, "unit": "positions/s", "cores": 1,
+            "kind": "oracle", "sample": f"{reps} whole calls of the same workload, "
+                                        f"{t_total:.1f} s of single-threaded numpy fp64"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def bench_lm_head(args):
     """The verification fused with the target LM head (specv_verify_lm_head)
     at B=64, K=4, V=128256 with a D=4096 LM head: the target logits are
@@ -285,10 +405,11 @@ def main():
                     help="synthetic workload of the verify op (3, the default, is the headline)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["verify", "sample", "lm_head"], default="verify",
+    ap.add_argument("--op", choices=["verify", "sample", "lm_head", "rates"], default="verify",
                     help="verify: the verification step (default, the headline); sample: the "
                          "draft-side draw of the same workload (256 draft rows); lm_head: the "
-                         "verification fused with a D=4096 target LM head; the last two are "
+                         "verification fused with a D=4096 target LM head; rates: the "
+                         "acceptance diagnostics of the same workload; the last three are "
                          "reported for reference")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
@@ -310,6 +431,8 @@ def main():
         return bench_sample(args)
     if args.op == "lm_head":
         return bench_lm_head(args)
+    if args.op == "rates":
+        return bench_rates(args)
 
     import torch
     from speculative_decoding_sampling_amd import binding
