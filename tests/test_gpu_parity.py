@@ -403,6 +403,30 @@ def test_sample_matches_oracle_filtered(top_k, top_p):
     assert_sample_parity(rows, u, w.T, top_k, top_p, w.dtype, label="cfg4 rows")
 
 
+def test_sample_filtered_sparse_and_tied_rows():
+    # The filter's radix select at its edges: fewer finite logits than top_k
+    # (every one kept), exactly top_k, top_k + 1 with a tie at the k-th value
+    # (both kept), finite logits only in the last chunk, many duplicates, and
+    # an ordinary row; every row drawn at several uniforms.
+    rng = np.random.default_rng(17)
+    V, top_k = 20000, 50
+    base = np.full((6, V), -np.inf, dtype=np.float32)
+    base[0, rng.choice(V, 3, replace=False)] = rng.normal(0, 2, 3)
+    base[1, rng.choice(V, top_k, replace=False)] = rng.normal(0, 2, top_k)
+    ids = rng.choice(V, top_k + 1, replace=False)
+    vals = np.sort(rng.normal(0, 2, top_k + 1))[::-1].copy()
+    vals[top_k] = vals[top_k - 1]                    # a tie at the k-th largest
+    base[2, ids] = vals
+    base[3, V - 300:] = rng.normal(0, 2, 300)        # only the tail chunk is finite
+    base[4] = np.round(rng.normal(0, 2, V) * 4) / 4  # many equal values
+    base[5] = rng.normal(0, 2, V)
+    rows = np.repeat(base, 4, axis=0)
+    from speculative_decoding_sampling_amd.workloads import uniforms
+    u = uniforms(np.random.default_rng(18), rows.shape[0])
+    assert_sample_parity(rows, u, 0.7, top_k, 0.9, "f32", label="sparse/tied rows")
+    assert_sample_parity(rows, u, 1.0, top_k, 1.0, "f32", label="sparse/tied rows, top-k only")
+
+
 def test_sample_edge_cases():
     # u = 0 and the largest uniform below 1; a row with one finite logit; rows
     # with no finite logit or a uniform outside [0, 1) give -1, alone.
