@@ -352,11 +352,27 @@ def bench_lm_head(args):
                           temperature=w.T, stream=stream, start=ev.arr[0], stop=ev.arr[1])
     torch.cuda.synchronize()
     k_us = ev.elapsed_ms(0, 1) / reps * 1e3
+    # context only: the vendor GEMM (torch.matmul, hipBLASLt on ROCm) on the
+    # same row-major bf16 operands, logits alone, no statistics
+    wt = torch.from_numpy(w.weight.view(np.int16)).to(dev).view(torch.bfloat16)
+    ref = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+    hid2 = a["hidden"].view(M, D)
+    for _ in range(3):
+        torch.matmul(hid2, wt.t(), out=ref)
+    torch.cuda.synchronize()
+    ev.lib.hipEventRecord(ev.arr[0], stream.cuda_stream)
+    for _ in range(reps):
+        torch.matmul(hid2, wt.t(), out=ref)
+    ev.lib.hipEventRecord(ev.arr[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    blas_us = ev.elapsed_ms(0, 1) / reps * 1e3
+    del wt, ref
     ev.close()
     flops = 2.0 * M * V * D
     hbm_bytes = V * D * 2 + M * D * 2 + M * V * 2       # weights and hidden read once, logits written
     log(f"lm_head fused step {ms * 1e3:.1f} us; LM-head kernel {k_us:.1f} us "
-        f"({flops / k_us / 1e6:.0f} TFLOP/s, {hbm_bytes / k_us / 1e3:.0f} GB/s)")
+        f"({flops / k_us / 1e6:.0f} TFLOP/s, {hbm_bytes / k_us / 1e3:.0f} GB/s); "
+        f"torch.matmul on the same operands {blas_us:.1f} us")
     result = {
         "metric": "verified draft positions/sec, verification fused with the target LM head",
         "value": w.positions / (ms * 1e-3), "unit": "positions/s", "n_gpus": 1,
@@ -370,6 +386,9 @@ def bench_lm_head(args):
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": flops / k_us / 1e6 / 2500.0,
                      "traffic": None, "launch_us": k_us, "flops_per_launch": flops,
                      "hbm_gbps": hbm_bytes / k_us / 1e3, "hbm_bytes_per_launch": hbm_bytes},
+        "reference_gemm": {"what": "torch.matmul (hipBLASLt) on the same row-major bf16 "
+                                   "operands: logits only, no statistics; context",
+                           "us_per_launch": blas_us, "tflops": flops / blas_us / 1e6},
     }
     if not args.no_cpu_baseline:
         # the oracle on whole requests: its LM-head rows in float64, then verify
