@@ -48,6 +48,7 @@ def run_fused(w, **kw):
     (2, 0, 4100, 64, False, 4),        # no drafts: bonus draws only
     (1, 5, 32000, 1024, False, 5),     # single request, low-latency shape
     (3, 2, 4097, 192, True, 6),        # V odd: element stores; D = 3 k blocks
+    (2, 2, 200, 64, False, 7),         # V < 256: half a workgroup's waves past V
 ])
 def test_fused_exact_parity(B, K, V, D, ragged, seed):
     print(f"[lm_head] B={B} K={K} V={V} D={D} ragged={ragged} seed={seed}", flush=True)
