@@ -46,20 +46,50 @@ static_assert(kFiltMaxChunks <= kWave, "one wave scans a row's chunk counts");
 constexpr int kRadixBins = 2048;               // the merge's radix select: 11-bit digits
 static_assert(kFiltSortMax / kFiltThreads <= 16, "a thread's block of the list stays small");
 
+// The value of lane (lane ^ S).  S = 1, 2: one DPP quad permutation; S = 4:
+// the half-row mirror (lane i of each 8 takes 7 - i) then the quad reversal,
+// which together send i to i ^ 4; S = 8: the half-row mirror then the row
+// mirror (i of each 16 takes 15 - i), together i ^ 8; S = 16: a swizzle in
+// bit-mask mode (xor 16 within each 32 lanes); S = 32: a permute.  Only the
+// last two go through the LDS unit.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (S == 1) return dpp_u32<0xb1>(v);                       // quad_perm [1,0,3,2]
+  else if constexpr (S == 2) return dpp_u32<0x4e>(v);                  // quad_perm [2,3,0,1]
+  else if constexpr (S == 4) return dpp_u32<0x1b>(dpp_u32<0x141>(v));  // half mirror, [3,2,1,0]
+  else if constexpr (S == 8) return dpp_u32<0x140>(dpp_u32<0x141>(v)); // half mirror, mirror
+  else if constexpr (S == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401f);
+  else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((threadIdx.x % kWave) ^ 32) << 2, (int)v);
+}
+
+// One compare-exchange stage of the bitonic network at a fixed size and stride.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t bitonic_stage(uint32_t key, int lane) {
+  const uint32_t other = lane_xor<STRIDE>(key);
+  const bool up = (lane & SIZE) == 0;
+  const bool lower = (lane & STRIDE) == 0;
+  return (lower == up) ? max(key, other) : min(key, other);
+}
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t bitonic_merge(uint32_t key, int lane) {
+  key = bitonic_stage<SIZE, STRIDE>(key, lane);
+  if constexpr (STRIDE > 1) key = bitonic_merge<SIZE, STRIDE / 2>(key, lane);
+  return key;
+}
+template <int SIZE>
+__device__ __forceinline__ uint32_t bitonic_sort(uint32_t key, int lane) {
+  if constexpr (SIZE > 2) key = bitonic_sort<SIZE / 2>(key, lane);
+  return bitonic_merge<SIZE, SIZE / 2>(key, lane);
+}
+
 // Descending sort of one key per lane across a wave (bitonic network).
 __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t key) {
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-    for (int stride = size / 2; stride > 0; stride >>= 1) {
-      const uint32_t other = __shfl_xor(key, stride, kWave);
-      const bool up = (lane & size) == 0;
-      const bool lower = (lane & stride) == 0;
-      key = (lower == up) ? max(key, other) : min(key, other);
-    }
-  }
-  return key;
+  static_assert(kWave == 64, "the lane exchanges are written for wave64");
+  return bitonic_sort<kWave>(key, (int)(threadIdx.x % kWave));
 }
 
 template <typename V>
@@ -195,17 +225,21 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
     for (int j = 0; j < kFiltPerThread; ++j) tmax = max(tmax, kx[j]);
     lists[threadIdx.x] = wave_sort_desc(tmax);        // wave w's list at [64w, 64w + 64)
     __syncthreads();
-    int rank = 0;                                    // thread maxima >= tmax
+    // rank = thread maxima >= tmax: in each descending list the count of
+    // entries >= tmax, by binary lifting (pos only grows while its entry
+    // is >= tmax), the four lists interleaved so their reads overlap
+    constexpr int kLists = kFiltThreads / kWave;
+    int pos[kLists];
 #pragma unroll
-    for (int w = 0; w < kFiltThreads / kWave; ++w) {
-      int lo = 0, hi = kWave;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (lists[w * kWave + mid] >= tmax) lo = mid + 1;
-        else hi = mid;
-      }
-      rank += lo;
-    }
+    for (int w = 0; w < kLists; ++w) pos[w] = 0;
+#pragma unroll
+    for (int step = kWave / 2; step >= 1; step >>= 1)
+#pragma unroll
+      for (int w = 0; w < kLists; ++w)
+        if (lists[w * kWave + pos[w] + step - 1] >= tmax) pos[w] += step;
+    int rank = 0;                                    // pos <= 63: one last entry to test
+#pragma unroll
+    for (int w = 0; w < kLists; ++w) rank += pos[w] + (lists[w * kWave + pos[w]] >= tmax ? 1 : 0);
     uint32_t best = rank >= top_k ? tmax : 0u;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) best = max(best, (uint32_t)__shfl_xor(best, o, kWave));
