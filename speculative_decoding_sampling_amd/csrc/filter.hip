@@ -86,6 +86,23 @@ __device__ __forceinline__ uint32_t bitonic_sort(uint32_t key, int lane) {
   return bitonic_merge<SIZE, SIZE / 2>(key, lane);
 }
 
+// Inclusive prefix sum over the wave's lanes on DPP alone: shifts by 1, 2, 4
+// and 8 within each row of 16 (a lane with no source adds 0), then row 15's
+// total broadcast into rows 1 and 3, then lane 31's into rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v = dpp_add<0x111, 0xf>(v);                        // row_shr:1
+  v = dpp_add<0x112, 0xf>(v);                        // row_shr:2
+  v = dpp_add<0x114, 0xf>(v);                        // row_shr:4
+  v = dpp_add<0x118, 0xf>(v);                        // row_shr:8
+  v = dpp_add<0x142, 0xa>(v);                        // row_bcast:15 into rows 1, 3
+  v = dpp_add<0x143, 0xc>(v);                        // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Descending sort of one key per lane across a wave (bitonic network).
 __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t key) {
   static_assert(kWave == 64, "the lane exchanges are written for wave64");
@@ -241,8 +258,12 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
 #pragma unroll
     for (int w = 0; w < kLists; ++w) rank += pos[w] + (lists[w * kWave + pos[w]] >= tmax ? 1 : 0);
     uint32_t best = rank >= top_k ? tmax : 0u;
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) best = max(best, (uint32_t)__shfl_xor(best, o, kWave));
+    best = max(best, lane_xor<32>(best));
+    best = max(best, lane_xor<16>(best));
+    best = max(best, lane_xor<8>(best));
+    best = max(best, lane_xor<4>(best));
+    best = max(best, lane_xor<2>(best));
+    best = max(best, lane_xor<1>(best));
     if (lane == 0) tw[wid] = best;
     __syncthreads();
     tc = tw[0];
@@ -257,8 +278,18 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
 #pragma unroll
   for (int j = 0; j < kFiltPerThread; ++j)
     cm |= (uint32_t)(kx[j] >= tc && kx[j] > kNegInfKey) << j;
-  int total;
-  int off = block_scan_excl<int>(__popc(cm), il, total);
+  // exclusive offset of this thread's candidates in the block: a DPP scan
+  // per wave, the four wave totals through LDS (il is not used before here)
+  const int mine = __popc(cm);
+  const int incl = wave_incl_scan_dpp(mine);
+  if (lane == kWave - 1) il[wid] = incl;
+  __syncthreads();
+  int total = 0, off = incl - mine;
+#pragma unroll
+  for (int w = 0; w < kFiltThreads / kWave; ++w) {
+    if (w < wid) off += il[w];
+    total += il[w];
+  }
   uint64_t* dst = cand + (size_t)rr * row_stride + (size_t)chunk * cap;
 #pragma unroll
   for (int j = 0; j < kFiltPerThread; ++j) {
