@@ -66,22 +66,28 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
   else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((threadIdx.x % kWave) ^ 32) << 2, (int)v);
 }
 
+template <int S>
+__device__ __forceinline__ uint64_t lane_xor(uint64_t v) {
+  const uint32_t lo = lane_xor<S>((uint32_t)v), hi = lane_xor<S>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // One compare-exchange stage of the bitonic network at a fixed size and stride.
-template <int SIZE, int STRIDE>
-__device__ __forceinline__ uint32_t bitonic_stage(uint32_t key, int lane) {
-  const uint32_t other = lane_xor<STRIDE>(key);
+template <int SIZE, int STRIDE, typename K>
+__device__ __forceinline__ K bitonic_stage(K key, int lane) {
+  const K other = lane_xor<STRIDE>(key);
   const bool up = (lane & SIZE) == 0;
   const bool lower = (lane & STRIDE) == 0;
-  return (lower == up) ? max(key, other) : min(key, other);
+  return (lower == up) ? (key > other ? key : other) : (key < other ? key : other);
 }
-template <int SIZE, int STRIDE>
-__device__ __forceinline__ uint32_t bitonic_merge(uint32_t key, int lane) {
+template <int SIZE, int STRIDE, typename K>
+__device__ __forceinline__ K bitonic_merge(K key, int lane) {
   key = bitonic_stage<SIZE, STRIDE>(key, lane);
   if constexpr (STRIDE > 1) key = bitonic_merge<SIZE, STRIDE / 2>(key, lane);
   return key;
 }
-template <int SIZE>
-__device__ __forceinline__ uint32_t bitonic_sort(uint32_t key, int lane) {
+template <int SIZE, typename K>
+__device__ __forceinline__ K bitonic_sort(K key, int lane) {
   if constexpr (SIZE > 2) key = bitonic_sort<SIZE / 2>(key, lane);
   return bitonic_merge<SIZE, SIZE / 2>(key, lane);
 }
@@ -103,8 +109,10 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int v) {
   return v;
 }
 
-// Descending sort of one key per lane across a wave (bitonic network).
-__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t key) {
+// Descending sort of one key per lane across a wave (bitonic network), for
+// 32- and 64-bit keys.
+template <typename K>
+__device__ __forceinline__ K wave_sort_desc(K key) {
   static_assert(kWave == 64, "the lane exchanges are written for wave64");
   return bitonic_sort<kWave>(key, (int)(threadIdx.x % kWave));
 }
@@ -408,23 +416,29 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   // chosen so far, then the bin where the count from the top reaches the
   // remaining rank.  Only the keys >= tau_k (the top-k and its ties) are
   // sorted afterwards; the other candidates never need an order.
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   const int kk = min(top_k, n_all);
   uint32_t tau_k = 0u;
   if (n_all > 0) {
     constexpr int kPer = kRadixBins / kFiltThreads;
     uint32_t prefix = 0u, pmask = 0u;
     int need = kk;
+    for (int i = threadIdx.x; i < kRadixBins; i += kFiltThreads) hist[i] = 0;
+    __syncthreads();
+    // Three barriers a pass: (A) the histogram is complete; (B) the wave
+    // totals of the bin scan are in il, every read of the histogram done,
+    // so it is cleared for the next pass; (C) the chosen digit is visible
+    // and the histogram clear.  s_digit and il are rewritten only after
+    // the next (A), by which time every thread has read them.
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
       const int bits = pass < 2 ? 11 : 10, shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
       const int nbins = 1 << bits;
-      for (int i = threadIdx.x; i < kRadixBins; i += kFiltThreads) hist[i] = 0;
-      __syncthreads();
       for (int f = threadIdx.x; f < n_all; f += kFiltThreads) {
         const uint32_t k32 = (uint32_t)(keys[f] >> 32);
         if ((k32 & pmask) == prefix) atomicAdd(&hist[(k32 >> shift) & (uint32_t)(nbins - 1)], 1);
       }
-      __syncthreads();
+      __syncthreads();                               // (A)
       // thread t takes bins nbins-1-(kPer t + i), i < kPer: digits from the top
       int c[kPer], csum = 0;
 #pragma unroll
@@ -433,8 +447,14 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
         c[i] = d >= 0 ? hist[d] : 0;
         csum += c[i];
       }
-      int tot;
-      int above = block_scan_excl<int>(csum, il, tot);   // matching keys in higher bins
+      const int incl = wave_incl_scan_dpp(csum);
+      if (lane == kWave - 1) il[wid] = incl;
+      __syncthreads();                               // (B)
+      for (int i = threadIdx.x; i < kRadixBins; i += kFiltThreads) hist[i] = 0;
+      int above = incl - csum;                       // matching keys in higher bins
+#pragma unroll
+      for (int w = 0; w < kFiltThreads / kWave; ++w)
+        if (w < wid) above += il[w];
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         if (above < need && need <= above + c[i]) {      // exactly one bin of the block
@@ -443,11 +463,10 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
         }
         above += c[i];
       }
-      __syncthreads();
+      __syncthreads();                               // (C)
       prefix |= (uint32_t)s_digit << shift;
       pmask |= (uint32_t)(nbins - 1) << shift;
       need = s_need;
-      __syncthreads();                               // s_digit read before it is rewritten
     }
     tau_k = prefix;
   }
@@ -458,8 +477,8 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   const int a_lo = min(n_all, (int)threadIdx.x * qa), a_hi = min(n_all, a_lo + qa);
   int mine_n = 0;
   for (int f = a_lo; f < a_hi; ++f) mine_n += (uint32_t)(keys[f] >> 32) >= tau_k ? 1 : 0;
-  int L;
-  int pos = block_scan_excl<int>(mine_n, il, L);
+  const int incl_n = wave_incl_scan_dpp(mine_n);
+  if (lane == kWave - 1) il[wid] = incl_n;           // il's last readers passed (C)
   uint64_t kept_keys[kGather];
   int nk = 0;
 #pragma unroll
@@ -468,14 +487,31 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
     kept_keys[j] = f < a_hi ? keys[f] : 0ull;
   }
   __syncthreads();                                   // every read of the list is done
+  int L = 0, pos = incl_n - mine_n;
+#pragma unroll
+  for (int w = 0; w < kFiltThreads / kWave; ++w) {
+    if (w < wid) pos += il[w];
+    L += il[w];
+  }
 #pragma unroll
   for (int j = 0; j < kGather; ++j) {
     if (a_lo + j < a_hi && (uint32_t)(kept_keys[j] >> 32) >= tau_k) keys[pos + nk++] = kept_keys[j];
   }
-  int P = 2;
-  while (P < L) P <<= 1;
-  for (int i = L + (int)threadIdx.x; i < P; i += kFiltThreads) keys[i] = 0ull;   // sorts last
-  lds_bitonic_desc(keys, P);
+  if (L <= kWave) {
+    // the usual case (top-k and a few ties): one wave sorts in registers
+    __syncthreads();
+    if (wid == 0) {
+      uint64_t x = lane < L ? keys[lane] : 0ull;     // 0 sorts last
+      x = wave_sort_desc(x);
+      if (lane < L) keys[lane] = x;
+    }
+    __syncthreads();
+  } else {
+    int P = 2;
+    while (P < L) P <<= 1;
+    for (int i = L + (int)threadIdx.x; i < P; i += kFiltThreads) keys[i] = 0ull;   // sorts last
+    lds_bitonic_desc(keys, P);
+  }
 
   FiltRow out;
   out.status = s_status;
@@ -523,18 +559,28 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   if (Lk > kKeptCap) out.status = 1;
 
   // kept tokens re-sorted by id ascending: key (~id << 32 | logit bits), descending
-  __syncthreads();
-  int P2 = 2;
-  while (P2 < Lk) P2 <<= 1;
-  if (Lk <= kKeptCap) {
-    for (int i = threadIdx.x; i < P2; i += kFiltThreads) {
-      uint64_t x = 0ull;
-      if (i < Lk) {
-        const uint64_t e = keys[i];
-        const uint32_t id = 0xffffffffu - (uint32_t)e;
-        x = ((uint64_t)(0xffffffffu - id) << 32) | (uint64_t)__float_as_uint(unkey((uint32_t)(e >> 32)));
+  auto id_key = [&](uint64_t e) -> uint64_t {
+    const uint32_t id = 0xffffffffu - (uint32_t)e;
+    return ((uint64_t)(0xffffffffu - id) << 32) | (uint64_t)__float_as_uint(unkey((uint32_t)(e >> 32)));
+  };
+  if (Lk <= kWave) {
+    // one wave in registers, straight to the kept list
+    if (wid == 0) {
+      uint64_t x = lane < Lk ? id_key(keys[lane]) : 0ull;
+      x = wave_sort_desc(x);
+      if (lane < Lk) {
+        Kept e;
+        e.id = (int)(0xffffffffu - (uint32_t)(x >> 32));
+        e.z = __uint_as_float((uint32_t)x);
+        kept[(size_t)rr * kKeptCap + lane] = e;
       }
-      keys[kFiltSortMax / 2 + i] = x;
+    }
+  } else if (Lk <= kKeptCap) {
+    __syncthreads();
+    int P2 = 2;
+    while (P2 < Lk) P2 <<= 1;
+    for (int i = threadIdx.x; i < P2; i += kFiltThreads) {
+      keys[kFiltSortMax / 2 + i] = i < Lk ? id_key(keys[i]) : 0ull;
     }
     lds_bitonic_desc(keys + kFiltSortMax / 2, P2);
     Kept* dst = kept + (size_t)rr * kKeptCap;
