@@ -519,6 +519,36 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   const float m = n_all > 0 ? unkey((uint32_t)(keys[0] >> 32)) : -INFINITY;
   const double md = (double)m;
 
+  int Lk = L;                                        // kept prefix length
+  uint32_t tau = tau_k;
+  double keep_sum = 0.0;
+  if (L <= kWave) {
+    // The usual case: the whole sorted prefix is one wave, lane i holding
+    // entry i; the running sums are one inclusive scan in lane order, the
+    // crossing and the first entry below tau are ballots.  Every thread
+    // keeps Lk = L <= 64 so all take the same branch below; wave 0 refines it.
+    if (wid == 0) {
+      const bool in = lane < L;
+      const uint32_t k32 = in ? (uint32_t)(keys[lane] >> 32) : 0u;
+      const double wgt = in ? exp64(((double)unkey(k32) - md) * invT, tbl) : 0.0;
+      double run = wgt;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const double y = __shfl_up(run, o, kWave);
+        if (lane >= o) run += y;
+      }
+      const double tot = __shfl(run, kWave - 1, kWave);
+      if (top_p < 1.0f && L > 0) {
+        // M = first sorted index whose running mass reaches top_p of the total
+        const uint64_t hit = __ballot(in && run / tot >= (double)top_p);
+        const int M = hit ? __ffsll((unsigned long long)hit) - 1 : L - 1;
+        tau = (uint32_t)__shfl((int)k32, M, kWave);
+        const uint64_t below = __ballot(in && k32 < tau);
+        Lk = below ? __ffsll((unsigned long long)below) - 1 : L;
+      }
+      keep_sum = wave_sum(lane < Lk ? wgt : 0.0);   // normaliser over the kept prefix
+    }
+  } else {
   // float64 weights of the sorted prefix, blocked scan in sorted order
   const int q = (L + kFiltThreads - 1) / kFiltThreads;
   const int i_lo = min(L, (int)threadIdx.x * q), i_hi = min(L, i_lo + q);
@@ -527,8 +557,6 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
     mine += exp64(((double)unkey((uint32_t)(keys[i] >> 32)) - md) * invT, tbl);
   double tot;
   const double excl = block_scan_excl<double>(mine, dl, tot);
-  int Lk = L;                                        // kept prefix length
-  uint32_t tau = tau_k;
   if (top_p < 1.0f && L > 0) {
     // M = first sorted index whose running mass reaches top_p of the total
     int hit = INT_MAX;
@@ -547,7 +575,6 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
     if (Lk == INT_MAX) Lk = L;
   }
   // normaliser over the kept prefix, same blocked order
-  double keep_sum = 0.0;
   {
     const int j_lo = min(Lk, (int)threadIdx.x * q), j_hi = min(Lk, j_lo + q);
     for (int i = j_lo; i < j_hi; ++i)
@@ -555,6 +582,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
     double stot;
     (void)block_scan_excl<double>(keep_sum, dl, stot);
     keep_sum = stot;
+  }
   }
   if (Lk > kKeptCap) out.status = 1;
 
