@@ -45,6 +45,10 @@ HBM_PEAK_GBPS = 8000.0
 # FETCH_SIZE and WRITE_SIZE runs scaled by a plain-copy calibration (see the
 # profiles directory); valid only for the sources they were taken with.
 ROW_STATS_TRAFFIC = {"sources_sha256_16": "f0804ab9644a5c5b", "bytes": 148139654}
+# The same for one LM-head launch at M=320, D=4096, V=128256 (FETCH_SIZE and
+# WRITE_SIZE of the lm_head op, scaled by the copy calibration taken with the
+# row-statistics figure).
+LM_HEAD_TRAFFIC = {"sources_sha256_16": "948c3dc50465589f", "bytes": 1180341477}
 WORKLOAD = 3
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,K=4,V=128k"
 
@@ -81,10 +85,10 @@ class HipEvents:
             self.lib.hipEventDestroy(h)
 
 
-def row_stats_sources_hash():
+def sources_hash(files=("row_stats.hip", "common.h")):
     import hashlib
     h = hashlib.sha256()
-    for f in ("row_stats.hip", "common.h"):
+    for f in files:
         with open(os.path.join(ROOT, "speculative_decoding_sampling_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -384,7 +388,9 @@ def bench_lm_head(args):
                    "input_sets": 1, "weight_layout": "packed once before timing"},
         "roofline": {"bound": "mfma", "kernel": "lm_head", "achieved": flops / k_us / 1e6,
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": flops / k_us / 1e6 / 2500.0,
-                     "traffic": None, "launch_us": k_us, "flops_per_launch": flops,
+                     "traffic": (LM_HEAD_TRAFFIC["bytes"] if sources_hash(("lm_head.hip", "common.h"))
+                                 == LM_HEAD_TRAFFIC["sources_sha256_16"] else None),
+                     "launch_us": k_us, "flops_per_launch": flops,
                      "hbm_gbps": hbm_bytes / k_us / 1e3, "hbm_bytes_per_launch": hbm_bytes},
         "reference_gemm": {"what": "torch.matmul (hipBLASLt) on the same row-major bf16 "
                                    "operands: logits only, no statistics; context",
@@ -604,7 +610,7 @@ def main():
         # the counters were taken on the headline workload's launch
         traffic = (ROW_STATS_TRAFFIC["bytes"]
                    if wl == WORKLOAD and
-                   row_stats_sources_hash() == ROW_STATS_TRAFFIC["sources_sha256_16"] else None)
+                   sources_hash() == ROW_STATS_TRAFFIC["sources_sha256_16"] else None)
         evb.close()
         log(f"row_stats alone: {k1_us:.2f} us/launch over {reps} launches")
     if filtered:
