@@ -48,6 +48,8 @@ ROW_STATS_TRAFFIC = {"sources_sha256_16": "f0804ab9644a5c5b", "bytes": 148139654
 # The same for one LM-head launch at M=320, D=4096, V=128256 (FETCH_SIZE and
 # WRITE_SIZE of the lm_head op, scaled by the copy calibration taken with the
 # row-statistics figure).
+# And for one top-k candidate pass of workload 4 (B=256, K=8, V=152064 fp32).
+FILTER_TRAFFIC = {"sources_sha256_16": "54dd29cf094e0150", "bytes": 2687313229}
 LM_HEAD_TRAFFIC = {"sources_sha256_16": "948c3dc50465589f", "bytes": 1180341477}
 WORKLOAD = 3
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,K=4,V=128k"
@@ -593,7 +595,8 @@ def main():
         # needed row); its duration is the per-call stage mean above.
         dominant = "filter_cand"
         k1_us = stage_us[dominant]
-        traffic = None
+        traffic = (FILTER_TRAFFIC["bytes"] if wl == 4 and sources_hash(("filter.hip", "common.h"))
+                   == FILTER_TRAFFIC["sources_sha256_16"] else None)
         log(f"filter_cand: {k1_us:.2f} us/launch (stage mean)")
     else:
         # The dominant kernel alone, for the roofline: a burst of row-statistics
