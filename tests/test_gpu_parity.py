@@ -153,6 +153,31 @@ def test_unaligned_and_tiny_vocabularies(V):
         assert_parity(w, label=f"V={V}")
 
 
+@pytest.mark.parametrize("V", [4097, 10007, 20011])
+def test_unaligned_vocabularies_filtered(V):
+    # Rows that are not 16-byte aligned and a ragged last chunk on the top-k /
+    # top-p path (the candidate pass's element loads), drafts drawn from the
+    # filtered draft distribution.
+    rng = np.random.default_rng(V + 1)
+    B, K, top_k, top_p = 5, 3, 20, 0.9
+    t = rng.normal(0, 2, size=(B, K + 1, V)).astype(np.float32)
+    d = (t[:, :K] + rng.normal(0, 0.6, size=(B, K, V))).astype(np.float32)
+    from speculative_decoding_sampling_amd.workloads import Workload, to_bf16_bits, uniforms
+    for dtype in ("f32", "bf16"):
+        tt = to_bf16_bits(t) if dtype == "bf16" else t
+        dd = to_bf16_bits(d) if dtype == "bf16" else d
+        uni = uniforms(rng, (B, K))
+        toks = np.array([[oracle_sampler(O.widen_row(dd[b, k], dtype), f32(0.9), top_k,
+                                         f32(top_p), float(uni[b, k])) for k in range(K)]
+                         for b in range(B)], dtype=np.int32)
+        w = Workload(cfg=0, seed=V, B=B, K=K, V=V, dtype=dtype, T=f32(0.9), top_k=top_k,
+                     top_p=f32(top_p), eos_id=-1, target=np.ascontiguousarray(tt),
+                     draft=np.ascontiguousarray(dd), draft_tokens=toks,
+                     draft_len=np.array([3, 2, 1, 0, 3], np.int32),
+                     u=uniforms(rng, (B, K)), u_final=uniforms(rng, (B,)))
+        assert_parity(w, label=f"V={V} filtered {dtype}")
+
+
 def test_exhaustive_cells_match_oracle():
     # Thousands of random V=3, K=2 requests over the worked example's
     # distributions: tokens must match the oracle request for request.
