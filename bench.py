@@ -581,6 +581,27 @@ def main():
     n = sets[0]["n_emitted"].cpu().numpy()
     assert np.all((n >= 1) & (n <= w0.draft_len + 1)), n
 
+    # Context for the roofline: what a plain device copy of 512 MiB reaches on
+    # this box (bytes read + written per second), timed like the steps.  Not
+    # in counter runs, whose calibration copies are told apart by kernel name.
+    copy_gbps = None
+    if not args.copy_calibration_mib:
+        cal_bytes = 512 << 20
+        csrc = torch.empty(cal_bytes // 4, dtype=torch.float32, device=dev).normal_()
+        cdst = torch.empty_like(csrc)
+        cdst.copy_(csrc)
+        evm = HipEvents(2)
+        torch.cuda.synchronize()
+        evm.lib.hipEventRecord(evm.arr[0], stream.cuda_stream)
+        for _ in range(10):
+            cdst.copy_(csrc)
+        evm.lib.hipEventRecord(evm.arr[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * cal_bytes * 10 / (evm.elapsed_ms(0, 1) * 1e-3) / 1e9
+        evm.close()
+        del csrc, cdst
+        log(f"plain 512 MiB device copy: {copy_gbps:.0f} GB/s (read + write)")
+
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
@@ -648,6 +669,7 @@ def main():
                      "traffic": traffic, "launch_us": k1_us,
                      "bytes_per_launch": burst_bytes},
         "stages_us": stage_us,
+        "copy_512mib_gbps_read_plus_write": copy_gbps,
     }
     if not args.no_cpu_baseline:
         log(f"timing the oracle for about {args.cpu_seconds:.0f} s")
