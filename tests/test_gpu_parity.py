@@ -281,6 +281,21 @@ def test_parity_topk_topp_reduced():
     assert rep["positions"] > 0
 
 
+def test_parity_topk_topp_with_eos():
+    # EOS on the filtered path. The EOS id is the token the oracle accepts
+    # furthest into some request's draft, so that request must stop there
+    # on the EOS path rather than run on to a rejection or the bonus token.
+    w = make_workload(4, B=16, draft_sampler=oracle_sampler)
+    o0 = run_oracle(w, eos_id=-1)
+    # without an EOS id every request ends on a rejection or the bonus token,
+    # and its last accepted draft position is one before its stop position
+    j, b = max((int(o0["stop_pos"][b]) - 1, b) for b in range(w.B))
+    assert j >= 0, "no request accepts any draft token"
+    w.eos_id = int(o0["out_tokens"][b, j])
+    rep, g, o = assert_parity(w, label=f"filtered, eos={w.eos_id} at b={b} pos={j}")
+    assert o["path"][b] == O.PATH_EOS and o["stop_pos"][b] <= j
+
+
 def test_parity_topk_topp_full_size_sampled():
     w = make_workload(4, draft_sampler=oracle_sampler)          # B=256, K=8, V=152064 fp32
     rep, g, o = assert_parity(w, requests=list(range(0, w.B, 5)), label="full size, sampled")
