@@ -82,7 +82,6 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 }
 
 // s_waitcnt immediates (vector-memory count only; LDS / export counts untouched)
-constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm13 = 0x0F7D;
 static_assert(kLmKB == 64 && kLmHPer == 5,
               "wait immediates assume 5 staging and 4 weight loads per block");
@@ -137,10 +136,19 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
           0);
     }
   };
-  auto load_w = [&](int k0, uint4* w) {
+  // The weight loads are inline asm and their waits explicit.  Left to the
+  // compiler, the wait for a ring register loaded in an earlier trip of the
+  // block loop below drains every load in flight, the prefetches just issued
+  // included: once per trip the weights' two-block lead collapses (310 vs
+  // 284 us per launch at M = 320, D = 4096, V = 128256).  The compiler sees
+  // each asm output as written at once, so no register of the ring may look
+  // dead while its load flies (see the final drain).
+  auto load_w = [&](int k0, lm_u32x4* w) {
     const bf16_t* src = wbase + (size_t)(k0 / kLmKB) * kLmPackBlock;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) w[s] = *reinterpret_cast<const uint4*>(src + s * kWave * 8);
+#define SPECV_LDW(i, off) \
+  asm volatile("global_load_dwordx4 %0, %1, off offset:" #off : "=v"(w[i]) : "v"(src))
+    SPECV_LDW(0, 0); SPECV_LDW(1, 1024); SPECV_LDW(2, 2048); SPECV_LDW(3, 3072);
+#undef SPECV_LDW
   };
 
   lm_f32x16 acc[kLmMTiles];
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
   for (int s = 0; s < 4; ++s) boff[s] = (((4 * h + s) ^ ((l32 >> 1) & 7)) * 8);   // 32 t: no effect
 
   const int nkb = D / kLmKB;
-  uint4 wr0[4], wr1[4], wr2[4];                      // weight ring: blocks kb, kb+1, kb+2
+  lm_u32x4 wr0[4], wr1[4], wr2[4];                   // weight ring: blocks kb, kb+1, kb+2
   const int klast = (nkb - 1) * kLmKB;
   stage_h(0, lds0);
   load_w(0, wr0);
@@ -169,11 +177,15 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
   // The prefetches are unconditional (past the last block they repeat it:
   // valid addresses, unused data), so the count of loads in flight is the
   // same at every block boundary and the compiler's waits stay exact.
-  auto block = [&](int kb, const uint4* wa, uint4* w2, const bf16_t* cur, bf16_t* next) {
+  auto block = [&](int kb, lm_u32x4* wa, lm_u32x4* w2, const bf16_t* cur, bf16_t* next) {
     stage_h(min((kb + 2) * kLmKB, klast), next);
     asm volatile("" ::: "memory");                   // keep the staging loads first in the count
     load_w(min((kb + 2) * kLmKB, klast), w2);
-    asm volatile("" ::: "memory");
+    // This block's weights (loaded two blocks ago) have landed once at most
+    // 18 younger loads fly: the staging and weights of blocks kb + 1 and
+    // kb + 2.  The wait takes the ring registers as in-out operands, so no
+    // MFMA reading them can move above it.
+    asm volatile("s_waitcnt vmcnt(18)" : "+v"(wa[0]), "+v"(wa[1]), "+v"(wa[2]), "+v"(wa[3]));
     // The fragment reads are inline ds_read_b128 with explicit LDS waits: the
     // compiler cannot tell them from the staging DMA into the other buffer
     // and would otherwise wait for every load, weights included, before the
@@ -230,7 +242,13 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
   }
   // the last blocks' repeated prefetches are still landing: drain them before
   // the epilogue reuses LDS
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  // The ring registers stay live until every load has landed: the
+  // prefetches past the last block are never read, and a register the
+  // compiler took for dead could be reused while its load is still in flight.
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(wr0[0]), "+v"(wr0[1]), "+v"(wr0[2]), "+v"(wr0[3]), "+v"(wr1[0]),
+                 "+v"(wr1[1]), "+v"(wr1[2]), "+v"(wr1[3]), "+v"(wr2[0]), "+v"(wr2[1]),
+                 "+v"(wr2[2]), "+v"(wr2[3]));
   __builtin_amdgcn_s_barrier();
 
   // Epilogue.  acc[t][r] is logit (row m0 + 32 t + l32, id vbase + vof(r)).
