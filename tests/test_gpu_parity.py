@@ -153,6 +153,49 @@ def test_unaligned_and_tiny_vocabularies(V):
         assert_parity(w, label=f"V={V}")
 
 
+def _custom_workload(t, d, draft_len, rng, dtype="f32", T=1.0, seed=0):
+    from speculative_decoding_sampling_amd.workloads import Workload, to_bf16_bits, uniforms
+    B, K1, V = t.shape
+    K = K1 - 1
+    # draft tokens drawn from the draft rows (Gumbel-max on z / T)
+    toks = np.array([[int(np.argmax(d[b, k] / np.float32(T) + rng.gumbel(size=V)))
+                      for k in range(K)] for b in range(B)], dtype=np.int32).reshape(B, K)
+    tt = to_bf16_bits(t) if dtype == "bf16" else t
+    dd = to_bf16_bits(d) if dtype == "bf16" else d
+    return Workload(cfg=0, seed=seed, B=B, K=K, V=V, dtype=dtype, T=f32(T), top_k=0, top_p=1.0,
+                    eos_id=-1, target=np.ascontiguousarray(tt), draft=np.ascontiguousarray(dd),
+                    draft_tokens=toks, draft_len=np.asarray(draft_len, np.int32),
+                    u=uniforms(rng, (B, K)), u_final=uniforms(rng, (B,)))
+
+
+def test_maximum_draft_length():
+    # K = 63, the largest draft length the call takes (SPECV_MAX_K): drafts
+    # close to the target so the first-rejection scan runs deep, one request
+    # whose draft rows equal its target rows (every draft accepted, then the
+    # bonus draw from target row 63), and ragged lengths from 0 to 63
+    rng = np.random.default_rng(63)
+    B, K, V = 6, 63, 1500
+    t = rng.normal(0, 2, size=(B, K + 1, V)).astype(np.float32)
+    d = (t[:, :K] + rng.normal(0, 0.03, size=(B, K, V))).astype(np.float32)
+    d[1] = t[1, :K]
+    w = _custom_workload(t, d, [63, 63, 40, 0, 63, 17], rng, seed=63)
+    rep, g, o = assert_parity(w, label="K=63")
+    assert o["path"][1] == O.PATH_BONUS and o["n_emitted"][1] == 64
+    # a rejection in the upper half of the 64-lane scan
+    assert any(o["path"][b] == O.PATH_REJECT and o["stop_pos"][b] >= 32 for b in range(B))
+
+
+def test_maximum_vocabulary():
+    # V = 4194304, the largest vocabulary the call takes (SPECV_MAX_V): the
+    # sampler's 2048-token chunks reach their table limit of 2048 per row
+    rng = np.random.default_rng(22)
+    B, K, V = 2, 2, 1 << 22
+    t = rng.normal(0, 2, size=(B, K + 1, V)).astype(np.float32)
+    d = (t[:, :K] + rng.normal(0, 0.7, size=(B, K, V)).astype(np.float32)).astype(np.float32)
+    w = _custom_workload(t, d, [2, 1], rng, dtype="bf16", seed=22)
+    assert_parity(w, label="V=2^22")
+
+
 @pytest.mark.parametrize("V", [4097, 10007, 20011])
 def test_unaligned_vocabularies_filtered(V):
     # Rows that are not 16-byte aligned and a ragged last chunk on the top-k /
