@@ -85,6 +85,9 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 constexpr int kWaitVm13 = 0x0F7D;
 static_assert(kLmKB == 64 && kLmHPer == 5,
               "wait immediates assume 5 staging and 4 weight loads per block");
+constexpr int kLmWLoads = 4;                        // weight loads per wave and block
+// the block-start wait in lm_head_kernel lets two blocks' loads fly: vmcnt(18)
+static_assert(2 * (kLmHPer + kLmWLoads) == 18, "block-start wait immediate");
 static_assert(kLmMTiles == 10, "the fragment pipeline is written out for 20 pairs");
 static_assert(kLmTilesPerChunk <= kWave, "one chunk's tiles fold in one wave");
 
