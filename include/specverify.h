@@ -55,7 +55,7 @@ typedef enum {
   SPECV_EINVAL = 1,       /* bad argument (null/misaligned pointer, bad size or parameter) */
   SPECV_EWORKSPACE = 2,   /* workspace missing, misaligned (16 B) or smaller than specv_workspace_bytes() */
   SPECV_EHIP = 3,         /* a HIP launch failed */
-  SPECV_EUNSUPPORTED = 4  /* valid request this build does not implement (see specv_verify) */
+  SPECV_EUNSUPPORTED = 4  /* valid request the library does not implement (see specv_verify) */
 } specv_status_t;
 
 typedef enum {
