@@ -444,7 +444,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "single-GPU implementation; --gpus must be 1"}))
+        print(json.dumps({"error": "runs on one GPU only; --gpus must be 1"}))
         log("multi-GPU runs are not implemented: the path would shard over requests "
             "with no communication (see the design notes); run with --gpus 1")
         sys.exit(2)
