@@ -354,6 +354,22 @@ def test_parity_topk_bf16_with_ties(top_k, top_p):
     assert_parity(w, label=f"bf16 top_k={top_k} top_p={top_p}")
 
 
+def test_parity_filtered_ragged_bf16_with_eos():
+    # the mixed-batch workload (ragged draft lengths, drafts equal to or far
+    # from the target, bf16) through the top-k/top-p path, with an EOS id the
+    # oracle accepts mid-draft
+    w = make_workload(5, B=16)
+    w.top_k, w.top_p, w.T = 40, f32(0.92), f32(0.8)
+    redraw_tokens(w, 5)
+    o0 = run_oracle(w, eos_id=-1)
+    j, b = max((int(o0["stop_pos"][b]) - 1, b) for b in range(w.B))
+    assert j >= 1, "no request accepts two draft tokens"
+    w.eos_id = int(o0["out_tokens"][b, j])
+    rep, g, o = assert_parity(w, label=f"filtered, eos={w.eos_id} at b={b} pos={j}")
+    assert o["path"][b] == O.PATH_EOS and o["stop_pos"][b] <= j
+    assert len(set(w.draft_len.tolist())) > 1
+
+
 def test_filter_capacity_limit_is_a_request_error():
     # A row whose logits are all equal keeps every token under top-k (ties
     # kept): more than the 512-token kept list, so that request is reported
