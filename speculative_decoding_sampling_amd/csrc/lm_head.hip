@@ -145,7 +145,9 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
   // included: once per trip the weights' two-block lead collapses (310 vs
   // 284 us per launch at M = 320, D = 4096, V = 128256).  The compiler sees
   // each asm output as written at once, so no register of the ring may look
-  // dead while its load flies (see the final drain).
+  // dead while its load flies (see the final drain), and the block loop must
+  // move no registers: a move of a ring register would copy a value still in
+  // flight.  A CPU test compiles this file and checks the loop for moves.
   auto load_w = [&](int k0, lm_u32x4* w) {
     const bf16_t* src = wbase + (size_t)(k0 / kLmKB) * kLmPackBlock;
 #define SPECV_LDW(i, off) \
