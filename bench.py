@@ -50,7 +50,7 @@ ROW_STATS_TRAFFIC = {"sources_sha256_16": "f0804ab9644a5c5b", "bytes": 148139654
 # row-statistics figure).
 # And for one top-k candidate pass of workload 4 (B=256, K=8, V=152064 fp32).
 FILTER_TRAFFIC = {"sources_sha256_16": "54dd29cf094e0150", "bytes": 2687313229}
-LM_HEAD_TRAFFIC = {"sources_sha256_16": "885ef8a696da9172", "bytes": 1180237459}
+LM_HEAD_TRAFFIC = {"sources_sha256_16": "e410f425f4f93b97", "bytes": 1180262001}
 WORKLOAD = 3
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,K=4,V=128k"
 

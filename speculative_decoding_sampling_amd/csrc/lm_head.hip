@@ -71,6 +71,15 @@ constexpr int kLmPackGroups = kLmPackVocab / 32;       // 32-id groups (one wave
 constexpr int kLmPackWave = 4 * kWave * 8;             // packed elements of one group's block
 constexpr int kLmPackBlock = kLmPackGroups * kLmPackWave;   // of one tile's block (16 KB)
 static_assert(kLmVocab % kLmPackVocab == 0, "a workgroup covers whole packed tiles");
+// epilogue transpose: half a row block of logits, rows padded to 264 ids
+constexpr int kLmTrStride = kLmVocab + 8;
+constexpr int kLmTrElems = (kLmRows / 2) * kLmTrStride;
+constexpr int kLmTrPieces = (kLmRows / 2) * kLmVocab / 8;   // 16-byte pieces of a half
+static_assert(kLmTrPieces % kLmThreads == 0, "transpose pieces per thread");
+static_assert(kLmMTiles % 2 == 0, "the epilogue stores the row block in two halves");
+static_assert(kLmTrElems * 2 % 16 == 0 &&
+                  kLmTrElems * 2 + kLmWaves * kLmRows * 8 <= 3 * kLmRows * kLmKB * 2,
+              "transpose buffer and statistics fit the staging buffers");
 
 __device__ __forceinline__ lm_bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(lm_bf16x8, w); }
 __device__ __forceinline__ lm_bf16x8 as_bf16x8(lm_u32x4 w) { return __builtin_bit_cast(lm_bf16x8, w); }
@@ -99,9 +108,11 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
   // banks (even rows one half, odd rows the other), and one 16-lane pass of a
   // fragment read (16 consecutive rows, one piece) then touches every bank
   // once: 8 distinct slots among the even rows and 8 among the odd.
-  __shared__ __attribute__((aligned(16))) bf16_t lds0[kLmRows * kLmKB];
-  __shared__ __attribute__((aligned(16))) bf16_t lds1[kLmRows * kLmKB];
-  __shared__ __attribute__((aligned(16))) bf16_t lds2[kLmRows * kLmKB];
+  // The three buffers are one array: the epilogue reuses all of it.
+  __shared__ __attribute__((aligned(16))) bf16_t lds[3 * kLmRows * kLmKB];
+  bf16_t* const lds0 = lds;
+  bf16_t* const lds1 = lds + kLmRows * kLmKB;
+  bf16_t* const lds2 = lds + 2 * kLmRows * kLmKB;
 
   const int tile = blockIdx.x % ntile;
   const int m0 = (blockIdx.x / ntile) * kLmRows;
@@ -257,13 +268,31 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
   __builtin_amdgcn_s_barrier();
 
   // Epilogue.  acc[t][r] is logit (row m0 + 32 t + l32, id vbase + vof(r)).
-  float2* red = reinterpret_cast<float2*>(lds0);   // [kLmWaves][kLmRows]; LDS is free now
-  const int vbase = tile * kLmVocab + wave * 32 + 4 * h;
+  // A lane holds one row, so its own stores would touch 32 rows 2 V bytes
+  // apart: 64 cache lines per store instruction (the logit stores cost 16-26
+  // us per launch at M = 320, D = 4096, V = 128256).  When every row starts
+  // 16-byte aligned, each half of the row block (160 rows x 256 ids) goes
+  // through LDS instead and the workgroup stores whole 512-byte row segments
+  // (~11 us less per launch).  Rows are padded to 264 ids: 16-byte aligned
+  // for the reads, at most 2-way bank conflicts for the writes.
+  // The indices are derived afresh from the thread and block ids: values kept
+  // live across the block loop for the epilogue made the register allocator
+  // move ring registers inside the loop, copying weights still in flight.
+  int e_tid = threadIdx.x, e_bid = blockIdx.x;
+  asm volatile("" : "+v"(e_tid), "+s"(e_bid));
+  const int e_lane = e_tid % kWave;
+  const int e_wave = __builtin_amdgcn_readfirstlane(e_tid / kWave);
+  const int e_h = e_lane / 32, e_l32 = e_lane % 32;
+  const int e_tile = e_bid % ntile, e_m0 = (e_bid / ntile) * kLmRows;
+  float2* red = reinterpret_cast<float2*>(lds + kLmTrElems);   // [kLmWaves][kLmRows]
+  bf16_t* tr = lds;                                            // [kLmRows / 2][kLmTrStride]
+  const int vbase = e_tile * kLmVocab + e_wave * 32 + 4 * e_h;
+  const bool rows16 = (V & 7) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   // 8-byte stores need every row to start 8-byte aligned
   const bool vec_ok = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0;
 #pragma unroll
   for (int t = 0; t < kLmMTiles; ++t) {
-    const int m = m0 + t * 32 + l32;
+    const int m = e_m0 + t * 32 + e_l32;
     float z[16];
     uint32_t zb[16];
 #pragma unroll
@@ -272,7 +301,17 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
       z[r] = __uint_as_float(zb[r] << 16);
     }
     // ids of register r: vbase + 8 (r / 4) + r % 4: four runs of four
-    if (m < M) {
+    if (rows16) {
+      bf16_t* trow =
+          tr + ((t % (kLmMTiles / 2)) * 32 + e_l32) * kLmTrStride + e_wave * 32 + 4 * e_h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint2 pk;
+        pk.x = zb[4 * q] | (zb[4 * q + 1] << 16);
+        pk.y = zb[4 * q + 2] | (zb[4 * q + 3] << 16);
+        *reinterpret_cast<uint2*>(trow + 8 * q) = pk;
+      }
+    } else if (m < M) {
       bf16_t* orow = out + (size_t)m * V;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -302,7 +341,23 @@ __global__ __launch_bounds__(kLmThreads, 1) void lm_head_kernel(
         if (vbase + 8 * (r / 4) + r % 4 < V) s += __builtin_amdgcn_exp2f(fmaf(z[r], c, -mc));
     }
     s += __shfl_xor(s, 32, kWave);
-    if (h == 0) red[wave * kLmRows + t * 32 + l32] = make_float2(mx, s);
+    if (e_h == 0) red[e_wave * kLmRows + t * 32 + e_l32] = make_float2(mx, s);
+    if (rows16 && t % (kLmMTiles / 2) == kLmMTiles / 2 - 1) {
+      // a half is in LDS: store its rows, 16 bytes per lane, 32 lanes a row
+      __syncthreads();
+      const int r0 = e_m0 + (t / (kLmMTiles / 2)) * (kLmRows / 2);
+      const int vend = min(kLmVocab, V - e_tile * kLmVocab);   // a multiple of 8
+#pragma unroll
+      for (int i = 0; i < kLmTrPieces / kLmThreads; ++i) {
+        const int p = threadIdx.x + i * kLmThreads;
+        const int lr = p / 32, c8 = (p % 32) * 8;
+        if (r0 + lr < M && c8 < vend) {
+          const uint4 v = *reinterpret_cast<const uint4*>(tr + lr * kLmTrStride + c8);
+          *reinterpret_cast<uint4*>(out + (size_t)(r0 + lr) * V + e_tile * kLmVocab + c8) = v;
+        }
+      }
+      __syncthreads();                               // the next half overwrites tr
+    }
   }
   __syncthreads();
   for (int rr = threadIdx.x; rr < kLmRows; rr += kLmThreads) {
