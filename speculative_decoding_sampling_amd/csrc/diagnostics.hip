@@ -38,6 +38,17 @@ __device__ __forceinline__ void wave_row_stats(const float2* __restrict__ p, int
   S = wave_sum(scaled);
 }
 
+// The same from one partial per lane (lanes past the row hold (-inf, 0)): what
+// the loop above computes when n <= kWave, so a caller can issue the loads
+// of several rows before the first wait.
+__device__ __forceinline__ void wave_row_stats1(float2 v, float c, float& M, float& S) {
+  const float m = v.x;
+  const float s = m == -INFINITY ? 0.f : v.y;
+  M = wave_max(m);
+  const float scaled = m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f(__fmul_rn(m, c) - __fmul_rn(M, c));
+  S = wave_sum(scaled);
+}
+
 template <typename T, int VECS>
 __global__ __launch_bounds__(kRowThreads) void beta_pass_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
@@ -75,8 +86,19 @@ __global__ __launch_bounds__(kRowThreads) void beta_pass_kernel(
     }
   }
   float Mt, St, Md, Sd;
-  wave_row_stats(part + ((size_t)b * R + k) * nchunk, nchunk, c, Mt, St);
-  wave_row_stats(part + ((size_t)b * R + K + 1 + k) * nchunk, nchunk, c, Md, Sd);
+  const float2* pt = part + ((size_t)b * R + k) * nchunk;
+  const float2* pd = part + ((size_t)b * R + K + 1 + k) * nchunk;
+  if (nchunk <= kWave) {
+    // both rows' partials requested together: one wait covers them and the logits
+    const float2 none = make_float2(-INFINITY, 0.f);
+    const float2 vt = lane < nchunk ? pt[lane] : none;
+    const float2 vd = lane < nchunk ? pd[lane] : none;
+    wave_row_stats1(vt, c, Mt, St);
+    wave_row_stats1(vd, c, Md, Sd);
+  } else {
+    wave_row_stats(pt, nchunk, c, Mt, St);
+    wave_row_stats(pd, nchunk, c, Md, Sd);
+  }
   const bool ok = Mt != -INFINITY && Md != -INFINITY;
   const float mtc = __fmul_rn(Mt, c), mdc = __fmul_rn(Md, c);
   const float rt = 1.f / St, rd = 1.f / Sd;
