@@ -109,6 +109,23 @@ def test_fused_general_inputs_logits_within_accumulation_bound():
     assert agree > 0.99
 
 
+@pytest.mark.parametrize("offset", [4, 1])
+def test_fused_output_alignment_store_paths_agree(offset):
+    # The logits written 16-byte aligned (whole rows through LDS) and at an
+    # element offset of 8 bytes (8-byte stores per lane) or 2 bytes (element
+    # stores): the same logits, statistics and draws.
+    w = make_lm_head_workload(4, 3, 5000, 256, seed=41)
+    print(f"[lm_head] output offset {2 * offset} bytes", flush=True)
+    a = run_fused(w)
+    n = w.B * (w.K + 1) * w.V
+    buf = torch.zeros(n + 8, dtype=torch.bfloat16, device=DEV)
+    b = run_fused(w, target_logits=buf[offset:offset + n].view(w.B, w.K + 1, w.V))
+    for k in a:
+        x, y = np.asarray(a[k]), np.asarray(b[k])
+        same = np.array_equal(x, y, equal_nan=True) if x.dtype.kind == "f" else np.array_equal(x, y)
+        assert same, k
+
+
 def test_fused_deterministic():
     w = make_lm_head_workload(6, 4, 9000, 256, seed=31)
     a, b = run_fused(w), run_fused(w)
