@@ -10,12 +10,22 @@ import numpy as np
 import oracle as O
 
 
+def flag_ceiling(positions):
+    """The most flagged requests one parity case may have: the flag budget of
+    1e-4 of the verified positions, plus one.  An oracle that flags too much
+    would otherwise let parity pass on the few decisions left to compare."""
+    return 1 + int(1e-4 * positions)
+
+
 def to_numpy(res):
     return {k: v.detach().cpu().numpy() for k, v in res.items()}
 
 
-def compare(gpu, ora, K, alpha_tol=1e-5, mass_tol=1e-5):
-    """Return a report dict; ``report['mismatches']`` lists every failure."""
+def compare(gpu, ora, K, alpha_tol=1e-5, mass_tol=1e-5, check_flags=True):
+    """Return a report dict; ``report['mismatches']`` lists every failure.
+
+    With ``check_flags`` more than flag_ceiling(positions) flagged requests
+    is a failure too (cases that force near-ties on purpose turn it off)."""
     out_g, n_g = gpu["out_tokens"], gpu["n_emitted"]
     rep = {"requests": 0, "flagged": 0, "positions": 0, "mismatches": [], "flag_kinds": {},
            "max_alpha_err": 0.0, "max_mass_err": 0.0}
@@ -65,4 +75,7 @@ def compare(gpu, ora, K, alpha_tol=1e-5, mass_tol=1e-5):
                 if err > mass_tol:
                     rep["mismatches"].append((int(b), "residual mass", float(gpu["residual_mass"][b]),
                                               float(ora["residual_mass"][b])))
+    if check_flags and rep["flagged"] > flag_ceiling(rep["positions"]):
+        rep["mismatches"].append(("flag budget", rep["flagged"], rep["positions"],
+                                  rep["flag_kinds"]))
     return rep

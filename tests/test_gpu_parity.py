@@ -43,12 +43,15 @@ def run_oracle(w, requests=None, **kw):
                     requests=requests)
 
 
-def assert_parity(w, requests=None, label=""):
+def assert_parity(w, requests=None, label="", check_flags=True):
+    """GPU against oracle on one workload; unless the case forces near-ties on
+    purpose (check_flags=False), the oracle may flag at most
+    flag_ceiling(positions) requests (checked by compare)."""
     print(f"[parity] cfg={w.cfg} seed={w.seed} B={w.B} K={w.K} V={w.V} {w.dtype} {label}",
           flush=True)
     g = run_gpu(w)
     o = run_oracle(w, requests)
-    rep = compare(g, o, w.K)
+    rep = compare(g, o, w.K, check_flags=check_flags)
     print(f"  requests={rep['requests']} positions={rep['positions']} flagged={rep['flagged']} "
           f"kinds={rep['flag_kinds']} max_alpha_err={rep['max_alpha_err']:.2e} "
           f"max_mass_err={rep['max_mass_err']:.2e}", flush=True)
@@ -299,7 +302,7 @@ def test_sampler_exact_path_with_many_near_ties():
     w.draft = np.ascontiguousarray(t[:, :w.K] + rng.normal(0, 1e-4, size=t[:, :w.K].shape)
                                    .astype(np.float32))
     w.u[:] = np.float32(1.0 - 2.0 ** -24)
-    rep, g, o = assert_parity(w, label="near-identical rows")
+    rep, g, o = assert_parity(w, label="near-identical rows", check_flags=False)
     assert (o["path"] == O.PATH_REJECT).sum() >= 4
 
 

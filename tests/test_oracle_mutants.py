@@ -30,6 +30,19 @@ MUTANTS = {
                            "            stop, path = k, PATH_REJECT"),
     "eos_ignored": ("            if x == eos_id:", "            if x == eos_id and False:"),
     "beta_uses_max": ("return np.minimum(P, Q).sum()", "return np.maximum(P, Q).sum()"),
+    "topp_margin_one_sided": ("            margin = min(margin, top_p - c[M - 1])",
+                              "            margin = min(margin, margin)"),
+    "topp_margin_unnormalised": ("        margin = c[M] - top_p\n", "        margin = running[M] - top_p\n"),
+    "topp_margin_overflags": ("        margin = c[M] - top_p\n", "        margin = (c[M] - top_p) * 1e-9\n"),
+    "topp_flag_window_narrow": ("        if min(topp_rows) < TOPP_FLAG_ABS:",
+                                "        if min(topp_rows) < TOPP_FLAG_ABS * 1e-3:"),
+    "topp_flag_pos_next": ("            flag_kind, flag_pos = FLAG_TOPP, k\n",
+                           "            flag_kind, flag_pos = FLAG_TOPP, k + 1\n"),
+    "bonus_topp_flag_ignored": ('res["topp_margin_rows"][b, nb] < TOPP_FLAG_ABS:',
+                                'res["topp_margin_rows"][b, nb] < 0.0:'),
+    "topp_flag_past_stop": ("    last_decided = min(stop, nb - 1)", "    last_decided = nb - 1"),
+    "topp_margin_row_mixup": ('res["topp_margin_rows"][b, K + 1 + k] = info["topp_margin"]',
+                              'res["topp_margin_rows"][b, k] = info["topp_margin"]'),
     "beta_rows_swapped": ("zd = widen_row(draft[b, k], dtype)\n            if not",
                           "zd = widen_row(draft[b, (k + 1) % draft.shape[1]], dtype)\n            if not"),
 }
@@ -47,6 +60,9 @@ CHECKS = [
     "test_eos_truncation_invariant",
     "test_acceptance_rate_worked_example",
     "test_acceptance_rates_equal_expected_acceptance_per_position",
+    "test_topp_margin_exact_decimal",
+    "test_topp_flag_marks_the_cut_inside_its_window",
+    "test_topp_flag_on_the_bonus_row_and_not_past_the_stop",
 ]
 
 

@@ -6,9 +6,11 @@ pages' printed output, exact rational arithmetic, closed forms, library
 routines or brute force.
 """
 
+import decimal
 import json
 import math
 import os
+from decimal import Decimal as D
 from fractions import Fraction as F
 
 import numpy as np
@@ -224,6 +226,127 @@ def test_topp_brute_force_over_thresholds():
         np.testing.assert_allclose(P, want / want.sum(), rtol=1e-13, atol=1e-300)
         checked += 1
     assert checked > 300
+
+
+def _exact_topp(z, T, k, top_p, prec=60):
+    """The top-p cut of one row in 60-digit decimal arithmetic, by brute force.
+
+    The top-k base set comes from counting strictly larger logits (ties kept),
+    each weight exp((z - m) / T) is evaluated by decimal's own exp from the
+    exact binary values of z, T and top_p, and the shares are accumulated in
+    (logit descending, id ascending) order.  M is the first share reaching
+    top_p; the margin is the distance of top_p from the nearer of the two
+    shares around the cut, c_M and c_{M-1}.  Returns (tau_p, margin, order).
+    """
+    with decimal.localcontext() as ctx:
+        ctx.prec = prec
+        V = len(z)
+        if 0 < k < V:
+            idx = [v for v in range(V) if sum(1 for x in z if x > z[v]) < k]
+        else:
+            idx = list(range(V))
+        m = max(D(float(z[v])) for v in idx)
+        w = {v: ((D(float(z[v])) - m) / D(float(T))).exp() for v in idx}
+        order = sorted(idx, key=lambda v: (-z[v], v))
+        total = sum(w[v] for v in order)
+        shares, run = [], D(0)
+        for v in order:
+            run += w[v]
+            shares.append(run / total)
+        tp = D(float(top_p))
+        M = next(j for j, c in enumerate(shares) if c >= tp)
+        margin = shares[M] - tp
+        if M > 0:
+            margin = min(margin, tp - shares[M - 1])
+        return float(z[order[M]]), float(margin), order, shares
+
+
+def test_topp_margin_exact_decimal():
+    # The flag that guards the top-p cut measures how far top_p lies from the
+    # shares on either side of the crossing token (the cumulative mass in
+    # sorted order).  Checked against an exact-decimal brute force of the same
+    # quantity: its value, and the kept set whenever the cut is not a near tie.
+    rng = np.random.default_rng(31)
+    lower_side = 0
+    for _ in range(300):
+        V = int(rng.integers(2, 10))
+        z = np.round(rng.normal(0, 1.5, size=V), 1)
+        k = int(rng.integers(0, V + 1))
+        top_p = float(rng.uniform(0.05, 0.99))
+        T = float(rng.uniform(0.5, 1.5))
+        P, info = O.processed_distribution(z, T, top_k=k, top_p=top_p)
+        tau, margin, order, shares = _exact_topp(z, T, k, top_p)
+        assert abs(info["topp_margin"] - margin) <= 1e-14, (z, k, top_p, T)
+        if margin > 1e-12:
+            assert info["tau_p"] == tau
+            base = np.ones(V, dtype=bool)
+            if 0 < k < V:
+                base = np.array([(z > z[v]).sum() < k for v in range(V)])
+            assert np.array_equal(P > 0, base & (z >= tau))
+        j = next(i for i, c in enumerate(shares) if c >= decimal.Decimal(top_p))
+        lower_side += j > 0 and float(decimal.Decimal(top_p) - shares[j - 1]) < margin + 1e-15
+    assert lower_side > 50          # the share below the cut decided the margin often
+
+
+def _topp_flag_request(critical_pos, delta, reject0=False, bonus=False):
+    """One request (K = 2, V = 6, T = 1, top-p only) whose target row
+    ``critical_pos`` has a top-p cut exactly ``delta`` away from top_p.
+
+    top_p is set to the exact share of that row's third token plus delta
+    (so |margin| = |delta|); every other row's margin is checked (exactly) to
+    be far larger.  Each draft token is its draft row's top token, which
+    that row keeps; with ``reject0`` target row 0 gives draft token 0 a logit
+    far below its others, so top-p drops it and position 0 rejects at
+    u[0] = 0.5 (u is 0 elsewhere).
+    """
+    rng = np.random.default_rng(5)
+    K, V = 2, 6
+    t = np.round(rng.normal(0, 1.0, size=(1, K + 1, V)), 2)
+    d = np.round(t[:, :K] + rng.normal(0, 0.5, size=(1, K, V)), 2)
+    crit = np.array([2.0, 1.0, 0.5, 0.0, -1.0, -2.0])
+    t[0, critical_pos] = crit
+    if reject0:
+        t[0, 0, int(np.argmax(d[0, 0]))] = t[0, 0].min() - 8.0
+    _, _, _, shares = _exact_topp(crit, 1.0, 0, 0.5)
+    top_p = float(shares[2]) + delta
+    for k in range(K + 1):
+        if k != critical_pos:
+            assert abs(_exact_topp(t[0, k], 1.0, 0, top_p)[1]) > 1e-6
+    for k in range(K):
+        assert abs(_exact_topp(d[0, k], 1.0, 0, top_p)[1]) > 1e-6
+    toks = np.array([[int(np.argmax(d[0, k])) for k in range(K)]], dtype=np.int32)
+    if not bonus:
+        # position 1 drafts a token the target row keeps (its top token)
+        toks[0, 1] = int(np.argmax(t[0, 1]))
+        d[0, 1, toks[0, 1]] = d[0, 1].max() + 1.0
+    u = np.array([[0.5 if reject0 else 0.0, 0.0]], dtype=np.float32)
+    return O.verify(t, d, toks, np.array([K], np.int32), u, np.array([0.37], np.float32), 1.0,
+                    top_k=0, top_p=top_p, dtype="f64")
+
+
+def test_topp_flag_marks_the_cut_inside_its_window():
+    # A decided position whose target row has a top-p cut within 1e-10 of
+    # top_p is flagged FLAG_TOPP at that position, on both sides of the
+    # share; 4e-10 away it is not.
+    for delta in (4e-11, -4e-11):
+        r = _topp_flag_request(1, delta)
+        assert r["flag_kind"][0] == O.FLAG_TOPP and r["flag_pos"][0] == 1, delta
+        assert abs(r["topp_margin_rows"][0, 1] - abs(delta)) < 1e-15
+    for delta in (4e-10, -4e-10):
+        r = _topp_flag_request(1, delta)
+        assert r["flag_kind"][0] == O.FLAG_NONE, delta
+
+
+def test_topp_flag_on_the_bonus_row_and_not_past_the_stop():
+    # Every draft accepted: the bonus row's cut is checked too (flag at n).
+    r = _topp_flag_request(2, 3e-11, bonus=True)
+    assert r["path"][0] == O.PATH_BONUS
+    assert r["flag_kind"][0] == O.FLAG_TOPP and r["flag_pos"][0] == 2
+    # A rejection at position 0 leaves position 1 undecided: its cut does not
+    # matter, so it is not flagged.
+    r = _topp_flag_request(1, 3e-11, reject0=True)
+    assert r["path"][0] == O.PATH_REJECT and r["stop_pos"][0] == 0
+    assert r["flag_kind"][0] == O.FLAG_NONE
 
 
 def test_filters_off_is_unfiltered_bit_for_bit():
