@@ -96,14 +96,28 @@ def sources_hash(files=("row_stats.hip", "common.h")):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, budget_s, group=None):
-    """Time the fp64 oracle on the same workload, single core: whole calls, or
-    groups of ``group`` requests in turn where a whole call is too long for
-    the budget."""
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where it is absent)."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_groups(B, group):
+    return ([list(range(B))] if group is None else
+            [list(range(i, min(i + group, B))) for i in range(0, B, group)])
+
+
+def _time_oracle(w, groups, budget_s):
+    """Verify ``groups`` of requests of ``w`` in turn with the oracle until
+    ``budget_s`` seconds of oracle time; returns (positions, seconds, calls)."""
     import oracle as O
     reps, t_total, positions = 0, 0.0, 0
-    groups = ([list(range(w.B))] if group is None else
-              [list(range(i, min(i + group, w.B))) for i in range(0, w.B, group)])
     while t_total < budget_s:
         reqs = groups[reps % len(groups)]
         t0 = time.perf_counter()
@@ -112,14 +126,68 @@ def cpu_baseline(w, budget_s, group=None):
         t_total += time.perf_counter() - t0
         positions += int(np.sum(w.draft_len[reqs]))
         reps += 1
+    return positions, t_total, reps
+
+
+def _oracle_worker(job):
+    """One process of the all-cores leg: rebuild the workload from its seed
+    (the drafted tokens are passed in when they came from the GPU sampler),
+    then time the oracle on this worker's share of the requests."""
+    wl, seed, tokens, groups, budget_s = job
+    from speculative_decoding_sampling_amd.workloads import make_workload
+    w = make_workload(wl, seed=seed,
+                      draft_sampler=(lambda z, T, k, p, x: 0) if tokens is not None else None)
+    if tokens is not None:
+        w.draft_tokens = tokens
+    t0 = time.perf_counter()
+    pos, secs, calls = _time_oracle(w, groups, budget_s)
+    return pos, secs, calls, time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s, group=None, tokens_from_gpu=False):
+    """Time the fp64 oracle on the same workload on this host's cores.
+
+    Single core: whole calls (or groups of ``group`` requests in turn where a
+    whole call is too long for the budget), pinned to one core.  All cores:
+    one spawned process per core (at most 16), each rebuilding the workload
+    from its seed and timing the oracle on its own share of the requests for
+    the same budget; the rate is all their positions over the longest
+    worker's timed span.  The all-cores figure is the reported value."""
+    groups = _oracle_groups(w.B, group)
+    allowed = os.sched_getaffinity(0)
+    try:
+        os.sched_setaffinity(0, {min(allowed)})
+        pos1, t1, reps1 = _time_oracle(w, groups, budget_s)
+    finally:
+        os.sched_setaffinity(0, allowed)
     if group is None:
-        what = f"{reps} whole calls of the same workload (B={w.B}, K={w.K}, V={w.V})"
+        what = f"whole calls of the same workload (B={w.B}, K={w.K}, V={w.V})"
     else:
-        what = (f"{reps} groups of {group} requests of the same workload (B={w.B}, K={w.K}, "
-                f"V={w.V})")
-    return {"value": positions / t_total, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}, {t_total:.1f} s of single-threaded numpy fp64",
-            "seconds_per_call": t_total / reps * (1 if group is None else w.B / group)}
+        what = f"groups of {group} requests of the same workload (B={w.B}, K={w.K}, V={w.V})"
+    single = {"value": pos1 / t1, "cores": 1,
+              "sample": f"{reps1} {what}, {t1:.1f} s of numpy fp64 pinned to one core",
+              "seconds_per_call": t1 / reps1 * (1 if group is None else w.B / group)}
+
+    ncores = max(1, min(16, len(allowed)))
+    import multiprocessing as mp
+    share = [[b for b in range(w.B) if b % ncores == i] for i in range(ncores)]
+    jobs = []
+    for i in range(ncores):
+        if not share[i]:
+            continue
+        sub = ([share[i]] if group is None else
+               [share[i][j:j + group] for j in range(0, len(share[i]), group)])
+        jobs.append((w.cfg, w.seed, w.draft_tokens if tokens_from_gpu else None, sub, budget_s))
+    with mp.get_context("spawn").Pool(len(jobs)) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    pos_all = sum(r[0] for r in res)
+    span = max(r[3] for r in res)
+    calls = sum(r[2] for r in res)
+    return {"value": pos_all / span, "unit": "positions/s", "cores": len(jobs), "kind": "oracle",
+            "sample": (f"{len(jobs)} processes, each verifying its share of the requests of the "
+                       f"same workload (B={w.B}, K={w.K}, V={w.V}) for {budget_s:.0f} s of numpy "
+                       f"fp64 ({calls} oracle calls in all, {span:.1f} s wall)"),
+            "single_core": single, "cpu_model": cpu_model()}
 
 
 def bench_sample(args):
@@ -186,7 +254,7 @@ def bench_rates(args):
     bf16, T=1): specv_acceptance_rates (the row statistics, then a second
     pass over each drafted row pair for sum_x min(p(x), q(x))), and on one
     verified round's outcome specv_round_stats and the device-resident
-    AcceptRateMonitor update.  Reported for reference next to the headline."""
+    DraftLengthMonitor update.  Reported for reference next to the headline."""
     import torch
     from speculative_decoding_sampling_amd import binding
     from speculative_decoding_sampling_amd.build import LIB
@@ -243,7 +311,7 @@ def bench_rates(args):
         r = binding.verify(**{k: v for k, v in st.items() if k != "beta"}, workspace=ws,
                            stream=stream)
         outs.append((st, r["out_tokens"], r["n_emitted"]))
-    mon = binding.AcceptRateMonitor(B, 16, 8, dev, stream=stream)
+    mon = binding.DraftLengthMonitor(B, 16, 8, dev, stream=stream)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
     rate = torch.empty(B, dtype=torch.float64, device=dev)
 
@@ -674,7 +742,8 @@ def main():
     if not args.no_cpu_baseline:
         log(f"timing the oracle for about {args.cpu_seconds:.0f} s")
         result["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds,
-                                              group=8 if wl == 4 else None)
+                                              group=8 if wl == 4 else None,
+                                              tokens_from_gpu=filtered)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -64,7 +64,7 @@ typedef enum {
 } specv_dtype_t;
 
 /* Largest draft length K the call accepts. */
-#define SPECV_MAX_K 63
+#define SPECV_MAX_K 64
 /* Largest vocabulary the call accepts (larger V returns SPECV_EUNSUPPORTED). */
 #define SPECV_MAX_V 4194304
 /* Largest top_k the filter path accepts (candidates per row are held on chip). */

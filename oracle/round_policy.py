@@ -8,9 +8,9 @@ Sources (page title and section):
 * [TB] tbxsx.cn, "推测解码采样验证优化策略 —— 深度调研报告", section
   "4. 实现逻辑": after each round the decode loop hands the round's accepted
   and drafted counts to an acceptance-rate monitor that keeps a window of
-  rounds, and ``_adjust_K`` moves the draft length K up by one (never above
-  the maximum draft length) when the monitored rate exceeds 0.85 and down by
-  one (never below 1) when it falls under 0.60.
+  rounds, and the draft length K moves up by one (never above the maximum
+  draft length) when the monitored rate exceeds 0.85 and down by one (never
+  below 1) when it falls under 0.60.
 * [NW] nickwang.xyz, "推测解码：草稿、验证与实际加速", section
   "好草稿也要算得便宜": E[N] = 1 + a + ... + a^gamma tokens per round when
   every position accepts independently with the same rate a; when the rate
@@ -35,7 +35,6 @@ Readings where the pages leave a step open:
   the window.
 """
 
-from collections import deque
 from fractions import Fraction
 
 import numpy as np
@@ -130,43 +129,53 @@ def expected_tokens_per_request(beta, draft_len):
     return out
 
 
-def adjust_k(rate, k, max_k):
-    """[TB] "4. 实现逻辑", _adjust_K: one step up above 0.85 (at most max_k),
-    one step down below 0.60 (at least 1); rate None keeps k.  The result is
-    kept in [1, max_k]."""
-    if rate is not None:
-        if rate > RAISE_ABOVE:
-            k = min(max_k, k + 1)
-        elif rate < LOWER_BELOW:
-            k = max(1, k - 1)
-    return min(max(k, 1), max_k)
+def next_draft_length(accepted, drafted, k, max_k):
+    """The draft length after a window holding ``accepted`` of ``drafted``
+    drafts ([TB] "4. 实现逻辑": one more when the rate is above 0.85, one
+    fewer when it is below 0.60).
+
+    The rate a/d is compared with 17/20 and 3/5 by cross-multiplying the
+    integers (20a > 17d raises, 5a < 3d lowers), so no rounding enters.  An
+    empty window (d = 0) leaves k as it is.  The result lies in [1, max_k].
+    """
+    a, d = int(accepted), int(drafted)
+    step = 0
+    if d > 0:
+        if RAISE_ABOVE.denominator * a > RAISE_ABOVE.numerator * d:
+            step = 1
+        elif LOWER_BELOW.denominator * a < LOWER_BELOW.numerator * d:
+            step = -1
+    return min(max(int(k) + step, 1), int(max_k))
 
 
-class AcceptRateMonitor:
-    """Acceptance rate over a request's last ``window`` rounds ([TB]
-    "4. 实现逻辑", AcceptRateMonitor(window) and its update call)."""
+class RateWindow:
+    """The (accepted, drafted) counts of a request's last ``window`` rounds;
+    the monitored rate is their ratio of sums ([TB] "4. 实现逻辑" keeps such a
+    window of rounds per sequence)."""
 
     def __init__(self, window):
         if window < 1:
             raise ValueError("window must be >= 1")
-        self.rounds = deque(maxlen=window)
+        self.window = int(window)
+        self.counts = []
 
-    def update(self, accepted_count, draft_count):
-        """Add one round; return the window's rate as a Fraction, or None
-        when the window holds no drafted position."""
-        self.rounds.append((int(accepted_count), int(draft_count)))
-        return self.rate()
+    def push(self, accepted, drafted):
+        """Record one round, dropping the oldest beyond the window."""
+        self.counts = (self.counts + [(int(accepted), int(drafted))])[-self.window:]
+
+    def totals(self):
+        return sum(c[0] for c in self.counts), sum(c[1] for c in self.counts)
 
     def rate(self):
-        a = sum(r[0] for r in self.rounds)
-        d = sum(r[1] for r in self.rounds)
+        """The window's rate as a Fraction, or None with no drafted position."""
+        a, d = self.totals()
         return Fraction(a, d) if d > 0 else None
 
 
 def monitor_round(monitors, draft_tokens, draft_len, out_tokens, n_emitted, max_k):
-    """One batched round of the adaptive draft length: each request's monitor
+    """One batched round of the adaptive draft length: each request's window
     takes its round (failed rounds add nothing), then the next draft_len is
-    _adjust_K of the request's draft_len under the window's rate.
+    next_draft_length of the request's draft_len under the window's counts.
 
     Returns (next_draft_len [B] int, rate [B] float64 with -1 where it is
     undefined).
@@ -177,9 +186,9 @@ def monitor_round(monitors, draft_tokens, draft_len, out_tokens, n_emitted, max_
     rate = np.full(B, -1.0)
     for b in range(B):
         if acc[b] >= 0:
-            monitors[b].update(acc[b], draft_len[b])
+            monitors[b].push(acc[b], draft_len[b])
         r = monitors[b].rate()
         if r is not None:
             rate[b] = float(r)                 # correctly rounded to float64
-        nxt[b] = adjust_k(r, int(draft_len[b]), max_k)
+        nxt[b] = next_draft_length(*monitors[b].totals(), int(draft_len[b]), max_k)
     return nxt, rate

@@ -4,13 +4,13 @@ The HIP library (``libspecverify.so``, C ABI in ``include/specverify.h``) does
 all of the work; ``binding`` marshals torch tensors into it: ``verify`` (one
 verification step), ``sample`` (draws from processed distributions, e.g. the
 draft model's), ``acceptance_rates`` (per-position sum_x min(p, q)),
-``round_stats`` and ``AcceptRateMonitor`` (round statistics and the adaptive
+``round_stats`` and ``DraftLengthMonitor`` (round statistics and the adaptive
 draft length, on the device).
 """
 
 from .binding import (  # noqa: F401
     TOTAL_FIELDS,
-    AcceptRateMonitor,
+    DraftLengthMonitor,
     acceptance_rates,
     round_stats,
     sample,

@@ -17,7 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecver
 
 SPECV_F32, SPECV_BF16 = 0, 1
 SPECV_OK, SPECV_EINVAL, SPECV_EWORKSPACE, SPECV_EHIP, SPECV_EUNSUPPORTED = 0, 1, 2, 3, 4
-MAX_K = 63
+MAX_K = 64
 MAX_WINDOW = 4096
 TOTAL_FIELDS = ("requests", "errors", "drafted", "accepted", "emitted", "eos_stops",
                 "full_accepts", "rejections")
@@ -241,7 +241,7 @@ def round_stats(draft_tokens, draft_len, out_tokens, n_emitted, beta=None, *, ac
     return accepted, expected, totals
 
 
-class AcceptRateMonitor:
+class DraftLengthMonitor:
     """Per-request acceptance-rate windows and the adaptive draft length, held
     in device memory (``specv_monitor_*``).  ``update`` takes one verified
     round and returns the next round's draft lengths, without a host sync."""

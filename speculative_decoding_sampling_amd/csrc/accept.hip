@@ -1,4 +1,5 @@
-// Accept scan kernel: one wave64 per request, lane k owns draft position k.
+// Accept scan kernel: one wave64 per request, lane k owns draft position k
+// (K <= 64; target row 64, the bonus row of 64 drafts, is read by every lane).
 // The decision itself is accept_scan (accept_core.h); this kernel gathers
 // its inputs.  Without filters the row statistics are the chunk partials of
 // the row-statistics pass and the logits at the drafted tokens are the ones
@@ -44,10 +45,15 @@ __global__ __launch_bounds__(kWave) void accept_kernel(
     }
     if (lane <= K) rs.ft = frows[(size_t)b * R + lane];
     if (lane < K) rs.fd = frows[(size_t)b * R + K + 1 + lane];
+    if (K == kWave) rs.fk = frows[(size_t)b * R + K];       // uniform: the bonus row of 64 drafts
   } else {
     const float2* prow = part + (size_t)b * R * nch_row;
     combine_rows(prow + (size_t)lane * nch_row, prow + (size_t)(K + 1 + lane) * nch_row, nch_row,
                  c, lane <= K, lane < K, rs.Mt, rs.St, rs.Md, rs.Sd);
+    if (K == kWave) {                                        // uniform: the bonus row of 64 drafts
+      float md, sd;
+      combine_rows(prow + (size_t)K * nch_row, prow, nch_row, c, true, false, rs.Mk, rs.Sk, md, sd);
+    }
   }
   accept_scan<FILT>(b, lane, K, c, invT, eos_id, nb_raw, uf, x, uk, xin, zt, zd, rs, out);
 }

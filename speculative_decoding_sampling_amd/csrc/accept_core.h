@@ -68,10 +68,14 @@ __device__ __forceinline__ double filt_prob(float z, const FiltRow& fr, double i
 
 // Statistics of lane k's rows: target row k (lane <= K) and draft row k
 // (lane < K).  Unfiltered rows carry the combined float32 (max, normaliser),
-// filtered rows their FiltRow.
+// filtered rows their FiltRow.  With K = 64 target row 64 (the bonus row of
+// a request that drafted 64 tokens) has no lane of its own: every lane then
+// also holds its statistics in Mk, Sk / fk.
 struct LaneRows {
   float Mt = -INFINITY, St = 0.f, Md = -INFINITY, Sd = 0.f;
   FiltRow ft, fd;
+  float Mk = -INFINITY, Sk = 0.f;
+  FiltRow fk;
 };
 
 // Outputs of the scan; pointers may be null where the caller wants none.
@@ -101,6 +105,10 @@ __device__ __forceinline__ void accept_scan(int b, int lane, int K, float c, dou
   if (!bad && lane <= nb) {                                  // target row usable
     if constexpr (FILT) ok = rs.ft.status == 0;
     else ok = rs.Mt != -INFINITY;
+  }
+  if (!bad && nb == kWave) {                                 // the bonus row past the lanes
+    if constexpr (FILT) bad = rs.fk.status != 0;
+    else bad = rs.Mk == -INFINITY;
   }
   if (!bad && lane < nb) {
     if constexpr (FILT) ok = ok && rs.fd.status == 0;
@@ -152,15 +160,18 @@ __device__ __forceinline__ void accept_scan(int b, int lane, int K, float c, dou
 
   if (lane <= K)
     out.out_tokens[row + lane] = (lane < stop || (lane == stop && path == kPathEos)) ? x : -1;
+  if (K == kWave && lane == 0) out.out_tokens[row + K] = -1;   // the draw fills it if stop = 64
   if (out.alpha_out && lane < K)
     out.alpha_out[(size_t)b * K + lane] = lane < nb ? (float)alpha : -1.f;
-  if (lane == stop) {
+  // the lane at the stop position writes the plan; a stop at 64 (every one
+  // of 64 drafts accepted) is written by lane 0 from the bonus row's Mk
+  if (lane == (stop < kWave ? stop : 0)) {
     Plan pl;
     pl.path = path;
     pl.stop = stop;
     pl.trow = stop;
     pl.drow = path == kPathReject ? stop : -1;
-    pl.mt = FILT ? 0.f : rs.Mt;
+    pl.mt = FILT ? 0.f : (stop < kWave ? rs.Mt : rs.Mk);
     pl.md = FILT ? 0.f : rs.Md;
     pl.pad0 = pl.pad1 = 0;
     // S_t / S_d in natural-exp units: each base-2 normaliser is relative to

@@ -172,20 +172,36 @@ def _custom_workload(t, d, draft_len, rng, dtype="f32", T=1.0, seed=0):
 
 
 def test_maximum_draft_length():
-    # K = 63, the largest draft length the call takes (SPECV_MAX_K): drafts
+    # K = 64, the largest draft length the call takes (SPECV_MAX_K): drafts
     # close to the target so the first-rejection scan runs deep, one request
     # whose draft rows equal its target rows (every draft accepted, then the
-    # bonus draw from target row 63), and ragged lengths from 0 to 63
-    rng = np.random.default_rng(63)
-    B, K, V = 6, 63, 1500
+    # bonus draw from target row 64, which has no scan lane of its own), and
+    # ragged lengths from 0 to 64
+    rng = np.random.default_rng(64)
+    B, K, V = 6, 64, 1500
     t = rng.normal(0, 2, size=(B, K + 1, V)).astype(np.float32)
     d = (t[:, :K] + rng.normal(0, 0.03, size=(B, K, V))).astype(np.float32)
     d[1] = t[1, :K]
-    w = _custom_workload(t, d, [63, 63, 40, 0, 63, 17], rng, seed=63)
-    rep, g, o = assert_parity(w, label="K=63")
-    assert o["path"][1] == O.PATH_BONUS and o["n_emitted"][1] == 64
+    w = _custom_workload(t, d, [64, 64, 40, 0, 63, 17], rng, seed=64)
+    rep, g, o = assert_parity(w, label="K=64")
+    assert o["path"][1] == O.PATH_BONUS and o["n_emitted"][1] == 65
     # a rejection in the upper half of the 64-lane scan
     assert any(o["path"][b] == O.PATH_REJECT and o["stop_pos"][b] >= 32 for b in range(B))
+
+
+def test_maximum_draft_length_filtered():
+    # K = 64 on the top-k / top-p path: the scan reads the bonus row's
+    # filtered statistics apart from the 64 lanes' rows.
+    rng = np.random.default_rng(65)
+    B, K, V = 4, 64, 3000
+    t = rng.normal(0, 2, size=(B, K + 1, V)).astype(np.float32)
+    d = (t[:, :K] + rng.normal(0, 0.02, size=(B, K, V))).astype(np.float32)
+    d[0] = t[0, :K]
+    w = _custom_workload(t, d, [64, 64, 31, 64], rng, seed=65)
+    w.top_k, w.top_p = 30, f32(0.9)
+    redraw_tokens(w, 65)
+    rep, g, o = assert_parity(w, label="K=64 filtered")
+    assert o["path"][0] == O.PATH_BONUS and o["n_emitted"][0] == 65
 
 
 def test_maximum_vocabulary():

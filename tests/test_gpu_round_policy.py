@@ -102,8 +102,8 @@ def test_expected_tokens_from_rates():
                                                         (5, 4, 1, 20, 3), (17, 6, 4096, 12, 4)])
 def test_monitor_sequence(B, max_k, window, rounds, seed):
     K = max_k
-    mons = [RP.AcceptRateMonitor(window) for _ in range(B)]
-    gm = binding.AcceptRateMonitor(B, window, max_k, DEV)
+    mons = [RP.RateWindow(window) for _ in range(B)]
+    gm = binding.DraftLengthMonitor(B, window, max_k, DEV)
     rng = np.random.default_rng(seed)
     dl = rng.integers(1, max_k + 1, size=B).astype(np.int32)
     changes = 0
@@ -126,13 +126,13 @@ def test_monitor_sequence(B, max_k, window, rounds, seed):
 
 def test_monitor_in_place_and_reset():
     B, K, W = 33, 8, 3
-    mons = [RP.AcceptRateMonitor(W) for _ in range(B)]
-    gm = binding.AcceptRateMonitor(B, W, K, DEV)
+    mons = [RP.RateWindow(W) for _ in range(B)]
+    gm = binding.DraftLengthMonitor(B, W, K, DEV)
     dl = np.full(B, 4, dtype=np.int32)
     for r in range(4):
         if r == 3:                                  # a reset empties every window
             gm.reset()
-            mons = [RP.AcceptRateMonitor(W) for _ in range(B)]
+            mons = [RP.RateWindow(W) for _ in range(B)]
         toks, dl_r, out, n = make_round_outcomes(B, K, 77 + r, draft_len=dl)
         nxt_o, rate_o = RP.monitor_round(mons, toks, dl_r, out, n, K)
         dl_dev = dev(dl_r)
@@ -161,7 +161,7 @@ def test_device_resident_decode_loop():
     u_draft = [(rng.integers(0, 1 << 24, size=(B, K)) * 2.0 ** -24).astype(np.float32)
                for _ in range(rounds)]
     # GPU chain
-    gm = binding.AcceptRateMonitor(B, W, K, DEV)
+    gm = binding.DraftLengthMonitor(B, W, K, DEV)
     dl_dev = dev(np.full(B, 2, dtype=np.int32))
     gpu_out = []
     for r, w in enumerate(ws):
@@ -174,7 +174,7 @@ def test_device_resident_decode_loop():
         gpu_out.append((toks, res["out_tokens"], res["n_emitted"], dl_dev.clone()))
     torch.cuda.synchronize()
     # Oracle chain
-    mons = [RP.AcceptRateMonitor(W) for _ in range(B)]
+    mons = [RP.RateWindow(W) for _ in range(B)]
     dl = np.full(B, 2, dtype=np.int32)
     for r, w in enumerate(ws):
         toks = oracle_sample(w.draft.reshape(B * K, V), u_draft[r].reshape(-1), w.T,

@@ -68,7 +68,8 @@ def test_workspace_sizes(lib):
     assert f(64, 4, 128256, 1, 0, 1.0) == n3                      # pure function of sizes
     assert f(128, 4, 128256, 1, 0, 1.0) > n3
     assert f(0, 4, 100, 0, 0, 1.0) == 0                           # B < 1
-    assert f(1, 64, 100, 0, 0, 1.0) == 0                          # K > SPECV_MAX_K
+    assert f(1, 65, 100, 0, 0, 1.0) == 0                          # K > SPECV_MAX_K
+    assert f(1, 64, 100, 0, 0, 1.0) > 0                           # K = SPECV_MAX_K
     assert f(1, 4, 0, 0, 0, 1.0) == 0                             # V < 1
     assert f(1, 4, 100, 7, 0, 1.0) == 0                           # unknown dtype
     assert f(1, 4, 100, 0, 0, 0.0) == 0                           # top_p out of range
@@ -95,7 +96,7 @@ def test_validation_returns_before_any_gpu_work(lib):
         return v(*args)
 
     assert call(B=0) == 1
-    assert call(K=64) == 1
+    assert call(K=65) == 1
     assert call(V=0) == 1
     assert call(T=0.0) == 1
     assert call(T=float("nan")) == 1
@@ -214,7 +215,7 @@ def test_round_stats_reject_bad_arguments(lib):
                  a["exp"], a["tot"], None)
 
     assert call(B=0) == 1
-    assert call(K=64) == 1 and call(K=-1) == 1
+    assert call(K=65) == 1 and call(K=-1) == 1
     assert call(dt=None) == 1
     assert call(out=None) == 1 and call(n=None) == 1 and call(dl=None) == 1
     assert call(exp=16) == 1                         # expected tokens need beta
@@ -245,8 +246,8 @@ def test_monitor_sizes_and_bad_arguments(lib):
         return f(a["dt"], a["dl"], a["out"], a["n"], a["B"], a["K"], a["mk"], a["W"], a["st"],
                  a["nxt"], a["rate"], None)
 
-    assert call(B=0) == 1 and call(K=64) == 1
-    assert call(mk=0) == 1 and call(mk=64) == 1
+    assert call(B=0) == 1 and call(K=65) == 1
+    assert call(mk=0) == 1 and call(mk=65) == 1
     assert call(W=0) == 1 and call(W=4097) == 1
     assert call(st=None) == 1 and call(nxt=None) == 1 and call(dt=None) == 1
     assert call(st=20) == 1 and call(rate=20) == 1
@@ -267,7 +268,7 @@ def test_lm_head_workspace_sizes(lib):
     assert f(64, 4, 128256, 100) == 0                             # D not a multiple of 64
     assert f(64, 4, 128256, 0) == 0
     assert f(64, 4, 128256, 65536 + 64) == 0                      # above SPECV_MAX_D
-    assert f(0, 4, 100, 64) == 0 and f(1, 64, 100, 64) == 0 and f(1, 4, 0, 64) == 0
+    assert f(0, 4, 100, 64) == 0 and f(1, 65, 100, 64) == 0 and f(1, 4, 0, 64) == 0
 
 
 def test_lm_head_packed_weight_sizes_and_validation(lib):
@@ -316,7 +317,7 @@ def test_lm_head_validation_returns_before_any_gpu_work(lib):
     assert call(D=100) == 1
     assert call(D=0) == 1
     assert call(B=0) == 1
-    assert call(K=64) == 1
+    assert call(K=65) == 1
     assert call(T=0.0) == 1
     assert call(eos=1000) == 1
     assert call(hidden=None) == 1

@@ -157,15 +157,15 @@ def test_rational_thresholds_match_the_printed_rule():
     for d in range(1, 513):
         for a in range(d + 1):
             for k, mk in ((1, 8), (4, 8), (8, 8)):
-                assert RP.adjust_k(F(a, d), k, mk) == _page_rule(a / d, k, mk), (a, d, k)
+                assert RP.next_draft_length(a, d, k, mk) == _page_rule(a / d, k, mk), (a, d, k)
 
 
 def test_thresholds_at_and_around_the_edges():
-    assert RP.adjust_k(F(17, 20), 4, 8) == 4 and RP.adjust_k(F(3, 5), 4, 8) == 4
-    assert RP.adjust_k(F(18, 20), 4, 8) == 5 and RP.adjust_k(F(11, 20), 4, 8) == 3
-    assert RP.adjust_k(F(1), 8, 8) == 8 and RP.adjust_k(F(0), 1, 8) == 1
-    assert RP.adjust_k(None, 5, 8) == 5
-    assert RP.adjust_k(None, 0, 8) == 1 and RP.adjust_k(None, 12, 8) == 8
+    assert RP.next_draft_length(17, 20, 4, 8) == 4 and RP.next_draft_length(3, 5, 4, 8) == 4
+    assert RP.next_draft_length(18, 20, 4, 8) == 5 and RP.next_draft_length(11, 20, 4, 8) == 3
+    assert RP.next_draft_length(1, 1, 8, 8) == 8 and RP.next_draft_length(0, 1, 1, 8) == 1
+    assert RP.next_draft_length(0, 0, 5, 8) == 5
+    assert RP.next_draft_length(0, 0, 0, 8) == 1 and RP.next_draft_length(0, 0, 12, 8) == 8
 
 
 def test_monitor_hand_worked_sequence():
@@ -173,32 +173,34 @@ def test_monitor_hand_worked_sequence():
     rounds = [(4, 4), (2, 5), (0, 5), (4, 4), (3, 3), (2, 2)]
     want_rate = [F(4, 4), F(6, 9), F(6, 14), F(6, 14), F(7, 12), F(9, 9)]
     want_k = [5, 5, 4, 3, 2, 3]
-    m, k = RP.AcceptRateMonitor(3), 4
+    m, k = RP.RateWindow(3), 4
     for (a, d), wr, wk in zip(rounds, want_rate, want_k):
-        r = m.update(a, d)
-        k = RP.adjust_k(r, k, 6)
-        assert r == wr and k == wk
+        m.push(a, d)
+        k = RP.next_draft_length(*m.totals(), k, 6)
+        assert m.rate() == wr and k == wk
 
 
 def test_monitor_is_a_ratio_of_sums():
     # (1 of 1) then (2 of 5): 3/6 lowers K; the mean of the two ratios (0.7)
     # would keep it.
-    m = RP.AcceptRateMonitor(2)
-    m.update(1, 1)
-    assert m.update(2, 5) == F(1, 2)
-    assert RP.adjust_k(m.rate(), 4, 8) == 3
+    m = RP.RateWindow(2)
+    m.push(1, 1)
+    m.push(2, 5)
+    assert m.rate() == F(1, 2)
+    assert RP.next_draft_length(*m.totals(), 4, 8) == 3
 
 
 def test_monitor_window_brute_force():
     rng = np.random.default_rng(9)
     for W in (1, 2, 5, 16):
-        m = RP.AcceptRateMonitor(W)
+        m = RP.RateWindow(W)
         hist = []
         for _ in range(60):
             d = int(rng.integers(0, 9))
             a = int(rng.integers(0, d + 1))
             hist.append((a, d))
-            r = m.update(a, d)
+            m.push(a, d)
+            r = m.rate()
             last = hist[-W:]
             sd = sum(x[1] for x in last)
             assert r == (F(sum(x[0] for x in last), sd) if sd else None)
@@ -207,14 +209,14 @@ def test_monitor_window_brute_force():
 def test_monitor_round_batch():
     # Requests keep separate windows; a failed round adds nothing and keeps K
     # (clamped to [1, max_k]).
-    mons = [RP.AcceptRateMonitor(2) for _ in range(3)]
+    mons = [RP.RateWindow(2) for _ in range(3)]
     toks = np.array([[1, 2, 3]] * 3)
     # request 0 accepts everything, 1 rejects at 0, 2 fails
     out = np.array([[1, 2, 3, 7], [5, -1, -1, -1], [-1, -1, -1, -1]])
     nxt, rate = RP.monitor_round(mons, toks, np.array([3, 3, 3]), out, np.array([4, 1, -1]),
                                  max_k=4)
     assert list(nxt) == [4, 2, 3] and list(rate) == [1.0, 0.0, -1.0]
-    assert len(mons[2].rounds) == 0
+    assert len(mons[2].counts) == 0
     out2 = np.array([[1, 2, 3, 7], [1, 2, 8, -1], [1, 9, -1, -1]])
     nxt, rate = RP.monitor_round(mons, toks, np.array([3, 2, 3]), out2,
                                  np.array([4, 3, 2]), max_k=4)
@@ -233,15 +235,19 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 MUTANTS = {
     "eos_stop_not_counted": ("        return n\n    return n - 1", "        return n - 1\n    return n - 1"),
     "correction_counted": ("    return n - 1\n\n\ndef round_stats", "    return n\n\n\ndef round_stats"),
-    "raise_not_strict": ("if rate > RAISE_ABOVE:", "if rate >= RAISE_ABOVE:"),
-    "lower_not_strict": ("elif rate < LOWER_BELOW:", "elif rate <= LOWER_BELOW:"),
+    "raise_not_strict": ("RAISE_ABOVE.denominator * a > RAISE_ABOVE.numerator * d",
+                         "RAISE_ABOVE.denominator * a >= RAISE_ABOVE.numerator * d"),
+    "lower_not_strict": ("LOWER_BELOW.denominator * a < LOWER_BELOW.numerator * d",
+                         "LOWER_BELOW.denominator * a <= LOWER_BELOW.numerator * d"),
     "thresholds_swapped": ("RAISE_ABOVE = Fraction(17, 20)", "RAISE_ABOVE = Fraction(3, 5)"),
-    "window_off_by_one": ("deque(maxlen=window)", "deque(maxlen=window + 1)"),
+    "window_off_by_one": ("[-self.window:]", "[-(self.window + 1):]"),
     "mean_of_ratios": ("return Fraction(a, d) if d > 0 else None",
-                       "return (sum(Fraction(x, y) for x, y in self.rounds if y) / "
-                       "sum(1 for _, y in self.rounds if y)) if d > 0 else None"),
-    "failed_round_counted": ("        if acc[b] >= 0:\n            monitors[b].update",
-                             "        if True:\n            monitors[b].update"),
+                       "return (sum(Fraction(x, y) for x, y in self.counts if y) / "
+                       "sum(1 for _, y in self.counts if y)) if d > 0 else None"),
+    "last_round_only": ("return sum(c[0] for c in self.counts), sum(c[1] for c in self.counts)",
+                        "return self.counts[-1] if self.counts else (0, 0)"),
+    "failed_round_counted": ("        if acc[b] >= 0:\n            monitors[b].push",
+                             "        if True:\n            monitors[b].push"),
     "expected_off_by_one": ("        run *= float(beta)\n        total += run",
                             "        total += run\n        run *= float(beta)"),
 }
