@@ -630,7 +630,7 @@ def main():
     log(f"single calls: median {med:.2f} us, p10 {p10:.2f}, p90 {p90:.2f}")
 
     # Per-kernel durations: the same steps through the timing entry point.
-    names = binding.stage_names(filtered)
+    names = binding.stage_names(binding.path_kind(w0.V, w0.top_k, w0.top_p))
     nst = len(names)
     evs = [HipEvents(nst + 1) for _ in range(args.steps)]
     torch.cuda.synchronize()

@@ -67,8 +67,6 @@ typedef enum {
 #define SPECV_MAX_K 64
 /* Largest vocabulary the call accepts (larger V returns SPECV_EUNSUPPORTED). */
 #define SPECV_MAX_V 4194304
-/* Largest top_k the filter path accepts (candidates per row are held on chip). */
-#define SPECV_MAX_TOPK 128
 /* Largest hidden size the fused LM-head call accepts. */
 #define SPECV_MAX_D 65536
 
@@ -98,15 +96,14 @@ SPECV_API size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype,
  *  top_p          1 = off; otherwise in (0, 1): keep the shortest prefix of
  *                 the top-k renormalised distribution, by logit descending,
  *                 whose mass reaches top_p (crossing token and its ties kept).
- *                 Filters are supported (else SPECV_EUNSUPPORTED) when
- *                 0 < top_k <= SPECV_MAX_TOPK, top_k < V, V <= 262144 and the
- *                 row's candidate slots fit on chip: (ceil(V / 8192) - 1) * c
- *                 + max(c, 256) <= 4096 with c = 8 * ceil((1.5 * top_k + 40) / 8)
- *                 (top_k = 50 at V = 152064 uses 2416).  top_p < 1 without an active top-k is
- *                 not supported.  A request whose filtered row keeps more than
- *                 512 tokens, or whose 8192-token chunk holds more candidates
- *                 than its slot (massive ties), is reported as a per-request
- *                 error (n_emitted = -1, debug path -1).
+ *                 Every combination is supported, for any kept-set size.  A
+ *                 small active top-k (0 < top_k <= 128 whose per-chunk
+ *                 candidate slots fit on chip: (ceil(V / 8192) - 1) * c
+ *                 + max(c, 256) <= 4096 with c = 8 * ceil((1.5 * top_k + 40) / 8);
+ *                 top_k = 50 at V = 152064 uses 2416) takes a candidate
+ *                 select; every other setting (top-p alone, larger top_k) a
+ *                 radix select that reads each needed row once per key digit
+ *                 (specv_path_kind tells which).
  *  eos_id         -1 = off; else in [0, V): the round stops right after the
  *                 first emitted EOS (accepted draft or drawn token).
  *  out_tokens     [B][K+1] int32 output: emitted tokens, -1 beyond n_emitted.
@@ -356,11 +353,11 @@ SPECV_API specv_status_t specv_verify_lm_head(const void *hidden, const void *pa
 /*
  * Timing variant of specv_verify, for benchmarks: identical work, plus
  * hipEventRecord on `stream` of events[0] before the first kernel launch and
- * of events[i+1] after kernel stage i.  `events` holds specv_num_stages(f) + 1
- * caller-created HIP events, f being whether this call's top-k / top-p is
- * active (SPECV_EINVAL if NULL or any of those entries is NULL); the caller
- * reads stage durations with hipEventElapsedTime after synchronising.  The
- * stages differ with and without filters (specv_stage_name).
+ * of events[i+1] after kernel stage i.  `events` holds specv_num_stages(p) + 1
+ * caller-created HIP events, p = specv_path_kind(V, top_k, top_p) (SPECV_EINVAL
+ * if NULL or any of those entries is NULL); the caller reads stage durations
+ * with hipEventElapsedTime after synchronising.  The stages differ by path
+ * (specv_stage_name).
  */
 SPECV_API specv_status_t specv_verify_timed(const void *target_logits, const void *draft_logits,
                                             specv_dtype_t dtype, const int32_t *draft_tokens,
@@ -371,11 +368,14 @@ SPECV_API specv_status_t specv_verify_timed(const void *target_logits, const voi
                                             void *workspace, size_t workspace_bytes,
                                             hipStream_t stream, hipEvent_t *events);
 
-/* Number of kernel stages one call launches, and the static name of stage i
- * (NULL when out of range); `filtered` is nonzero for calls with top-k /
- * top-p active. */
-SPECV_API int specv_num_stages(int filtered);
-SPECV_API const char *specv_stage_name(int filtered, int i);
+/* Which kernel path a call with these settings takes: 0 without filters
+ * (row statistics, accept scan, float64 sampler), 1 top-k / top-p through the
+ * candidate select, 2 top-k / top-p through the radix select. */
+SPECV_API int specv_path_kind(int V, int top_k, float top_p);
+/* Number of kernel stages a call on path `kind` launches (0 for an unknown
+ * kind), and the static name of stage i (NULL when out of range). */
+SPECV_API int specv_num_stages(int kind);
+SPECV_API const char *specv_stage_name(int kind, int i);
 
 /* Static, human-readable name of a status code. */
 SPECV_API const char *specv_status_string(specv_status_t status);

@@ -76,6 +76,8 @@ def load_library():
         lib.specv_monitor_update.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                              c_vp, c_vp, c_vp, c_vp]
         lib.specv_monitor_update.restype = c_int
+        lib.specv_path_kind.argtypes = [c_int, c_int, ctypes.c_float]
+        lib.specv_path_kind.restype = c_int
         lib.specv_num_stages.argtypes = [c_int]
         lib.specv_num_stages.restype = c_int
         lib.specv_stage_name.argtypes = [c_int, c_int]
@@ -111,11 +113,15 @@ def status_string(status):
     return load_library().specv_status_string(int(status)).decode()
 
 
-def stage_names(filtered=False):
-    """Names of the kernel stages one call launches, in order."""
+def path_kind(V, top_k=0, top_p=1.0):
+    """0: no filters; 1: top-k / top-p by the candidate select; 2: by the radix select."""
+    return int(load_library().specv_path_kind(int(V), int(top_k), float(top_p)))
+
+
+def stage_names(kind=0):
+    """Names of the kernel stages a call on path ``kind`` (see path_kind) launches, in order."""
     lib = load_library()
-    f = 1 if filtered else 0
-    return [lib.specv_stage_name(f, i).decode() for i in range(lib.specv_num_stages(f))]
+    return [lib.specv_stage_name(int(kind), i).decode() for i in range(lib.specv_num_stages(int(kind)))]
 
 
 def selftest_exp64(x):

@@ -170,6 +170,20 @@ __device__ __forceinline__ uint4 load_raw_checked(const T* __restrict__ row, lon
   }
 }
 
+// Order-preserving 32-bit key of a float (larger float -> larger key): the
+// sign bit set for a positive float, every bit flipped for a negative one.
+// Written as one XOR with a sign-derived mask, no select, so a key costs one
+// register where it is kept.  -0 is first made +0 (adding +0 does that), so
+// that keys compare exactly as the floats do.
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float unkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+constexpr uint32_t kNegInfKey = 0x007fffffu;   // fkey(-inf)
+
 __device__ __forceinline__ bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 }

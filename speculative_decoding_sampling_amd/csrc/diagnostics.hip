@@ -148,11 +148,13 @@ __global__ void beta_finish_kernel(const int* __restrict__ draft_len, int B, int
 
 // Filtered path: one workgroup per (request, position); p is zero off the
 // target row's kept list, so beta = sum over that list of min(p, q), q read
-// from the draft row at the same id (zero unless kept there).
+// from the draft row at the same id (zero unless kept there).  A target row
+// whose kept set has no list (more than kKeptCap tokens) is streamed whole.
 template <typename T>
 __global__ __launch_bounds__(kFiltThreads) void beta_list_kernel(
-    const T* __restrict__ dft, const int* __restrict__ draft_len, int K, int V, double invT,
-    const FiltRow* __restrict__ rows, const Kept* __restrict__ kept, float* __restrict__ beta) {
+    const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
+    int K, int V, double invT, const FiltRow* __restrict__ rows, const Kept* __restrict__ kept,
+    float* __restrict__ beta) {
   __shared__ double tbl[SPECV_EXP64_N];
   __shared__ double red[kFiltThreads / kWave];
   const int bk = blockIdx.x;
@@ -173,14 +175,27 @@ __global__ __launch_bounds__(kFiltThreads) void beta_list_kernel(
   }
   const Kept* list = kept + ((size_t)b * R + k) * kKeptCap;
   const T* drow = dft + draft_row_off(b, k, K, V);
+  auto q_at = [&](float zd) -> double {
+    if (!(zd >= dr.tau) || zd == -INFINITY) return 0.0;
+    return exp64(((double)zd - (double)dr.m) * invT, tbl) / dr.S;
+  };
   double s = 0.0;
-  for (int i = threadIdx.x; i < tr.count; i += kFiltThreads) {
-    const Kept e = list[i];
-    const double p = exp64(((double)e.z - (double)tr.m) * invT, tbl) / tr.S;
-    const float zd = to_f32(drow[e.id]);
-    double q = 0.0;
-    if (zd >= dr.tau && zd > -INFINITY) q = exp64(((double)zd - (double)dr.m) * invT, tbl) / dr.S;
-    s += p < q ? p : q;
+  if (tr.count <= kKeptCap) {
+    for (int i = threadIdx.x; i < tr.count; i += kFiltThreads) {
+      const Kept e = list[i];
+      const double p = exp64(((double)e.z - (double)tr.m) * invT, tbl) / tr.S;
+      const double q = q_at(to_f32(drow[e.id]));
+      s += p < q ? p : q;
+    }
+  } else {
+    const T* trow = tgt + target_row_off(b, k, K, V);
+    for (long e = threadIdx.x; e < V; e += kFiltThreads) {
+      const float zt = to_f32(trow[e]);
+      if (!(zt >= tr.tau) || zt == -INFINITY) continue;
+      const double p = exp64(((double)zt - (double)tr.m) * invT, tbl) / tr.S;
+      const double q = q_at(to_f32(drow[e]));
+      s += p < q ? p : q;
+    }
   }
   s = wave_sum(s);
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
@@ -203,10 +218,12 @@ hipError_t launch_beta(bool bf16, bool filt, const void* tgt, const void* dft,
     const size_t blocks = (size_t)B * K;
     if (bf16)
       beta_list_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
-          static_cast<const bf16_t*>(dft), draft_len, K, V, invT, frows, kept, beta);
+          static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V, invT,
+          frows, kept, beta);
     else
       beta_list_kernel<float><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
-          static_cast<const float*>(dft), draft_len, K, V, invT, frows, kept, beta);
+          static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, invT,
+          frows, kept, beta);
     return hipGetLastError();
   }
   const size_t blocks = (size_t)B * K * nch_row;

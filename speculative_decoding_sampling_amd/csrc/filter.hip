@@ -26,21 +26,10 @@
 
 #include "common.h"
 #include "exp64.h"
+#include "radix_select.h"
 
 namespace specv {
 
-// Order-preserving 32-bit key of a float (larger float -> larger key): the
-// sign bit set for a positive float, every bit flipped for a negative one.
-// Written as one XOR with a sign-derived mask, no select, so a key costs one
-// register where it is kept.
-__device__ __forceinline__ uint32_t fkey(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-__device__ __forceinline__ float unkey(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-constexpr uint32_t kNegInfKey = 0x007fffffu;   // fkey(-inf)
 static_assert(kFiltSortMax % kFiltThreads == 0, "the merge gather gives each thread whole steps");
 static_assert(kFiltMaxChunks <= kWave, "one wave scans a row's chunk counts");
 constexpr int kRadixBins = 2048;               // the merge's radix select: 11-bit digits
@@ -337,18 +326,28 @@ __device__ __forceinline__ void lds_bitonic_desc(uint64_t* a, int n) {
   __syncthreads();
 }
 
+// The candidate list and the radix histogram share their LDS with the
+// general select, which a row runs instead when a chunk had more candidates
+// than its slot (massive ties at a chunk's threshold).
+constexpr size_t kMergeListBytes = kFiltSortMax * sizeof(uint64_t) + kRadixBins * sizeof(int);
+constexpr size_t kMergePoolBytes =
+    sizeof(SelectLds) > kMergeListBytes ? sizeof(SelectLds) : kMergeListBytes;
+
+template <typename T>
 __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
-    const int* __restrict__ draft_len, int K, int nch, int cap, int row_stride, int top_k,
-    float top_p, double invT, const uint64_t* __restrict__ cand, const int* __restrict__ counts,
+    const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
+    int K, int V, int nch, int cap, int row_stride, int top_k, float top_p, double invT,
+    const uint64_t* __restrict__ cand, const int* __restrict__ counts,
     FiltRow* __restrict__ rows, Kept* __restrict__ kept) {
-  __shared__ uint64_t keys[kFiltSortMax];
+  __shared__ __align__(16) unsigned char pool[kMergePoolBytes];
   __shared__ double tbl[SPECV_EXP64_N];
   __shared__ double dl[kFiltThreads / kWave];
   __shared__ int il[kFiltThreads / kWave];
   __shared__ int s_off[kFiltMaxChunks + 1];
   __shared__ int s_status;
   __shared__ int s_digit, s_need;
-  __shared__ int hist[kRadixBins];
+  uint64_t* const keys = reinterpret_cast<uint64_t*>(pool);
+  int* const hist = reinterpret_cast<int*>(pool + kFiltSortMax * sizeof(uint64_t));
   const int R = 2 * K + 1;
   const int rr = blockIdx.x;
   const int r = rr % R, b = rr / R;
@@ -384,6 +383,14 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
     }
   }
   __syncthreads();
+  if (s_status != 0) {                               // uniform: a chunk overflowed its slot
+    const T* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
+    const FiltRow o = select_row<T, kFiltThreads>(row, V, sizeof(T) == 2, top_k, top_p, invT, tbl,
+                                                  reinterpret_cast<SelectLds*>(pool),
+                                                  kept + (size_t)rr * kKeptCap);
+    if (threadIdx.x == 0) rows[rr] = o;
+    return;
+  }
   const int n_all = s_off[nch];
   // gather: every load of this thread first (flat index f, its chunk found
   // by binary search over the offsets), then the stores to LDS
@@ -584,7 +591,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
     keep_sum = stot;
   }
   }
-  if (Lk > kKeptCap) out.status = 1;
+  // a kept set above kKeptCap gets no list: its samplers stream the row
 
   // kept tokens re-sorted by id ascending: key (~id << 32 | logit bits), descending
   auto id_key = [&](uint64_t e) -> uint64_t {
@@ -631,16 +638,175 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The residual or bonus draw streamed over a whole filtered row pair, for a
+// target row whose kept set has no list (more than kKeptCap tokens).  Chunks
+// of 2048 tokens, wave w taking chunks w, w + 4, ...; lane l holds tokens
+// c0 + 512 j + 8 l .. + 7 (j < 4), so a chunk's tokens in order are (j, lane,
+// element).  Weights in float64 from the rows' FiltRows: p = e_t / S_t on
+// the target's kept tokens, and after a rejection max(p - q, 0) with q the
+// same over the draft's kept tokens.  Chunk masses go to LDS; every wave then
+// finds the chunk holding t = u_final * total by a blocked prefix of its own,
+// and wave 0 scans inside that chunk.
+constexpr int kStreamSub = kWave * 8;                  // 512 tokens per sub-block
+constexpr int kStreamChunk = 4 * kStreamSub;           // 2048 tokens per chunk
+
+template <typename T>
+__device__ __forceinline__ void load8_checked(const T* __restrict__ row, long e0, int V, float* z) {
+  constexpr int N = Elem<T>::kPerVec;
+  const bool al = aligned16(row);
+#pragma unroll
+  for (int v = 0; v < 8 / N; ++v) load_vec_checked(row, e0 + v * N, V, al, z + v * N);
+}
+
+__device__ __forceinline__ double kept_prob(float z, const FiltRow& fr, double invT,
+                                            const double* tbl) {
+  if (!(z >= fr.tau) || z == -INFINITY) return 0.0;
+  return exp64(((double)z - (double)fr.m) * invT, tbl) / fr.S;
+}
+
+template <typename T>
+__device__ void stream_draw(const T* __restrict__ trow, const T* __restrict__ drow, int V,
+                            bool rej, const FiltRow& tr, const FiltRow& dr, double invT,
+                            const double* tbl, double uf, double* csum, int& y_out,
+                            double& rmass_out) {
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  constexpr int kWaves = kFiltThreads / kWave;
+  const int nch = (V + kStreamChunk - 1) / kStreamChunk;
+  auto weights = [&](long e0, bool resid, double* w) {
+    float zt[8], zd[8];
+    load8_checked(trow, e0, V, zt);
+    if (resid) load8_checked(drow, e0, V, zd);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      double x = kept_prob(zt[i], tr, invT, tbl);
+      if (resid) {
+        x -= kept_prob(zd[i], dr, invT, tbl);
+        x = x > 0.0 ? x : 0.0;
+      }
+      w[i] = x;
+    }
+  };
+  bool resid = rej;
+  double total = 0.0, t = 0.0, pre = 0.0;
+  int cstar = -1, clast = -1;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    for (int c = wid; c < nch; c += kWaves) {
+      double acc = 0.0;
+      for (int j = 0; j < 4; ++j) {
+        double w[8];
+        weights((long)c * kStreamChunk + j * kStreamSub + lane * 8, resid, w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += w[i];
+      }
+      acc = wave_sum(acc);
+      if (lane == 0) csum[c] = acc;
+    }
+    __syncthreads();
+    // every wave: blocked prefix over the chunk masses (lane l owns chunks
+    // [l q, l q + q)), the same in every wave
+    const int q = (nch + kWave - 1) / kWave;
+    const int c_lo = min(nch, lane * q), c_hi = min(nch, c_lo + q);
+    double mine = 0.0;
+    for (int c = c_lo; c < c_hi; ++c) mine += csum[c];
+    double incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
+    }
+    total = __shfl(incl, kWave - 1, kWave);
+    if (resid && !(total > 0.0)) {       // unreachable in exact arithmetic: draw from p_j
+      resid = false;
+      __syncthreads();                   // every wave has read csum
+      continue;
+    }
+    t = uf * total;
+    double run = incl - mine;
+    int cand = -1, lastp = -1;
+    double cpre = 0.0;
+    for (int c = c_lo; c < c_hi; ++c) {
+      const double before = run;
+      run += csum[c];
+      if (cand < 0 && t < run) {
+        cand = c;
+        cpre = before;
+      }
+      if (csum[c] > 0.0) lastp = c;
+    }
+    const uint64_t hit = __ballot(cand >= 0);
+    if (hit) {
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      cstar = __shfl(cand, L, kWave);
+      pre = __shfl(cpre, L, kWave);
+    } else {
+      const uint64_t pos = __ballot(lastp >= 0);
+      clast = pos ? __shfl(lastp, 63 - __clzll((long long)pos), kWave) : -1;
+    }
+    break;
+  }
+  rmass_out = (rej && resid) ? total : 0.0;
+  y_out = -1;
+  if (wid != 0) return;
+  if (cstar >= 0) {                      // in-chunk scan: sub-blocks in order, lanes in order
+    double off = pre;
+    int y = INT_MAX, ylast = -1;
+    for (int j = 0; j < 4 && y == INT_MAX; ++j) {
+      const long e0 = (long)cstar * kStreamChunk + j * kStreamSub + lane * 8;
+      double w[8];
+      weights(e0, resid, w);
+      double mysum = 0.0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mysum += w[i];
+      double incl = mysum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const double yv = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += yv;
+      }
+      double run = off + incl - mysum;
+      int v = INT_MAX, vl = -1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        run += w[i];
+        if (v == INT_MAX && t < run) v = (int)(e0 + i);
+        if (w[i] > 0.0) vl = (int)(e0 + i);
+      }
+      const uint64_t h1 = __ballot(v != INT_MAX), h2 = __ballot(vl >= 0);
+      if (h1) y = __shfl(v, __ffsll((unsigned long long)h1) - 1, kWave);
+      if (h2) ylast = __shfl(vl, 63 - __clzll((long long)h2), kWave);
+      off += __shfl(incl, kWave - 1, kWave);
+    }
+    y_out = y != INT_MAX ? y : ylast;    // rounding fall-through inside the chunk
+  } else if (clast >= 0) {               // rounding fall-through: the last positive token
+    int ylast = -1;
+    for (int j = 0; j < 4; ++j) {
+      const long e0 = (long)clast * kStreamChunk + j * kStreamSub + lane * 8;
+      double w[8];
+      weights(e0, resid, w);
+      int vl = -1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (w[i] > 0.0) vl = (int)(e0 + i);
+      const uint64_t h2 = __ballot(vl >= 0);
+      if (h2) ylast = __shfl(vl, 63 - __clzll((long long)h2), kWave);
+    }
+    y_out = ylast;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // sample_list: per request, the residual or bonus draw over the target row's
-// kept tokens in id order.
+// kept tokens in id order (streamed over the rows when the kept set has no
+// list).
 template <typename T>
 __global__ __launch_bounds__(kFiltThreads) void sample_list_kernel(
-    const T* __restrict__ dft, const float* __restrict__ u_final, int K, int V, double invT,
-    const Plan* __restrict__ plan, const FiltRow* __restrict__ rows, const Kept* __restrict__ kept,
-    int* __restrict__ out_tokens, double* __restrict__ rmass_out) {
+    const T* __restrict__ tgt, const T* __restrict__ dft, const float* __restrict__ u_final,
+    int K, int V, double invT, const Plan* __restrict__ plan, const FiltRow* __restrict__ rows,
+    const Kept* __restrict__ kept, int* __restrict__ out_tokens, double* __restrict__ rmass_out) {
   __shared__ double tbl[SPECV_EXP64_N];
   __shared__ double dl[kFiltThreads / kWave];
   __shared__ int il[kFiltThreads / kWave];
+  __shared__ double csum[kMaxSampChunks];
   const int b = blockIdx.x;
   exp64_stage_table<kFiltThreads>(tbl);
   const Plan pl = plan[b];
@@ -654,6 +820,17 @@ __global__ __launch_bounds__(kFiltThreads) void sample_list_kernel(
   const Kept* list = kept + ((size_t)b * R + pl.trow) * kKeptCap;
   const T* drow = rej ? dft + draft_row_off(b, pl.drow, K, V) : nullptr;
   __syncthreads();
+  if (tr.count > kKeptCap) {                         // uniform: no list for this row
+    int y;
+    double rm;
+    stream_draw(tgt + target_row_off(b, pl.trow, K, V), drow, V, rej, tr, dr, invT, tbl,
+                (double)u_final[b], csum, y, rm);
+    if (threadIdx.x == 0) {
+      out_tokens[(size_t)b * (K + 1) + pl.stop] = y;
+      if (rmass_out) rmass_out[b] = rm;
+    }
+    return;
+  }
   const int n = tr.count;
   const int q = (n + kFiltThreads - 1) / kFiltThreads;
   const int i_lo = min(n, (int)threadIdx.x * q), i_hi = min(n, i_lo + q);
@@ -743,22 +920,76 @@ hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mid && (e = hipEventRecord(mid, stream)) != hipSuccess) return e;
-  filter_merge_kernel<<<dim3((unsigned)((size_t)B * (2 * K + 1))), dim3(kFiltThreads), 0, stream>>>(
-      draft_len, K, nch, cap, stride, top_k, top_p, invT, cand, counts, rows, kept);
+  const dim3 grid((unsigned)((size_t)B * (2 * K + 1)));
+  if (bf16)
+    filter_merge_kernel<bf16_t><<<grid, dim3(kFiltThreads), 0, stream>>>(
+        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V, nch,
+        cap, stride, top_k, top_p, invT, cand, counts, rows, kept);
+  else
+    filter_merge_kernel<float><<<grid, dim3(kFiltThreads), 0, stream>>>(
+        static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, nch, cap,
+        stride, top_k, top_p, invT, cand, counts, rows, kept);
   return hipGetLastError();
 }
 
-hipError_t launch_sample_list(bool bf16, const void* dft, const float* u_final, int B, int K, int V,
-                              double invT, const Plan* plan, const FiltRow* rows, const Kept* kept,
-                              int* out_tokens, double* rmass_out, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// filter_rows: the general select (radix_select.h) for every needed row, one
+// 1024-thread workgroup per row: any top_k, top-p with or without top-k, any
+// kept-set size.
+constexpr int kSelThreads = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(kSelThreads) void filter_rows_kernel(
+    const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
+    int K, int V, int top_k, float top_p, double invT, FiltRow* __restrict__ rows,
+    Kept* __restrict__ kept) {
+  __shared__ SelectLds sl;
+  __shared__ double tbl[SPECV_EXP64_N];
+  const int R = 2 * K + 1;
+  const int rr = blockIdx.x;
+  const int r = rr % R, b = rr / R;
+  const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
+  if (nb < 0 || nb > K) return;
+  bool is_target;
+  int k;
+  if (!row_needed(r, K, nb, is_target, k)) return;
+  for (int i = threadIdx.x; i < SPECV_EXP64_N; i += kSelThreads) tbl[i] = kExp64Table[i];
+  __syncthreads();
+  const T* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
+  const FiltRow o = select_row<T, kSelThreads>(row, V, sizeof(T) == 2, top_k, top_p, invT, tbl,
+                                               &sl, kept + (size_t)rr * kKeptCap);
+  if (threadIdx.x == 0) rows[rr] = o;
+}
+
+hipError_t launch_filter_rows(bool bf16, const void* tgt, const void* dft, const int* draft_len,
+                              int B, int K, int V, int top_k, float top_p, double invT,
+                              FiltRow* rows, Kept* kept, hipStream_t stream) {
+  const size_t blocks = (size_t)B * (2 * K + 1);
+  if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  if (bf16)
+    filter_rows_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kSelThreads), 0, stream>>>(
+        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V,
+        top_k, top_p, invT, rows, kept);
+  else
+    filter_rows_kernel<float><<<dim3((unsigned)blocks), dim3(kSelThreads), 0, stream>>>(
+        static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, top_k,
+        top_p, invT, rows, kept);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_list(bool bf16, const void* tgt, const void* dft, const float* u_final,
+                              int B, int K, int V, double invT, const Plan* plan,
+                              const FiltRow* rows, const Kept* kept, int* out_tokens,
+                              double* rmass_out, hipStream_t stream) {
+  if ((V + kStreamChunk - 1) / kStreamChunk > kMaxSampChunks) return hipErrorInvalidConfiguration;
   if (bf16)
     sample_list_kernel<bf16_t><<<dim3(B), dim3(kFiltThreads), 0, stream>>>(
-        static_cast<const bf16_t*>(dft), u_final, K, V, invT, plan, rows, kept, out_tokens,
-        rmass_out);
+        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), u_final, K, V, invT,
+        plan, rows, kept, out_tokens, rmass_out);
   else
     sample_list_kernel<float><<<dim3(B), dim3(kFiltThreads), 0, stream>>>(
-        static_cast<const float*>(dft), u_final, K, V, invT, plan, rows, kept, out_tokens,
-        rmass_out);
+        static_cast<const float*>(tgt), static_cast<const float*>(dft), u_final, K, V, invT, plan,
+        rows, kept, out_tokens, rmass_out);
   return hipGetLastError();
 }
 

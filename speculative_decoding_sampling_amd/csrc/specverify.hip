@@ -37,9 +37,13 @@ hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int*
                          int K, int V, int nch, int top_k, float top_p, double invT,
                          uint64_t* cand, int* counts, FiltRow* rows, Kept* kept,
                          hipStream_t stream, hipEvent_t mid);
-hipError_t launch_sample_list(bool bf16, const void* dft, const float* u_final, int B, int K, int V,
-                              double invT, const Plan* plan, const FiltRow* rows, const Kept* kept,
-                              int* out_tokens, double* rmass_out, hipStream_t stream);
+hipError_t launch_filter_rows(bool bf16, const void* tgt, const void* dft, const int* draft_len,
+                              int B, int K, int V, int top_k, float top_p, double invT,
+                              FiltRow* rows, Kept* kept, hipStream_t stream);
+hipError_t launch_sample_list(bool bf16, const void* tgt, const void* dft, const float* u_final,
+                              int B, int K, int V, double invT, const Plan* plan,
+                              const FiltRow* rows, const Kept* kept, int* out_tokens,
+                              double* rmass_out, hipStream_t stream);
 hipError_t launch_sample_pass(bool bf16, const void* tgt, const void* dft, int B, int K, int V,
                               int nch, double invT, const Plan* plan, ChunkRec* recs, Tie* ties,
                               hipStream_t stream);
@@ -64,11 +68,14 @@ hipError_t launch_monitor_update(const int32_t* draft_tokens, const int32_t* dra
                                  int32_t* next_draft_len, double* rate, hipStream_t stream);
 
 // Kernel stages of one call, in launch order (specv_verify_timed records an
-// event after each): without filters, and with top-k / top-p.
-const char* const kStageNames[2][4] = {
+// event after each), by path: without filters; top-k / top-p through the
+// candidate select (0 < top_k <= kFiltMaxTopK, candidates fitting the merge);
+// top-k / top-p through the general radix select (every other setting).
+const char* const kStageNames[3][4] = {
     {"row_stats", "accept", "sample_pass", "sample_finish"},
-    {"filter_cand", "filter_merge", "accept", "sample_list"}};
-constexpr int kNumStages[2] = {4, 4};
+    {"filter_cand", "filter_merge", "accept", "sample_list"},
+    {"filter_rows", "accept", "sample_list", nullptr}};
+constexpr int kNumStages[3] = {4, 4, 3};
 
 namespace {
 
@@ -92,12 +99,27 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 //   kept lists     Kept     [B][2K+1][kKeptCap]
 struct Layout {
   bool filt = false;
+  bool cand = false;         // filtered through the candidate select
   int nch_row = 0, nch_samp = 0, nch_filt = 0, cap = 0;
   size_t off_row = 0, off_zx = 0, off_beta = 0, off_plan = 0, off_recs = 0, off_ties = 0;
   size_t off_cand = 0, off_counts = 0, off_frows = 0, off_kept = 0, total = 0;
 };
 
 bool filters_on(int V, int top_k, float top_p) { return (top_k > 0 && top_k < V) || top_p < 1.0f; }
+
+// The candidate select serves a small active top-k whose per-chunk slots fit
+// the merge's on-chip list; every other filtered call takes the radix select.
+bool candidate_path(int V, int top_k) {
+  if (!(top_k > 0 && top_k < V && top_k <= kFiltMaxTopK)) return false;
+  const int nch = (V + kFiltChunk - 1) / kFiltChunk;
+  return nch <= kFiltMaxChunks && filter_row_stride(nch, top_k) <= kFiltSortMax;
+}
+
+// Stage-table index of a call: 0 unfiltered, 1 candidate select, 2 radix select.
+int path_kind(int V, int top_k, float top_p) {
+  if (!filters_on(V, top_k, top_p)) return 0;
+  return candidate_path(V, top_k) ? 1 : 2;
+}
 
 Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p) {
   Layout L;
@@ -121,14 +143,17 @@ Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p) {
     L.off_ties = off;
     off = align_up(off + (size_t)B * L.nch_samp * kTieCap * sizeof(Tie));
   } else {
-    L.nch_filt = (V + kFiltChunk - 1) / kFiltChunk;
-    L.cap = filter_cap(top_k);
+    L.cand = candidate_path(V, top_k);
     L.off_plan = off;
     off = align_up(off + (size_t)B * sizeof(Plan));
-    L.off_cand = off;
-    off = align_up(off + (size_t)B * R * filter_row_stride(L.nch_filt, top_k) * sizeof(uint64_t));
-    L.off_counts = off;
-    off = align_up(off + (size_t)B * R * L.nch_filt * sizeof(int));
+    if (L.cand) {
+      L.nch_filt = (V + kFiltChunk - 1) / kFiltChunk;
+      L.cap = filter_cap(top_k);
+      L.off_cand = off;
+      off = align_up(off + (size_t)B * R * filter_row_stride(L.nch_filt, top_k) * sizeof(uint64_t));
+      L.off_counts = off;
+      off = align_up(off + (size_t)B * R * L.nch_filt * sizeof(int));
+    }
     L.off_frows = off;
     off = align_up(off + (size_t)B * R * sizeof(FiltRow));
     L.off_kept = off;
@@ -147,14 +172,6 @@ specv_status_t check_sizes(int B, int K, int V, specv_dtype_t dtype, int top_k, 
   if ((double)B * (double)(K + 1) * (double)V > 4.0e18) return SPECV_EINVAL;
   if (V > SPECV_MAX_V) return SPECV_EUNSUPPORTED;
   if ((size_t)B * (2 * K + 1) * (size_t)((V + 1023) / 1024) > 0x7fffffffu) return SPECV_EUNSUPPORTED;
-  if (filters_on(V, top_k, top_p)) {
-    // top-p needs an active top-k; the candidate select handles k <= 256 and
-    // a row's candidates must fit the LDS merge.
-    if (!(top_k > 0 && top_k < V) || top_k > SPECV_MAX_TOPK) return SPECV_EUNSUPPORTED;
-    const int nch = (V + kFiltChunk - 1) / kFiltChunk;
-    if (nch > kFiltMaxChunks || filter_row_stride(nch, top_k) > kFiltSortMax)
-      return SPECV_EUNSUPPORTED;
-  }
   return SPECV_OK;
 }
 
@@ -233,15 +250,21 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
     int* counts = reinterpret_cast<int*>(ws + L.off_counts);
     FiltRow* frows = reinterpret_cast<FiltRow*>(ws + L.off_frows);
     Kept* kept = reinterpret_cast<Kept*>(ws + L.off_kept);
-    e = launch_filter(bf16, target, draft, draft_len, B, K, V, L.nch_filt, top_k, top_p, invT,
-                      cand, counts, frows, kept, stream, events ? events[1] : nullptr);
-    if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
+    // the candidate path has two select stages, the radix path one
+    const int s0 = L.cand ? 2 : 1;
+    if (L.cand)
+      e = launch_filter(bf16, target, draft, draft_len, B, K, V, L.nch_filt, top_k, top_p, invT,
+                        cand, counts, frows, kept, stream, events ? events[1] : nullptr);
+    else
+      e = launch_filter_rows(bf16, target, draft, draft_len, B, K, V, top_k, top_p, invT, frows,
+                             kept, stream);
+    if (e != hipSuccess || !mark(s0)) return SPECV_EHIP;
     e = launch_accept(bf16, true, target, draft, tokens, draft_len, u, u_final, B, K, V, 0, c,
                       invT, eos_id, nullptr, nullptr, frows, out, stream);
-    if (e != hipSuccess || !mark(3)) return SPECV_EHIP;
-    e = launch_sample_list(bf16, draft, u_final, B, K, V, invT, plan, frows, kept, out_tokens,
-                           rmass_out, stream);
-    if (e != hipSuccess || !mark(4)) return SPECV_EHIP;
+    if (e != hipSuccess || !mark(s0 + 1)) return SPECV_EHIP;
+    e = launch_sample_list(bf16, target, draft, u_final, B, K, V, invT, plan, frows, kept,
+                           out_tokens, rmass_out, stream);
+    if (e != hipSuccess || !mark(s0 + 2)) return SPECV_EHIP;
   }
   return SPECV_OK;
 }
@@ -385,7 +408,7 @@ specv_status_t specv_verify_timed(const void* target_logits, const void* draft_l
                                   int32_t* n_emitted, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream, hipEvent_t* events) {
   if (!events) return SPECV_EINVAL;
-  const int nst = specv::kNumStages[specv::filters_on(V, top_k, top_p) ? 1 : 0];
+  const int nst = specv::kNumStages[specv::path_kind(V, top_k, top_p)];
   for (int i = 0; i <= nst; ++i)
     if (!events[i]) return SPECV_EINVAL;
   return specv::run(target_logits, draft_logits, dtype, draft_tokens, draft_len, u, u_final, B,
@@ -393,7 +416,9 @@ specv_status_t specv_verify_timed(const void* target_logits, const void* draft_l
                     workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr, events);
 }
 
-int specv_num_stages(int filtered) { return specv::kNumStages[filtered ? 1 : 0]; }
+int specv_num_stages(int kind) { return (kind >= 0 && kind < 3) ? specv::kNumStages[kind] : 0; }
+
+int specv_path_kind(int V, int top_k, float top_p) { return specv::path_kind(V, top_k, top_p); }
 
 specv_status_t specv_bench_row_stats(const void* const* targets, const void* const* drafts,
                                      const int32_t* const* draft_tokens,
@@ -544,8 +569,12 @@ specv_status_t specv_acceptance_rates(const void* target_logits, const void* dra
     int* counts = reinterpret_cast<int*>(ws + L.off_counts);
     FiltRow* frows = reinterpret_cast<FiltRow*>(ws + L.off_frows);
     Kept* kept = reinterpret_cast<Kept*>(ws + L.off_kept);
-    e = launch_filter(bf16, target_logits, draft_logits, draft_len, B, K, V, L.nch_filt, top_k,
-                      top_p, invT, cand, counts, frows, kept, stream, nullptr);
+    if (L.cand)
+      e = launch_filter(bf16, target_logits, draft_logits, draft_len, B, K, V, L.nch_filt, top_k,
+                        top_p, invT, cand, counts, frows, kept, stream, nullptr);
+    else
+      e = launch_filter_rows(bf16, target_logits, draft_logits, draft_len, B, K, V, top_k, top_p,
+                             invT, frows, kept, stream);
     if (e == hipSuccess)
       e = launch_beta(bf16, true, target_logits, draft_logits, draft_len, B, K, V, 0, c, invT,
                       nullptr, frows, kept, nullptr, beta, stream);
@@ -608,9 +637,9 @@ specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream
   return specv::launch_exp64_selftest(x, y, n, stream) == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }
 
-const char* specv_stage_name(int filtered, int i) {
-  const int f = filtered ? 1 : 0;
-  return (i >= 0 && i < specv::kNumStages[f]) ? specv::kStageNames[f][i] : nullptr;
+const char* specv_stage_name(int kind, int i) {
+  if (kind < 0 || kind >= 3) return nullptr;
+  return (i >= 0 && i < specv::kNumStages[kind]) ? specv::kStageNames[kind][i] : nullptr;
 }
 
 const char* specv_status_string(specv_status_t status) {

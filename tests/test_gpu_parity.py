@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 import oracle as O  # noqa: E402
 from speculative_decoding_sampling_amd import binding  # noqa: E402
 from speculative_decoding_sampling_amd.workloads import f32, make_workload, upload  # noqa: E402
-from tests.parity import compare, to_numpy  # noqa: E402
+from tests.parity import compare, flag_ceiling, to_numpy  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -389,17 +389,70 @@ def test_parity_filtered_ragged_bf16_with_eos():
     assert len(set(w.draft_len.tolist())) > 1
 
 
-def test_filter_capacity_limit_is_a_request_error():
+def test_filter_capacity_overflow_matches_oracle():
     # A row whose logits are all equal keeps every token under top-k (ties
-    # kept): more than the 512-token kept list, so that request is reported
-    # as an error while the others are unaffected.
+    # kept): its 8192-token chunks hold far more candidates than their slots,
+    # so the candidate merge hands the row to the radix select, and the kept
+    # set (all 152064 tokens) is far beyond the kept list, so the draw is
+    # streamed over the row.  Every request must still match the oracle.
     w = make_workload(4, B=4, draft_sampler=oracle_sampler)
     w.target[2, 0, :] = 0.0
-    g = run_gpu(w)
-    o = run_oracle(w)
-    assert g["n_emitted"][2] == -1 and o["n_emitted"][2] > 0
-    for b in (0, 1, 3):
-        assert g["n_emitted"][b] == o["n_emitted"][b] or o["flag_kind"][b] != O.FLAG_NONE
+    w.draft_tokens[2, 0] = int(np.argmax(w.draft[2, 0]))    # a draft token q keeps
+    rep, g, o = assert_parity(w, label="all-equal target row")
+    assert o["n_emitted"][2] > 0 and g["n_emitted"][2] == o["n_emitted"][2]
+
+
+# ---------------------------------------------------------------------------
+# top-k / top-p through the radix select: top-p alone, large top-k, kept sets
+# beyond the 512-token list (streamed draws)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,B,top_k,top_p", [
+    (3, 8, 0, 0.9),          # top-p alone, bf16 V=128256 (thousands of tokens kept)
+    (4, 6, 0, 0.9),          # top-p alone, fp32 V=152064
+    (3, 6, 1000, 1.0),       # top-k 1000 alone: 1000 kept, beyond the list
+    (4, 6, 1000, 0.95),      # top-k 1000 then top-p
+    (1, None, 300, 0.8),     # fp32 V=4096
+    (2, 1, 0, 0.5),          # B=1, bf16 V=32000
+])
+def test_parity_radix_select(cfg, B, top_k, top_p):
+    from speculative_decoding_sampling_amd import binding as bd
+    w = make_workload(cfg, B=B, draft_sampler=oracle_sampler)
+    w.top_k, w.top_p = top_k, f32(top_p)
+    assert bd.path_kind(w.V, w.top_k, w.top_p) == 2
+    redraw_tokens(w, 100 + cfg)
+    rep, g, o = assert_parity(w, label=f"radix select top_k={top_k} top_p={top_p}")
+    assert rep["positions"] > 0
+
+
+def test_parity_radix_select_kept_sets_of_every_size():
+    # top-p over rows whose spread differs request by request, so kept sets
+    # run from one token to most of the vocabulary, on both sides of the list
+    # size; ties from bf16 rounding and -inf masks in some rows.
+    rng = np.random.default_rng(77)
+    B, K, V = 8, 3, 20011
+    scale = np.array([0.05, 0.5, 1.0, 2.0, 4.0, 8.0, 16.0, 0.2], dtype=np.float32)
+    t = (rng.normal(0, 1, size=(B, K + 1, V)).astype(np.float32) * scale[:, None, None])
+    d = (t[:, :K] + rng.normal(0, 0.3, size=(B, K, V)).astype(np.float32) * scale[:, None, None])
+    t[1, :, rng.random(V) < 0.5] = -np.inf
+    d[1, :, :] = np.where(np.isinf(t[1, :K]), -np.inf, d[1])
+    w = _custom_workload(t, d.astype(np.float32), [3, 3, 2, 3, 1, 3, 0, 3], rng, dtype="bf16",
+                         T=0.9, seed=77)
+    w.top_k, w.top_p = 0, f32(0.95)
+    redraw_tokens(w, 77)
+    rep, g, o = assert_parity(w, label="kept sets of every size")
+    P, _ = O.processed_distribution(O.widen_row(w.target[0, 0], "bf16"), f32(0.9), 0, f32(0.95))
+    Q, _ = O.processed_distribution(O.widen_row(w.target[6, 0], "bf16"), f32(0.9), 0, f32(0.95))
+    assert (P > 0).sum() > 512 and (Q > 0).sum() < 512
+
+
+def test_radix_select_deterministic_bitwise():
+    w = make_workload(4, B=4, draft_sampler=oracle_sampler)
+    w.top_k, w.top_p = 0, f32(0.9)
+    redraw_tokens(w, 9)
+    a, b = run_gpu(w), run_gpu(w)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
 
 
 def test_many_draws_large_vocabulary_non_unit_temperature():
@@ -499,6 +552,7 @@ def assert_sample_parity(logits, u, T, top_k, top_p, dtype, label=""):
     print(f"[sample] {label} R={len(u)} V={logits.shape[1]} {dtype} T={T} k={top_k} p={top_p}: "
           f"flagged {int((~certain).sum())}, mismatches {len(bad)}", flush=True)
     assert len(bad) == 0, [(int(r), int(y[r]), int(yo[r])) for r in bad[:5]]
+    assert int((~certain).sum()) <= flag_ceiling(len(u))
     return y, yo
 
 
@@ -521,6 +575,17 @@ def test_sample_matches_oracle_filtered(top_k, top_p):
     from speculative_decoding_sampling_amd.workloads import uniforms
     u = uniforms(np.random.default_rng(800 + top_k), rows.shape[0])
     assert_sample_parity(rows, u, w.T, top_k, top_p, w.dtype, label="cfg4 rows")
+
+
+@pytest.mark.parametrize("top_k,top_p", [(0, 0.9), (1000, 1.0), (2000, 0.99)])
+def test_sample_matches_oracle_radix_select(top_k, top_p):
+    # the draft-side draw through the radix select, kept sets beyond the list
+    # (the draw streamed over the row)
+    w = make_workload(4, B=3, draft_sampler=oracle_sampler)
+    rows = w.draft.reshape(-1, w.V)[:16]
+    from speculative_decoding_sampling_amd.workloads import uniforms
+    u = uniforms(np.random.default_rng(900 + top_k), rows.shape[0])
+    assert_sample_parity(rows, u, w.T, top_k, top_p, w.dtype, label="cfg4 rows, radix select")
 
 
 def test_sample_filtered_sparse_and_tied_rows():
@@ -613,6 +678,14 @@ def test_acceptance_rates_unfiltered(cfg, B):
 def test_acceptance_rates_filtered():
     # float64 inside; the float32 result is within half an ulp (6e-8 at <= 1).
     assert_beta_parity(make_workload(4, B=6, draft_sampler=oracle_sampler), 1e-7)
+
+
+@pytest.mark.parametrize("cfg,B,top_k,top_p", [(3, 4, 0, 0.9), (4, 3, 1000, 0.95)])
+def test_acceptance_rates_radix_select(cfg, B, top_k, top_p):
+    # beta through the radix select; kept sets beyond the list are streamed
+    w = make_workload(cfg, B=B, draft_sampler=oracle_sampler)
+    w.top_k, w.top_p = top_k, f32(top_p)
+    assert_beta_parity(w, 1e-7, label=f"radix select top_k={top_k} top_p={top_p}")
 
 
 def test_acceptance_rates_identical_rows_and_ragged():

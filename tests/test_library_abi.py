@@ -35,6 +35,7 @@ def test_header_declares_the_api():
     names = declared_functions()
     assert set(names) == {"specv_workspace_bytes", "specv_verify", "specv_verify_debug",
                           "specv_verify_timed", "specv_num_stages", "specv_stage_name",
+                          "specv_path_kind",
                           "specv_status_string", "specv_version", "specv_selftest_exp64",
                           "specv_bench_row_stats", "specv_sample",
                           "specv_acceptance_rates", "specv_round_stats",
@@ -74,7 +75,8 @@ def test_workspace_sizes(lib):
     assert f(1, 4, 100, 7, 0, 1.0) == 0                           # unknown dtype
     assert f(1, 4, 100, 0, 0, 0.0) == 0                           # top_p out of range
     assert f(256, 8, 152064, 0, 50, 0.9) > 0                      # the top-k/top-p workload
-    assert f(1, 4, 300000, 0, 50, 0.9) == 0                       # V above the filter limit
+    assert f(1, 4, 300000, 0, 50, 0.9) > 0                        # large V: the radix select
+    assert f(4, 4, 1000, 0, 0, 0.9) > 0 and f(4, 4, 1000, 0, 999, 1.0) > 0
 
 
 def test_validation_returns_before_any_gpu_work(lib):
@@ -104,8 +106,8 @@ def test_validation_returns_before_any_gpu_work(lib):
     assert call(eos=1000) == 1
     assert call(target=None) == 1
     assert call(top_k=10, ws_bytes=16) == 2    # filtered path: workspace too small
-    assert call(top_k=129) == 4                # top_k above the candidate-select limit
-    assert call(top_k=0, top_p=0.9) == 4       # top-p without top-k
+    assert call(top_k=129, ws_bytes=16) == 2   # radix-select path: workspace too small
+    assert call(top_k=0, top_p=0.9, ws_bytes=16) == 2
     assert call(ws_bytes=16) == 2              # workspace too small
 
 
@@ -113,12 +115,21 @@ def test_stage_names(lib):
     lib.specv_stage_name.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.specv_stage_name.restype = ctypes.c_char_p
     lib.specv_num_stages.argtypes = [ctypes.c_int]
-    for filtered, first in ((0, b"row_stats"), (1, b"filter_cand")):
-        n = lib.specv_num_stages(filtered)
-        names = [lib.specv_stage_name(filtered, i) for i in range(n)]
+    for kind, first in ((0, b"row_stats"), (1, b"filter_cand"), (2, b"filter_rows")):
+        n = lib.specv_num_stages(kind)
+        names = [lib.specv_stage_name(kind, i) for i in range(n)]
         assert n >= 1 and names[0] == first and all(names)
-        assert lib.specv_stage_name(filtered, n) is None
-        assert lib.specv_stage_name(filtered, -1) is None
+        assert lib.specv_stage_name(kind, n) is None
+        assert lib.specv_stage_name(kind, -1) is None
+    assert lib.specv_num_stages(3) == 0 and lib.specv_stage_name(3, 0) is None
+    pk = lib.specv_path_kind
+    pk.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_float]
+    pk.restype = ctypes.c_int
+    assert pk(128256, 0, 1.0) == 0 and pk(128256, 128256, 1.0) == 0   # filters off
+    assert pk(152064, 50, 0.9) == 1 and pk(152064, 100, 1.0) == 1      # candidate select
+    assert pk(152064, 128, 1.0) == 2        # 128 at 19 chunks: slots beyond the on-chip list
+    assert pk(152064, 0, 0.9) == 2 and pk(152064, 1000, 1.0) == 2      # radix select
+    assert pk(300000, 50, 0.9) == 2                                     # too many chunks
 
 
 def test_status_strings(lib):
@@ -196,7 +207,8 @@ def test_acceptance_rates_reject_bad_arguments(lib):
     assert call(beta=None) == 1
     assert call(d=None) == 1
     assert call(T=0.0) == 1
-    assert call(k=0, p=0.5) == 4                     # top-p without top-k
+    assert call(k=0, p=0.5, wsb=16) == 2             # top-p alone: radix-select workspace
+    assert call(p=1.5) == 1 and call(k=-1) == 1
     assert call(wsb=16) == 2
     assert call(K=0, d=None, wsb=1 << 20) == 0       # nothing to compute, nothing launched
 
