@@ -55,7 +55,8 @@ typedef enum {
   SPECV_EINVAL = 1,       /* bad argument (null/misaligned pointer, bad size or parameter) */
   SPECV_EWORKSPACE = 2,   /* workspace missing, misaligned (16 B) or smaller than specv_workspace_bytes() */
   SPECV_EHIP = 3,         /* a HIP launch failed */
-  SPECV_EUNSUPPORTED = 4  /* valid request the library does not implement (see specv_verify) */
+  SPECV_EUNSUPPORTED = 4, /* valid request the library does not implement (see specv_verify) */
+  SPECV_ESCRATCH = 5      /* specv_verify_noalloc: sizes beyond its fixed scratch */
 } specv_status_t;
 
 typedef enum {
@@ -67,6 +68,8 @@ typedef enum {
 #define SPECV_MAX_K 64
 /* Largest vocabulary the call accepts (larger V returns SPECV_EUNSUPPORTED). */
 #define SPECV_MAX_V 4194304
+/* Bytes of the fixed device scratch array behind specv_verify_noalloc. */
+#define SPECV_NOALLOC_SCRATCH_BYTES (16u << 20)
 /* Largest hidden size the fused LM-head call accepts. */
 #define SPECV_MAX_D 65536
 
@@ -118,6 +121,29 @@ SPECV_API specv_status_t specv_verify(const void *target_logits, const void *dra
                             int B, int K, int V, float temperature, int top_k, float top_p,
                             int eos_id, int32_t *out_tokens, int32_t *n_emitted,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * specv_verify for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, outputs and kernels as
+ * specv_verify without the workspace; the call allocates nothing (no
+ * hipMalloc, no allocating library routine).  Its scratch is one fixed
+ * device array of SPECV_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held until
+ * the process ends; its address is looked up once per device.  Sizes whose
+ * workspace (specv_workspace_bytes) exceeds it return SPECV_ESCRATCH before
+ * any device work.  It covers B=64, K=4, V=128256 (3.3 MB of workspace) and
+ * B=64, K=8, V=129280 (3.4 MB); top-k 50 / top-p 0.9 at K=8, V=152064 needs
+ * about 0.4 MB per request (B <= 40 fits).
+ * Every call on one GPU shares that GPU's array, so calls that overlap on
+ * one GPU (on different streams or host threads) race; calls in one stream
+ * order are safe.  The scratch needs no initialisation.
+ */
+SPECV_API specv_status_t specv_verify_noalloc(const void *target_logits, const void *draft_logits,
+                                    specv_dtype_t dtype, const int32_t *draft_tokens,
+                                    const int32_t *draft_len, const float *u, const float *u_final,
+                                    int B, int K, int V, float temperature, int top_k, float top_p,
+                                    int eos_id, int32_t *out_tokens, int32_t *n_emitted,
+                                    hipStream_t stream);
 
 /*
  * specv_verify plus diagnostic outputs, each nullable:

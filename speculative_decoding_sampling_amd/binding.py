@@ -17,6 +17,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecver
 
 SPECV_F32, SPECV_BF16 = 0, 1
 SPECV_OK, SPECV_EINVAL, SPECV_EWORKSPACE, SPECV_EHIP, SPECV_EUNSUPPORTED = 0, 1, 2, 3, 4
+SPECV_ESCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 16 << 20
 MAX_K = 64
 MAX_WINDOW = 4096
 TOTAL_FIELDS = ("requests", "errors", "drafted", "accepted", "emitted", "eos_stops",
@@ -60,6 +62,8 @@ def load_library():
         lib.specv_verify_debug.restype = c_int
         lib.specv_verify_timed.argtypes = common + [c_vp]
         lib.specv_verify_timed.restype = c_int
+        lib.specv_verify_noalloc.argtypes = common[:16] + [c_vp]
+        lib.specv_verify_noalloc.restype = c_int
         lib.specv_sample.argtypes = [c_vp, c_int, c_vp, c_int, c_int, c_float, c_int, c_float, c_vp,
                                      c_vp, c_size, c_vp]
         lib.specv_sample.restype = c_int
@@ -419,6 +423,38 @@ def verify(target_logits, draft_logits, draft_tokens, draft_len, u, u_final, tem
     if status != SPECV_OK:
         raise SpecVerifyError(status, status_string(status))
     return res
+
+
+def verify_noalloc(target_logits, draft_logits, draft_tokens, draft_len, u, u_final,
+                   temperature=1.0, top_k=0, top_p=1.0, eos_id=-1, *, out_tokens, n_emitted,
+                   stream=None):
+    """``specv_verify_noalloc``: the verification step with the library's fixed
+    device scratch instead of a workspace.  The outputs must be passed in;
+    nothing is allocated.  Same shapes and dtypes as ``verify``."""
+    lib = load_library()
+    dev = target_logits.device
+    if dev.type != "cuda" or target_logits.dim() != 3:
+        raise ValueError("target_logits must be a [B, K+1, V] GPU tensor")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits", None, (B, K + 1, V), dev)
+    _check(draft_logits, "draft_logits", target_logits.dtype, (B, K, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(draft_len, "draft_len", torch.int32, (B,), dev)
+    _check(u, "u", torch.float32, (B, K), dev)
+    _check(u_final, "u_final", torch.float32, (B,), dev)
+    _check(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+    _check(n_emitted, "n_emitted", torch.int32, (B,), dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    status = lib.specv_verify_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(draft_len),
+        _ptr(u), _ptr(u_final), B, K, V, float(temperature), int(top_k), float(top_p),
+        int(eos_id), _ptr(out_tokens), _ptr(n_emitted), ctypes.c_void_p(stream.cuda_stream))
+    if status != SPECV_OK:
+        raise SpecVerifyError(status, status_string(status))
+    return {"out_tokens": out_tokens, "n_emitted": n_emitted}
 
 
 class PackedLmHeadWeight:

@@ -4,8 +4,10 @@
 #include "specverify.h"
 #include "specverify_selftest.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "accept_core.h"
 #include "common.h"
@@ -365,6 +367,31 @@ specv_status_t run_lm_head(const void* hidden, const void* weight, const void* d
   return e == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }
 
+// Scratch of the allocation-free entry point: one fixed array in device
+// memory, held by every GPU the library runs on until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[SPECV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch address on `device` (the current device), or null on error.
+void* scratch_on(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[device].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[device].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[device].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace
 }  // namespace specv
 
@@ -384,6 +411,39 @@ specv_status_t specv_verify(const void* target_logits, const void* draft_logits,
   return specv::run(target_logits, draft_logits, dtype, draft_tokens, draft_len, u, u_final, B,
                     K, V, temperature, top_k, top_p, eos_id, out_tokens, n_emitted, workspace,
                     workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr, nullptr);
+}
+
+specv_status_t specv_verify_noalloc(const void* target_logits, const void* draft_logits,
+                                    specv_dtype_t dtype, const int32_t* draft_tokens,
+                                    const int32_t* draft_len, const float* u, const float* u_final,
+                                    int B, int K, int V, float temperature, int top_k,
+                                    float top_p, int eos_id, int32_t* out_tokens,
+                                    int32_t* n_emitted, hipStream_t stream) {
+  using namespace specv;
+  // Sizes first, on the host: too large for the fixed scratch is an error
+  // before any device is touched.
+  const specv_status_t st = check_sizes(B, K, V, dtype, top_k, top_p);
+  if (st != SPECV_OK) return st;
+  if (make_layout(B, K, V, dtype == SPECV_BF16, top_k, top_p).total > SPECV_NOALLOC_SCRATCH_BYTES)
+    return SPECV_ESCRATCH;
+  // The scratch of the device the stream belongs to, looked up with that
+  // device current.
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return SPECV_EHIP;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return SPECV_EHIP;
+  void* ws = nullptr;
+  if (dev == cur) {
+    ws = scratch_on(dev);
+  } else {
+    if (hipSetDevice(dev) != hipSuccess) return SPECV_EHIP;
+    ws = scratch_on(dev);
+    if (hipSetDevice(cur) != hipSuccess) return SPECV_EHIP;
+  }
+  if (!ws) return SPECV_EHIP;
+  return run(target_logits, draft_logits, dtype, draft_tokens, draft_len, u, u_final, B, K, V,
+             temperature, top_k, top_p, eos_id, out_tokens, n_emitted, ws,
+             SPECV_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
 specv_status_t specv_verify_debug(const void* target_logits, const void* draft_logits,
@@ -649,6 +709,8 @@ const char* specv_status_string(specv_status_t status) {
     case SPECV_EWORKSPACE: return "workspace missing, misaligned or too small";
     case SPECV_EHIP: return "HIP launch failed";
     case SPECV_EUNSUPPORTED: return "unsupported parameter combination";
+    case SPECV_ESCRATCH:
+      return "sizes need more scratch than the allocation-free call's fixed array holds";
   }
   return "unknown status";
 }

@@ -35,7 +35,7 @@ def test_header_declares_the_api():
     names = declared_functions()
     assert set(names) == {"specv_workspace_bytes", "specv_verify", "specv_verify_debug",
                           "specv_verify_timed", "specv_num_stages", "specv_stage_name",
-                          "specv_path_kind",
+                          "specv_path_kind", "specv_verify_noalloc",
                           "specv_status_string", "specv_version", "specv_selftest_exp64",
                           "specv_bench_row_stats", "specv_sample",
                           "specv_acceptance_rates", "specv_round_stats",
@@ -109,6 +109,21 @@ def test_validation_returns_before_any_gpu_work(lib):
     assert call(top_k=129, ws_bytes=16) == 2   # radix-select path: workspace too small
     assert call(top_k=0, top_p=0.9, ws_bytes=16) == 2
     assert call(ws_bytes=16) == 2              # workspace too small
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_without_device_work(lib):
+    v = lib.specv_verify_noalloc
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    v.argtypes = [vp, vp, ci, vp, vp, vp, vp, ci, ci, ci, cf, ci, cf, ci, vp, vp, vp]
+    v.restype = ci
+    d = ctypes.c_void_p(4096)
+    # B=256, K=8, V=152064 with top-k 50 needs ~98 MB: beyond the 16 MiB scratch
+    assert v(d, d, 0, d, d, d, d, 256, 8, 152064, 1.0, 50, 0.9, -1, d, d, None) == 5
+    assert v(d, d, 0, d, d, d, d, 0, 8, 152064, 1.0, 50, 0.9, -1, d, d, None) == 1   # B < 1
+    s = lib.specv_status_string
+    s.argtypes = [ctypes.c_int]
+    s.restype = ctypes.c_char_p
+    assert s(5).startswith(b"sizes need more scratch")
 
 
 def test_stage_names(lib):
