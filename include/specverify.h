@@ -341,9 +341,11 @@ SPECV_API specv_status_t specv_lm_head_pack_weight(const void *lm_head_weight,
  * step).  The target logits are computed on the matrix cores from the target
  * model's final hidden states, logits[b][k][v] = sum_d hidden[b][k][d] *
  * weight[v][d] (bf16 products, float32 accumulation, rounded to bf16
- * nearest-even), and the softmax statistics of each target row are taken in
- * the same kernel, from the rounded values, before the logits leave the chip;
- * the rest is specv_verify on those logits (no top-k / top-p).
+ * nearest-even).  Without top-k / top-p the softmax statistics of each target
+ * row are taken in the same kernel, from the rounded values, before the
+ * logits leave the chip, and the rest is specv_verify on those logits; with
+ * top-k / top-p (whose select needs the whole rows) the filtered
+ * specv_verify path runs on the logits the LM head wrote.
  *
  *  hidden          [B][K+1][D] bf16, device, 16-byte aligned: the hidden state
  *                  that produces target row k of request b.
@@ -353,9 +355,10 @@ SPECV_API specv_status_t specv_lm_head_pack_weight(const void *lm_head_weight,
  *  target_logits   [B][K+1][V] bf16, device output: the LM head's logits
  *                  (every row, whatever draft_len is); the draws read it.
  *  draft_logits, draft_tokens, draft_len, u, u_final, B, K, V, temperature,
- *  eos_id, out_tokens, n_emitted: as for specv_verify (bf16 draft logits).
- *  workspace       at least specv_lm_head_workspace_bytes(B, K, V, D) bytes,
- *                  16-byte aligned; no initialisation needed.
+ *  top_k, top_p, eos_id, out_tokens, n_emitted: as for specv_verify (bf16
+ *                  draft logits).
+ *  workspace       at least specv_lm_head_workspace_bytes(B, K, V, D, top_k,
+ *                  top_p) bytes, 16-byte aligned; no initialisation needed.
  *  accept_prob, residual_mass, stop_pos, path: nullable diagnostics, as for
  *                  specv_verify_debug.
  *
@@ -363,13 +366,15 @@ SPECV_API specv_status_t specv_lm_head_pack_weight(const void *lm_head_weight,
  * 64 or misaligned hidden / packed weight.  Per-request errors as specv_verify.
  * Asynchronous on `stream`; allocates nothing.
  */
-SPECV_API size_t specv_lm_head_workspace_bytes(int B, int K, int V, int D);
+SPECV_API size_t specv_lm_head_workspace_bytes(int B, int K, int V, int D, int top_k,
+                                               float top_p);
 SPECV_API specv_status_t specv_verify_lm_head(const void *hidden, const void *packed_weight,
                                               const void *draft_logits,
                                               const int32_t *draft_tokens,
                                               const int32_t *draft_len, const float *u,
                                               const float *u_final, int B, int K, int V, int D,
-                                              float temperature, int eos_id, void *target_logits,
+                                              float temperature, int top_k, float top_p,
+                                              int eos_id, void *target_logits,
                                               int32_t *out_tokens, int32_t *n_emitted,
                                               void *workspace, size_t workspace_bytes,
                                               hipStream_t stream, float *accept_prob,

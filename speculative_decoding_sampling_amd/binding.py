@@ -98,11 +98,12 @@ def load_library():
         lib.specv_lm_head_packed_weight_bytes.restype = c_size
         lib.specv_lm_head_pack_weight.argtypes = [c_vp, c_vp, c_int, c_int, c_vp]
         lib.specv_lm_head_pack_weight.restype = c_int
-        lib.specv_lm_head_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+        lib.specv_lm_head_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_float]
         lib.specv_lm_head_workspace_bytes.restype = c_size
         lib.specv_verify_lm_head.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
-                                             c_int, c_int, c_float, c_int, c_vp, c_vp, c_vp, c_vp,
-                                             c_size, c_vp, c_vp, c_vp, c_vp, c_vp]
+                                             c_int, c_int, c_float, c_int, c_float, c_int, c_vp,
+                                             c_vp, c_vp, c_vp, c_size, c_vp, c_vp, c_vp, c_vp,
+                                             c_vp]
         lib.specv_verify_lm_head.restype = c_int
         lib.specv_bench_lm_head.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_float, c_vp, c_vp,
                                             c_size, c_int, c_vp, c_vp, c_vp]
@@ -490,13 +491,14 @@ def pack_lm_head_weight(weight, stream=None):
     return PackedLmHeadWeight(data, V, D)
 
 
-def lm_head_workspace_bytes(B, K, V, D):
-    return int(load_library().specv_lm_head_workspace_bytes(int(B), int(K), int(V), int(D)))
+def lm_head_workspace_bytes(B, K, V, D, top_k=0, top_p=1.0):
+    return int(load_library().specv_lm_head_workspace_bytes(int(B), int(K), int(V), int(D),
+                                                            int(top_k), float(top_p)))
 
 
 def verify_lm_head(hidden, packed_weight, draft_logits, draft_tokens, draft_len, u, u_final,
-                   temperature=1.0, eos_id=-1, *, target_logits=None, out_tokens=None,
-                   n_emitted=None, workspace=None, debug=False, stream=None):
+                   temperature=1.0, eos_id=-1, *, top_k=0, top_p=1.0, target_logits=None,
+                   out_tokens=None, n_emitted=None, workspace=None, debug=False, stream=None):
     """The verification step fused with the target model's LM head.
 
     Shapes: hidden [B, K+1, D] bf16 (the target model's final hidden states),
@@ -534,7 +536,7 @@ def verify_lm_head(hidden, packed_weight, draft_logits, draft_tokens, draft_len,
     _check(target_logits, "target_logits", bf, (B, K + 1, V), dev)
     _check(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
     _check(n_emitted, "n_emitted", torch.int32, (B,), dev)
-    nbytes = lm_head_workspace_bytes(B, K, V, D)
+    nbytes = lm_head_workspace_bytes(B, K, V, D, top_k, top_p)
     if workspace is None:
         workspace = _workspace(dev, nbytes)
     if stream is None:
@@ -549,7 +551,8 @@ def verify_lm_head(hidden, packed_weight, draft_logits, draft_tokens, draft_len,
         diag = [res["accept_prob"], res["residual_mass"], res["stop_pos"], res["path"]]
     st = lib.specv_verify_lm_head(_ptr(hidden), _ptr(packed_weight.data), _ptr(draft_logits),
                                   _ptr(draft_tokens), _ptr(draft_len), _ptr(u), _ptr(u_final), B,
-                                  K, V, D, float(temperature), int(eos_id), _ptr(target_logits),
+                                  K, V, D, float(temperature), int(top_k), float(top_p),
+                                  int(eos_id), _ptr(target_logits),
                                   _ptr(out_tokens), _ptr(n_emitted), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(),
                                   ctypes.c_void_p(stream.cuda_stream), *[_ptr(t) for t in diag])

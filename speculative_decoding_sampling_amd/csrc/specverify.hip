@@ -278,17 +278,17 @@ struct LmLayout {
   size_t off_tpart = 0, total = 0;
 };
 
-LmLayout make_lm_layout(int B, int K, int V) {
+LmLayout make_lm_layout(int B, int K, int V, int top_k, float top_p) {
   LmLayout L;
-  L.base = make_layout(B, K, V, true, 0, 1.0f);
+  L.base = make_layout(B, K, V, true, top_k, top_p);
   L.off_tpart = L.base.total;
   L.total = align_up(L.off_tpart +
                      (size_t)B * (K + 1) * lm_head_tiles(V) * sizeof(float2));
   return L;
 }
 
-specv_status_t check_lm_sizes(int B, int K, int V, int D) {
-  const specv_status_t st = check_sizes(B, K, V, SPECV_BF16, 0, 1.0f);
+specv_status_t check_lm_sizes(int B, int K, int V, int D, int top_k, float top_p) {
+  const specv_status_t st = check_sizes(B, K, V, SPECV_BF16, top_k, top_p);
   if (st != SPECV_OK) return st;
   if (D < 1 || D % lm_head_kblock() != 0) return SPECV_EINVAL;
   if (D > SPECV_MAX_D) return SPECV_EUNSUPPORTED;
@@ -303,11 +303,11 @@ specv_status_t check_lm_sizes(int B, int K, int V, int D) {
 specv_status_t run_lm_head(const void* hidden, const void* weight, const void* draft,
                            const int32_t* tokens, const int32_t* draft_len, const float* u,
                            const float* u_final, int B, int K, int V, int D, float temperature,
-                           int eos_id, void* target_out, int32_t* out_tokens,
-                           int32_t* n_emitted, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream, float* alpha_out, double* rmass_out,
-                           int32_t* stop_out, int32_t* path_out) {
-  specv_status_t st = check_lm_sizes(B, K, V, D);
+                           int top_k, float top_p, int eos_id, void* target_out,
+                           int32_t* out_tokens, int32_t* n_emitted, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, float* alpha_out,
+                           double* rmass_out, int32_t* stop_out, int32_t* path_out) {
+  specv_status_t st = check_lm_sizes(B, K, V, D, top_k, top_p);
   if (st != SPECV_OK) return st;
   if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SPECV_EINVAL;
   if (eos_id < -1 || eos_id >= V) return SPECV_EINVAL;
@@ -324,10 +324,23 @@ specv_status_t run_lm_head(const void* hidden, const void* weight, const void* d
   if ((alpha_out && misaligned(alpha_out, 4)) || (rmass_out && misaligned(rmass_out, 8)) ||
       (stop_out && misaligned(stop_out, 4)) || (path_out && misaligned(path_out, 4)))
     return SPECV_EINVAL;
-  const LmLayout LL = make_lm_layout(B, K, V);
+  const LmLayout LL = make_lm_layout(B, K, V, top_k, top_p);
   const Layout& L = LL.base;
   if (!workspace || misaligned(workspace, 16) || workspace_bytes < LL.total)
     return SPECV_EWORKSPACE;
+  if (L.filt) {
+    // With top-k / top-p the LM head writes the target logits, then the
+    // filtered verification runs on them (its select needs the whole rows;
+    // the tile statistics of the LM head's epilogue are not used).
+    const float c = (float)(1.4426950408889634 / (double)temperature);
+    float2* tpart = reinterpret_cast<float2*>(static_cast<char*>(workspace) + LL.off_tpart);
+    if (launch_lm_head(hidden, weight, B * (K + 1), D, V, c, target_out, tpart, stream) !=
+        hipSuccess)
+      return SPECV_EHIP;
+    return run(target_out, draft, SPECV_BF16, tokens, draft_len, u, u_final, B, K, V, temperature,
+               top_k, top_p, eos_id, out_tokens, n_emitted, workspace, LL.off_tpart, stream,
+               alpha_out, rmass_out, stop_out, path_out, nullptr);
+  }
   char* ws = static_cast<char*>(workspace);
   Plan* plan = reinterpret_cast<Plan*>(ws + L.off_plan);
   float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
@@ -543,24 +556,24 @@ specv_status_t specv_lm_head_pack_weight(const void* lm_head_weight, void* packe
              : SPECV_EHIP;
 }
 
-size_t specv_lm_head_workspace_bytes(int B, int K, int V, int D) {
-  if (specv::check_lm_sizes(B, K, V, D) != SPECV_OK) return 0;
-  return specv::make_lm_layout(B, K, V).total;
+size_t specv_lm_head_workspace_bytes(int B, int K, int V, int D, int top_k, float top_p) {
+  if (specv::check_lm_sizes(B, K, V, D, top_k, top_p) != SPECV_OK) return 0;
+  return specv::make_lm_layout(B, K, V, top_k, top_p).total;
 }
 
 specv_status_t specv_verify_lm_head(const void* hidden, const void* packed_weight,
                                     const void* draft_logits, const int32_t* draft_tokens,
                                     const int32_t* draft_len, const float* u,
                                     const float* u_final, int B, int K, int V, int D,
-                                    float temperature, int eos_id, void* target_logits,
-                                    int32_t* out_tokens, int32_t* n_emitted, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream,
-                                    float* accept_prob, double* residual_mass,
-                                    int32_t* stop_pos, int32_t* path) {
+                                    float temperature, int top_k, float top_p, int eos_id,
+                                    void* target_logits, int32_t* out_tokens,
+                                    int32_t* n_emitted, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream, float* accept_prob,
+                                    double* residual_mass, int32_t* stop_pos, int32_t* path) {
   return specv::run_lm_head(hidden, packed_weight, draft_logits, draft_tokens, draft_len, u,
-                            u_final, B, K, V, D, temperature, eos_id, target_logits, out_tokens,
-                            n_emitted, workspace, workspace_bytes, stream, accept_prob,
-                            residual_mass, stop_pos, path);
+                            u_final, B, K, V, D, temperature, top_k, top_p, eos_id,
+                            target_logits, out_tokens, n_emitted, workspace, workspace_bytes,
+                            stream, accept_prob, residual_mass, stop_pos, path);
 }
 
 specv_status_t specv_bench_lm_head(const void* hidden, const void* packed_weight, int M, int D,

@@ -85,6 +85,34 @@ def test_fused_exact_parity_temperature_and_eos(T, eos_id, seed):
     assert not rep["mismatches"], rep["mismatches"][:5]
 
 
+@pytest.mark.parametrize("B,K,V,D,top_k,top_p,seed", [
+    (8, 4, 20000, 512, 50, 0.9, 71),     # the candidate select
+    (6, 3, 6000, 256, 0, 0.9, 72),       # top-p alone: the radix select
+    (3, 2, 4097, 192, 1000, 0.95, 73),   # top-k 1000 then top-p; V odd
+])
+def test_fused_exact_parity_filtered(B, K, V, D, top_k, top_p, seed):
+    # top-k / top-p on the fused call: the filtered path runs on the LM
+    # head's logits; drafts are drawn from the filtered draft rows
+    print(f"[lm_head] filtered top_k={top_k} top_p={top_p} B={B} K={K} V={V} D={D}", flush=True)
+    w = make_lm_head_workload(B, K, V, D, seed=seed, ragged=True, T=0.8)
+    tp = float(np.float32(top_p))
+    rng = np.random.default_rng(seed)
+    for b in range(B):
+        for k in range(K):
+            P, _ = O.processed_distribution(O.widen_row(w.draft[b, k], "bf16"), w.T, top_k, tp)
+            w.draft_tokens[b, k] = O.icdf(P, float(rng.random()))[0]
+    g = run_fused(w, top_k=top_k, top_p=tp)
+    t_bits = OL.lm_head_target_bits(w.hidden, w.weight)
+    assert np.array_equal(g["target_bits"], t_bits)
+    o = O.verify(t_bits, w.draft, w.draft_tokens, w.draft_len, w.u, w.u_final, w.T, top_k, tp,
+                 w.eos_id, "bf16")
+    rep = compare(g, o, w.K)
+    print(f"  requests={rep['requests']} positions={rep['positions']} flagged={rep['flagged']} "
+          f"max_alpha_err={rep['max_alpha_err']:.2e}", flush=True)
+    assert not rep["mismatches"], rep["mismatches"][:5]
+    assert rep["positions"] > 0
+
+
 def test_fused_general_inputs_logits_within_accumulation_bound():
     B, K, V, D = 3, 3, 3001, 1024
     w = make_lm_head_workload(B, K, V, D, seed=21, exact=False)
@@ -149,7 +177,8 @@ def test_fused_host_argument_errors():
         h = args["hidden"] if hidden is None else hidden
         return lib.specv_verify_lm_head(
             p(h), p(args["packed_weight"].data), p(args["draft_logits"]), p(args["draft_tokens"]),
-            p(args["draft_len"]), p(args["u"]), p(args["u_final"]), B, K, V, D_, T, -1, p(tl),
+            p(args["draft_len"]), p(args["u"]), p(args["u_final"]), B, K, V, D_, T, 0, 1.0, -1,
+            p(tl),
             p(out), p(n), p(ws), ws.numel() if ws_bytes is None else ws_bytes, s, None, None,
             None, None)
 

@@ -282,20 +282,25 @@ def test_monitor_sizes_and_bad_arguments(lib):
 
 def test_lm_head_workspace_sizes(lib):
     f = lib.specv_lm_head_workspace_bytes
-    f.argtypes = [ctypes.c_int] * 4
+    f.argtypes = [ctypes.c_int] * 5 + [ctypes.c_float]
     f.restype = ctypes.c_size_t
     g = lib.specv_workspace_bytes
     g.argtypes = [ctypes.c_int] * 5 + [ctypes.c_float]
     g.restype = ctypes.c_size_t
-    n = f(64, 4, 128256, 4096)
+    n = f(64, 4, 128256, 4096, 0, 1.0)
     # the unfiltered bf16 layout plus the LM head's tile statistics
     assert n >= g(64, 4, 128256, 1, 0, 1.0) + 64 * 5 * ((128256 + 255) // 256) * 8
     assert n % 256 == 0
-    assert f(64, 4, 128256, 4096) == f(64, 4, 128256, 64)        # D only validated
-    assert f(64, 4, 128256, 100) == 0                             # D not a multiple of 64
-    assert f(64, 4, 128256, 0) == 0
-    assert f(64, 4, 128256, 65536 + 64) == 0                      # above SPECV_MAX_D
-    assert f(0, 4, 100, 64) == 0 and f(1, 65, 100, 64) == 0 and f(1, 4, 0, 64) == 0
+    assert f(64, 4, 128256, 4096, 0, 1.0) == f(64, 4, 128256, 64, 0, 1.0)   # D only validated
+    assert f(64, 4, 128256, 100, 0, 1.0) == 0                     # D not a multiple of 64
+    assert f(64, 4, 128256, 0, 0, 1.0) == 0
+    assert f(64, 4, 128256, 65536 + 64, 0, 1.0) == 0              # above SPECV_MAX_D
+    assert f(0, 4, 100, 64, 0, 1.0) == 0 and f(1, 65, 100, 64, 0, 1.0) == 0
+    assert f(1, 4, 0, 64, 0, 1.0) == 0
+    # with top-k / top-p: the filtered layout plus the tile statistics
+    nf = f(64, 4, 128256, 4096, 50, 0.9)
+    assert nf >= g(64, 4, 128256, 1, 50, 0.9) + 64 * 5 * ((128256 + 255) // 256) * 8
+    assert f(64, 4, 128256, 4096, 0, 0.9) > 0 and f(64, 4, 128256, 4096, -1, 0.9) == 0
 
 
 def test_lm_head_packed_weight_sizes_and_validation(lib):
@@ -326,14 +331,14 @@ def test_lm_head_packed_weight_sizes_and_validation(lib):
 def test_lm_head_validation_returns_before_any_gpu_work(lib):
     v = lib.specv_verify_lm_head
     vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-    v.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, vp, vp,
+    v.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, cf, ci, vp, vp, vp, vp,
                   ctypes.c_size_t, vp, vp, vp, vp, vp]
     v.restype = ci
     d = ctypes.c_void_p(4096)
-    base = [d, d, d, d, d, d, d, 4, 4, 1000, 64, 1.0, -1, d, d, d, d, 1 << 30, None,
+    base = [d, d, d, d, d, d, d, 4, 4, 1000, 64, 1.0, 0, 1.0, -1, d, d, d, d, 1 << 30, None,
             None, None, None, None]
-    idx = {"hidden": 0, "weight": 1, "B": 7, "K": 8, "V": 9, "D": 10, "T": 11, "eos": 12,
-           "out": 13, "ws": 16, "ws_bytes": 17}
+    idx = {"hidden": 0, "weight": 1, "B": 7, "K": 8, "V": 9, "D": 10, "T": 11, "top_k": 12,
+           "top_p": 13, "eos": 14, "out": 15, "ws": 18, "ws_bytes": 19}
 
     def call(**kw):
         args = list(base)
@@ -354,3 +359,5 @@ def test_lm_head_validation_returns_before_any_gpu_work(lib):
     assert call(ws_bytes=16) == 2
     assert call(ws=None) == 2
     assert call(D=65536 + 64) == 4                                # SPECV_EUNSUPPORTED
+    assert call(top_k=-1) == 1 and call(top_p=0.0) == 1
+    assert call(top_k=50, top_p=0.9, ws_bytes=16) == 2            # filtered: workspace
