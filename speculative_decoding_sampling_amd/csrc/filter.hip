@@ -326,6 +326,281 @@ __device__ __forceinline__ void lds_bitonic_desc(uint64_t* a, int n) {
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// filter_merge_wave: the merge of one row by one wave, four rows per
+// workgroup, for the usual row: at most kWaveCand candidates (held in
+// registers, kWaveCand / 64 per lane) and at most 64 of them >= tau_k (the
+// top-k and its ties).  Nothing waits at a workgroup barrier.
+//  - chunk offsets: one lane per chunk, a wave scan;
+//  - gather: every load first, the chunk of flat index f by binary search
+//    over the offsets (in this wave's LDS);
+//  - tau_k = the largest 32-bit key v with #{keys >= v} >= k, bit by bit
+//    from the top (32 rounds of compare-and-count, wave sums on DPP);
+//  - the keys >= tau_k, one per lane, sorted descending in registers; top-p
+//    in float64 by a lane-order scan and ballots; the kept list sorted by id
+//    in registers.
+// A row outside those bounds (a chunk over its slot, more candidates, more
+// than 64 keys >= tau_k) is marked kStatusRedo and merged by
+// filter_merge_kernel, which runs next and leaves every other row alone.
+constexpr int kWaveCand = 2048;
+constexpr int kWavePer = kWaveCand / kWave;           // candidates per lane
+constexpr int kStatusRedo = 3;                        // internal: the block merge takes the row
+constexpr int kMergeWaves = kFiltThreads / kWave;     // rows per workgroup
+
+// Sum of an int over the wave on DPP (quad swaps, half-row and row
+// mirrors), then the four row sums read as scalars: short latency, no LDS.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<0xb1>(v);                               // quad_perm [1,0,3,2]
+  v += dpp_i<0x4e>(v);                               // quad_perm [2,3,0,1]
+  v += dpp_i<0x141>(v);                              // row_half_mirror
+  v += dpp_i<0x140>(v);                              // row_mirror
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+__global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
+    const int* __restrict__ draft_len, int B, int K, int nch, int cap, int row_stride,
+    int top_k, float top_p, double invT, const uint64_t* __restrict__ cand,
+    const int* __restrict__ counts, FiltRow* __restrict__ rows, Kept* __restrict__ kept) {
+  __shared__ double tbl[SPECV_EXP64_N];
+  __shared__ uint64_t s_buf[kMergeWaves][kWave];
+  __shared__ uint32_t s_sel[kMergeWaves][4 * kWave];
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  const int R = 2 * K + 1;
+  const int rr = blockIdx.x * kMergeWaves + wid;
+  exp64_stage_table<kFiltThreads>(tbl);
+  __syncthreads();                                   // the only barrier: the exp table
+  if (rr >= B * R) return;
+  const int r = rr % R, b = rr / R;
+  // the row's chunk counts are requested with draft_len (lane c = chunk c)
+  const int cnt = lane < nch ? counts[(size_t)rr * nch + lane] : 0;
+  const int nb = draft_len ? draft_len[b] : 0;       // null: no drafts (sampling)
+  if (nb < 0 || nb > K) return;
+  bool is_target;
+  int k;
+  if (!row_needed(r, K, nb, is_target, k)) return;
+
+  FiltRow out;
+  out.pad = 0;
+  // chunk offsets and the candidate total
+  int n = 0, over = 0;
+  if (lane < nch) {
+    const int slot = lane == nch - 1 ? row_stride - (nch - 1) * cap : cap;
+    over = cnt > slot;
+    n = min(cnt, slot);
+  }
+  int incl = n;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  const int n_all = __shfl(incl, kWave - 1, kWave);
+  // lanes per chunk: lane l reads chunk l / q, its entries l % q, l % q + q, ...
+  const int q = kWave / max(nch, 1);
+  int nmax = n;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) nmax = max(nmax, __shfl_xor(nmax, o, kWave));
+  if (__ballot(over) != 0 || nmax > q * kWavePer) {  // the block merge takes it
+    if (lane == 0) {
+      out.m = 0.f;
+      out.tau = 0.f;
+      out.S = 0.0;
+      out.count = 0;
+      out.status = kStatusRedo;
+      rows[rr] = out;
+    }
+    return;
+  }
+  if (n_all == 0) {                                  // no finite logit in the row
+    if (lane == 0) {
+      out.m = -INFINITY;
+      out.tau = INFINITY;
+      out.S = 0.0;
+      out.count = 0;
+      out.status = 2;
+      rows[rr] = out;
+    }
+    return;
+  }
+  // gather the key halves (a candidate is key << 32 | ~id): every address is
+  // arithmetic, every load unconditional (clamped into the chunk's slot), so
+  // the loads leave back to back; entries past the chunk's count read 0,
+  // below every key
+  const int c_me = min(lane / q, nch - 1), s_me = lane % q;
+  const bool lane_on = lane < q * nch;
+  const int n_me = lane_on ? __shfl(n, c_me, kWave) : 0;
+  const uint64_t* rowc = cand + (size_t)rr * row_stride;
+  const uint32_t* rowh = reinterpret_cast<const uint32_t*>(rowc);
+  const int base = c_me * cap;
+  uint32_t key[kWavePer];
+#pragma unroll
+  for (int i = 0; i < kWavePer; ++i)
+    key[i] = rowh[2 * (base + min(s_me + q * i, max(n_me - 1, 0))) + 1];
+#pragma unroll
+  for (int i = 0; i < kWavePer; ++i)
+    if (s_me + q * i >= n_me) key[i] = 0u;
+
+  // tau_k, the largest key v with #{keys >= v} >= kk.  T0 = the kk-th
+  // largest of the 64 lane maxima is a lower bound (kk lanes hold a key
+  // >= T0); the keys >= T0 (usually a few more than kk) are compacted, at
+  // most four per lane, and tau_k is found among them bit by bit from the
+  // top.  With more than 256 such keys, among all of them.
+  const int kk = min(top_k, n_all);
+  uint32_t lmax = 0u;
+#pragma unroll
+  for (int i = 0; i < kWavePer; ++i) lmax = max(lmax, key[i]);
+  uint32_t t0 = 0u, kmax;
+  if (kk <= kWave) {
+    const uint32_t sm = wave_sort_desc(lmax);
+    t0 = (uint32_t)__shfl((int)sm, kk - 1, kWave);
+    kmax = (uint32_t)__shfl((int)sm, 0, kWave);
+  } else {
+    kmax = lmax;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, kWave));
+  }
+  // tau_k lies in [t0, kmax]: the bits above their highest difference are
+  // known, the walk starts below them
+  const int top = 32 - __clz((int)(t0 ^ kmax));     // bits left to decide
+  const uint32_t known = top >= 32 ? 0u : kmax & (0xffffffffu << top);
+  int c0 = 0;
+#pragma unroll
+  for (int i = 0; i < kWavePer; ++i) c0 += key[i] >= t0 && key[i] > 0u ? 1 : 0;
+  int incl0 = c0;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl0, o, kWave);
+    if (lane >= o) incl0 += y;
+  }
+  const int nt = __shfl(incl0, kWave - 1, kWave);
+  uint32_t tk = known;
+  int L = nt;                                        // #{keys >= tk} (every key >= t0 here)
+  if (nt <= 4 * kWave) {
+    int qpos = incl0 - c0;
+#pragma unroll
+    for (int i = 0; i < kWavePer; ++i)
+      if (key[i] >= t0 && key[i] > 0u) s_sel[wid][qpos++] = key[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t k4[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int e = lane + kWave * r4;
+      k4[r4] = e < nt ? s_sel[wid][e] : 0u;
+    }
+#pragma unroll 1
+    for (int bit = top - 1; bit >= 0; --bit) {
+      const uint32_t tryv = tk | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) c += k4[r4] >= tryv ? 1 : 0;
+      c = wave_sum_i(c);
+      if (c >= kk) {
+        tk = tryv;
+        L = c;
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int bit = top - 1; bit >= 0; --bit) {
+      const uint32_t tryv = tk | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < kWavePer; ++i) c += key[i] >= tryv ? 1 : 0;
+      c = wave_sum_i(c);
+      if (c >= kk) {
+        tk = tryv;
+        L = c;
+      }
+    }
+  }
+  if (L > kWave) {                                   // the top-k and its ties exceed a wave
+    if (lane == 0) {
+      out.m = 0.f;
+      out.tau = 0.f;
+      out.S = 0.0;
+      out.count = 0;
+      out.status = kStatusRedo;
+      rows[rr] = out;
+    }
+    return;
+  }
+  // the keys >= tau_k: their candidate words' indices compacted one per
+  // lane, then each lane reads its whole word (one round trip); sorted
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kWavePer; ++i) mine += key[i] >= tk ? 1 : 0;
+  int pincl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(pincl, o, kWave);
+    if (lane >= o) pincl += y;
+  }
+  int pos = pincl - mine;
+#pragma unroll
+  for (int i = 0; i < kWavePer; ++i)
+    if (key[i] >= tk) reinterpret_cast<int*>(s_buf[wid])[pos++] = base + s_me + q * i;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint64_t x = 0ull;                                 // 0 sorts last
+  if (lane < L) x = rowc[reinterpret_cast<int*>(s_buf[wid])[lane]];
+  x = wave_sort_desc(x);
+
+  // top-p over the sorted prefix, float64 (lane i holds entry i)
+  const uint32_t k32 = lane < L ? (uint32_t)(x >> 32) : 0u;
+  const float m = unkey((uint32_t)(__shfl((long long)x, 0, kWave) >> 32));
+  const double md = (double)m;
+  const bool in = lane < L;
+  const double wgt = in ? exp64(((double)unkey(k32) - md) * invT, tbl) : 0.0;
+  double run = wgt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(run, o, kWave);
+    if (lane >= o) run += y;
+  }
+  const double tot = __shfl(run, kWave - 1, kWave);
+  uint32_t tau = tk;
+  int Lk = L;
+  if (top_p < 1.0f) {
+    // M = first sorted index whose running mass reaches top_p of the total
+    const uint64_t hit = __ballot(in && run / tot >= (double)top_p);
+    const int M = hit ? __ffsll((unsigned long long)hit) - 1 : L - 1;
+    tau = (uint32_t)__shfl((int)k32, M, kWave);
+    const uint64_t below = __ballot(in && k32 < tau);
+    Lk = below ? __ffsll((unsigned long long)below) - 1 : L;
+  }
+  const double keep_sum = wave_sum(lane < Lk ? wgt : 0.0);
+
+  // the kept tokens by id ascending: key (~id << 32 | logit bits), descending
+  uint64_t y = 0ull;
+  if (lane < Lk) {
+    const uint32_t id = 0xffffffffu - (uint32_t)x;
+    y = ((uint64_t)(0xffffffffu - id) << 32) | (uint64_t)__float_as_uint(unkey(k32));
+  }
+  y = wave_sort_desc(y);
+  if (lane < Lk) {
+    Kept e;
+    e.id = (int)(0xffffffffu - (uint32_t)(y >> 32));
+    e.z = __uint_as_float((uint32_t)y);
+    kept[(size_t)rr * kKeptCap + lane] = e;
+  }
+  if (lane == 0) {
+    out.m = m;
+    out.tau = unkey(tau);
+    out.S = keep_sum;
+    out.count = Lk;
+    out.status = 0;
+    rows[rr] = out;
+  }
+}
+
 // The candidate list and the radix histogram share their LDS with the
 // general select, which a row runs instead when a chunk had more candidates
 // than its slot (massive ties at a chunk's threshold).
@@ -357,6 +632,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   bool is_target;
   int k;
   if (!row_needed(r, K, nb, is_target, k)) return;
+  if (rows[rr].status != kStatusRedo) return;        // uniform: merged by its wave already
 
   // the chunks' candidate counts, clipped to their slots, and their offsets
   // in the row's list: one wave, lane c = chunk c (nch <= kFiltMaxChunks)
@@ -920,7 +1196,12 @@ hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mid && (e = hipEventRecord(mid, stream)) != hipSuccess) return e;
-  const dim3 grid((unsigned)((size_t)B * (2 * K + 1)));
+  const size_t nrows = (size_t)B * (2 * K + 1);
+  filter_merge_wave_kernel<<<dim3((unsigned)((nrows + kMergeWaves - 1) / kMergeWaves)),
+                             dim3(kFiltThreads), 0, stream>>>(
+      draft_len, B, K, nch, cap, stride, top_k, top_p, invT, cand, counts, rows, kept);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 grid((unsigned)nrows);
   if (bf16)
     filter_merge_kernel<bf16_t><<<grid, dim3(kFiltThreads), 0, stream>>>(
         static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V, nch,
