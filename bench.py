@@ -48,8 +48,14 @@ ROW_STATS_TRAFFIC = {"sources_sha256_16": "f0804ab9644a5c5b", "bytes": 148139654
 # The same for one LM-head launch at M=320, D=4096, V=128256 (FETCH_SIZE and
 # WRITE_SIZE of the lm_head op, scaled by the copy calibration taken with the
 # row-statistics figure).
-# And for one top-k candidate pass of workload 4 (B=256, K=8, V=152064 fp32).
-FILTER_TRAFFIC = {"sources_sha256_16": "54dd29cf094e0150", "bytes": 2687313229}
+# And for the first pass of a filtered path, keyed by workload: the top-k
+# candidate pass at B=256, K=8, V=152064 fp32 (top-k 50, top-p 0.9), the
+# radix select at B=64, K=4, V=128256 bf16 (top-p 0.9 alone).
+FILTER_SOURCES = ("filter.hip", "radix_select.h", "common.h")
+FILTER_TRAFFIC = {
+    "B256_K8_V152064_f32_topk50_topp0.9": {"sources_sha256_16": "54dd29cf094e0150",
+                                           "bytes": 2687313229},
+}
 LM_HEAD_TRAFFIC = {"sources_sha256_16": "e410f425f4f93b97", "bytes": 1180262001}
 WORKLOAD = 3
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,K=4,V=128k"
@@ -506,6 +512,10 @@ def main():
                          "verification fused with a D=4096 target LM head; rates: the "
                          "acceptance diagnostics of the same workload; the last three are "
                          "reported for reference")
+    ap.add_argument("--top-k", type=int, default=None,
+                    help="override the verify workload's top-k (0 = off); reported separately")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="override the verify workload's top-p (1.0 = off); reported separately")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -519,8 +529,9 @@ def main():
 
     if args.sets is None:
         args.sets = 1 if args.workload == 4 else 4
-    if args.op != "verify" and args.workload != WORKLOAD:
-        log("--workload applies to the verify op only")
+    if args.op != "verify" and (args.workload != WORKLOAD or args.top_k is not None
+                                or args.top_p is not None):
+        log("--workload, --top-k and --top-p apply to the verify op only")
         sys.exit(2)
     if args.op == "sample":
         return bench_sample(args)
@@ -542,7 +553,19 @@ def main():
     torch.cuda.set_device(dev)
 
     wl = args.workload
-    spec = WORKLOADS[wl]
+    spec = dict(WORKLOADS[wl])
+    overridden = args.top_k is not None or args.top_p is not None
+    if overridden:
+        # the same logits under other filter settings: a separate line, never
+        # the headline
+        if args.top_k is not None:
+            spec["top_k"] = args.top_k
+        if args.top_p is not None:
+            spec["top_p"] = args.top_p
+        base = spec["name"].split("_topk")[0]
+        spec["name"] = base + "".join(
+            f"_{n}{v:g}" for n, v, off in (("topk", spec["top_k"], 0), ("topp", spec["top_p"], 1.0))
+            if v != off)
     filtered = 0 < spec["top_k"] < spec["V"] or spec["top_p"] < 1.0
     sets, hosts = [], []
     for i in range(args.sets):
@@ -551,9 +574,10 @@ def main():
         if filtered:
             # placeholder drafts, replaced below by draws from the processed
             # draft rows made on the GPU by specv_sample
-            w = make_workload(wl, seed=seed, draft_sampler=lambda z, T, k, p, x: 0)
+            w = make_workload(wl, seed=seed, draft_sampler=lambda z, T, k, p, x: 0,
+                              top_k=spec["top_k"], top_p=spec["top_p"])
         else:
-            w = make_workload(wl, seed=seed)
+            w = make_workload(wl, seed=seed, top_k=spec["top_k"], top_p=spec["top_p"])
         hosts.append(w)
         a = upload(w, dev)
         if filtered:
@@ -680,13 +704,15 @@ def main():
         log(f"copy calibration: 5 copies of {args.copy_calibration_mib} MiB")
 
     if filtered:
-        # The dominant kernel is the top-k candidate pass (one read of every
-        # needed row); its duration is the per-call stage mean above.
-        dominant = "filter_cand"
+        # The dominant kernel is the path's first pass, the top-k candidate
+        # pass or the radix select (each reads every needed row); its duration
+        # is the per-call stage mean above.
+        dominant = names[0]
         k1_us = stage_us[dominant]
-        traffic = (FILTER_TRAFFIC["bytes"] if wl == 4 and sources_hash(("filter.hip", "common.h"))
-                   == FILTER_TRAFFIC["sources_sha256_16"] else None)
-        log(f"filter_cand: {k1_us:.2f} us/launch (stage mean)")
+        tr = FILTER_TRAFFIC.get(spec["name"])
+        traffic = (tr["bytes"] if tr and sources_hash(FILTER_SOURCES) == tr["sources_sha256_16"]
+                   else None)
+        log(f"{dominant}: {k1_us:.2f} us/launch (stage mean)")
     else:
         # The dominant kernel alone, for the roofline: a burst of row-statistics
         # launches cycling over the input sets between two events on the stream.

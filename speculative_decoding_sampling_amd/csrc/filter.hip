@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "exp64.h"
+#include "hist_select.h"
 #include "radix_select.h"
 
 namespace specv {
@@ -916,13 +917,14 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
 // ---------------------------------------------------------------------------
 // The residual or bonus draw streamed over a whole filtered row pair, for a
 // target row whose kept set has no list (more than kKeptCap tokens).  Chunks
-// of 2048 tokens, wave w taking chunks w, w + 4, ...; lane l holds tokens
-// c0 + 512 j + 8 l .. + 7 (j < 4), so a chunk's tokens in order are (j, lane,
-// element).  Weights in float64 from the rows' FiltRows: p = e_t / S_t on
-// the target's kept tokens, and after a rejection max(p - q, 0) with q the
-// same over the draft's kept tokens.  Chunk masses go to LDS; every wave then
-// finds the chunk holding t = u_final * total by a blocked prefix of its own,
-// and wave 0 scans inside that chunk.
+// of 2048 tokens; in a chunk, lane l of a wave holds tokens c0 + 512 j + 8 l
+// .. + 7 (j < 4), so the chunk's tokens in order are (j, lane, element).
+// Weights in float64 from the rows' FiltRows: p = e_t / S_t on the target's
+// kept tokens, and after a rejection max(p - q, 0) with q the same over the
+// draft's kept tokens.  The chunk pass (one wave per chunk, the whole chip)
+// writes each chunk's mass; the draw copies them to LDS, every wave finds the
+// chunk holding t = u_final * total by a blocked prefix of its own, and wave
+// 0 scans inside that chunk.
 constexpr int kStreamSub = kWave * 8;                  // 512 tokens per sub-block
 constexpr int kStreamChunk = 4 * kStreamSub;           // 2048 tokens per chunk
 
@@ -940,13 +942,86 @@ __device__ __forceinline__ double kept_prob(float z, const FiltRow& fr, double i
   return exp64(((double)z - (double)fr.m) * invT, tbl) / fr.S;
 }
 
+// Element i (0..7) of eight registers, by a select tree (no indexed access).
+__device__ __forceinline__ float pick8(const float* z, uint32_t i) {
+  const float a = (i & 1u) ? z[1] : z[0], b = (i & 1u) ? z[3] : z[2];
+  const float c = (i & 1u) ? z[5] : z[4], d = (i & 1u) ? z[7] : z[6];
+  const float ab = (i & 2u) ? b : a, cd = (i & 2u) ? d : c;
+  return (i & 4u) ? cd : ab;
+}
+
+// One chunk's masses, summed in a fixed order (per lane j then element, then
+// the wave): .x the first attempt's (the residual after a rejection, else p),
+// .y p alone (the fall-back when the residual has no mass).  A token outside
+// the target's kept set adds exactly zero to both (p = 0, so p - q <= 0), so
+// each lane visits only its kept tokens, in element order: the same sums,
+// with far fewer exps when the kept set is a small share of the row.
+template <typename T>
+__device__ __forceinline__ double2 chunk_masses(const T* __restrict__ trow,
+                                                const T* __restrict__ drow, int V, long c0,
+                                                bool rej, const FiltRow& tr, const FiltRow& dr,
+                                                double invT, const double* tbl) {
+  const int lane = threadIdx.x % kWave;
+  double acc_r = 0.0, acc_p = 0.0;
+  for (int j = 0; j < 4; ++j) {
+    const long e0 = c0 + j * kStreamSub + lane * 8;
+    float zt[8], zd[8];
+    load8_checked(trow, e0, V, zt);
+    if (rej) load8_checked(drow, e0, V, zd);
+    uint32_t km = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) km |= (zt[i] >= tr.tau && zt[i] != -INFINITY) ? 1u << i : 0u;
+    while (km) {
+      const uint32_t i = (uint32_t)__builtin_ctz(km);
+      km &= km - 1u;
+      const double p = kept_prob(pick8(zt, i), tr, invT, tbl);
+      acc_p += p;
+      if (rej) {
+        const double x = p - kept_prob(pick8(zd, i), dr, invT, tbl);
+        acc_r += x > 0.0 ? x : 0.0;
+      }
+    }
+  }
+  acc_p = wave_sum(acc_p);
+  acc_r = rej ? wave_sum(acc_r) : acc_p;
+  return make_double2(acc_r, acc_p);
+}
+
+// The chunk pass of the streamed draw: wave g of the grid takes chunk
+// g % nch of request g / nch, when that request draws from a target row with
+// no kept list.
+template <typename T>
+__global__ __launch_bounds__(kFiltThreads) void stream_chunks_kernel(
+    const T* __restrict__ tgt, const T* __restrict__ dft, int B, int K, int V, int nch,
+    double invT, const Plan* __restrict__ plan, const FiltRow* __restrict__ rows,
+    double2* __restrict__ cmass) {
+  __shared__ double tbl[SPECV_EXP64_N];
+  exp64_stage_table<kFiltThreads>(tbl);
+  __syncthreads();
+  const long g = (long)blockIdx.x * (kFiltThreads / kWave) + threadIdx.x / kWave;
+  const int b = (int)(g / nch), c = (int)(g % nch);
+  if (b >= B) return;
+  const Plan pl = plan[b];
+  if (pl.path != kPathReject && pl.path != kPathBonus) return;   // uniform per wave
+  const int R = 2 * K + 1;
+  const FiltRow tr = rows[(size_t)b * R + pl.trow];
+  if (tr.count <= kKeptCap) return;                  // the list draw serves it
+  const bool rej = pl.path == kPathReject;
+  FiltRow dr;
+  dr.m = 0.f; dr.tau = 0.f; dr.S = 1.0; dr.count = 0; dr.status = 0; dr.pad = 0;
+  if (rej) dr = rows[(size_t)b * R + K + 1 + pl.drow];
+  const T* trow = tgt + target_row_off(b, pl.trow, K, V);
+  const T* drow = rej ? dft + draft_row_off(b, pl.drow, K, V) : trow;
+  const double2 r = chunk_masses(trow, drow, V, (long)c * kStreamChunk, rej, tr, dr, invT, tbl);
+  if (threadIdx.x % kWave == 0) cmass[(size_t)b * nch + c] = r;
+}
+
 template <typename T>
 __device__ void stream_draw(const T* __restrict__ trow, const T* __restrict__ drow, int V,
                             bool rej, const FiltRow& tr, const FiltRow& dr, double invT,
-                            const double* tbl, double uf, double* csum, int& y_out,
-                            double& rmass_out) {
+                            const double* tbl, double uf, const double2* __restrict__ cm,
+                            double* csum, int& y_out, double& rmass_out) {
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  constexpr int kWaves = kFiltThreads / kWave;
   const int nch = (V + kStreamChunk - 1) / kStreamChunk;
   auto weights = [&](long e0, bool resid, double* w) {
     float zt[8], zd[8];
@@ -966,17 +1041,7 @@ __device__ void stream_draw(const T* __restrict__ trow, const T* __restrict__ dr
   double total = 0.0, t = 0.0, pre = 0.0;
   int cstar = -1, clast = -1;
   for (int attempt = 0; attempt < 2; ++attempt) {
-    for (int c = wid; c < nch; c += kWaves) {
-      double acc = 0.0;
-      for (int j = 0; j < 4; ++j) {
-        double w[8];
-        weights((long)c * kStreamChunk + j * kStreamSub + lane * 8, resid, w);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc += w[i];
-      }
-      acc = wave_sum(acc);
-      if (lane == 0) csum[c] = acc;
-    }
+    for (int c = threadIdx.x; c < nch; c += kFiltThreads) csum[c] = attempt == 0 ? cm[c].x : cm[c].y;
     __syncthreads();
     // every wave: blocked prefix over the chunk masses (lane l owns chunks
     // [l q, l q + q)), the same in every wave
@@ -1078,7 +1143,8 @@ template <typename T>
 __global__ __launch_bounds__(kFiltThreads) void sample_list_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const float* __restrict__ u_final,
     int K, int V, double invT, const Plan* __restrict__ plan, const FiltRow* __restrict__ rows,
-    const Kept* __restrict__ kept, int* __restrict__ out_tokens, double* __restrict__ rmass_out) {
+    const Kept* __restrict__ kept, const double2* __restrict__ cmass, int* __restrict__ out_tokens,
+    double* __restrict__ rmass_out) {
   __shared__ double tbl[SPECV_EXP64_N];
   __shared__ double dl[kFiltThreads / kWave];
   __shared__ int il[kFiltThreads / kWave];
@@ -1099,8 +1165,9 @@ __global__ __launch_bounds__(kFiltThreads) void sample_list_kernel(
   if (tr.count > kKeptCap) {                         // uniform: no list for this row
     int y;
     double rm;
+    const int nch = (V + kStreamChunk - 1) / kStreamChunk;
     stream_draw(tgt + target_row_off(b, pl.trow, K, V), drow, V, rej, tr, dr, invT, tbl,
-                (double)u_final[b], csum, y, rm);
+                (double)u_final[b], cmass + (size_t)b * nch, csum, y, rm);
     if (threadIdx.x == 0) {
       out_tokens[(size_t)b * (K + 1) + pl.stop] = y;
       if (rmass_out) rmass_out[b] = rm;
@@ -1242,13 +1309,38 @@ __global__ __launch_bounds__(kSelThreads) void filter_rows_kernel(
   if (threadIdx.x == 0) rows[rr] = o;
 }
 
+// bfloat16 rows: the histogram select (hist_select.h), 142 KB of LDS, one
+// workgroup per CU.
+__global__ __launch_bounds__(kSelThreads) void filter_rows_hist_kernel(
+    const bf16_t* __restrict__ tgt, const bf16_t* __restrict__ dft,
+    const int* __restrict__ draft_len, int K, int V, int top_k, float top_p, double invT,
+    FiltRow* __restrict__ rows, Kept* __restrict__ kept) {
+  __shared__ HistPool pool;
+  __shared__ HistAux aux;
+  __shared__ double tbl[SPECV_EXP64_N];
+  const int R = 2 * K + 1;
+  const int rr = blockIdx.x;
+  const int r = rr % R, b = rr / R;
+  const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
+  if (nb < 0 || nb > K) return;
+  bool is_target;
+  int k;
+  if (!row_needed(r, K, nb, is_target, k)) return;
+  for (int i = threadIdx.x; i < SPECV_EXP64_N; i += kSelThreads) tbl[i] = kExp64Table[i];
+  const bf16_t* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
+  // the histogram pass's first barrier makes the table visible
+  const FiltRow o = select_row_hist<kSelThreads>(row, V, top_k, top_p, invT, tbl, &pool, &aux,
+                                                 kept + (size_t)rr * kKeptCap);
+  if (threadIdx.x == 0) rows[rr] = o;
+}
+
 hipError_t launch_filter_rows(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                               int B, int K, int V, int top_k, float top_p, double invT,
                               FiltRow* rows, Kept* kept, hipStream_t stream) {
   const size_t blocks = (size_t)B * (2 * K + 1);
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   if (bf16)
-    filter_rows_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kSelThreads), 0, stream>>>(
+    filter_rows_hist_kernel<<<dim3((unsigned)blocks), dim3(kSelThreads), 0, stream>>>(
         static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V,
         top_k, top_p, invT, rows, kept);
   else
@@ -1258,19 +1350,32 @@ hipError_t launch_filter_rows(bool bf16, const void* tgt, const void* dft, const
   return hipGetLastError();
 }
 
+int stream_chunks(int V) { return (V + kStreamChunk - 1) / kStreamChunk; }
+
 hipError_t launch_sample_list(bool bf16, const void* tgt, const void* dft, const float* u_final,
                               int B, int K, int V, double invT, const Plan* plan,
-                              const FiltRow* rows, const Kept* kept, int* out_tokens,
-                              double* rmass_out, hipStream_t stream) {
-  if ((V + kStreamChunk - 1) / kStreamChunk > kMaxSampChunks) return hipErrorInvalidConfiguration;
-  if (bf16)
+                              const FiltRow* rows, const Kept* kept, double2* cmass,
+                              int* out_tokens, double* rmass_out, hipStream_t stream) {
+  const int nch = stream_chunks(V);
+  if (nch > kMaxSampChunks) return hipErrorInvalidConfiguration;
+  constexpr int kWavesPer = kFiltThreads / kWave;
+  const size_t blocks = ((size_t)B * nch + kWavesPer - 1) / kWavesPer;
+  if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  if (bf16) {
+    stream_chunks_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
+        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), B, K, V, nch, invT,
+        plan, rows, cmass);
     sample_list_kernel<bf16_t><<<dim3(B), dim3(kFiltThreads), 0, stream>>>(
         static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), u_final, K, V, invT,
-        plan, rows, kept, out_tokens, rmass_out);
-  else
+        plan, rows, kept, cmass, out_tokens, rmass_out);
+  } else {
+    stream_chunks_kernel<float><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
+        static_cast<const float*>(tgt), static_cast<const float*>(dft), B, K, V, nch, invT, plan,
+        rows, cmass);
     sample_list_kernel<float><<<dim3(B), dim3(kFiltThreads), 0, stream>>>(
         static_cast<const float*>(tgt), static_cast<const float*>(dft), u_final, K, V, invT, plan,
-        rows, kept, out_tokens, rmass_out);
+        rows, kept, cmass, out_tokens, rmass_out);
+  }
   return hipGetLastError();
 }
 

@@ -50,10 +50,14 @@ struct SelectLds {
   int nlist;
 };
 
-// A mass in 2^-64 units: sum(hi) 2^40 + sum(lo), each part at most V 2^40.
+// A mass in 2^-64 units, h 2^40 + l, rounded once to the nearest double.
+// With h <= V 2^24 and l <= V 2^40 (V <= 2^22), it is (h + l_hi) 2^40 + l_lo
+// with l = l_hi 2^40 + l_lo: both terms are exact doubles (h + l_hi < 2^53,
+// l_lo < 2^40), and one fma adds them with a single rounding -- the correctly
+// rounded value of the exact sum, as a 128-bit conversion would give.
 __device__ __forceinline__ double fixed_to_double(unsigned long long h, unsigned long long l) {
-  const unsigned __int128 x = ((unsigned __int128)h << 40) + (unsigned __int128)l;
-  return (double)x * 0x1p-64;
+  const unsigned long long H = h + (l >> 40), L = l & ((1ull << 40) - 1ull);
+  return fma((double)H, 0x1p40, (double)L) * 0x1p-64;
 }
 // w in (0, 1] split exactly into floor(w 2^24) and floor(frac(w 2^24) 2^40).
 __device__ __forceinline__ void fixed_parts(double w, unsigned long long& h, unsigned long long& l) {
@@ -90,10 +94,11 @@ __device__ __forceinline__ void for_each_logit(const T* __restrict__ row, int V,
 }
 
 // Exclusive scan over the block's threads (thread order) of a count and a
-// two-part mass; also returns the block totals.
-template <int NT>
+// two-part mass; also returns the block totals.  S holds the wave totals
+// (wc, wh, wl; one entry per wave).
+template <int NT, typename S>
 __device__ __forceinline__ void block_scan3(uint32_t c, unsigned long long h, unsigned long long l,
-                                            SelectLds* s, uint32_t& ec, unsigned long long& eh,
+                                            S* s, uint32_t& ec, unsigned long long& eh,
                                             unsigned long long& el, uint32_t& tc,
                                             unsigned long long& th, unsigned long long& tl) {
   constexpr int W = NT / kWave;
@@ -271,6 +276,38 @@ struct RowSelect {
   }
 };
 
+// The kept list from its (id << 32 | logit bits) entries in LDS, any order:
+// an ascending bitonic sort by id over the next power of two (padding sorts
+// last, within kKeptCap entries), then the first n written out.  The caller
+// has made the entries visible (a barrier after the last append).
+template <int NT>
+__device__ void sort_kept_by_id(unsigned long long* ids, int n, Kept* __restrict__ kept) {
+  int P = 1;
+  while (P < n) P <<= 1;
+  for (int i = n + threadIdx.x; i < P; i += NT) ids[i] = ~0ull;
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < P / 2; i += NT) {
+        const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const unsigned long long a = ids[lo], b = ids[hi];
+        if ((a > b) == up) {
+          ids[lo] = b;
+          ids[hi] = a;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += NT) {
+    Kept e;
+    e.id = (int)(ids[i] >> 32);
+    e.z = __uint_as_float((uint32_t)ids[i]);
+    kept[i] = e;
+  }
+}
+
 // The whole select for one row.  Writes the kept list (sorted by id) when
 // the kept set has at most kKeptCap tokens; returns the row's FiltRow.
 // top_k: 0 or >= V is off; top_p: 1 is off (at least one is on).  NT is the
@@ -365,33 +402,7 @@ __device__ FiltRow select_row(const T* __restrict__ row, int V, bool bf16, int t
       mh = s->kept_h;
       ml = s->kept_l;
     }
-    if (list) {
-      // ascending bitonic sort by id over the next power of two (padding sorts last)
-      int P = 1;
-      while (P < (int)cnt) P <<= 1;
-      for (int i = (int)cnt + threadIdx.x; i < P; i += NT) ids[i] = ~0ull;
-      for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size / 2; stride > 0; stride >>= 1) {
-          __syncthreads();
-          for (int i = threadIdx.x; i < P / 2; i += NT) {
-            const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
-            const bool up = (lo & size) == 0;
-            const unsigned long long a = ids[lo], b = ids[hi];
-            if ((a > b) == up) {
-              ids[lo] = b;
-              ids[hi] = a;
-            }
-          }
-        }
-      }
-      __syncthreads();
-      for (int i = threadIdx.x; i < (int)cnt; i += NT) {
-        Kept e;
-        e.id = (int)(ids[i] >> 32);
-        e.z = __uint_as_float((uint32_t)ids[i]);
-        kept[i] = e;
-      }
-    }
+    if (list) sort_kept_by_id<NT>(ids, (int)cnt, kept);
   }
   out.m = m;
   out.tau = unkey(tau);

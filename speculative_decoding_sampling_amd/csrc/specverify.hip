@@ -42,10 +42,11 @@ hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int*
 hipError_t launch_filter_rows(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                               int B, int K, int V, int top_k, float top_p, double invT,
                               FiltRow* rows, Kept* kept, hipStream_t stream);
+int stream_chunks(int V);
 hipError_t launch_sample_list(bool bf16, const void* tgt, const void* dft, const float* u_final,
                               int B, int K, int V, double invT, const Plan* plan,
-                              const FiltRow* rows, const Kept* kept, int* out_tokens,
-                              double* rmass_out, hipStream_t stream);
+                              const FiltRow* rows, const Kept* kept, double2* cmass,
+                              int* out_tokens, double* rmass_out, hipStream_t stream);
 hipError_t launch_sample_pass(bool bf16, const void* tgt, const void* dft, int B, int K, int V,
                               int nch, double invT, const Plan* plan, ChunkRec* recs, Tie* ties,
                               hipStream_t stream);
@@ -104,7 +105,7 @@ struct Layout {
   bool cand = false;         // filtered through the candidate select
   int nch_row = 0, nch_samp = 0, nch_filt = 0, cap = 0;
   size_t off_row = 0, off_zx = 0, off_beta = 0, off_plan = 0, off_recs = 0, off_ties = 0;
-  size_t off_cand = 0, off_counts = 0, off_frows = 0, off_kept = 0, total = 0;
+  size_t off_cand = 0, off_counts = 0, off_frows = 0, off_kept = 0, off_cmass = 0, total = 0;
 };
 
 bool filters_on(int V, int top_k, float top_p) { return (top_k > 0 && top_k < V) || top_p < 1.0f; }
@@ -160,6 +161,8 @@ Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p) {
     off = align_up(off + (size_t)B * R * sizeof(FiltRow));
     L.off_kept = off;
     off = align_up(off + (size_t)B * R * kKeptCap * sizeof(Kept));
+    L.off_cmass = off;
+    off = align_up(off + (size_t)B * stream_chunks(V) * sizeof(double2));
   }
   L.total = off;
   return L;
@@ -265,7 +268,8 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
                       invT, eos_id, nullptr, nullptr, frows, out, stream);
     if (e != hipSuccess || !mark(s0 + 1)) return SPECV_EHIP;
     e = launch_sample_list(bf16, target, draft, u_final, B, K, V, invT, plan, frows, kept,
-                           out_tokens, rmass_out, stream);
+                           reinterpret_cast<double2*>(ws + L.off_cmass), out_tokens, rmass_out,
+                           stream);
     if (e != hipSuccess || !mark(s0 + 2)) return SPECV_EHIP;
   }
   return SPECV_OK;

@@ -107,10 +107,12 @@ def gumbel_max_token(z, T, rng):
     return int(np.argmax(z / T + g))
 
 
-def make_workload(cfg, seed=None, B=None, draft_sampler=None):
+def make_workload(cfg, seed=None, B=None, draft_sampler=None, top_k=None, top_p=None):
     """Build workload ``cfg`` (1..5) with ``seed`` (default 1000 + cfg).
 
-    ``B`` overrides the batch size (per-request shapes stay the same).
+    ``B`` overrides the batch size (per-request shapes stay the same);
+    ``top_k`` / ``top_p`` override the workload's filter settings (the logits
+    are the same).
     Filtered workloads (top-k / top-p) need ``draft_sampler(z, T, top_k, top_p,
     uniform) -> token`` so that draft tokens come from the processed draft
     distribution; unfiltered workloads use Gumbel-max on z / T.
@@ -121,7 +123,9 @@ def make_workload(cfg, seed=None, B=None, draft_sampler=None):
     K, V, dtype = spec["K"], spec["V"], spec["dtype"]
     # The call takes temperature and top_p as float32: keep the values both
     # sides see identical.
-    T, top_k, top_p = f32(spec["T"]), spec["top_k"], f32(spec["top_p"])
+    top_k = spec["top_k"] if top_k is None else int(top_k)
+    top_p = spec["top_p"] if top_p is None else top_p
+    T, top_p = f32(spec["T"]), f32(top_p)
     filtered = (0 < top_k < V) or top_p < 1.0
     if filtered and draft_sampler is None:
         raise ValueError("filtered workloads need a draft_sampler for the processed draft distribution")
