@@ -41,22 +41,37 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-# HBM bytes of one row-statistics launch on this workload, from rocprofv3
+# HBM bytes of one launch of each workload's dominant kernel, from rocprofv3
 # FETCH_SIZE and WRITE_SIZE runs scaled by a plain-copy calibration (see the
-# profiles directory); valid only for the sources they were taken with.
-ROW_STATS_TRAFFIC = {"sources_sha256_16": "f0804ab9644a5c5b", "bytes": 148139654}
-# The same for one LM-head launch at M=320, D=4096, V=128256 (FETCH_SIZE and
-# WRITE_SIZE of the lm_head op, scaled by the copy calibration taken with the
-# row-statistics figure).
-# And for the first pass of a filtered path, keyed by workload: the top-k
-# candidate pass at B=256, K=8, V=152064 fp32 (top-k 50, top-p 0.9), the
-# radix select at B=64, K=4, V=128256 bf16 (top-p 0.9 alone).
-FILTER_SOURCES = ("filter.hip", "radix_select.h", "common.h")
-FILTER_TRAFFIC = {
-    "B256_K8_V152064_f32_topk50_topp0.9": {"sources_sha256_16": "54dd29cf094e0150",
-                                           "bytes": 2687313229},
+# profiles directory), each valid only for the sources it was measured on:
+# the row-statistics pass of the headline workload, the top-k candidate pass
+# of B=256, K=8, V=152064 fp32 (top-k 50, top-p 0.9) and the radix select of
+# the headline shape with top-p 0.9 alone.
+TRAFFIC = {
+    "B64_K4_V128256_bf16": {
+        "sources": ("row_stats.hip", "common.h"),
+        "sources_sha256_16": "83d31da22561004c", "bytes": 148137711},
+    "B256_K8_V152064_f32_topk50_topp0.9": {
+        "sources": ("filter.hip", "filter_common.h", "radix_select.h", "exp64.h", "common.h"),
+        "sources_sha256_16": "8a57328987c3919c", "bytes": 2687321286},
+    "B64_K4_V128256_bf16_topp0.9": {
+        "sources": ("filter_rows.hip", "filter_common.h", "hist_select.h", "radix_select.h",
+                    "exp64.h", "common.h"),
+        "sources_sha256_16": "2997e4d3dde29baf", "bytes": 148271409},
 }
-LM_HEAD_TRAFFIC = {"sources_sha256_16": "e410f425f4f93b97", "bytes": 1180262001}
+# The same for one LM-head launch at M=320, D=4096, V=128256 (scaled by the
+# copy calibration taken with the row-statistics figure).
+LM_HEAD_TRAFFIC = {"sources": ("lm_head.hip", "common.h"),
+                   "sources_sha256_16": "c8b83f06b627162b", "bytes": 1180276782}
+
+
+def measured_traffic(entry):
+    """An entry's bytes while its sources are the measured ones, else None."""
+    if entry is None or entry["bytes"] is None:
+        return None
+    return entry["bytes"] if sources_hash(entry["sources"]) == entry["sources_sha256_16"] else None
+
+
 WORKLOAD = 3
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,K=4,V=128k"
 
@@ -464,8 +479,7 @@ def bench_lm_head(args):
                    "input_sets": 1, "weight_layout": "packed once before timing"},
         "roofline": {"bound": "mfma", "kernel": "lm_head", "achieved": flops / k_us / 1e6,
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": flops / k_us / 1e6 / 2500.0,
-                     "traffic": (LM_HEAD_TRAFFIC["bytes"] if sources_hash(("lm_head.hip", "common.h"))
-                                 == LM_HEAD_TRAFFIC["sources_sha256_16"] else None),
+                     "traffic": measured_traffic(LM_HEAD_TRAFFIC),
                      "launch_us": k_us, "flops_per_launch": flops,
                      "hbm_gbps": hbm_bytes / k_us / 1e3, "hbm_bytes_per_launch": hbm_bytes},
         "reference_gemm": {"what": "torch.matmul (hipBLASLt) on the same row-major bf16 "
@@ -709,9 +723,7 @@ def main():
         # is the per-call stage mean above.
         dominant = names[0]
         k1_us = stage_us[dominant]
-        tr = FILTER_TRAFFIC.get(spec["name"])
-        traffic = (tr["bytes"] if tr and sources_hash(FILTER_SOURCES) == tr["sources_sha256_16"]
-                   else None)
+        traffic = measured_traffic(TRAFFIC.get(spec["name"]))
         log(f"{dominant}: {k1_us:.2f} us/launch (stage mean)")
     else:
         # The dominant kernel alone, for the roofline: a burst of row-statistics
@@ -726,9 +738,7 @@ def main():
         burst_bytes = float(np.mean([hosts[i % len(hosts)].algorithmic_bytes
                                      for i in range(reps)]))
         # the counters were taken on the headline workload's launch
-        traffic = (ROW_STATS_TRAFFIC["bytes"]
-                   if wl == WORKLOAD and
-                   sources_hash() == ROW_STATS_TRAFFIC["sources_sha256_16"] else None)
+        traffic = measured_traffic(TRAFFIC.get(spec["name"])) if not overridden else None
         evb.close()
         log(f"row_stats alone: {k1_us:.2f} us/launch over {reps} launches")
     if filtered:

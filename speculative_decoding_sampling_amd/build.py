@@ -21,7 +21,8 @@ LIB = os.path.join(HERE, "libspecverify.so")
 
 ARCH = "gfx950"
 SOURCES = ["specverify.hip", "row_stats.hip", "accept.hip", "sample.hip", "filter.hip",
-           "diagnostics.hip", "round_policy.hip", "lm_head.hip"]
+           "filter_rows.hip", "sample_list.hip", "diagnostics.hip", "round_policy.hip",
+           "lm_head.hip"]
 # Packed FP32 instructions stay off: the compiler must not form v_pk_* FP32 ops.
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",

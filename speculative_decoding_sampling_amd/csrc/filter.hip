@@ -1,4 +1,4 @@
-// Top-k / top-p filtering and the sampler over the kept tokens.
+// Top-k / top-p filtering for a small top-k: the candidate select.
 //
 // p and q are the target's and the draft's distributions after temperature,
 // top-k and top-p, each row filtered on its own (nickwang.xyz
@@ -26,7 +26,7 @@
 
 #include "common.h"
 #include "exp64.h"
-#include "hist_select.h"
+#include "filter_common.h"
 #include "radix_select.h"
 
 namespace specv {
@@ -105,51 +105,6 @@ template <typename K>
 __device__ __forceinline__ K wave_sort_desc(K key) {
   static_assert(kWave == 64, "the lane exchanges are written for wave64");
   return bitonic_sort<kWave>(key, (int)(threadIdx.x % kWave));
-}
-
-template <typename V>
-__device__ __forceinline__ V block_scan_excl(V v, V* lds, V& total) {
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  V x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const V y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  V excl = __shfl_up(x, 1, kWave);
-  if (lane == 0) excl = V(0);
-  __syncthreads();
-  if (lane == kWave - 1) lds[wid] = x;
-  __syncthreads();
-  V off = V(0);
-  total = V(0);
-#pragma unroll
-  for (int w = 0; w < kFiltThreads / kWave; ++w) {
-    if (w < wid) off += lds[w];
-    total += lds[w];
-  }
-  return off + excl;
-}
-
-__device__ __forceinline__ int block_min_i(int v, int* lds) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  __syncthreads();
-  if (lane == 0) lds[wid] = v;
-  __syncthreads();
-  int r = lds[0];
-#pragma unroll
-  for (int w = 1; w < kFiltThreads / kWave; ++w) r = min(r, lds[w]);
-  return r;
-}
-
-// Row index r in [0, 2K+1) of request b: needed when it is target row
-// k <= n_b or draft row k < n_b.
-__device__ __forceinline__ bool row_needed(int r, int K, int nb, bool& is_target, int& k) {
-  is_target = r <= K;
-  k = is_target ? r : r - (K + 1);
-  return k <= (is_target ? nb : nb - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -915,326 +870,6 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// The residual or bonus draw streamed over a whole filtered row pair, for a
-// target row whose kept set has no list (more than kKeptCap tokens).  Chunks
-// of 2048 tokens; in a chunk, lane l of a wave holds tokens c0 + 512 j + 8 l
-// .. + 7 (j < 4), so the chunk's tokens in order are (j, lane, element).
-// Weights in float64 from the rows' FiltRows: p = e_t / S_t on the target's
-// kept tokens, and after a rejection max(p - q, 0) with q the same over the
-// draft's kept tokens.  The chunk pass (one wave per chunk, the whole chip)
-// writes each chunk's mass; the draw copies them to LDS, every wave finds the
-// chunk holding t = u_final * total by a blocked prefix of its own, and wave
-// 0 scans inside that chunk.
-constexpr int kStreamSub = kWave * 8;                  // 512 tokens per sub-block
-constexpr int kStreamChunk = 4 * kStreamSub;           // 2048 tokens per chunk
-
-template <typename T>
-__device__ __forceinline__ void load8_checked(const T* __restrict__ row, long e0, int V, float* z) {
-  constexpr int N = Elem<T>::kPerVec;
-  const bool al = aligned16(row);
-#pragma unroll
-  for (int v = 0; v < 8 / N; ++v) load_vec_checked(row, e0 + v * N, V, al, z + v * N);
-}
-
-__device__ __forceinline__ double kept_prob(float z, const FiltRow& fr, double invT,
-                                            const double* tbl) {
-  if (!(z >= fr.tau) || z == -INFINITY) return 0.0;
-  return exp64(((double)z - (double)fr.m) * invT, tbl) / fr.S;
-}
-
-// Element i (0..7) of eight registers, by a select tree (no indexed access).
-__device__ __forceinline__ float pick8(const float* z, uint32_t i) {
-  const float a = (i & 1u) ? z[1] : z[0], b = (i & 1u) ? z[3] : z[2];
-  const float c = (i & 1u) ? z[5] : z[4], d = (i & 1u) ? z[7] : z[6];
-  const float ab = (i & 2u) ? b : a, cd = (i & 2u) ? d : c;
-  return (i & 4u) ? cd : ab;
-}
-
-// One chunk's masses, summed in a fixed order (per lane j then element, then
-// the wave): .x the first attempt's (the residual after a rejection, else p),
-// .y p alone (the fall-back when the residual has no mass).  A token outside
-// the target's kept set adds exactly zero to both (p = 0, so p - q <= 0), so
-// each lane visits only its kept tokens, in element order: the same sums,
-// with far fewer exps when the kept set is a small share of the row.
-template <typename T>
-__device__ __forceinline__ double2 chunk_masses(const T* __restrict__ trow,
-                                                const T* __restrict__ drow, int V, long c0,
-                                                bool rej, const FiltRow& tr, const FiltRow& dr,
-                                                double invT, const double* tbl) {
-  const int lane = threadIdx.x % kWave;
-  double acc_r = 0.0, acc_p = 0.0;
-  for (int j = 0; j < 4; ++j) {
-    const long e0 = c0 + j * kStreamSub + lane * 8;
-    float zt[8], zd[8];
-    load8_checked(trow, e0, V, zt);
-    if (rej) load8_checked(drow, e0, V, zd);
-    uint32_t km = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) km |= (zt[i] >= tr.tau && zt[i] != -INFINITY) ? 1u << i : 0u;
-    while (km) {
-      const uint32_t i = (uint32_t)__builtin_ctz(km);
-      km &= km - 1u;
-      const double p = kept_prob(pick8(zt, i), tr, invT, tbl);
-      acc_p += p;
-      if (rej) {
-        const double x = p - kept_prob(pick8(zd, i), dr, invT, tbl);
-        acc_r += x > 0.0 ? x : 0.0;
-      }
-    }
-  }
-  acc_p = wave_sum(acc_p);
-  acc_r = rej ? wave_sum(acc_r) : acc_p;
-  return make_double2(acc_r, acc_p);
-}
-
-// The chunk pass of the streamed draw: wave g of the grid takes chunk
-// g % nch of request g / nch, when that request draws from a target row with
-// no kept list.
-template <typename T>
-__global__ __launch_bounds__(kFiltThreads) void stream_chunks_kernel(
-    const T* __restrict__ tgt, const T* __restrict__ dft, int B, int K, int V, int nch,
-    double invT, const Plan* __restrict__ plan, const FiltRow* __restrict__ rows,
-    double2* __restrict__ cmass) {
-  __shared__ double tbl[SPECV_EXP64_N];
-  exp64_stage_table<kFiltThreads>(tbl);
-  __syncthreads();
-  const long g = (long)blockIdx.x * (kFiltThreads / kWave) + threadIdx.x / kWave;
-  const int b = (int)(g / nch), c = (int)(g % nch);
-  if (b >= B) return;
-  const Plan pl = plan[b];
-  if (pl.path != kPathReject && pl.path != kPathBonus) return;   // uniform per wave
-  const int R = 2 * K + 1;
-  const FiltRow tr = rows[(size_t)b * R + pl.trow];
-  if (tr.count <= kKeptCap) return;                  // the list draw serves it
-  const bool rej = pl.path == kPathReject;
-  FiltRow dr;
-  dr.m = 0.f; dr.tau = 0.f; dr.S = 1.0; dr.count = 0; dr.status = 0; dr.pad = 0;
-  if (rej) dr = rows[(size_t)b * R + K + 1 + pl.drow];
-  const T* trow = tgt + target_row_off(b, pl.trow, K, V);
-  const T* drow = rej ? dft + draft_row_off(b, pl.drow, K, V) : trow;
-  const double2 r = chunk_masses(trow, drow, V, (long)c * kStreamChunk, rej, tr, dr, invT, tbl);
-  if (threadIdx.x % kWave == 0) cmass[(size_t)b * nch + c] = r;
-}
-
-template <typename T>
-__device__ void stream_draw(const T* __restrict__ trow, const T* __restrict__ drow, int V,
-                            bool rej, const FiltRow& tr, const FiltRow& dr, double invT,
-                            const double* tbl, double uf, const double2* __restrict__ cm,
-                            double* csum, int& y_out, double& rmass_out) {
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  const int nch = (V + kStreamChunk - 1) / kStreamChunk;
-  auto weights = [&](long e0, bool resid, double* w) {
-    float zt[8], zd[8];
-    load8_checked(trow, e0, V, zt);
-    if (resid) load8_checked(drow, e0, V, zd);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      double x = kept_prob(zt[i], tr, invT, tbl);
-      if (resid) {
-        x -= kept_prob(zd[i], dr, invT, tbl);
-        x = x > 0.0 ? x : 0.0;
-      }
-      w[i] = x;
-    }
-  };
-  bool resid = rej;
-  double total = 0.0, t = 0.0, pre = 0.0;
-  int cstar = -1, clast = -1;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    for (int c = threadIdx.x; c < nch; c += kFiltThreads) csum[c] = attempt == 0 ? cm[c].x : cm[c].y;
-    __syncthreads();
-    // every wave: blocked prefix over the chunk masses (lane l owns chunks
-    // [l q, l q + q)), the same in every wave
-    const int q = (nch + kWave - 1) / kWave;
-    const int c_lo = min(nch, lane * q), c_hi = min(nch, c_lo + q);
-    double mine = 0.0;
-    for (int c = c_lo; c < c_hi; ++c) mine += csum[c];
-    double incl = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const double y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
-    total = __shfl(incl, kWave - 1, kWave);
-    if (resid && !(total > 0.0)) {       // unreachable in exact arithmetic: draw from p_j
-      resid = false;
-      __syncthreads();                   // every wave has read csum
-      continue;
-    }
-    t = uf * total;
-    double run = incl - mine;
-    int cand = -1, lastp = -1;
-    double cpre = 0.0;
-    for (int c = c_lo; c < c_hi; ++c) {
-      const double before = run;
-      run += csum[c];
-      if (cand < 0 && t < run) {
-        cand = c;
-        cpre = before;
-      }
-      if (csum[c] > 0.0) lastp = c;
-    }
-    const uint64_t hit = __ballot(cand >= 0);
-    if (hit) {
-      const int L = __ffsll((unsigned long long)hit) - 1;
-      cstar = __shfl(cand, L, kWave);
-      pre = __shfl(cpre, L, kWave);
-    } else {
-      const uint64_t pos = __ballot(lastp >= 0);
-      clast = pos ? __shfl(lastp, 63 - __clzll((long long)pos), kWave) : -1;
-    }
-    break;
-  }
-  rmass_out = (rej && resid) ? total : 0.0;
-  y_out = -1;
-  if (wid != 0) return;
-  if (cstar >= 0) {                      // in-chunk scan: sub-blocks in order, lanes in order
-    double off = pre;
-    int y = INT_MAX, ylast = -1;
-    for (int j = 0; j < 4 && y == INT_MAX; ++j) {
-      const long e0 = (long)cstar * kStreamChunk + j * kStreamSub + lane * 8;
-      double w[8];
-      weights(e0, resid, w);
-      double mysum = 0.0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mysum += w[i];
-      double incl = mysum;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const double yv = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += yv;
-      }
-      double run = off + incl - mysum;
-      int v = INT_MAX, vl = -1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        run += w[i];
-        if (v == INT_MAX && t < run) v = (int)(e0 + i);
-        if (w[i] > 0.0) vl = (int)(e0 + i);
-      }
-      const uint64_t h1 = __ballot(v != INT_MAX), h2 = __ballot(vl >= 0);
-      if (h1) y = __shfl(v, __ffsll((unsigned long long)h1) - 1, kWave);
-      if (h2) ylast = __shfl(vl, 63 - __clzll((long long)h2), kWave);
-      off += __shfl(incl, kWave - 1, kWave);
-    }
-    y_out = y != INT_MAX ? y : ylast;    // rounding fall-through inside the chunk
-  } else if (clast >= 0) {               // rounding fall-through: the last positive token
-    int ylast = -1;
-    for (int j = 0; j < 4; ++j) {
-      const long e0 = (long)clast * kStreamChunk + j * kStreamSub + lane * 8;
-      double w[8];
-      weights(e0, resid, w);
-      int vl = -1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (w[i] > 0.0) vl = (int)(e0 + i);
-      const uint64_t h2 = __ballot(vl >= 0);
-      if (h2) ylast = __shfl(vl, 63 - __clzll((long long)h2), kWave);
-    }
-    y_out = ylast;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// sample_list: per request, the residual or bonus draw over the target row's
-// kept tokens in id order (streamed over the rows when the kept set has no
-// list).
-template <typename T>
-__global__ __launch_bounds__(kFiltThreads) void sample_list_kernel(
-    const T* __restrict__ tgt, const T* __restrict__ dft, const float* __restrict__ u_final,
-    int K, int V, double invT, const Plan* __restrict__ plan, const FiltRow* __restrict__ rows,
-    const Kept* __restrict__ kept, const double2* __restrict__ cmass, int* __restrict__ out_tokens,
-    double* __restrict__ rmass_out) {
-  __shared__ double tbl[SPECV_EXP64_N];
-  __shared__ double dl[kFiltThreads / kWave];
-  __shared__ int il[kFiltThreads / kWave];
-  __shared__ double csum[kMaxSampChunks];
-  const int b = blockIdx.x;
-  exp64_stage_table<kFiltThreads>(tbl);
-  const Plan pl = plan[b];
-  if (pl.path != kPathReject && pl.path != kPathBonus) return;   // uniform per block
-  const int R = 2 * K + 1;
-  const FiltRow tr = rows[(size_t)b * R + pl.trow];
-  const bool rej = pl.path == kPathReject;
-  FiltRow dr;
-  dr.m = 0.f; dr.tau = 0.f; dr.S = 1.0; dr.count = 0; dr.status = 0; dr.pad = 0;
-  if (rej) dr = rows[(size_t)b * R + K + 1 + pl.drow];
-  const Kept* list = kept + ((size_t)b * R + pl.trow) * kKeptCap;
-  const T* drow = rej ? dft + draft_row_off(b, pl.drow, K, V) : nullptr;
-  __syncthreads();
-  if (tr.count > kKeptCap) {                         // uniform: no list for this row
-    int y;
-    double rm;
-    const int nch = (V + kStreamChunk - 1) / kStreamChunk;
-    stream_draw(tgt + target_row_off(b, pl.trow, K, V), drow, V, rej, tr, dr, invT, tbl,
-                (double)u_final[b], cmass + (size_t)b * nch, csum, y, rm);
-    if (threadIdx.x == 0) {
-      out_tokens[(size_t)b * (K + 1) + pl.stop] = y;
-      if (rmass_out) rmass_out[b] = rm;
-    }
-    return;
-  }
-  const int n = tr.count;
-  const int q = (n + kFiltThreads - 1) / kFiltThreads;
-  const int i_lo = min(n, (int)threadIdx.x * q), i_hi = min(n, i_lo + q);
-  constexpr int kMaxPer = (kKeptCap + kFiltThreads - 1) / kFiltThreads;
-  double w[kMaxPer];
-  int ids[kMaxPer];
-  double wp[kMaxPer];
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    w[j] = wp[j] = 0.0;
-    ids[j] = -1;
-    const int i = i_lo + j;
-    if (i < i_hi) {
-      const Kept e = list[i];
-      ids[j] = e.id;
-      wp[j] = exp64(((double)e.z - (double)tr.m) * invT, tbl);
-      w[j] = wp[j];
-      if (rej) {
-        const float zd = to_f32(drow[e.id]);
-        double qv = 0.0;
-        if (zd >= dr.tau && zd > -INFINITY) qv = exp64(((double)zd - (double)dr.m) * invT, tbl) / dr.S;
-        const double r = wp[j] / tr.S - qv;
-        w[j] = r > 0.0 ? r : 0.0;
-      }
-    }
-  }
-  double mine = 0.0;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) mine += w[j];
-  double total;
-  double excl = block_scan_excl<double>(mine, dl, total);
-  bool resid = rej;
-  if (resid && !(total > 0.0)) {                     // unreachable in exact arithmetic: draw from p_j
-    resid = false;
-    mine = 0.0;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      w[j] = wp[j];
-      mine += w[j];
-    }
-    excl = block_scan_excl<double>(mine, dl, total);
-  }
-  const double t = (double)u_final[b] * total;
-  int hit = INT_MAX, last = -1;
-  double run = excl;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    if (ids[j] < 0) continue;
-    run += w[j];
-    if (hit == INT_MAX && t < run) hit = ids[j];
-    if (w[j] > 0.0) last = ids[j];
-  }
-  int y = block_min_i(hit, il);
-  if (y == INT_MAX) y = -block_min_i(-last, il);     // rounding fall-through: last positive
-  if (threadIdx.x == 0) {
-    out_tokens[(size_t)b * (K + 1) + pl.stop] = y;
-    if (rmass_out) rmass_out[b] = (rej && resid) ? total : 0.0;
-  }
-}
-
-// ---------------------------------------------------------------------------
 int filter_cap(int top_k) { return ((3 * top_k) / 2 + 40 + 7) / 8 * 8; }
 
 // Candidate slots of one row: cap per chunk, at least 256 for the last one
@@ -1277,105 +912,6 @@ hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int*
     filter_merge_kernel<float><<<grid, dim3(kFiltThreads), 0, stream>>>(
         static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, nch, cap,
         stride, top_k, top_p, invT, cand, counts, rows, kept);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// filter_rows: the general select (radix_select.h) for every needed row, one
-// 1024-thread workgroup per row: any top_k, top-p with or without top-k, any
-// kept-set size.
-constexpr int kSelThreads = 1024;
-
-template <typename T>
-__global__ __launch_bounds__(kSelThreads) void filter_rows_kernel(
-    const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
-    int K, int V, int top_k, float top_p, double invT, FiltRow* __restrict__ rows,
-    Kept* __restrict__ kept) {
-  __shared__ SelectLds sl;
-  __shared__ double tbl[SPECV_EXP64_N];
-  const int R = 2 * K + 1;
-  const int rr = blockIdx.x;
-  const int r = rr % R, b = rr / R;
-  const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
-  if (nb < 0 || nb > K) return;
-  bool is_target;
-  int k;
-  if (!row_needed(r, K, nb, is_target, k)) return;
-  for (int i = threadIdx.x; i < SPECV_EXP64_N; i += kSelThreads) tbl[i] = kExp64Table[i];
-  __syncthreads();
-  const T* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
-  const FiltRow o = select_row<T, kSelThreads>(row, V, sizeof(T) == 2, top_k, top_p, invT, tbl,
-                                               &sl, kept + (size_t)rr * kKeptCap);
-  if (threadIdx.x == 0) rows[rr] = o;
-}
-
-// bfloat16 rows: the histogram select (hist_select.h), 142 KB of LDS, one
-// workgroup per CU.
-__global__ __launch_bounds__(kSelThreads) void filter_rows_hist_kernel(
-    const bf16_t* __restrict__ tgt, const bf16_t* __restrict__ dft,
-    const int* __restrict__ draft_len, int K, int V, int top_k, float top_p, double invT,
-    FiltRow* __restrict__ rows, Kept* __restrict__ kept) {
-  __shared__ HistPool pool;
-  __shared__ HistAux aux;
-  __shared__ double tbl[SPECV_EXP64_N];
-  const int R = 2 * K + 1;
-  const int rr = blockIdx.x;
-  const int r = rr % R, b = rr / R;
-  const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
-  if (nb < 0 || nb > K) return;
-  bool is_target;
-  int k;
-  if (!row_needed(r, K, nb, is_target, k)) return;
-  for (int i = threadIdx.x; i < SPECV_EXP64_N; i += kSelThreads) tbl[i] = kExp64Table[i];
-  const bf16_t* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
-  // the histogram pass's first barrier makes the table visible
-  const FiltRow o = select_row_hist<kSelThreads>(row, V, top_k, top_p, invT, tbl, &pool, &aux,
-                                                 kept + (size_t)rr * kKeptCap);
-  if (threadIdx.x == 0) rows[rr] = o;
-}
-
-hipError_t launch_filter_rows(bool bf16, const void* tgt, const void* dft, const int* draft_len,
-                              int B, int K, int V, int top_k, float top_p, double invT,
-                              FiltRow* rows, Kept* kept, hipStream_t stream) {
-  const size_t blocks = (size_t)B * (2 * K + 1);
-  if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  if (bf16)
-    filter_rows_hist_kernel<<<dim3((unsigned)blocks), dim3(kSelThreads), 0, stream>>>(
-        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V,
-        top_k, top_p, invT, rows, kept);
-  else
-    filter_rows_kernel<float><<<dim3((unsigned)blocks), dim3(kSelThreads), 0, stream>>>(
-        static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, top_k,
-        top_p, invT, rows, kept);
-  return hipGetLastError();
-}
-
-int stream_chunks(int V) { return (V + kStreamChunk - 1) / kStreamChunk; }
-
-hipError_t launch_sample_list(bool bf16, const void* tgt, const void* dft, const float* u_final,
-                              int B, int K, int V, double invT, const Plan* plan,
-                              const FiltRow* rows, const Kept* kept, double2* cmass,
-                              int* out_tokens, double* rmass_out, hipStream_t stream) {
-  const int nch = stream_chunks(V);
-  if (nch > kMaxSampChunks) return hipErrorInvalidConfiguration;
-  constexpr int kWavesPer = kFiltThreads / kWave;
-  const size_t blocks = ((size_t)B * nch + kWavesPer - 1) / kWavesPer;
-  if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  if (bf16) {
-    stream_chunks_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
-        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), B, K, V, nch, invT,
-        plan, rows, cmass);
-    sample_list_kernel<bf16_t><<<dim3(B), dim3(kFiltThreads), 0, stream>>>(
-        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), u_final, K, V, invT,
-        plan, rows, kept, cmass, out_tokens, rmass_out);
-  } else {
-    stream_chunks_kernel<float><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
-        static_cast<const float*>(tgt), static_cast<const float*>(dft), B, K, V, nch, invT, plan,
-        rows, cmass);
-    sample_list_kernel<float><<<dim3(B), dim3(kFiltThreads), 0, stream>>>(
-        static_cast<const float*>(tgt), static_cast<const float*>(dft), u_final, K, V, invT, plan,
-        rows, kept, cmass, out_tokens, rmass_out);
-  }
   return hipGetLastError();
 }
 

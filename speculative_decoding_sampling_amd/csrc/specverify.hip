@@ -161,8 +161,10 @@ Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p) {
     off = align_up(off + (size_t)B * R * sizeof(FiltRow));
     L.off_kept = off;
     off = align_up(off + (size_t)B * R * kKeptCap * sizeof(Kept));
-    L.off_cmass = off;
-    off = align_up(off + (size_t)B * stream_chunks(V) * sizeof(double2));
+    if (!L.cand) {
+      L.off_cmass = off;
+      off = align_up(off + (size_t)B * stream_chunks(V) * sizeof(double2));
+    }
   }
   L.total = off;
   return L;
@@ -267,9 +269,11 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
     e = launch_accept(bf16, true, target, draft, tokens, draft_len, u, u_final, B, K, V, 0, c,
                       invT, eos_id, nullptr, nullptr, frows, out, stream);
     if (e != hipSuccess || !mark(s0 + 1)) return SPECV_EHIP;
+    // the candidate path keeps at most top_k <= 128 tokens but for ties: no
+    // chunk pass for it
     e = launch_sample_list(bf16, target, draft, u_final, B, K, V, invT, plan, frows, kept,
-                           reinterpret_cast<double2*>(ws + L.off_cmass), out_tokens, rmass_out,
-                           stream);
+                           L.cand ? nullptr : reinterpret_cast<double2*>(ws + L.off_cmass),
+                           out_tokens, rmass_out, stream);
     if (e != hipSuccess || !mark(s0 + 2)) return SPECV_EHIP;
   }
   return SPECV_OK;
