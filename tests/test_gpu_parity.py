@@ -464,14 +464,21 @@ def test_many_draws_large_vocabulary_non_unit_temperature():
     assert rep["requests"] == 1024
 
 
-@pytest.mark.parametrize("cfg,B", [(3, 8), (4, 6)])
-def test_graph_replay_matches_eager(cfg, B):
+@pytest.mark.parametrize("cfg,B,top_k,top_p", [(3, 8, None, None), (4, 6, None, None),
+                                              (3, 6, 0, 0.9), (4, 3, 0, 0.9)])
+def test_graph_replay_matches_eager(cfg, B, top_k, top_p):
     # One call captured in a HIP graph and replayed several times, with eager
     # calls on other inputs and synchronisations in between: every replay
     # gives the eager result on its inputs (the call records no memset, so
-    # replays after the first are as good as the first).
-    w = make_workload(cfg, B=B, draft_sampler=oracle_sampler if cfg == 4 else None)
-    other = make_workload(cfg, B=B, seed=77, draft_sampler=oracle_sampler if cfg == 4 else None)
+    # replays after the first are as good as the first).  The last two cases
+    # take the radix path (top-p alone): the bf16 histogram select with the
+    # streamed draw's chunk pass, and the float32 multi-pass select.
+    filt = cfg == 4 or top_p is not None
+    kw = dict(top_k=top_k, top_p=top_p, draft_sampler=oracle_sampler) if filt else {}
+    w = make_workload(cfg, B=B, **kw)
+    other = make_workload(cfg, B=B, seed=77, **kw)
+    if top_p is not None:
+        assert binding.path_kind(w.V, w.top_k, w.top_p) == 2
     a = upload(w, DEV)
     b = upload(other, DEV)
     ws = torch.empty(binding.workspace_bytes(w.B, w.K, w.V,
