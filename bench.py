@@ -530,6 +530,11 @@ def main():
                     help="override the verify workload's top-k (0 = off); reported separately")
     ap.add_argument("--top-p", type=float, default=None,
                     help="override the verify workload's top-p (1.0 = off); reported separately")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="override the verify workload's batch size; reported separately")
+    ap.add_argument("--small-batch-limit", type=int, default=None,
+                    help="set the library's small-batch limit (B (K+1) ceil(V/2048) up to which "
+                         "unfiltered calls take the one-kernel tail; 0 = never)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -544,8 +549,8 @@ def main():
     if args.sets is None:
         args.sets = 1 if args.workload == 4 else 4
     if args.op != "verify" and (args.workload != WORKLOAD or args.top_k is not None
-                                or args.top_p is not None):
-        log("--workload, --top-k and --top-p apply to the verify op only")
+                                or args.top_p is not None or args.batch is not None):
+        log("--workload, --top-k, --top-p and --batch apply to the verify op only")
         sys.exit(2)
     if args.op == "sample":
         return bench_sample(args)
@@ -568,8 +573,14 @@ def main():
 
     wl = args.workload
     spec = dict(WORKLOADS[wl])
-    overridden = args.top_k is not None or args.top_p is not None
-    if overridden:
+    if args.small_batch_limit is not None:
+        binding.set_small_batch_limit(args.small_batch_limit)
+    if args.batch is not None:
+        # another batch size of the same workload: a separate line
+        spec["B"] = args.batch
+        spec["name"] = f"B{args.batch}_" + spec["name"].split("_", 1)[1]
+    overridden = args.top_k is not None or args.top_p is not None or args.batch is not None
+    if args.top_k is not None or args.top_p is not None:
         # the same logits under other filter settings: a separate line, never
         # the headline
         if args.top_k is not None:
@@ -588,10 +599,10 @@ def main():
         if filtered:
             # placeholder drafts, replaced below by draws from the processed
             # draft rows made on the GPU by specv_sample
-            w = make_workload(wl, seed=seed, draft_sampler=lambda z, T, k, p, x: 0,
+            w = make_workload(wl, seed=seed, B=spec["B"], draft_sampler=lambda z, T, k, p, x: 0,
                               top_k=spec["top_k"], top_p=spec["top_p"])
         else:
-            w = make_workload(wl, seed=seed, top_k=spec["top_k"], top_p=spec["top_p"])
+            w = make_workload(wl, seed=seed, B=spec["B"], top_k=spec["top_k"], top_p=spec["top_p"])
         hosts.append(w)
         a = upload(w, dev)
         if filtered:
@@ -668,7 +679,7 @@ def main():
     log(f"single calls: median {med:.2f} us, p10 {p10:.2f}, p90 {p90:.2f}")
 
     # Per-kernel durations: the same steps through the timing entry point.
-    names = binding.stage_names(binding.path_kind(w0.V, w0.top_k, w0.top_p))
+    names = binding.stage_names(binding.path_kind(w0.B, w0.K, w0.V, w0.top_k, w0.top_p))
     nst = len(names)
     evs = [HipEvents(nst + 1) for _ in range(args.steps)]
     torch.cuda.synchronize()

@@ -77,7 +77,9 @@ typedef enum {
  * Bytes of device workspace specv_verify needs for these sizes.  Returns 0
  * for sizes specv_verify would reject.  The workspace holds per-row
  * statistics, per-request decisions and fp64 chunk partials; its contents
- * need no initialisation and are meaningless after the call.
+ * need no initialisation and are meaningless after the call.  The size
+ * depends on the path the call takes (specv_path_kind), so query it after
+ * any specv_set_small_batch_limit.
  */
 SPECV_API size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype, int top_k, float top_p);
 
@@ -105,8 +107,9 @@ SPECV_API size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype,
  *                 + max(c, 256) <= 4096 with c = 8 * ceil((1.5 * top_k + 40) / 8);
  *                 top_k = 50 at V = 152064 uses 2416) takes a candidate
  *                 select; every other setting (top-p alone, larger top_k) a
- *                 radix select that reads each needed row once per key digit
- *                 (specv_path_kind tells which).
+ *                 radix select: a one-read histogram select for bf16 rows, a
+ *                 select that reads each needed row once per key digit for
+ *                 float32 rows (specv_path_kind tells which).
  *  eos_id         -1 = off; else in [0, V): the round stops right after the
  *                 first emitted EOS (accepted draft or drawn token).
  *  out_tokens     [B][K+1] int32 output: emitted tokens, -1 beyond n_emitted.
@@ -385,7 +388,7 @@ SPECV_API specv_status_t specv_verify_lm_head(const void *hidden, const void *pa
  * Timing variant of specv_verify, for benchmarks: identical work, plus
  * hipEventRecord on `stream` of events[0] before the first kernel launch and
  * of events[i+1] after kernel stage i.  `events` holds specv_num_stages(p) + 1
- * caller-created HIP events, p = specv_path_kind(V, top_k, top_p) (SPECV_EINVAL
+ * caller-created HIP events, p = specv_path_kind(B, K, V, top_k, top_p) (SPECV_EINVAL
  * if NULL or any of those entries is NULL); the caller reads stage durations
  * with hipEventElapsedTime after synchronising.  The stages differ by path
  * (specv_stage_name).
@@ -399,10 +402,22 @@ SPECV_API specv_status_t specv_verify_timed(const void *target_logits, const voi
                                             void *workspace, size_t workspace_bytes,
                                             hipStream_t stream, hipEvent_t *events);
 
-/* Which kernel path a call with these settings takes: 0 without filters
- * (row statistics, accept scan, float64 sampler), 1 top-k / top-p through the
- * candidate select, 2 top-k / top-p through the radix select. */
-SPECV_API int specv_path_kind(int V, int top_k, float top_p);
+/* Which kernel path a call with these sizes and settings takes: 0 without
+ * filters (row statistics, accept scan, float64 chunk pass, draw: four
+ * kernels), 1 top-k / top-p through the candidate select, 2 top-k / top-p
+ * through the radix select, 3 without filters at small sizes (row
+ * statistics, then one kernel that runs the accept scan and the chunk pass
+ * of every row pair the request could draw from, and draws from the one the
+ * scan picks; tbxsx.cn "推测解码采样验证优化策略 —— 深度调研报告", section
+ * "6. 扩展性与安全性", operator fusion against launch overhead).  Paths 0 and
+ * 3 give the same results. */
+SPECV_API int specv_path_kind(int B, int K, int V, int top_k, float top_p);
+/* Sets the size up to which unfiltered calls take path 3: calls with
+ * B * (K+1) * ceil(V / 2048) <= limit do (default 1024; 0 turns the path
+ * off, a huge value forces it).  Process-wide, for all devices; returns the
+ * previous limit.  A call made while another thread changes the limit may
+ * take either path; workspace sizes follow the limit in force. */
+SPECV_API long long specv_set_small_batch_limit(long long limit);
 /* Number of kernel stages a call on path `kind` launches (0 for an unknown
  * kind), and the static name of stage i (NULL when out of range). */
 SPECV_API int specv_num_stages(int kind);

@@ -80,8 +80,10 @@ def load_library():
         lib.specv_monitor_update.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                              c_vp, c_vp, c_vp, c_vp]
         lib.specv_monitor_update.restype = c_int
-        lib.specv_path_kind.argtypes = [c_int, c_int, ctypes.c_float]
+        lib.specv_path_kind.argtypes = [c_int, c_int, c_int, c_int, ctypes.c_float]
         lib.specv_path_kind.restype = c_int
+        lib.specv_set_small_batch_limit.argtypes = [ctypes.c_longlong]
+        lib.specv_set_small_batch_limit.restype = ctypes.c_longlong
         lib.specv_num_stages.argtypes = [c_int]
         lib.specv_num_stages.restype = c_int
         lib.specv_stage_name.argtypes = [c_int, c_int]
@@ -118,9 +120,17 @@ def status_string(status):
     return load_library().specv_status_string(int(status)).decode()
 
 
-def path_kind(V, top_k=0, top_p=1.0):
-    """0: no filters; 1: top-k / top-p by the candidate select; 2: by the radix select."""
-    return int(load_library().specv_path_kind(int(V), int(top_k), float(top_p)))
+def path_kind(B, K, V, top_k=0, top_p=1.0):
+    """0: no filters; 1: top-k / top-p by the candidate select; 2: by the radix
+    select; 3: no filters, small sizes (one kernel after the row statistics)."""
+    return int(load_library().specv_path_kind(int(B), int(K), int(V), int(top_k), float(top_p)))
+
+
+def set_small_batch_limit(limit):
+    """Largest B * (K+1) * ceil(V / 2048) of an unfiltered call that takes
+    path 3 (0: never, a huge value: always).  Process-wide; returns the
+    previous limit."""
+    return int(load_library().specv_set_small_batch_limit(int(limit)))
 
 
 def stage_names(kind=0):

@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libspecverify.so")
 ARCH = "gfx950"
 SOURCES = ["specverify.hip", "row_stats.hip", "accept.hip", "sample.hip", "filter.hip",
            "filter_rows.hip", "sample_list.hip", "diagnostics.hip", "round_policy.hip",
-           "lm_head.hip"]
+           "lm_head.hip", "small.hip"]
 # Packed FP32 instructions stay off: the compiler must not form v_pk_* FP32 ops.
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",

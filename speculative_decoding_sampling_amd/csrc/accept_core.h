@@ -60,6 +60,16 @@ __device__ __forceinline__ void combine_rows(const float2* __restrict__ pt,
   Sd = sd;
 }
 
+// S_t / S_d in natural-exp units from the two rows' combined float32
+// statistics: each base-2 normaliser is relative to 2^fl(M*c); undo that
+// offset exactly (M*c is exact in float64).
+__device__ __forceinline__ double normaliser_ratio(float Mt, float St, float Md, float Sd,
+                                                   float c) {
+  const double off_t = (double)__fmul_rn(Mt, c) - (double)Mt * (double)c;
+  const double off_d = (double)__fmul_rn(Md, c) - (double)Md * (double)c;
+  return ((double)St / (double)Sd) * exp2(off_t - off_d);
+}
+
 // Probability of token x in a filtered row: exp((z - m)/T) / S if z is kept.
 __device__ __forceinline__ double filt_prob(float z, const FiltRow& fr, double invT) {
   if (!(z >= fr.tau) || z == -INFINITY) return 0.0;
@@ -174,14 +184,8 @@ __device__ __forceinline__ void accept_scan(int b, int lane, int K, float c, dou
     pl.mt = FILT ? 0.f : (stop < kWave ? rs.Mt : rs.Mk);
     pl.md = FILT ? 0.f : rs.Md;
     pl.pad0 = pl.pad1 = 0;
-    // S_t / S_d in natural-exp units: each base-2 normaliser is relative to
-    // 2^fl(M*c); undo that offset exactly (M*c is exact in float64).
-    pl.g = 0.0;
-    if (!FILT && path == kPathReject) {
-      const double off_t = (double)__fmul_rn(rs.Mt, c) - (double)rs.Mt * (double)c;
-      const double off_d = (double)__fmul_rn(rs.Md, c) - (double)rs.Md * (double)c;
-      pl.g = ((double)rs.St / (double)rs.Sd) * exp2(off_t - off_d);
-    }
+    // S_t / S_d in natural-exp units, for the sampler's classification
+    pl.g = (!FILT && path == kPathReject) ? normaliser_ratio(rs.Mt, rs.St, rs.Md, rs.Sd, c) : 0.0;
     pl.pad2 = 0.0;
     out.plan[b] = pl;
     if (out.n_emitted) out.n_emitted[b] = stop + 1;
@@ -189,6 +193,56 @@ __device__ __forceinline__ void accept_scan(int b, int lane, int K, float c, dou
     if (out.stop_out) out.stop_out[b] = stop;
     if (out.path_out) out.path_out[b] = path;
   }
+}
+
+// The scan of request b by one wave (lane 0..63), with its inputs gathered:
+// the drafted tokens and uniforms, the logits at the drafted tokens and the
+// statistics of all K+1 target and K draft rows, every load that does not
+// depend on another issued up front (rows beyond draft_len are loaded but
+// never used).  Without filters the row statistics are the chunk partials
+// of the row-statistics pass and the logits at the drafted tokens the ones
+// it recorded; with top-k / top-p they are the per-row FiltRow and two
+// gathers from the logits.
+template <typename T, bool FILT>
+__device__ __forceinline__ void accept_request(
+    int b, int lane, const T* __restrict__ tgt, const T* __restrict__ dft,
+    const int* __restrict__ tokens, const int* __restrict__ draft_len, const float* __restrict__ u,
+    const float* __restrict__ u_final, int K, int V, int nch_row, float c, double invT,
+    int eos_id, const float2* __restrict__ part, const float* __restrict__ zx,
+    const FiltRow* __restrict__ frows, const AcceptOut& out) {
+  const int R = 2 * K + 1;
+  const int nb_raw = draft_len ? draft_len[b] : 0;   // null: no drafts (sampling)
+  const float uf = u_final[b];
+  int x = -1;
+  float uk = 0.f, zt = -INFINITY, zd = -INFINITY;
+  if (lane < K) {
+    x = tokens[(size_t)b * K + lane];
+    uk = u[(size_t)b * K + lane];
+    if constexpr (!FILT) {
+      zt = zx[(size_t)b * 2 * K + lane];            // meaningful where the scan reads it
+      zd = zx[(size_t)b * 2 * K + K + lane];
+    }
+  }
+  const bool xin = lane < K && x >= 0 && x < V;
+  LaneRows rs;
+  if constexpr (FILT) {
+    if (xin) {
+      zt = to_f32(tgt[target_row_off(b, lane, K, V) + x]);
+      zd = to_f32(dft[draft_row_off(b, lane, K, V) + x]);
+    }
+    if (lane <= K) rs.ft = frows[(size_t)b * R + lane];
+    if (lane < K) rs.fd = frows[(size_t)b * R + K + 1 + lane];
+    if (K == kWave) rs.fk = frows[(size_t)b * R + K];       // uniform: the bonus row of 64 drafts
+  } else {
+    const float2* prow = part + (size_t)b * R * nch_row;
+    combine_rows(prow + (size_t)lane * nch_row, prow + (size_t)(K + 1 + lane) * nch_row, nch_row,
+                 c, lane <= K, lane < K, rs.Mt, rs.St, rs.Md, rs.Sd);
+    if (K == kWave) {                                        // uniform: the bonus row of 64 drafts
+      float md, sd;
+      combine_rows(prow + (size_t)K * nch_row, prow, nch_row, c, true, false, rs.Mk, rs.Sk, md, sd);
+    }
+  }
+  accept_scan<FILT>(b, lane, K, c, invT, eos_id, nb_raw, uf, x, uk, xin, zt, zd, rs, out);
 }
 
 }  // namespace specv

@@ -23,7 +23,7 @@ template <typename T, int VECS>
 __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
     const int* __restrict__ tokens, int K, int V, int nchunk, int row_lo, float c,
-    float2* __restrict__ part, float* __restrict__ zx) {
+    float2* __restrict__ part, float* __restrict__ zx, int* __restrict__ arrivals) {
   constexpr int N = Elem<T>::kPerVec;
   constexpr int kChunk = kRowThreads * VECS * N;
   const int R = 2 * K + 1;
@@ -34,6 +34,9 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   const int r = row_lo + rq % (R - row_lo);
   const int b = rq / (R - row_lo);
   const size_t rr = (size_t)b * R + r;
+  // Clears the request's arrival counter of the small-batch kernel that
+  // follows (null otherwise), whatever the request's rows.
+  if (arrivals && chunk == 0 && r == row_lo) arrivals[b] = 0;
   const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
   if (nb < 0 || nb > K) return;                      // the accept scan reports the error
   const bool is_target = r <= K;
@@ -130,7 +133,8 @@ int row_stats_chunk(bool bf16) {
 
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                             const int* tokens, int B, int K, int V, int nchunk, float c,
-                            float2* part, float* zx, hipStream_t stream, int row_lo) {
+                            float2* part, float* zx, hipStream_t stream, int row_lo,
+                            int* arrivals) {
   if (row_lo < 0 || row_lo > 2 * K) return hipErrorInvalidValue;
   const size_t blocks = (size_t)B * (2 * K + 1 - row_lo) * nchunk;
   if (blocks == 0) return hipSuccess;
@@ -138,11 +142,11 @@ hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const i
   if (bf16)
     row_stats_kernel<bf16_t, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
         static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, tokens, K, V,
-        nchunk, row_lo, c, part, zx);
+        nchunk, row_lo, c, part, zx, arrivals);
   else
     row_stats_kernel<float, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
         static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, tokens, K, V,
-        nchunk, row_lo, c, part, zx);
+        nchunk, row_lo, c, part, zx, arrivals);
   return hipGetLastError();
 }
 

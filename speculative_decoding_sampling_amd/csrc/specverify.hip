@@ -11,12 +11,14 @@
 
 #include "accept_core.h"
 #include "common.h"
+#include "sample_core.h"
 
 namespace specv {
 int row_stats_chunk(bool bf16);
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                             const int* tokens, int B, int K, int V, int nchunk, float c,
-                            float2* part, float* zx, hipStream_t stream, int row_lo = 0);
+                            float2* part, float* zx, hipStream_t stream, int row_lo = 0,
+                            int* arrivals = nullptr);
 int lm_head_tiles(int V);
 size_t lm_head_packed_elems(int V, int D);
 hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int D,
@@ -54,6 +56,13 @@ hipError_t launch_sample_finish(bool bf16, const void* tgt, const void* dft, con
                                 int B, int K, int V, int nch, double invT, const Plan* plan,
                                 const ChunkRec* recs, const Tie* ties, int* out_tokens,
                                 double* rmass_out, hipStream_t stream);
+size_t small_blocks(int B, int K, int V);
+hipError_t launch_verify_small(bool bf16, const void* tgt, const void* dft, const int* tokens,
+                               const int* draft_len, const float* u, const float* u_final, int B,
+                               int K, int V, int nch_row, float c, double invT, int eos_id,
+                               const float2* part, const float* zx, ChunkRec* recs, Tie* ties,
+                               PairStat* pstat, int* arrivals, const AcceptOut& out,
+                               hipStream_t stream);
 hipError_t launch_exp64_selftest(const double* x, double* y, int n, hipStream_t stream);
 hipError_t launch_beta(bool bf16, bool filt, const void* tgt, const void* dft,
                        const int* draft_len, int B, int K, int V, int nch_row, float c,
@@ -73,12 +82,23 @@ hipError_t launch_monitor_update(const int32_t* draft_tokens, const int32_t* dra
 // Kernel stages of one call, in launch order (specv_verify_timed records an
 // event after each), by path: without filters; top-k / top-p through the
 // candidate select (0 < top_k <= kFiltMaxTopK, candidates fitting the merge);
-// top-k / top-p through the general radix select (every other setting).
-const char* const kStageNames[3][4] = {
+// top-k / top-p through the general radix select (every other setting);
+// without filters at small sizes, through the one-kernel tail.
+constexpr int kNumPaths = 4;
+const char* const kStageNames[kNumPaths][4] = {
     {"row_stats", "accept", "sample_pass", "sample_finish"},
     {"filter_cand", "filter_merge", "accept", "sample_list"},
-    {"filter_rows", "accept", "sample_list", nullptr}};
-constexpr int kNumStages[3] = {4, 4, 3};
+    {"filter_rows", "accept", "sample_list", nullptr},
+    {"row_stats", "verify_small", nullptr, nullptr}};
+constexpr int kNumStages[kNumPaths] = {4, 4, 3, 2};
+
+// Unfiltered calls with at most this many (request, row pair, 2048-token
+// chunk) triples, B (K+1) ceil(V/2048), take the small-batch path
+// (specv_set_small_batch_limit changes it).  Measured on MI355X: the
+// one-kernel tail wins while its speculative float64 passes over every row
+// pair stay below a couple of workgroups per CU.
+constexpr long long kSmallBatchLimitDefault = 1024;
+std::atomic<long long> g_small_limit{kSmallBatchLimitDefault};
 
 namespace {
 
@@ -94,6 +114,10 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 //   plans          Plan     [B]
 //   chunk records  ChunkRec [B][nch_samp]             (fp64 sums per sampler chunk)
 //   near ties      Tie      [B][nch_samp][kTieCap]
+// and on the small-batch path, where the chunk pass runs for every row pair,
+// chunk records and near ties [B][K+1][nch_samp](...) instead, plus
+//   pair statistics PairStat [B][K+1]
+//   arrival counters int     [B]
 // With top-k / top-p:
 //   plans          Plan     [B]
 //   candidates     uint64   [B][2K+1][row_stride]     (key, id); cap per chunk, >= 256 last
@@ -103,9 +127,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   bool filt = false;
   bool cand = false;         // filtered through the candidate select
+  bool small = false;        // unfiltered, through the one-kernel tail
   int nch_row = 0, nch_samp = 0, nch_filt = 0, cap = 0;
   size_t off_row = 0, off_zx = 0, off_beta = 0, off_plan = 0, off_recs = 0, off_ties = 0;
-  size_t off_cand = 0, off_counts = 0, off_frows = 0, off_kept = 0, off_cmass = 0, total = 0;
+  size_t off_cand = 0, off_counts = 0, off_frows = 0, off_kept = 0, off_cmass = 0;
+  size_t off_pstat = 0, off_arrive = 0, total = 0;
 };
 
 bool filters_on(int V, int top_k, float top_p) { return (top_k > 0 && top_k < V) || top_p < 1.0f; }
@@ -118,18 +144,30 @@ bool candidate_path(int V, int top_k) {
   return nch <= kFiltMaxChunks && filter_row_stride(nch, top_k) <= kFiltSortMax;
 }
 
-// Stage-table index of a call: 0 unfiltered, 1 candidate select, 2 radix select.
-int path_kind(int V, int top_k, float top_p) {
-  if (!filters_on(V, top_k, top_p)) return 0;
+// An unfiltered call small enough for the one-kernel tail.
+bool small_path(int B, int K, int V) {
+  const size_t blocks = small_blocks(B, K, V);
+  return blocks > 0 && (long long)(blocks - B) <= g_small_limit.load(std::memory_order_relaxed);
+}
+
+// Stage-table index of a call: 0 unfiltered, 1 candidate select, 2 radix
+// select, 3 unfiltered through the small-batch tail.
+int path_kind(int B, int K, int V, int top_k, float top_p) {
+  if (!filters_on(V, top_k, top_p)) return small_path(B, K, V) ? 3 : 0;
   return candidate_path(V, top_k) ? 1 : 2;
 }
 
-Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p) {
+// allow_small = false keeps an unfiltered call on the four-kernel layout
+// (the fused LM-head call, which runs those kernels whatever the size).
+Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p,
+                   bool allow_small = true) {
   Layout L;
   const size_t R = (size_t)(2 * K + 1);
   size_t off = 0;
   L.filt = filters_on(V, top_k, top_p);
   if (!L.filt) {
+    L.small = allow_small && small_path(B, K, V);
+    const size_t pairs = L.small ? (size_t)(K + 1) : 1;   // chunk-pass row pairs per request
     const int ch = row_stats_chunk(bf16);
     L.nch_row = (V + ch - 1) / ch;
     L.nch_samp = (V + kSampChunk - 1) / kSampChunk;
@@ -142,9 +180,15 @@ Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p) {
     L.off_plan = off;
     off = align_up(off + (size_t)B * sizeof(Plan));
     L.off_recs = off;
-    off = align_up(off + (size_t)B * L.nch_samp * sizeof(ChunkRec));
+    off = align_up(off + (size_t)B * pairs * L.nch_samp * sizeof(ChunkRec));
     L.off_ties = off;
-    off = align_up(off + (size_t)B * L.nch_samp * kTieCap * sizeof(Tie));
+    off = align_up(off + (size_t)B * pairs * L.nch_samp * kTieCap * sizeof(Tie));
+    if (L.small) {
+      L.off_pstat = off;
+      off = align_up(off + (size_t)B * pairs * sizeof(PairStat));
+      L.off_arrive = off;
+      off = align_up(off + (size_t)B * sizeof(int));
+    }
   } else {
     L.cand = candidate_path(V, top_k);
     L.off_plan = off;
@@ -240,9 +284,18 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
     float* zx = reinterpret_cast<float*>(ws + L.off_zx);
     ChunkRec* recs = reinterpret_cast<ChunkRec*>(ws + L.off_recs);
     Tie* ties = reinterpret_cast<Tie*>(ws + L.off_ties);
+    int* arrivals = L.small ? reinterpret_cast<int*>(ws + L.off_arrive) : nullptr;
     e = launch_row_stats(bf16, target, draft, draft_len, tokens, B, K, V, L.nch_row, c, row_part,
-                         zx, stream);
+                         zx, stream, 0, arrivals);
     if (e != hipSuccess || !mark(1)) return SPECV_EHIP;
+    if (L.small) {
+      PairStat* pstat = reinterpret_cast<PairStat*>(ws + L.off_pstat);
+      e = launch_verify_small(bf16, target, draft, tokens, draft_len, u, u_final, B, K, V,
+                              L.nch_row, c, invT, eos_id, row_part, zx, recs, ties, pstat,
+                              arrivals, out, stream);
+      if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
+      return SPECV_OK;
+    }
     e = launch_accept(bf16, false, target, draft, tokens, draft_len, u, u_final, B, K, V,
                       L.nch_row, c, invT, eos_id, row_part, zx, nullptr, out, stream);
     if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
@@ -288,7 +341,7 @@ struct LmLayout {
 
 LmLayout make_lm_layout(int B, int K, int V, int top_k, float top_p) {
   LmLayout L;
-  L.base = make_layout(B, K, V, true, top_k, top_p);
+  L.base = make_layout(B, K, V, true, top_k, top_p, false);
   L.off_tpart = L.base.total;
   L.total = align_up(L.off_tpart +
                      (size_t)B * (K + 1) * lm_head_tiles(V) * sizeof(float2));
@@ -489,7 +542,7 @@ specv_status_t specv_verify_timed(const void* target_logits, const void* draft_l
                                   int32_t* n_emitted, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream, hipEvent_t* events) {
   if (!events) return SPECV_EINVAL;
-  const int nst = specv::kNumStages[specv::path_kind(V, top_k, top_p)];
+  const int nst = specv::kNumStages[specv::path_kind(B, K, V, top_k, top_p)];
   for (int i = 0; i <= nst; ++i)
     if (!events[i]) return SPECV_EINVAL;
   return specv::run(target_logits, draft_logits, dtype, draft_tokens, draft_len, u, u_final, B,
@@ -497,9 +550,17 @@ specv_status_t specv_verify_timed(const void* target_logits, const void* draft_l
                     workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr, events);
 }
 
-int specv_num_stages(int kind) { return (kind >= 0 && kind < 3) ? specv::kNumStages[kind] : 0; }
+int specv_num_stages(int kind) {
+  return (kind >= 0 && kind < specv::kNumPaths) ? specv::kNumStages[kind] : 0;
+}
 
-int specv_path_kind(int V, int top_k, float top_p) { return specv::path_kind(V, top_k, top_p); }
+int specv_path_kind(int B, int K, int V, int top_k, float top_p) {
+  return specv::path_kind(B, K, V, top_k, top_p);
+}
+
+long long specv_set_small_batch_limit(long long limit) {
+  return specv::g_small_limit.exchange(limit < 0 ? 0 : limit);
+}
 
 specv_status_t specv_bench_row_stats(const void* const* targets, const void* const* drafts,
                                      const int32_t* const* draft_tokens,
@@ -719,7 +780,7 @@ specv_status_t specv_selftest_exp64(const double* x, double* y, int n, hipStream
 }
 
 const char* specv_stage_name(int kind, int i) {
-  if (kind < 0 || kind >= 3) return nullptr;
+  if (kind < 0 || kind >= specv::kNumPaths) return nullptr;
   return (i >= 0 && i < specv::kNumStages[kind]) ? specv::kStageNames[kind][i] : nullptr;
 }
 
@@ -736,6 +797,6 @@ const char* specv_status_string(specv_status_t status) {
   return "unknown status";
 }
 
-int specv_version(void) { return 102; }
+int specv_version(void) { return 103; }
 
 }  // extern "C"

@@ -21,6 +21,16 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
+@pytest.fixture(params=["four_kernel", "one_kernel_tail"])
+def unfiltered_path(request):
+    """Runs a test on each unfiltered path: the four-kernel path (the
+    small-batch limit at 0) and the small-batch tail (the limit so large
+    that every unfiltered call takes it)."""
+    old = binding.set_small_batch_limit(0 if request.param == "four_kernel" else 1 << 40)
+    yield request.param
+    binding.set_small_batch_limit(old)
+
+
 def oracle_sampler(z, T, k, p, uni):
     P, _ = O.processed_distribution(z, f32(T), k, f32(p))
     return O.icdf(P, uni)[0]
@@ -60,7 +70,7 @@ def assert_parity(w, requests=None, label="", check_flags=True):
 
 
 @pytest.mark.parametrize("cfg,B", [(1, None), (2, None), (3, 8), (5, 16)])
-def test_parity_reduced_batch(cfg, B):
+def test_parity_reduced_batch(cfg, B, unfiltered_path):
     assert_parity(make_workload(cfg, B=B))
 
 
@@ -83,7 +93,36 @@ def test_parity_full_size(cfg):
     assert np.all((n == -1) | ((n >= 1) & (n <= w.draft_len + 1)))
 
 
-def test_p_equals_q_is_always_bonus_with_alpha_exactly_one():
+@pytest.mark.parametrize("cfg,B", [(1, None), (2, None), (3, 8), (5, 16)])
+def test_small_batch_tail_equals_four_kernel_path(cfg, B):
+    # The same inputs through both unfiltered paths: the small-batch tail runs
+    # the same accept scan, chunk pass and draw code on the same row
+    # statistics, so every output agrees (the residual mass up to the order
+    # of float64 sums, which is the same too).  Workload 5 brings ragged
+    # lengths, p == q requests and EOS; the default limit puts workloads 1
+    # and 2 on the tail.
+    w = make_workload(cfg, B=B)
+    print(f"[tail] cfg={cfg} B={w.B} K={w.K} V={w.V} kind="
+          f"{binding.path_kind(w.B, w.K, w.V)}", flush=True)
+    if cfg in (1, 2):
+        assert binding.path_kind(w.B, w.K, w.V) == 3
+    old = binding.set_small_batch_limit(0)
+    try:
+        four = run_gpu(w)
+        binding.set_small_batch_limit(1 << 40)
+        tail = run_gpu(w)
+    finally:
+        binding.set_small_batch_limit(old)
+    for k in ("out_tokens", "n_emitted", "stop_pos", "path", "accept_prob"):
+        assert np.array_equal(four[k], tail[k], equal_nan=True), k
+    rel = np.abs(four["residual_mass"] - tail["residual_mass"]) / np.maximum(
+        np.abs(four["residual_mass"]), 1e-300)
+    assert np.all(rel <= 1e-12), float(rel.max())
+    rep = compare(tail, run_oracle(w), w.K)
+    assert not rep["mismatches"], rep["mismatches"][:3]
+
+
+def test_p_equals_q_is_always_bonus_with_alpha_exactly_one(unfiltered_path):
     # EOS off: with p == q an accepted draft may itself be the EOS token.
     w = make_workload(5, B=16)
     w.draft[:] = w.target[:, :w.K]
@@ -96,14 +135,14 @@ def test_p_equals_q_is_always_bonus_with_alpha_exactly_one():
     assert not rep["mismatches"], rep["mismatches"][:3]
 
 
-def test_deterministic_bitwise():
+def test_deterministic_bitwise(unfiltered_path):
     w = make_workload(3, B=8)
     a, b = run_gpu(w), run_gpu(w)
     for k in a:
         assert np.array_equal(a[k], b[k], equal_nan=True), k
 
 
-def test_per_request_errors_are_isolated():
+def test_per_request_errors_are_isolated(unfiltered_path):
     w = make_workload(1)
     w.draft_len[0] = 5                       # draft_len > K
     w.draft_len[1] = -1                      # negative draft_len
@@ -119,7 +158,7 @@ def test_per_request_errors_are_isolated():
     assert not rep["mismatches"], rep["mismatches"][:3]
 
 
-def test_draft_len_zero_and_k_zero():
+def test_draft_len_zero_and_k_zero(unfiltered_path):
     w = make_workload(1)
     w.draft_len[:] = 0
     assert_parity(w, label="draft_len=0")
@@ -138,7 +177,7 @@ def test_draft_len_zero_and_k_zero():
 
 
 @pytest.mark.parametrize("V", [1, 3, 4097, 10007])
-def test_unaligned_and_tiny_vocabularies(V):
+def test_unaligned_and_tiny_vocabularies(V, unfiltered_path):
     rng = np.random.default_rng(V)
     B, K = 6, 3
     t = rng.normal(0, 2, size=(B, K + 1, V)).astype(np.float32)
@@ -171,7 +210,7 @@ def _custom_workload(t, d, draft_len, rng, dtype="f32", T=1.0, seed=0):
                     u=uniforms(rng, (B, K)), u_final=uniforms(rng, (B,)))
 
 
-def test_maximum_draft_length():
+def test_maximum_draft_length(unfiltered_path):
     # K = 64, the largest draft length the call takes (SPECV_MAX_K): drafts
     # close to the target so the first-rejection scan runs deep, one request
     # whose draft rows equal its target rows (every draft accepted, then the
@@ -305,7 +344,7 @@ def test_exp64_against_numpy():
     assert np.all(z == 0.0)
 
 
-def test_sampler_exact_path_with_many_near_ties():
+def test_sampler_exact_path_with_many_near_ties(unfiltered_path):
     # Draft = target + N(0, 1e-4^2): nearly every token is a near tie, so the
     # chunks overflow their tie slots and the sampler takes its exact path.
     # u close to 1 forces rejections whenever p(x) < q(x).
@@ -419,7 +458,7 @@ def test_parity_radix_select(cfg, B, top_k, top_p):
     from speculative_decoding_sampling_amd import binding as bd
     w = make_workload(cfg, B=B, draft_sampler=oracle_sampler)
     w.top_k, w.top_p = top_k, f32(top_p)
-    assert bd.path_kind(w.V, w.top_k, w.top_p) == 2
+    assert bd.path_kind(w.B, w.K, w.V, w.top_k, w.top_p) == 2
     redraw_tokens(w, 100 + cfg)
     rep, g, o = assert_parity(w, label=f"radix select top_k={top_k} top_p={top_p}")
     assert rep["positions"] > 0
@@ -465,20 +504,25 @@ def test_many_draws_large_vocabulary_non_unit_temperature():
 
 
 @pytest.mark.parametrize("cfg,B,top_k,top_p", [(3, 8, None, None), (4, 6, None, None),
-                                              (3, 6, 0, 0.9), (4, 3, 0, 0.9)])
+                                              (3, 6, 0, 0.9), (4, 3, 0, 0.9),
+                                              (1, None, None, None), (2, None, None, None)])
 def test_graph_replay_matches_eager(cfg, B, top_k, top_p):
     # One call captured in a HIP graph and replayed several times, with eager
     # calls on other inputs and synchronisations in between: every replay
     # gives the eager result on its inputs (the call records no memset, so
-    # replays after the first are as good as the first).  The last two cases
-    # take the radix path (top-p alone): the bf16 histogram select with the
-    # streamed draw's chunk pass, and the float32 multi-pass select.
+    # replays after the first are as good as the first).  Cases 3 and 4 take
+    # the radix path (top-p alone): the bf16 histogram select with the
+    # streamed draw's chunk pass, and the float32 multi-pass select; the last
+    # two the small-batch tail, whose arrival counters the row-statistics
+    # kernel clears in every call.
     filt = cfg == 4 or top_p is not None
     kw = dict(top_k=top_k, top_p=top_p, draft_sampler=oracle_sampler) if filt else {}
     w = make_workload(cfg, B=B, **kw)
     other = make_workload(cfg, B=B, seed=77, **kw)
     if top_p is not None:
-        assert binding.path_kind(w.V, w.top_k, w.top_p) == 2
+        assert binding.path_kind(w.B, w.K, w.V, w.top_k, w.top_p) == 2
+    if cfg in (1, 2):
+        assert binding.path_kind(w.B, w.K, w.V, w.top_k, w.top_p) == 3
     a = upload(w, DEV)
     b = upload(other, DEV)
     ws = torch.empty(binding.workspace_bytes(w.B, w.K, w.V,
@@ -564,7 +608,7 @@ def assert_sample_parity(logits, u, T, top_k, top_p, dtype, label=""):
 
 
 @pytest.mark.parametrize("cfg,R", [(1, 32), (2, None), (3, 48), (5, 32)])
-def test_sample_matches_oracle_unfiltered(cfg, R):
+def test_sample_matches_oracle_unfiltered(cfg, R, unfiltered_path):
     w = make_workload(cfg, B=R if cfg != 2 else None)
     rows = w.draft.reshape(-1, w.V)
     rng = np.random.default_rng(700 + cfg)
@@ -619,7 +663,7 @@ def test_sample_filtered_sparse_and_tied_rows():
     assert_sample_parity(rows, u, 1.0, top_k, 1.0, "f32", label="sparse/tied rows, top-k only")
 
 
-def test_sample_edge_cases():
+def test_sample_edge_cases(unfiltered_path):
     # u = 0 and the largest uniform below 1; a row with one finite logit; rows
     # with no finite logit or a uniform outside [0, 1) give -1, alone.
     rng = np.random.default_rng(11)

@@ -35,7 +35,8 @@ def test_header_declares_the_api():
     names = declared_functions()
     assert set(names) == {"specv_workspace_bytes", "specv_verify", "specv_verify_debug",
                           "specv_verify_timed", "specv_num_stages", "specv_stage_name",
-                          "specv_path_kind", "specv_verify_noalloc",
+                          "specv_path_kind", "specv_set_small_batch_limit",
+                          "specv_verify_noalloc",
                           "specv_status_string", "specv_version", "specv_selftest_exp64",
                           "specv_bench_row_stats", "specv_sample",
                           "specv_acceptance_rates", "specv_round_stats",
@@ -130,21 +131,43 @@ def test_stage_names(lib):
     lib.specv_stage_name.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.specv_stage_name.restype = ctypes.c_char_p
     lib.specv_num_stages.argtypes = [ctypes.c_int]
-    for kind, first in ((0, b"row_stats"), (1, b"filter_cand"), (2, b"filter_rows")):
+    for kind, first in ((0, b"row_stats"), (1, b"filter_cand"), (2, b"filter_rows"),
+                        (3, b"row_stats")):
         n = lib.specv_num_stages(kind)
         names = [lib.specv_stage_name(kind, i) for i in range(n)]
         assert n >= 1 and names[0] == first and all(names)
         assert lib.specv_stage_name(kind, n) is None
         assert lib.specv_stage_name(kind, -1) is None
-    assert lib.specv_num_stages(3) == 0 and lib.specv_stage_name(3, 0) is None
+    assert lib.specv_num_stages(4) == 0 and lib.specv_stage_name(4, 0) is None
+    assert lib.specv_stage_name(3, 1) == b"verify_small"
     pk = lib.specv_path_kind
-    pk.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_float]
+    pk.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float]
     pk.restype = ctypes.c_int
-    assert pk(128256, 0, 1.0) == 0 and pk(128256, 128256, 1.0) == 0   # filters off
-    assert pk(152064, 50, 0.9) == 1 and pk(152064, 100, 1.0) == 1      # candidate select
-    assert pk(152064, 128, 1.0) == 2        # 128 at 19 chunks: slots beyond the on-chip list
-    assert pk(152064, 0, 0.9) == 2 and pk(152064, 1000, 1.0) == 2      # radix select
-    assert pk(300000, 50, 0.9) == 2                                     # too many chunks
+    assert pk(64, 4, 128256, 0, 1.0) == 0 and pk(64, 4, 128256, 128256, 1.0) == 0   # filters off
+    assert pk(256, 8, 152064, 50, 0.9) == 1 and pk(1, 0, 152064, 100, 1.0) == 1      # candidates
+    assert pk(1, 1, 152064, 128, 1.0) == 2   # 128 at 19 chunks: slots beyond the on-chip list
+    assert pk(64, 4, 152064, 0, 0.9) == 2 and pk(1, 4, 152064, 1000, 1.0) == 2      # radix
+    assert pk(1, 4, 300000, 50, 0.9) == 2                                           # chunks
+    # small sizes without filters: B (K+1) ceil(V/2048) within the limit (1024 by default)
+    assert pk(8, 4, 4096, 0, 1.0) == 3 and pk(1, 5, 32000, 0, 1.0) == 3
+    assert pk(1, 5, 32000, 0, 0.9) == 2                   # filters keep their own paths
+    assert pk(64, 3, 2048 * 4, 0, 1.0) == 3 and pk(64, 3, 2048 * 4 + 1, 0, 1.0) == 0
+    lim = lib.specv_set_small_batch_limit
+    lim.argtypes = [ctypes.c_longlong]
+    lim.restype = ctypes.c_longlong
+    old = lim(0)
+    try:
+        assert old == 1024 and pk(8, 4, 4096, 0, 1.0) == 0
+        ws = lib.specv_workspace_bytes
+        ws.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                       ctypes.c_float]
+        ws.restype = ctypes.c_size_t
+        big = ws(8, 4, 4096, 0, 0, 1.0)
+        assert lim(1 << 40) == 0 and pk(64, 4, 128256, 0, 1.0) == 3
+        assert ws(8, 4, 4096, 0, 0, 1.0) > big            # the pass runs for every row pair
+        assert lim(-5) == 1 << 40 and pk(8, 4, 4096, 0, 1.0) == 0   # negative: off
+    finally:
+        lim(old)
 
 
 def test_status_strings(lib):
@@ -152,7 +175,7 @@ def test_status_strings(lib):
     s.argtypes = [ctypes.c_int]
     s.restype = ctypes.c_char_p
     assert s(0) == b"ok" and s(1) == b"invalid argument"
-    assert lib.specv_version() == 102
+    assert lib.specv_version() == 103
 
 
 def test_bench_hook_rejects_bad_arguments(lib):
