@@ -50,7 +50,7 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC = {
     "B64_K4_V128256_bf16": {
         "sources": ("row_stats.hip", "common.h"),
-        "sources_sha256_16": "83d31da22561004c", "bytes": 148137711},
+        "sources_sha256_16": "cb88da0f480d33cd", "bytes": 148152996},
     "B256_K8_V152064_f32_topk50_topp0.9": {
         "sources": ("filter.hip", "filter_common.h", "radix_select.h", "exp64.h", "common.h"),
         "sources_sha256_16": "8a57328987c3919c", "bytes": 2687321286},

@@ -413,7 +413,7 @@ SPECV_API specv_status_t specv_verify_timed(const void *target_logits, const voi
  * 3 give the same results. */
 SPECV_API int specv_path_kind(int B, int K, int V, int top_k, float top_p);
 /* Sets the size up to which unfiltered calls take path 3: calls with
- * B * (K+1) * ceil(V / 2048) <= limit do (default 1024; 0 turns the path
+ * B * (K+1) * ceil(V / 2048) <= limit do (default 384; 0 turns the path
  * off, a huge value forces it).  Process-wide, for all devices; returns the
  * previous limit.  A call made while another thread changes the limit may
  * take either path; workspace sizes follow the limit in force. */

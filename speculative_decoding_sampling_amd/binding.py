@@ -128,8 +128,8 @@ def path_kind(B, K, V, top_k=0, top_p=1.0):
 
 def set_small_batch_limit(limit):
     """Largest B * (K+1) * ceil(V / 2048) of an unfiltered call that takes
-    path 3 (0: never, a huge value: always).  Process-wide; returns the
-    previous limit."""
+    path 3 (default 384; 0: never, a huge value: always).  Process-wide;
+    returns the previous limit."""
     return int(load_library().specv_set_small_batch_limit(int(limit)))
 
 

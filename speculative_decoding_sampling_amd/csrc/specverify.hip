@@ -95,9 +95,10 @@ constexpr int kNumStages[kNumPaths] = {4, 4, 3, 2};
 // Unfiltered calls with at most this many (request, row pair, 2048-token
 // chunk) triples, B (K+1) ceil(V/2048), take the small-batch path
 // (specv_set_small_batch_limit changes it).  Measured on MI355X: the
-// one-kernel tail wins while its speculative float64 passes over every row
-// pair stay below a couple of workgroups per CU.
-constexpr long long kSmallBatchLimitDefault = 1024;
+// one-kernel tail is ~5 us faster up to ~320 triples, even at ~380, and
+// slower from ~600 on, where its per-workgroup L2 writebacks (one per
+// arriving workgroup, serialised within an XCD) outgrow the launches saved.
+constexpr long long kSmallBatchLimitDefault = 384;
 std::atomic<long long> g_small_limit{kSmallBatchLimitDefault};
 
 namespace {

@@ -148,16 +148,16 @@ def test_stage_names(lib):
     assert pk(1, 1, 152064, 128, 1.0) == 2   # 128 at 19 chunks: slots beyond the on-chip list
     assert pk(64, 4, 152064, 0, 0.9) == 2 and pk(1, 4, 152064, 1000, 1.0) == 2      # radix
     assert pk(1, 4, 300000, 50, 0.9) == 2                                           # chunks
-    # small sizes without filters: B (K+1) ceil(V/2048) within the limit (1024 by default)
+    # small sizes without filters: B (K+1) ceil(V/2048) within the limit (384 by default)
     assert pk(8, 4, 4096, 0, 1.0) == 3 and pk(1, 5, 32000, 0, 1.0) == 3
     assert pk(1, 5, 32000, 0, 0.9) == 2                   # filters keep their own paths
-    assert pk(64, 3, 2048 * 4, 0, 1.0) == 3 and pk(64, 3, 2048 * 4 + 1, 0, 1.0) == 0
+    assert pk(24, 3, 2048 * 4, 0, 1.0) == 3 and pk(24, 3, 2048 * 4 + 1, 0, 1.0) == 0
     lim = lib.specv_set_small_batch_limit
     lim.argtypes = [ctypes.c_longlong]
     lim.restype = ctypes.c_longlong
     old = lim(0)
     try:
-        assert old == 1024 and pk(8, 4, 4096, 0, 1.0) == 0
+        assert old == 384 and pk(8, 4, 4096, 0, 1.0) == 0
         ws = lib.specv_workspace_bytes
         ws.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                        ctypes.c_float]
