@@ -53,7 +53,7 @@ TRAFFIC = {
         "sources_sha256_16": "cb88da0f480d33cd", "bytes": 148152996},
     "B256_K8_V152064_f32_topk50_topp0.9": {
         "sources": ("filter.hip", "filter_common.h", "radix_select.h", "exp64.h", "common.h"),
-        "sources_sha256_16": "8a57328987c3919c", "bytes": 2687321286},
+        "sources_sha256_16": "1fb333c32823445b", "bytes": 2687321350},
     "B64_K4_V128256_bf16_topp0.9": {
         "sources": ("filter_rows.hip", "filter_common.h", "hist_select.h", "radix_select.h",
                     "exp64.h", "common.h"),

@@ -291,7 +291,8 @@ __device__ __forceinline__ void lds_bitonic_desc(uint64_t* a, int n) {
 //  - gather: every load first, the chunk of flat index f by binary search
 //    over the offsets (in this wave's LDS);
 //  - tau_k = the largest 32-bit key v with #{keys >= v} >= k, bit by bit
-//    from the top (32 rounds of compare-and-count, wave sums on DPP);
+//    from the top (up to 32 rounds of compare-and-count, counted with
+//    ballots and scalar popcounts);
 //  - the keys >= tau_k, one per lane, sorted descending in registers; top-p
 //    in float64 by a lane-order scan and ballots; the kept list sorted by id
 //    in registers.
@@ -303,19 +304,50 @@ constexpr int kWavePer = kWaveCand / kWave;           // candidates per lane
 constexpr int kStatusRedo = 3;                        // internal: the block merge takes the row
 constexpr int kMergeWaves = kFiltThreads / kWave;     // rows per workgroup
 
-// Sum of an int over the wave on DPP (quad swaps, half-row and row
-// mirrors), then the four row sums read as scalars: short latency, no LDS.
+// Maximum of an int over the wave on DPP (quad swaps, half-row and row
+// mirrors), then the four row maxima read as scalars: short latency, no LDS.
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
   return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-  v += dpp_i<0xb1>(v);                               // quad_perm [1,0,3,2]
-  v += dpp_i<0x4e>(v);                               // quad_perm [2,3,0,1]
-  v += dpp_i<0x141>(v);                              // row_half_mirror
-  v += dpp_i<0x140>(v);                              // row_mirror
-  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
-         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_i<0xb1>(v));
+  v = max(v, dpp_i<0x4e>(v));
+  v = max(v, dpp_i<0x141>(v));
+  v = max(v, dpp_i<0x140>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<0xb1>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x4e>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x141>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x140>((int)v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Inclusive prefix sum of one double per lane over the wave, in lane order,
+// on DPP lane moves (each 64-bit value moved as two 32-bit halves): shifts
+// by 1, 2, 4 and 8 within each row of 16, then row 15's total into rows 1
+// and 3, then lane 31's into rows 2 and 3.  A fixed order of additions.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_take_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xf, true);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_incl_scan_f64(double x) {
+  x += dpp_take_f64<0x111, 0xf>(x);
+  x += dpp_take_f64<0x112, 0xf>(x);
+  x += dpp_take_f64<0x114, 0xf>(x);
+  x += dpp_take_f64<0x118, 0xf>(x);
+  x += dpp_take_f64<0x142, 0xa>(x);
+  x += dpp_take_f64<0x143, 0xc>(x);
+  return x;
 }
 
 __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
@@ -349,18 +381,11 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
     over = cnt > slot;
     n = min(cnt, slot);
   }
-  int incl = n;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
-  const int n_all = __shfl(incl, kWave - 1, kWave);
+  const int incl = wave_incl_scan_dpp(n);
+  const int n_all = __builtin_amdgcn_readlane(incl, kWave - 1);
   // lanes per chunk: lane l reads chunk l / q, its entries l % q, l % q + q, ...
   const int q = kWave / max(nch, 1);
-  int nmax = n;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) nmax = max(nmax, __shfl_xor(nmax, o, kWave));
+  const int nmax = wave_max_i(n);
   if (__ballot(over) != 0 || nmax > q * kWavePer) {  // the block merge takes it
     if (lane == 0) {
       out.m = 0.f;
@@ -405,7 +430,9 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
   // largest of the 64 lane maxima is a lower bound (kk lanes hold a key
   // >= T0); the keys >= T0 (usually a few more than kk) are compacted, at
   // most four per lane, and tau_k is found among them bit by bit from the
-  // top.  With more than 256 such keys, among all of them.
+  // top.  With more than 256 such keys, among all of them.  (A bound from the
+  // kk-th largest of four group maxima per lane is tighter, but its own walk
+  // costs more than it saves.)
   const int kk = min(top_k, n_all);
   uint32_t lmax = 0u;
 #pragma unroll
@@ -413,27 +440,18 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
   uint32_t t0 = 0u, kmax;
   if (kk <= kWave) {
     const uint32_t sm = wave_sort_desc(lmax);
-    t0 = (uint32_t)__shfl((int)sm, kk - 1, kWave);
-    kmax = (uint32_t)__shfl((int)sm, 0, kWave);
+    t0 = (uint32_t)__builtin_amdgcn_readlane((int)sm, kk - 1);
+    kmax = (uint32_t)__builtin_amdgcn_readlane((int)sm, 0);
   } else {
-    kmax = lmax;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, kWave));
+    kmax = wave_max_u(lmax);
   }
-  // tau_k lies in [t0, kmax]: the bits above their highest difference are
-  // known, the walk starts below them
   const int top = 32 - __clz((int)(t0 ^ kmax));     // bits left to decide
   const uint32_t known = top >= 32 ? 0u : kmax & (0xffffffffu << top);
   int c0 = 0;
 #pragma unroll
   for (int i = 0; i < kWavePer; ++i) c0 += key[i] >= t0 && key[i] > 0u ? 1 : 0;
-  int incl0 = c0;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl0, o, kWave);
-    if (lane >= o) incl0 += y;
-  }
-  const int nt = __shfl(incl0, kWave - 1, kWave);
+  const int incl0 = wave_incl_scan_dpp(c0);
+  const int nt = __builtin_amdgcn_readlane(incl0, kWave - 1);
   uint32_t tk = known;
   int L = nt;                                        // #{keys >= tk} (every key >= t0 here)
   if (nt <= 4 * kWave) {
@@ -450,13 +468,14 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
       const int e = lane + kWave * r4;
       k4[r4] = e < nt ? s_sel[wid][e] : 0u;
     }
+    // each round counts with ballots and scalar popcounts: four VALU
+    // compares instead of a wave reduction
 #pragma unroll 1
     for (int bit = top - 1; bit >= 0; --bit) {
       const uint32_t tryv = tk | (1u << bit);
       int c = 0;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) c += k4[r4] >= tryv ? 1 : 0;
-      c = wave_sum_i(c);
+      for (int r4 = 0; r4 < 4; ++r4) c += __popcll(__ballot(k4[r4] >= tryv));
       if (c >= kk) {
         tk = tryv;
         L = c;
@@ -468,8 +487,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
       const uint32_t tryv = tk | (1u << bit);
       int c = 0;
 #pragma unroll
-      for (int i = 0; i < kWavePer; ++i) c += key[i] >= tryv ? 1 : 0;
-      c = wave_sum_i(c);
+      for (int i = 0; i < kWavePer; ++i) c += __popcll(__ballot(key[i] >= tryv));
       if (c >= kk) {
         tk = tryv;
         L = c;
@@ -492,12 +510,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
   int mine = 0;
 #pragma unroll
   for (int i = 0; i < kWavePer; ++i) mine += key[i] >= tk ? 1 : 0;
-  int pincl = mine;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(pincl, o, kWave);
-    if (lane >= o) pincl += y;
-  }
+  const int pincl = wave_incl_scan_dpp(mine);
   int pos = pincl - mine;
 #pragma unroll
   for (int i = 0; i < kWavePer; ++i)
@@ -511,24 +524,20 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
 
   // top-p over the sorted prefix, float64 (lane i holds entry i)
   const uint32_t k32 = lane < L ? (uint32_t)(x >> 32) : 0u;
-  const float m = unkey((uint32_t)(__shfl((long long)x, 0, kWave) >> 32));
+  const float m = unkey((uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), 0));
   const double md = (double)m;
   const bool in = lane < L;
   const double wgt = in ? exp64(((double)unkey(k32) - md) * invT, tbl) : 0.0;
-  double run = wgt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double y = __shfl_up(run, o, kWave);
-    if (lane >= o) run += y;
-  }
-  const double tot = __shfl(run, kWave - 1, kWave);
+  const double run = wave_incl_scan_f64(wgt);
+  const double tot = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(run), kWave - 1),
+                                      __builtin_amdgcn_readlane(__double2loint(run), kWave - 1));
   uint32_t tau = tk;
   int Lk = L;
   if (top_p < 1.0f) {
     // M = first sorted index whose running mass reaches top_p of the total
     const uint64_t hit = __ballot(in && run / tot >= (double)top_p);
     const int M = hit ? __ffsll((unsigned long long)hit) - 1 : L - 1;
-    tau = (uint32_t)__shfl((int)k32, M, kWave);
+    tau = (uint32_t)__builtin_amdgcn_readlane((int)k32, M);
     const uint64_t below = __ballot(in && k32 < tau);
     Lk = below ? __ffsll((unsigned long long)below) - 1 : L;
   }
