@@ -14,6 +14,7 @@
 #include "common.h"
 #include "exp64.h"
 #include "filter_common.h"
+#include "wave_scan.h"
 
 namespace specv {
 
@@ -26,8 +27,8 @@ namespace specv {
 // kept tokens, and after a rejection max(p - q, 0) with q the same over the
 // draft's kept tokens.  The chunk pass (one wave per chunk, the whole chip)
 // writes each chunk's mass; the draw copies them to LDS, every wave finds the
-// chunk holding t = u_final * total by a blocked prefix of its own, and wave
-// 0 scans inside that chunk.
+// chunk holding t = u_final * total by a blocked prefix of its own, and the
+// four waves scan inside that chunk, wave j its sub-block j.
 constexpr int kStreamSub = kWave * 8;                  // 512 tokens per sub-block
 constexpr int kStreamChunk = 4 * kStreamSub;           // 2048 tokens per chunk
 
@@ -58,7 +59,9 @@ __device__ __forceinline__ float pick8(const float* z, uint32_t i) {
 // .y p alone (the fall-back when the residual has no mass).  A token outside
 // the target's kept set adds exactly zero to both (p = 0, so p - q <= 0), so
 // each lane visits only its kept tokens, in element order: the same sums,
-// with far fewer exps when the kept set is a small share of the row.
+// with far fewer exps when the kept set is a small share of the row.  (All
+// four sub-blocks' loads issued before the first sum measured slower: 74
+// against 58 VGPRs, and the chunk pass already overlaps loads across waves.)
 template <typename T>
 __device__ __forceinline__ double2 chunk_masses(const T* __restrict__ trow,
                                                 const T* __restrict__ drow, int V, long c0,
@@ -123,7 +126,7 @@ template <typename T>
 __device__ void stream_draw(const T* __restrict__ trow, const T* __restrict__ drow, int V,
                             bool rej, const FiltRow& tr, const FiltRow& dr, double invT,
                             const double* tbl, double uf, const double2* __restrict__ cm,
-                            double* csum, int& y_out, double& rmass_out) {
+                            double* csum, double* dl, int* il, int& y_out, double& rmass_out) {
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   const int nch = (V + kStreamChunk - 1) / kStreamChunk;
   auto weights = [&](long e0, bool resid, double* w) {
@@ -160,20 +163,15 @@ __device__ void stream_draw(const T* __restrict__ trow, const T* __restrict__ dr
     const int c_lo = min(nch, lane * q), c_hi = min(nch, c_lo + q);
     double mine = 0.0;
     for (int c = c_lo; c < c_hi; ++c) mine += csum[c];
-    double incl = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const double y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
-    total = __shfl(incl, kWave - 1, kWave);
+    const double incl = wave_incl_scan(mine);
+    total = lane_value(incl, kWave - 1);
     if (resid && !(total > 0.0)) {       // unreachable in exact arithmetic: draw from p_j
       resid = false;
       __syncthreads();                   // every wave has read csum
       continue;
     }
     t = uf * total;
-    double run = incl - mine;
+    double run = wave_shr1(incl);
     int cand = -1, lastp = -1;
     double cpre = 0.0;
     for (int c = c_lo; c < c_hi; ++c) {
@@ -188,62 +186,56 @@ __device__ void stream_draw(const T* __restrict__ trow, const T* __restrict__ dr
     const uint64_t hit = __ballot(cand >= 0);
     if (hit) {
       const int L = __ffsll((unsigned long long)hit) - 1;
-      cstar = __shfl(cand, L, kWave);
-      pre = __shfl(cpre, L, kWave);
+      cstar = lane_value(cand, L);
+      pre = lane_value(cpre, L);
     } else {
       const uint64_t pos = __ballot(lastp >= 0);
-      clast = pos ? __shfl(lastp, 63 - __clzll((long long)pos), kWave) : -1;
+      clast = pos ? lane_value(lastp, 63 - __clzll((long long)pos)) : -1;
     }
     break;
   }
   rmass_out = (rej && resid) ? total : 0.0;
   y_out = -1;
-  if (wid != 0) return;
-  if (cstar >= 0) {                      // in-chunk scan: sub-blocks in order, lanes in order
-    double off = pre;
-    int y = INT_MAX, ylast = -1;
-    for (int j = 0; j < 4 && y == INT_MAX; ++j) {
-      const long e0 = (long)cstar * kStreamChunk + j * kStreamSub + lane * 8;
-      double w[8];
-      weights(e0, resid, w);
-      double mysum = 0.0;
+  const int cc = cstar >= 0 ? cstar : clast;         // uniform: every wave found the same
+  if (cc < 0) return;                                // no positive mass at all
+  // In-chunk scan by the four waves, wave w over sub-block w (lanes in
+  // order): one round trip for the chunk's logits, the sub-block totals
+  // combined in LDS in wave order.  After a rounding fall-through (no chunk
+  // holds t) only the last positive token of the last chunk with mass counts.
+  const long e0 = (long)cc * kStreamChunk + wid * kStreamSub + lane * 8;
+  double w[8];
+  weights(e0, resid, w);
+  double mysum = 0.0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mysum += w[i];
-      double incl = mysum;
+  for (int i = 0; i < 8; ++i) mysum += w[i];
+  const double incl = wave_incl_scan(mysum);
+  if (lane == kWave - 1) dl[wid] = incl;
+  __syncthreads();
+  double run = pre;
+  for (int v = 0; v < wid; ++v) run += dl[v];
+  run += wave_shr1(incl);
+  int v = INT_MAX, vl = -1;
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const double yv = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += yv;
-      }
-      double run = off + incl - mysum;
-      int v = INT_MAX, vl = -1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        run += w[i];
-        if (v == INT_MAX && t < run) v = (int)(e0 + i);
-        if (w[i] > 0.0) vl = (int)(e0 + i);
-      }
-      const uint64_t h1 = __ballot(v != INT_MAX), h2 = __ballot(vl >= 0);
-      if (h1) y = __shfl(v, __ffsll((unsigned long long)h1) - 1, kWave);
-      if (h2) ylast = __shfl(vl, 63 - __clzll((long long)h2), kWave);
-      off += __shfl(incl, kWave - 1, kWave);
-    }
-    y_out = y != INT_MAX ? y : ylast;    // rounding fall-through inside the chunk
-  } else if (clast >= 0) {               // rounding fall-through: the last positive token
-    int ylast = -1;
-    for (int j = 0; j < 4; ++j) {
-      const long e0 = (long)clast * kStreamChunk + j * kStreamSub + lane * 8;
-      double w[8];
-      weights(e0, resid, w);
-      int vl = -1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (w[i] > 0.0) vl = (int)(e0 + i);
-      const uint64_t h2 = __ballot(vl >= 0);
-      if (h2) ylast = __shfl(vl, 63 - __clzll((long long)h2), kWave);
-    }
-    y_out = ylast;
+  for (int i = 0; i < 8; ++i) {
+    run += w[i];
+    if (v == INT_MAX && t < run) v = (int)(e0 + i);
+    if (w[i] > 0.0) vl = (int)(e0 + i);
   }
+  // token order is wave order, then lane order: a wave's first hit is its
+  // smallest, the first wave's hit the chunk's
+  const uint64_t h1 = __ballot(v != INT_MAX), h2 = __ballot(vl >= 0);
+  if (lane == 0) {
+    il[wid] = h1 ? lane_value(v, __ffsll((unsigned long long)h1) - 1) : INT_MAX;
+    il[kFiltThreads / kWave + wid] = h2 ? lane_value(vl, 63 - __clzll((long long)h2)) : -1;
+  }
+  __syncthreads();
+  int y = INT_MAX, ylast = -1;
+#pragma unroll
+  for (int ww = 0; ww < kFiltThreads / kWave; ++ww) {
+    y = min(y, il[ww]);
+    ylast = max(ylast, il[kFiltThreads / kWave + ww]);
+  }
+  y_out = (cstar >= 0 && y != INT_MAX) ? y : ylast;  // rounding fall-through: last positive
 }
 
 // ---------------------------------------------------------------------------
@@ -258,7 +250,7 @@ __global__ __launch_bounds__(kFiltThreads) void sample_list_kernel(
     double* __restrict__ rmass_out) {
   __shared__ double tbl[SPECV_EXP64_N];
   __shared__ double dl[kFiltThreads / kWave];
-  __shared__ int il[kFiltThreads / kWave];
+  __shared__ int il[2 * (kFiltThreads / kWave)];
   __shared__ double csum[kMaxSampChunks];
   const int b = blockIdx.x;
   exp64_stage_table<kFiltThreads>(tbl);
@@ -278,7 +270,8 @@ __global__ __launch_bounds__(kFiltThreads) void sample_list_kernel(
     double rm;
     const int nch = (V + kStreamChunk - 1) / kStreamChunk;
     stream_draw(tgt + target_row_off(b, pl.trow, K, V), drow, V, rej, tr, dr, invT, tbl,
-                (double)u_final[b], cmass ? cmass + (size_t)b * nch : nullptr, csum, y, rm);
+                (double)u_final[b], cmass ? cmass + (size_t)b * nch : nullptr, csum, dl, il, y,
+                rm);
     if (threadIdx.x == 0) {
       out_tokens[(size_t)b * (K + 1) + pl.stop] = y;
       if (rmass_out) rmass_out[b] = rm;
