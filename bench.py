@@ -52,12 +52,13 @@ TRAFFIC = {
         "sources": ("row_stats.hip", "common.h"),
         "sources_sha256_16": "cb88da0f480d33cd", "bytes": 148152996},
     "B256_K8_V152064_f32_topk50_topp0.9": {
-        "sources": ("filter.hip", "filter_common.h", "radix_select.h", "exp64.h", "common.h"),
-        "sources_sha256_16": "1fb333c32823445b", "bytes": 2687321350},
+        "sources": ("filter.hip", "filter_common.h", "radix_select.h", "wave_scan.h", "exp64.h",
+                    "common.h"),
+        "sources_sha256_16": "ba1c83ae0c2d56b2", "bytes": 2687321222},
     "B64_K4_V128256_bf16_topp0.9": {
         "sources": ("filter_rows.hip", "filter_common.h", "hist_select.h", "radix_select.h",
-                    "exp64.h", "common.h"),
-        "sources_sha256_16": "2997e4d3dde29baf", "bytes": 148271409},
+                    "wave_scan.h", "exp64.h", "common.h"),
+        "sources_sha256_16": "68c84f77c130ec1a", "bytes": 148254002},
 }
 # The same for one LM-head launch at M=320, D=4096, V=128256 (scaled by the
 # copy calibration taken with the row-statistics figure).

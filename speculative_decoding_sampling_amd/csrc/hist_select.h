@@ -94,12 +94,6 @@ __device__ __forceinline__ void key_mass(uint32_t k, uint32_t c, float m, double
   l = pl * c;
 }
 
-template <typename V>
-__device__ __forceinline__ V wave_sum_u(V v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
 
 // Position of the k-th (from 0) set bit of m, counting from bit 0.
 __device__ __forceinline__ uint32_t select_bit(unsigned long long m, uint32_t k) {
@@ -326,18 +320,10 @@ __device__ __forceinline__ FiltRow select_row_hist(const bf16_t* __restrict__ ro
   const uint32_t np = (uint32_t)__popcll(pm);
   uint32_t mkey = pm ? 64u * t + 63u - (uint32_t)__clzll((long long)pm) : 0u;
   // block totals, and np's exclusive prefix (range order = ascending keys)
-  uint32_t nincl = np;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(nincl, o, kWave);
-    if (lane >= o) nincl += y;
-  }
-  tot = wave_sum_u(tot);
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    bad |= __shfl_xor(bad, o, kWave);
-    mkey = max(mkey, (uint32_t)__shfl_xor(mkey, o, kWave));
-  }
+  const uint32_t nincl = wave_incl_scan_u32(np);
+  tot = wave_sum_u32(tot);
+  bad = wave_or_u32(bad);
+  mkey = wave_max_u32(mkey);
   if (lane == kWave - 1) {
     a->wt[wid] = tot;
     a->wb[wid] = bad;
@@ -447,12 +433,7 @@ __device__ __forceinline__ FiltRow select_row_hist(const bf16_t* __restrict__ ro
     const int w_lo = min(nw, t * pw), w_hi = min(nw, w_lo + pw);
     uint32_t mine = 0u;
     for (int i = w_lo; i < w_hi; ++i) mine += __popc(bm[i]);
-    uint32_t incl = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
+    const uint32_t incl = wave_incl_scan_u32(mine);
     if (lane == kWave - 1) a->wc[wid] = incl;     // a's last readers passed the barriers above
     __syncthreads();
     uint32_t pos = incl - mine;

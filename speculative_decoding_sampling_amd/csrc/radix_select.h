@@ -29,6 +29,7 @@
 
 #include "common.h"
 #include "exp64.h"
+#include "wave_scan.h"
 
 namespace specv {
 
@@ -103,18 +104,8 @@ __device__ __forceinline__ void block_scan3(uint32_t c, unsigned long long h, un
                                             unsigned long long& th, unsigned long long& tl) {
   constexpr int W = NT / kWave;
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  uint32_t xc = c;
-  unsigned long long xh = h, xl = l;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t yc = __shfl_up(xc, o, kWave);
-    const unsigned long long yh = __shfl_up(xh, o, kWave), yl = __shfl_up(xl, o, kWave);
-    if (lane >= o) {
-      xc += yc;
-      xh += yh;
-      xl += yl;
-    }
-  }
+  const uint32_t xc = wave_incl_scan_u32(c);
+  const unsigned long long xh = wave_incl_scan_u64(h), xl = wave_incl_scan_u64(l);
   if (lane == kWave - 1) {
     s->wc[wid] = xc;
     s->wh[wid] = xh;
@@ -330,8 +321,7 @@ __device__ FiltRow select_row(const T* __restrict__ row, int V, bool bf16, int t
     nf += z > -INFINITY ? 1u : 0u;
   });
   mx = wave_max(mx);
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) nf += __shfl_xor(nf, o, kWave);
+  nf = wave_sum_u32(nf);
   if (lane == 0) {
     s->wmax[wid] = mx;
     s->wn[wid] = nf;
