@@ -82,23 +82,6 @@ __device__ __forceinline__ K bitonic_sort(K key, int lane) {
   return bitonic_merge<SIZE, SIZE / 2>(key, lane);
 }
 
-// Inclusive prefix sum over the wave's lanes on DPP alone: shifts by 1, 2, 4
-// and 8 within each row of 16 (a lane with no source adds 0), then row 15's
-// total broadcast into rows 1 and 3, then lane 31's into rows 2 and 3.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ int dpp_add(int v) {
-  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
-}
-__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
-  v = dpp_add<0x111, 0xf>(v);                        // row_shr:1
-  v = dpp_add<0x112, 0xf>(v);                        // row_shr:2
-  v = dpp_add<0x114, 0xf>(v);                        // row_shr:4
-  v = dpp_add<0x118, 0xf>(v);                        // row_shr:8
-  v = dpp_add<0x142, 0xa>(v);                        // row_bcast:15 into rows 1, 3
-  v = dpp_add<0x143, 0xc>(v);                        // row_bcast:31 into rows 2, 3
-  return v;
-}
-
 // Descending sort of one key per lane across a wave (bitonic network), for
 // 32- and 64-bit keys.
 template <typename K>
@@ -234,7 +217,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
   // exclusive offset of this thread's candidates in the block: a DPP scan
   // per wave, the four wave totals through LDS (il is not used before here)
   const int mine = __popc(cm);
-  const int incl = wave_incl_scan_dpp(mine);
+  const int incl = wave_incl_scan_i32(mine);
   if (lane == kWave - 1) il[wid] = incl;
   __syncthreads();
   int total = 0, off = incl - mine;
@@ -330,26 +313,6 @@ __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
-// Inclusive prefix sum of one double per lane over the wave, in lane order,
-// on DPP lane moves (each 64-bit value moved as two 32-bit halves): shifts
-// by 1, 2, 4 and 8 within each row of 16, then row 15's total into rows 1
-// and 3, then lane 31's into rows 2 and 3.  A fixed order of additions.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ double dpp_take_f64(double v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xf, true);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xf, true);
-  return __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ double wave_incl_scan_f64(double x) {
-  x += dpp_take_f64<0x111, 0xf>(x);
-  x += dpp_take_f64<0x112, 0xf>(x);
-  x += dpp_take_f64<0x114, 0xf>(x);
-  x += dpp_take_f64<0x118, 0xf>(x);
-  x += dpp_take_f64<0x142, 0xa>(x);
-  x += dpp_take_f64<0x143, 0xc>(x);
-  return x;
-}
-
 __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
     const int* __restrict__ draft_len, int B, int K, int nch, int cap, int row_stride,
     int top_k, float top_p, double invT, const uint64_t* __restrict__ cand,
@@ -381,7 +344,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
     over = cnt > slot;
     n = min(cnt, slot);
   }
-  const int incl = wave_incl_scan_dpp(n);
+  const int incl = wave_incl_scan_i32(n);
   const int n_all = __builtin_amdgcn_readlane(incl, kWave - 1);
   // lanes per chunk: lane l reads chunk l / q, its entries l % q, l % q + q, ...
   const int q = kWave / max(nch, 1);
@@ -450,7 +413,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
   int c0 = 0;
 #pragma unroll
   for (int i = 0; i < kWavePer; ++i) c0 += key[i] >= t0 && key[i] > 0u ? 1 : 0;
-  const int incl0 = wave_incl_scan_dpp(c0);
+  const int incl0 = wave_incl_scan_i32(c0);
   const int nt = __builtin_amdgcn_readlane(incl0, kWave - 1);
   uint32_t tk = known;
   int L = nt;                                        // #{keys >= tk} (every key >= t0 here)
@@ -510,7 +473,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
   int mine = 0;
 #pragma unroll
   for (int i = 0; i < kWavePer; ++i) mine += key[i] >= tk ? 1 : 0;
-  const int pincl = wave_incl_scan_dpp(mine);
+  const int pincl = wave_incl_scan_i32(mine);
   int pos = pincl - mine;
 #pragma unroll
   for (int i = 0; i < kWavePer; ++i)
@@ -528,9 +491,8 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
   const double md = (double)m;
   const bool in = lane < L;
   const double wgt = in ? exp64(((double)unkey(k32) - md) * invT, tbl) : 0.0;
-  const double run = wave_incl_scan_f64(wgt);
-  const double tot = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(run), kWave - 1),
-                                      __builtin_amdgcn_readlane(__double2loint(run), kWave - 1));
+  const double run = wave_incl_scan(wgt);
+  const double tot = lane_value(run, kWave - 1);
   uint32_t tau = tk;
   int Lk = L;
   if (top_p < 1.0f) {
@@ -610,12 +572,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
       over = cnt > slot;
       n = min(cnt, slot);
     }
-    int x = n;                                       // inclusive scan over the lanes
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(x, o, kWave);
-      if (c >= o) x += y;
-    }
+    const int x = wave_incl_scan_i32(n);             // inclusive scan over the lanes
     if (c < nch) s_off[c + 1] = x;
     const bool any_over = __ballot(over) != 0;
     if (c == 0) {
@@ -695,7 +652,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
         c[i] = d >= 0 ? hist[d] : 0;
         csum += c[i];
       }
-      const int incl = wave_incl_scan_dpp(csum);
+      const int incl = wave_incl_scan_i32(csum);
       if (lane == kWave - 1) il[wid] = incl;
       __syncthreads();                               // (B)
       for (int i = threadIdx.x; i < kRadixBins; i += kFiltThreads) hist[i] = 0;
@@ -725,7 +682,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   const int a_lo = min(n_all, (int)threadIdx.x * qa), a_hi = min(n_all, a_lo + qa);
   int mine_n = 0;
   for (int f = a_lo; f < a_hi; ++f) mine_n += (uint32_t)(keys[f] >> 32) >= tau_k ? 1 : 0;
-  const int incl_n = wave_incl_scan_dpp(mine_n);
+  const int incl_n = wave_incl_scan_i32(mine_n);
   if (lane == kWave - 1) il[wid] = incl_n;           // il's last readers passed (C)
   uint64_t kept_keys[kGather];
   int nk = 0;
@@ -779,18 +736,13 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
       const bool in = lane < L;
       const uint32_t k32 = in ? (uint32_t)(keys[lane] >> 32) : 0u;
       const double wgt = in ? exp64(((double)unkey(k32) - md) * invT, tbl) : 0.0;
-      double run = wgt;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const double y = __shfl_up(run, o, kWave);
-        if (lane >= o) run += y;
-      }
-      const double tot = __shfl(run, kWave - 1, kWave);
+      const double run = wave_incl_scan(wgt);
+      const double tot = lane_value(run, kWave - 1);
       if (top_p < 1.0f && L > 0) {
         // M = first sorted index whose running mass reaches top_p of the total
         const uint64_t hit = __ballot(in && run / tot >= (double)top_p);
         const int M = hit ? __ffsll((unsigned long long)hit) - 1 : L - 1;
-        tau = (uint32_t)__shfl((int)k32, M, kWave);
+        tau = (uint32_t)lane_value((int)k32, M);
         const uint64_t below = __ballot(in && k32 < tau);
         Lk = below ? __ffsll((unsigned long long)below) - 1 : L;
       }

@@ -2,21 +2,29 @@
 // sample_list.hip).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
+#include "wave_scan.h"
 
 namespace specv {
 
+// Exclusive scan of one value per thread over the block (thread order) and
+// the block total: the wave scans on DPP lane moves, the waves' totals in
+// a fixed order.
 template <typename V>
 __device__ __forceinline__ V block_scan_excl(V v, V* lds, V& total) {
+  static_assert(std::is_same<V, double>::value || std::is_same<V, int>::value,
+                "double or int");
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  V x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const V y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
+  V x, excl;
+  if constexpr (std::is_same<V, double>::value) {
+    x = wave_incl_scan(v);
+    excl = wave_shr1(x);
+  } else {
+    x = (int)wave_incl_scan_u32((uint32_t)v);
+    excl = x - v;                                    // exact for integers
   }
-  V excl = __shfl_up(x, 1, kWave);
-  if (lane == 0) excl = V(0);
   __syncthreads();
   if (lane == kWave - 1) lds[wid] = x;
   __syncthreads();
@@ -31,8 +39,9 @@ __device__ __forceinline__ V block_scan_excl(V v, V* lds, V& total) {
 }
 
 __device__ __forceinline__ int block_min_i(int v, int* lds) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  v = (int)wave_reduce_u32((uint32_t)v, [](uint32_t a, uint32_t b) {
+    return (uint32_t)min((int)a, (int)b);
+  });
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   __syncthreads();
   if (lane == 0) lds[wid] = v;

@@ -77,6 +77,10 @@ __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long l
   return x;
 }
 
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+  return (int)wave_incl_scan_u32((uint32_t)x);
+}
+
 // Reductions of a 32-bit value over the wave, returned wave-uniform.
 template <typename Op>
 __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
