@@ -22,10 +22,12 @@
 // the kept tokens sorted by id.  Nothing downstream reads the full rows
 // again: acceptance needs two gathers per position, and the residual or
 // bonus draw walks the target row's kept list (p is zero elsewhere).
+#include <algorithm>
 #include <climits>
 
 #include "common.h"
 #include "exp64.h"
+
 #include "filter_common.h"
 #include "radix_select.h"
 
@@ -106,13 +108,16 @@ template <typename T>
 __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
     int K, int V, int nch, int top_k, int cap, int row_stride, uint64_t* __restrict__ cand,
-    int* __restrict__ counts) {
+    int* __restrict__ counts, int* __restrict__ redo_count) {
   __shared__ uint32_t tw[kFiltThreads / kWave];
   __shared__ uint32_t lists[kFiltThreads];
   __shared__ int il[kFiltThreads / kWave];
   const int R = 2 * K + 1;
   const int chunk = blockIdx.x % nch;
   const int rr = blockIdx.x / nch;
+  // The block merge's row list starts empty (the merge kernels run after
+  // this one, so the clear is ordered before their appends).
+  if (blockIdx.x == 0 && threadIdx.x == 0) *redo_count = 0;
   const int r = rr % R, b = rr / R;
   const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
   if (nb < 0 || nb > K) return;
@@ -316,7 +321,8 @@ __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
 __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
     const int* __restrict__ draft_len, int B, int K, int nch, int cap, int row_stride,
     int top_k, float top_p, double invT, const uint64_t* __restrict__ cand,
-    const int* __restrict__ counts, FiltRow* __restrict__ rows, Kept* __restrict__ kept) {
+    const int* __restrict__ counts, FiltRow* __restrict__ rows, Kept* __restrict__ kept,
+    int* __restrict__ redo_count, int* __restrict__ redo_rows) {
   __shared__ double tbl[SPECV_EXP64_N];
   __shared__ uint64_t s_buf[kMergeWaves][kWave];
   __shared__ uint32_t s_sel[kMergeWaves][4 * kWave];
@@ -357,6 +363,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
       out.count = 0;
       out.status = kStatusRedo;
       rows[rr] = out;
+      redo_rows[atomicAdd(redo_count, 1)] = rr;      // the block merge's list
     }
     return;
   }
@@ -465,6 +472,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
       out.count = 0;
       out.status = kStatusRedo;
       rows[rr] = out;
+      redo_rows[atomicAdd(redo_count, 1)] = rr;      // the block merge's list
     }
     return;
   }
@@ -534,10 +542,12 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_wave_kernel(
 constexpr size_t kMergeListBytes = kFiltSortMax * sizeof(uint64_t) + kRadixBins * sizeof(int);
 constexpr size_t kMergePoolBytes =
     sizeof(SelectLds) > kMergeListBytes ? sizeof(SelectLds) : kMergeListBytes;
+constexpr size_t kMergeGrid = 512;                   // block-merge workgroups at most
 
+// The block merge of row rr (a row its wave marked), by the whole block.
 template <typename T>
-__global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
-    const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
+__device__ __forceinline__ void merge_row(
+    int rr, const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
     int K, int V, int nch, int cap, int row_stride, int top_k, float top_p, double invT,
     const uint64_t* __restrict__ cand, const int* __restrict__ counts,
     FiltRow* __restrict__ rows, Kept* __restrict__ kept) {
@@ -551,7 +561,6 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   uint64_t* const keys = reinterpret_cast<uint64_t*>(pool);
   int* const hist = reinterpret_cast<int*>(pool + kFiltSortMax * sizeof(uint64_t));
   const int R = 2 * K + 1;
-  const int rr = blockIdx.x;
   const int r = rr % R, b = rr / R;
   exp64_stage_table<kFiltThreads>(tbl);
   const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
@@ -830,6 +839,24 @@ __global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
   }
 }
 
+// The block merge over the rows the wave merge listed, a grid-stride loop
+// so the grid needs no row count from the host: with the usual empty list
+// every workgroup leaves after one load.
+template <typename T>
+__global__ __launch_bounds__(kFiltThreads) void filter_merge_kernel(
+    const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
+    int K, int V, int nch, int cap, int row_stride, int top_k, float top_p, double invT,
+    const uint64_t* __restrict__ cand, const int* __restrict__ counts,
+    FiltRow* __restrict__ rows, Kept* __restrict__ kept, const int* __restrict__ redo_count,
+    const int* __restrict__ redo_rows) {
+  const int n = *redo_count;
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {  // uniform per block
+    merge_row<T>(redo_rows[i], tgt, dft, draft_len, K, V, nch, cap, row_stride, top_k, top_p,
+                 invT, cand, counts, rows, kept);
+    __syncthreads();                                 // the next row reuses the LDS
+  }
+}
+
 // ---------------------------------------------------------------------------
 int filter_cap(int top_k) { return ((3 * top_k) / 2 + 40 + 7) / 8 * 8; }
 
@@ -842,7 +869,7 @@ int filter_row_stride(int nch, int top_k) {
 
 hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int* draft_len, int B,
                          int K, int V, int nch, int top_k, float top_p, double invT,
-                         uint64_t* cand, int* counts, FiltRow* rows, Kept* kept,
+                         uint64_t* cand, int* counts, FiltRow* rows, Kept* kept, int* redo,
                          hipStream_t stream, hipEvent_t mid) {
   const int cap = filter_cap(top_k);
   const int stride = filter_row_stride(nch, top_k);
@@ -851,28 +878,31 @@ hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int*
   if (bf16)
     filter_cand_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
         static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V, nch,
-        top_k, cap, stride, cand, counts);
+        top_k, cap, stride, cand, counts, redo);
   else
     filter_cand_kernel<float><<<dim3((unsigned)blocks), dim3(kFiltThreads), 0, stream>>>(
         static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, nch,
-        top_k, cap, stride, cand, counts);
+        top_k, cap, stride, cand, counts, redo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mid && (e = hipEventRecord(mid, stream)) != hipSuccess) return e;
   const size_t nrows = (size_t)B * (2 * K + 1);
   filter_merge_wave_kernel<<<dim3((unsigned)((nrows + kMergeWaves - 1) / kMergeWaves)),
                              dim3(kFiltThreads), 0, stream>>>(
-      draft_len, B, K, nch, cap, stride, top_k, top_p, invT, cand, counts, rows, kept);
+      draft_len, B, K, nch, cap, stride, top_k, top_p, invT, cand, counts, rows, kept, redo,
+      redo + 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 grid((unsigned)nrows);
+  // as many workgroups as fit at once (two per CU at the merge's register
+  // count), or one per row if fewer
+  const dim3 grid((unsigned)std::min<size_t>(nrows, kMergeGrid));
   if (bf16)
     filter_merge_kernel<bf16_t><<<grid, dim3(kFiltThreads), 0, stream>>>(
         static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, K, V, nch,
-        cap, stride, top_k, top_p, invT, cand, counts, rows, kept);
+        cap, stride, top_k, top_p, invT, cand, counts, rows, kept, redo, redo + 1);
   else
     filter_merge_kernel<float><<<grid, dim3(kFiltThreads), 0, stream>>>(
         static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, K, V, nch, cap,
-        stride, top_k, top_p, invT, cand, counts, rows, kept);
+        stride, top_k, top_p, invT, cand, counts, rows, kept, redo, redo + 1);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ int filter_cap(int top_k);
 int filter_row_stride(int nch, int top_k);
 hipError_t launch_filter(bool bf16, const void* tgt, const void* dft, const int* draft_len, int B,
                          int K, int V, int nch, int top_k, float top_p, double invT,
-                         uint64_t* cand, int* counts, FiltRow* rows, Kept* kept,
+                         uint64_t* cand, int* counts, FiltRow* rows, Kept* kept, int* redo,
                          hipStream_t stream, hipEvent_t mid);
 hipError_t launch_filter_rows(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                               int B, int K, int V, int top_k, float top_p, double invT,
@@ -123,6 +123,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 //   plans          Plan     [B]
 //   candidates     uint64   [B][2K+1][row_stride]     (key, id); cap per chunk, >= 256 last
 //   counts         int      [B][2K+1][nch_filt]
+//   block-merge list int    [1 + B (2K+1)]            (count, then the rows)
 //   filtered rows  FiltRow  [B][2K+1]
 //   kept lists     Kept     [B][2K+1][kKeptCap]
 struct Layout {
@@ -131,7 +132,7 @@ struct Layout {
   bool small = false;        // unfiltered, through the one-kernel tail
   int nch_row = 0, nch_samp = 0, nch_filt = 0, cap = 0;
   size_t off_row = 0, off_zx = 0, off_beta = 0, off_plan = 0, off_recs = 0, off_ties = 0;
-  size_t off_cand = 0, off_counts = 0, off_frows = 0, off_kept = 0, off_cmass = 0;
+  size_t off_cand = 0, off_counts = 0, off_redo = 0, off_frows = 0, off_kept = 0, off_cmass = 0;
   size_t off_pstat = 0, off_arrive = 0, total = 0;
 };
 
@@ -201,6 +202,8 @@ Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p,
       off = align_up(off + (size_t)B * R * filter_row_stride(L.nch_filt, top_k) * sizeof(uint64_t));
       L.off_counts = off;
       off = align_up(off + (size_t)B * R * L.nch_filt * sizeof(int));
+      L.off_redo = off;
+      off = align_up(off + (1 + (size_t)B * R) * sizeof(int));
     }
     L.off_frows = off;
     off = align_up(off + (size_t)B * R * sizeof(FiltRow));
@@ -315,7 +318,8 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
     const int s0 = L.cand ? 2 : 1;
     if (L.cand)
       e = launch_filter(bf16, target, draft, draft_len, B, K, V, L.nch_filt, top_k, top_p, invT,
-                        cand, counts, frows, kept, stream, events ? events[1] : nullptr);
+                        cand, counts, frows, kept, reinterpret_cast<int*>(ws + L.off_redo), stream,
+                        events ? events[1] : nullptr);
     else
       e = launch_filter_rows(bf16, target, draft, draft_len, B, K, V, top_k, top_p, invT, frows,
                              kept, stream);
@@ -714,7 +718,8 @@ specv_status_t specv_acceptance_rates(const void* target_logits, const void* dra
     Kept* kept = reinterpret_cast<Kept*>(ws + L.off_kept);
     if (L.cand)
       e = launch_filter(bf16, target_logits, draft_logits, draft_len, B, K, V, L.nch_filt, top_k,
-                        top_p, invT, cand, counts, frows, kept, stream, nullptr);
+                        top_p, invT, cand, counts, frows, kept,
+                        reinterpret_cast<int*>(ws + L.off_redo), stream, nullptr);
     else
       e = launch_filter_rows(bf16, target_logits, draft_logits, draft_len, B, K, V, top_k, top_p,
                              invT, frows, kept, stream);
