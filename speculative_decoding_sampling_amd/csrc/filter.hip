@@ -23,6 +23,7 @@
 // again: acceptance needs two gathers per position, and the residual or
 // bonus draw walks the target row's kept list (p is zero elsewhere).
 #include <algorithm>
+#include <cfloat>
 #include <climits>
 
 #include "common.h"
@@ -164,23 +165,19 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
     for (int j = 0; j < kFiltPerThread; ++j)
       if ((uint32_t)(j * kFiltThreads) + threadIdx.x > last) v[j] = -INFINITY;
   }
-  // order-preserving keys, formed once (the logits are not needed again);
-  // the empty asm makes each key exist here, so the compiler cannot sink
-  // half of its computation into the later uses and hold both halves
-  uint32_t kx[kFiltPerThread];
-#pragma unroll
-  for (int j = 0; j < kFiltPerThread; ++j) {
-    kx[j] = fkey(v[j]);
-    asm volatile("" : "+v"(kx[j]));
-  }
+  // The threshold search compares floats: for finite or -inf logits their
+  // order is exactly the order of the keys (fkey gives -0 and +0 one key,
+  // and float compares treat them as equal), so only the thread maxima and
+  // the candidates are turned into keys.
   uint32_t tc = kNegInfKey;                          // keep every valid logit ...
   if (n_valid > slot) {                              // ... unless the chunk is larger than its slot
     // T_c = the top_k-th largest of the 256 thread maxima: top_k distinct
     // threads each hold a logit >= T_c.  Each wave sorts its maxima; every
     // thread ranks its own maximum against the four sorted lists.
-    uint32_t tmax = kNegInfKey;
+    float fm = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kFiltPerThread; ++j) tmax = max(tmax, kx[j]);
+    for (int j = 0; j < kFiltPerThread; ++j) fm = fmaxf(fm, v[j]);
+    const uint32_t tmax = fkey(fm);
     lists[threadIdx.x] = wave_sort_desc(tmax);        // wave w's list at [64w, 64w + 64)
     __syncthreads();
     // rank = thread maxima >= tmax: in each descending list the count of
@@ -211,14 +208,18 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
 #pragma unroll
     for (int w = 1; w < kFiltThreads / kWave; ++w) tc = max(tc, tw[w]);
   }
-  // candidates: finite logits with key >= tc, written in thread order.  They
+  // candidates: finite logits with key >= tc, written in thread order, as
+  // one float compare each (key >= tc with tc above -inf's key is
+  // v >= unkey(tc); otherwise every finite logit, v >= -FLT_MAX).  They
   // are rare (~60 of 8192 on random data), so each thread keeps a bit mask
-  // of its own, and a position no lane of the wave has is skipped whole.
+  // of its own (logit j at bit 31 - j: shifting in each compare needs no
+  // per-bit constants), and a position no lane of the wave has is skipped
+  // whole.
   static_assert(kFiltPerThread <= 32, "one 32-bit mask per thread");
+  const float thr = tc > kNegInfKey ? unkey(tc) : -FLT_MAX;
   uint32_t cm = 0u;
 #pragma unroll
-  for (int j = 0; j < kFiltPerThread; ++j)
-    cm |= (uint32_t)(kx[j] >= tc && kx[j] > kNegInfKey) << j;
+  for (int j = 0; j < kFiltPerThread; ++j) cm = (cm << 1) | (uint32_t)(v[j] >= thr);   // bit 31-j
   // exclusive offset of this thread's candidates in the block: a DPP scan
   // per wave, the four wave totals through LDS (il is not used before here)
   const int mine = __popc(cm);
@@ -234,12 +235,12 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
   uint64_t* dst = cand + (size_t)rr * row_stride + (size_t)chunk * cap;
 #pragma unroll
   for (int j = 0; j < kFiltPerThread; ++j) {
-    const bool c = (cm >> j) & 1u;
+    const bool c = (cm >> (kFiltPerThread - 1 - j)) & 1u;
     if (__ballot(c) != 0ull) {
       if (c) {
-        // a fresh copy of the key for the 64-bit word: otherwise the register
-        // allocator places every key in the high half of a register pair
-        uint32_t hi = kx[j];
+        // the key, formed here for the 64-bit word (the empty asm keeps it a
+        // fresh register rather than the high half of a pair)
+        uint32_t hi = fkey(v[j]);
         asm volatile("" : "+v"(hi));
         if (off < slot) dst[off] = ((uint64_t)hi << 32) | (uint64_t)(0xffffffffu - id_of(j));
         ++off;
