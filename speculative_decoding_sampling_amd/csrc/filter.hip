@@ -66,12 +66,22 @@ __device__ __forceinline__ uint64_t lane_xor(uint64_t v) {
 }
 
 // One compare-exchange stage of the bitonic network at a fixed size and stride.
+// Lane l keeps the larger key where ((l & SIZE) == 0) == ((l & STRIDE) == 0),
+// the smaller elsewhere: a fixed set of lanes per stage, given to the select
+// as a constant lane mask (scalar moves) instead of being derived from the
+// lane id with vector instructions.
+template <int SIZE, int STRIDE>
+constexpr unsigned long long bitonic_max_lanes() {
+  unsigned long long m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (((l & SIZE) == 0) == ((l & STRIDE) == 0)) m |= 1ull << l;
+  return m;
+}
 template <int SIZE, int STRIDE, typename K>
-__device__ __forceinline__ K bitonic_stage(K key, int lane) {
+__device__ __forceinline__ K bitonic_stage(K key, int) {
   const K other = lane_xor<STRIDE>(key);
-  const bool up = (lane & SIZE) == 0;
-  const bool lower = (lane & STRIDE) == 0;
-  return (lower == up) ? (key > other ? key : other) : (key < other ? key : other);
+  const bool keep_max = __builtin_amdgcn_inverse_ballot_w64(bitonic_max_lanes<SIZE, STRIDE>());
+  return keep_max ? (key > other ? key : other) : (key < other ? key : other);
 }
 template <int SIZE, int STRIDE, typename K>
 __device__ __forceinline__ K bitonic_merge(K key, int lane) {
@@ -211,18 +221,15 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
   // candidates: finite logits with key >= tc, written in thread order, as
   // one float compare each (key >= tc with tc above -inf's key is
   // v >= unkey(tc); otherwise every finite logit, v >= -FLT_MAX).  They
-  // are rare (~60 of 8192 on random data), so each thread keeps a bit mask
-  // of its own (logit j at bit 31 - j: shifting in each compare needs no
-  // per-bit constants), and a position no lane of the wave has is skipped
-  // whole.
-  static_assert(kFiltPerThread <= 32, "one 32-bit mask per thread");
+  // are rare (~60 of 8192 on random data): each thread counts its own, and
+  // the store loop repeats the compare, skipping a position no lane of the
+  // wave has.
   const float thr = tc > kNegInfKey ? unkey(tc) : -FLT_MAX;
-  uint32_t cm = 0u;
+  int mine = 0;
 #pragma unroll
-  for (int j = 0; j < kFiltPerThread; ++j) cm = (cm << 1) | (uint32_t)(v[j] >= thr);   // bit 31-j
+  for (int j = 0; j < kFiltPerThread; ++j) mine += v[j] >= thr ? 1 : 0;
   // exclusive offset of this thread's candidates in the block: a DPP scan
   // per wave, the four wave totals through LDS (il is not used before here)
-  const int mine = __popc(cm);
   const int incl = wave_incl_scan_i32(mine);
   if (lane == kWave - 1) il[wid] = incl;
   __syncthreads();
@@ -235,7 +242,7 @@ __global__ __launch_bounds__(kFiltThreads) void filter_cand_kernel(
   uint64_t* dst = cand + (size_t)rr * row_stride + (size_t)chunk * cap;
 #pragma unroll
   for (int j = 0; j < kFiltPerThread; ++j) {
-    const bool c = (cm >> (kFiltPerThread - 1 - j)) & 1u;
+    const bool c = v[j] >= thr;
     if (__ballot(c) != 0ull) {
       if (c) {
         // the key, formed here for the 64-bit word (the empty asm keeps it a
