@@ -54,7 +54,7 @@ TRAFFIC = {
     "B256_K8_V152064_f32_topk50_topp0.9": {
         "sources": ("filter.hip", "filter_common.h", "radix_select.h", "wave_scan.h", "exp64.h",
                     "common.h"),
-        "sources_sha256_16": "440d340ca8966790", "bytes": 2687322694},
+        "sources_sha256_16": "6169525b906dbe31", "bytes": 2687319207},
     "B64_K4_V128256_bf16_topp0.9": {
         "sources": ("filter_rows.hip", "filter_common.h", "hist_select.h", "radix_select.h",
                     "wave_scan.h", "exp64.h", "common.h"),
