@@ -49,8 +49,8 @@ HBM_PEAK_GBPS = 8000.0
 # the headline shape with top-p 0.9 alone.
 TRAFFIC = {
     "B64_K4_V128256_bf16": {
-        "sources": ("row_stats.hip", "common.h"),
-        "sources_sha256_16": "49985db38e6b8ef5", "bytes": 148153492},
+        "sources": ("row_stats.hip", "row_core.h", "common.h"),
+        "sources_sha256_16": "6d89c0f827d39f43", "bytes": 148139093},
     "B256_K8_V152064_f32_topk50_topp0.9": {
         "sources": ("filter.hip", "filter_common.h", "radix_select.h", "wave_scan.h", "exp64.h",
                     "common.h"),
@@ -729,10 +729,11 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 5 copies of {args.copy_calibration_mib} MiB")
 
-    if filtered:
+    if filtered or len(names) == 1:
         # The dominant kernel is the path's first pass, the top-k candidate
-        # pass or the radix select (each reads every needed row); its duration
-        # is the per-call stage mean above.
+        # pass or the radix select (each reads every needed row), or the
+        # small-batch path's one kernel; its duration is the per-call stage
+        # mean above.
         dominant = names[0]
         k1_us = stage_us[dominant]
         traffic = measured_traffic(TRAFFIC.get(spec["name"]))
@@ -753,7 +754,7 @@ def main():
         traffic = measured_traffic(TRAFFIC.get(spec["name"])) if not overridden else None
         evb.close()
         log(f"row_stats alone: {k1_us:.2f} us/launch over {reps} launches")
-    if filtered:
+    if filtered or len(names) == 1:
         burst_bytes = alg_bytes
     achieved = burst_bytes / (k1_us * 1e-6) / 1e9
     step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9

@@ -77,9 +77,11 @@ typedef enum {
  * Bytes of device workspace specv_verify needs for these sizes.  Returns 0
  * for sizes specv_verify would reject.  The workspace holds per-row
  * statistics, per-request decisions and fp64 chunk partials; its contents
- * need no initialisation and are meaningless after the call.  The size
- * depends on the path the call takes (specv_path_kind), so query it after
- * any specv_set_small_batch_limit.
+ * need no initialisation and are meaningless to the caller after the call.
+ * (On path 3 it also keeps a per-request call counter from one call to the
+ * next, which the library reads whatever it holds.)  Two calls that overlap
+ * on one workspace race.  The size depends on the path the call takes
+ * (specv_path_kind), so query it after any specv_set_small_batch_limit.
  */
 SPECV_API size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype, int top_k, float top_p);
 
@@ -405,12 +407,15 @@ SPECV_API specv_status_t specv_verify_timed(const void *target_logits, const voi
 /* Which kernel path a call with these sizes and settings takes: 0 without
  * filters (row statistics, accept scan, float64 chunk pass, draw: four
  * kernels), 1 top-k / top-p through the candidate select, 2 top-k / top-p
- * through the radix select, 3 without filters at small sizes (row
- * statistics, then one kernel that runs the accept scan and the chunk pass
- * of every row pair the request could draw from, and draws from the one the
- * scan picks; tbxsx.cn "推测解码采样验证优化策略 —— 深度调研报告", section
- * "6. 扩展性与安全性", operator fusion against launch overhead).  Paths 0 and
- * 3 give the same results. */
+ * through the radix select, 3 without filters at small sizes (one kernel:
+ * the row statistics, the chunk pass of every row pair the request could
+ * draw from, and the accept scan with the draw from the pair it picks, each
+ * stage reading the previous one's results through tagged words in the
+ * workspace as soon as they land; tbxsx.cn "推测解码采样验证优化策略 —— 深度调研报告",
+ * section "6. 扩展性与安全性", operator fusion against launch overhead).
+ * Paths 0 and 3 give the same tokens but for a draw within float64 rounding
+ * of a CDF edge (their draws sum over other chunk sizes, so residual masses
+ * agree to rounding). */
 SPECV_API int specv_path_kind(int B, int K, int V, int top_k, float top_p);
 /* Sets the size up to which unfiltered calls take path 3: calls with
  * B * (K+1) * ceil(V / 2048) <= limit do (default 384; 0 turns the path

@@ -15,7 +15,7 @@
 // in LDS.  Partials are combined later in a fixed order, so the result is
 // deterministic and a draft row equal to its target row gets bit-identical
 // statistics.
-#include "common.h"
+#include "row_core.h"
 
 namespace specv {
 
@@ -23,7 +23,7 @@ template <typename T, int VECS>
 __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
     const int* __restrict__ tokens, int K, int V, int nchunk, int row_lo, float c,
-    float2* __restrict__ part, float* __restrict__ zx, int* __restrict__ arrivals) {
+    float2* __restrict__ part, float* __restrict__ zx) {
   constexpr int N = Elem<T>::kPerVec;
   constexpr int kChunk = kRowThreads * VECS * N;
   const int R = 2 * K + 1;
@@ -34,9 +34,6 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   const int r = row_lo + rq % (R - row_lo);
   const int b = rq / (R - row_lo);
   const size_t rr = (size_t)b * R + r;
-  // Clears the request's arrival counter of the small-batch kernel that
-  // follows (null otherwise), whatever the request's rows.
-  if (arrivals && chunk == 0 && r == row_lo) arrivals[b] = 0;
   const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
   if (nb < 0 || nb > K) return;                      // the accept scan reports the error
   const bool is_target = r <= K;
@@ -44,22 +41,10 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   if (k > (is_target ? nb : nb - 1)) return;         // row not needed for this request
   const T* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
 
-  // Each wave reads one contiguous segment of VECS * 1 KB: its loads are
-  // 1 KB apart, so concurrent loads spread over the HBM channels instead of
-  // striding by the workgroup width.
   uint4 w[VECS];
   const long e_base = (long)chunk * kChunk;
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  const long e_wave = e_base + (long)wid * VECS * kWave * N + (long)lane * N;
-  const bool aligned = aligned16(row);
-  if (aligned && e_base + kChunk <= V) {              // uniform: interior chunk
-#pragma unroll
-    for (int j = 0; j < VECS; ++j) w[j] = load_raw_stream(row, e_wave + (long)j * kWave * N);
-  } else {
-#pragma unroll
-    for (int j = 0; j < VECS; ++j)
-      w[j] = load_raw_checked(row, e_wave + (long)j * kWave * N, V, aligned);
-  }
+  row_chunk_load<T, VECS>(row, e_base, V, w);
 
   // Arrival counter of the end-of-workgroup combine, cleared while the loads
   // are in flight: every wave waits on memory here anyway.
@@ -67,9 +52,6 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
   __shared__ int arrived;
   if (threadIdx.x == 0) arrived = 0;
   __syncthreads();
-  float v[VECS][N];
-#pragma unroll
-  for (int j = 0; j < VECS; ++j) unpack(w[j], v[j], T{});
 
   // Drafted token of this row (draft position k < K): its logit, read after
   // the stream is in flight and stored at the end.  zx[b][k] is the target
@@ -84,45 +66,20 @@ __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
     }
   }
 
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < VECS; ++j)
-#pragma unroll
-    for (int i = 0; i < N; ++i) m = fmaxf(m, v[j][i]);
-  m = wave_max(m);
-
-  float s = 0.f;
-  if (m != -INFINITY) {
-    const float mc = __fmul_rn(m, c);                // the exact reference fl(m*c)
-#pragma unroll
-    for (int j = 0; j < VECS; ++j)
-#pragma unroll
-      for (int i = 0; i < N; ++i) s += __builtin_amdgcn_exp2f(fmaf(v[j][i], c, -mc));
-  }
-  s = wave_sum(s);
+  const float2 ws = row_wave_partial<T, VECS>(w, c);
 
   // The last wave to finish combines the four wave partials; the others
   // exit at once instead of waiting at a barrier.  The arrival increment is
   // a workgroup-scope acquire-release: each wave's partial is written before
   // it arrives, and the last arriver reads them after.
   if (lane == 0) {
-    red[wid] = make_float2(m, s);
+    red[wid] = ws;
     const int before = __hip_atomic_fetch_add(&arrived, 1, __ATOMIC_ACQ_REL,
                                               __HIP_MEMORY_SCOPE_WORKGROUP);
     if (before != kRowThreads / kWave - 1) return;
 
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kRowThreads / kWave; ++w) M = fmaxf(M, red[w].x);
-    float S = 0.f;
-    if (M != -INFINITY) {
-      const float Mc = __fmul_rn(M, c);
-#pragma unroll
-      for (int w = 0; w < kRowThreads / kWave; ++w)
-        if (red[w].x != -INFINITY)
-          S += red[w].y * __builtin_amdgcn_exp2f(__fmul_rn(red[w].x, c) - Mc);
-    }
-    part[(size_t)rr * nchunk + chunk] = make_float2(M, S);
+    const float2 cp = row_combine_waves(red, c);
+    part[(size_t)rr * nchunk + chunk] = cp;
     if (gx >= 0) zx[(size_t)b * 2 * K + (is_target ? k : K + k)] = gz;
   }
 }
@@ -133,8 +90,7 @@ int row_stats_chunk(bool bf16) {
 
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                             const int* tokens, int B, int K, int V, int nchunk, float c,
-                            float2* part, float* zx, hipStream_t stream, int row_lo,
-                            int* arrivals) {
+                            float2* part, float* zx, hipStream_t stream, int row_lo) {
   if (row_lo < 0 || row_lo > 2 * K) return hipErrorInvalidValue;
   const size_t blocks = (size_t)B * (2 * K + 1 - row_lo) * nchunk;
   if (blocks == 0) return hipSuccess;
@@ -142,11 +98,11 @@ hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const i
   if (bf16)
     row_stats_kernel<bf16_t, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
         static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, tokens, K, V,
-        nchunk, row_lo, c, part, zx, arrivals);
+        nchunk, row_lo, c, part, zx);
   else
     row_stats_kernel<float, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
         static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, tokens, K, V,
-        nchunk, row_lo, c, part, zx, arrivals);
+        nchunk, row_lo, c, part, zx);
   return hipGetLastError();
 }
 

@@ -20,20 +20,37 @@ struct PairStat {
   double g;
 };
 
-// This thread's 8 logits of the chunk starting at element c0 (thread t holds
-// elements c0 + 8t .. c0 + 8t + 7).  The interior test is uniform per chunk.
-template <typename T>
+// The sampler's chunks are kSampThreads * PT tokens, PT per thread: 8 on the
+// general path, kSmallPerThread on the one-kernel small-batch path: 4 tokens
+// per thread, 1024-token chunks.  Its chunk passes are few and each one's
+// dependency chain sets the time, so shorter per-thread chains win (measured
+// on MI355X against 2 and 8 tokens per thread: 12.0 against 12.6 and 13.0 us
+// at B=8, K=4, V=4096 fp32; 12.9 against 13.7 and 13.3 us at B=1, K=5,
+// V=32000 bf16).
+constexpr int kSmallPerThread = 4;
+constexpr int kSmallChunk = kSampThreads * kSmallPerThread;
+
+
+// This thread's PT logits of the chunk starting at element c0 (thread t holds
+// elements c0 + PT t .. c0 + PT t + PT - 1).  The interior test is uniform per
+// chunk.  Fewer than a vector's worth per thread load element by element.
+template <typename T, int PT = kSampPerThread>
 __device__ __forceinline__ void load8(const T* __restrict__ row, long c0, int V, float* out) {
   constexpr int N = Elem<T>::kPerVec;
-  const long e0 = c0 + (long)threadIdx.x * kSampPerThread;
-  const bool aligned = aligned16(row);
-  if (aligned && c0 + kSampChunk <= V) {
+  const long e0 = c0 + (long)threadIdx.x * PT;
+  if constexpr (PT % N == 0) {
+    const bool aligned = aligned16(row);
+    if (aligned && c0 + kSampThreads * PT <= V) {
 #pragma unroll
-    for (int j = 0; j < kSampPerThread / N; ++j) load_vec_fast(row, e0 + j * N, out + j * N);
+      for (int j = 0; j < PT / N; ++j) load_vec_fast(row, e0 + j * N, out + j * N);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PT / N; ++j)
+        load_vec_checked(row, e0 + j * N, V, aligned, out + j * N);
+    }
   } else {
 #pragma unroll
-    for (int j = 0; j < kSampPerThread / N; ++j)
-      load_vec_checked(row, e0 + j * N, V, aligned, out + j * N);
+    for (int i = 0; i < PT; ++i) out[i] = e0 + i < V ? to_f32(row[e0 + i]) : -INFINITY;
   }
 }
 
@@ -61,56 +78,71 @@ __device__ __forceinline__ double weight_e(float z, double mi, double invT, cons
 }
 
 // Residual weights max(e_t/S_t - e_d/S_d, 0) (resid) or target weights e_t of
-// one thread's 8 tokens; rSt = 1/S_t and rSd = 1/S_d.
-template <typename T>
+// one thread's PT tokens; rSt = 1/S_t and rSd = 1/S_d.
+template <typename T, int PT = kSampPerThread>
 __device__ __forceinline__ void chunk_weights(const T* trow, const T* drow, long c0, int V,
                                               bool resid, double mti, double mdi, double invT,
                                               double rSt, double rSd, const double* tbl,
                                               double* w) {
-  float zt[kSampPerThread];
-  load8(trow, c0, V, zt);
+  float zt[PT];
+  load8<T, PT>(trow, c0, V, zt);
   if (resid) {
-    float zd[kSampPerThread];
-    load8(drow, c0, V, zd);
+    float zd[PT];
+    load8<T, PT>(drow, c0, V, zd);
 #pragma unroll
-    for (int i = 0; i < kSampPerThread; ++i) {
+    for (int i = 0; i < PT; ++i) {
       const double r = fma(weight_e(zt[i], mti, invT, tbl), rSt,
                            -weight_e(zd[i], mdi, invT, tbl) * rSd);
       w[i] = r > 0.0 ? r : 0.0;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kSampPerThread; ++i) w[i] = weight_e(zt[i], mti, invT, tbl);
+    for (int i = 0; i < PT; ++i) w[i] = weight_e(zt[i], mti, invT, tbl);
   }
 }
 
-// Raw logits of one thread's 8 tokens, kept packed until used.
-template <typename T> struct Raw8 {
-  uint4 w[kSampPerThread / Elem<T>::kPerVec];
+// Raw logits of one thread's PT tokens, kept packed until used: 16-byte
+// vectors, or element bit patterns when PT is below a vector.
+template <typename T, int PT = kSampPerThread> struct Raw8 {
+  static constexpr bool kVec = PT % Elem<T>::kPerVec == 0;
+  uint4 w[kVec ? PT / Elem<T>::kPerVec : 1];
+  uint32_t e[kVec ? 1 : PT];
 };
 
-// This thread's 8 logits of the chunk starting at element c0, as raw words;
+// This thread's PT logits of the chunk starting at element c0, as raw words;
 // elements at or past V read as -inf.  The interior test is uniform per chunk.
-template <typename T>
+template <typename T, int PT = kSampPerThread>
 __device__ __forceinline__ void load_raw8(const T* __restrict__ row, long c0, int V,
-                                          Raw8<T>& r) {
-  constexpr int N = Elem<T>::kPerVec, NV = kSampPerThread / N;
-  const long e0 = c0 + (long)threadIdx.x * kSampPerThread;
-  const bool aligned = aligned16(row);
-  if (aligned && c0 + kSampChunk <= V) {
+                                          Raw8<T, PT>& r) {
+  constexpr int N = Elem<T>::kPerVec;
+  const long e0 = c0 + (long)threadIdx.x * PT;
+  if constexpr (Raw8<T, PT>::kVec) {
+    constexpr int NV = PT / N;
+    const bool aligned = aligned16(row);
+    if (aligned && c0 + kSampThreads * PT <= V) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) r.w[j] = *reinterpret_cast<const uint4*>(row + e0 + j * N);
+      for (int j = 0; j < NV; ++j) r.w[j] = *reinterpret_cast<const uint4*>(row + e0 + j * N);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) r.w[j] = load_raw_checked(row, e0 + j * N, V, aligned);
+    }
   } else {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) r.w[j] = load_raw_checked(row, e0 + j * N, V, aligned);
+    for (int i = 0; i < PT; ++i) r.e[i] = e0 + i < V ? elem_bits(row, e0 + i) : neg_inf_bits(T{});
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void unpack8(const Raw8<T>& r, float* z) {
+template <typename T, int PT = kSampPerThread>
+__device__ __forceinline__ void unpack8(const Raw8<T, PT>& r, float* z) {
   constexpr int N = Elem<T>::kPerVec;
+  if constexpr (Raw8<T, PT>::kVec) {
 #pragma unroll
-  for (int j = 0; j < kSampPerThread / N; ++j) unpack(r.w[j], z + j * N, T{});
+    for (int j = 0; j < PT / N; ++j) unpack(r.w[j], z + j * N, T{});
+  } else {
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+      z[i] = sizeof(T) == 2 ? __uint_as_float(r.e[i] << 16) : __uint_as_float(r.e[i]);
+  }
 }
 
 // Lane exchanges for the wave reductions, without per-lane index registers:
@@ -155,8 +187,8 @@ __device__ __forceinline__ double wave_sum4(double a, double b, double c, double
   return k;
 }
 
-// Sums and near ties of one 2048-token chunk whose logits this thread holds
-// (8 per thread, token order = thread order), written to the chunk's record.
+// Sums and near ties of one chunk whose logits this thread holds (PT per
+// thread, token order = thread order), written to the chunk's record.
 //
 // With d = e_t - e_d g and band = e_d g w: d > band means p > q for certain,
 // d < -band means p <= q for certain (the finish checks g against the exact
@@ -167,6 +199,7 @@ __device__ __forceinline__ double wave_sum4(double a, double b, double c, double
 // id) so that the stored slots do not depend on scheduling.  tcnt counts
 // this chunk's ties; tcnt_next (the counter of a following chunk, if the
 // caller loops) is cleared between the two barriers, after its last reader.
+template <int PT = kSampPerThread>
 __device__ __forceinline__ void pass_chunk(const float* zt, const float* zd, bool rej, long e0,
                                            double mti, double mdi, double invT, double g,
                                            const double* tbl, double* dl, Tie* tl, int* tcnt,
@@ -177,7 +210,7 @@ __device__ __forceinline__ void pass_chunk(const float* zt, const float* zd, boo
   const double gw = g * kTieWindow;
   bool anytie = false;
 #pragma unroll
-  for (int i = 0; i < kSampPerThread; ++i) {
+  for (int i = 0; i < PT; ++i) {
     const double et = weight_e(zt[i], mti, invT, tbl);
     st += et;
     if (rej) {
@@ -196,7 +229,7 @@ __device__ __forceinline__ void pass_chunk(const float* zt, const float* zd, boo
     // Recompute the weights (the same arithmetic, so the same classification)
     // and append each near tie to the chunk's list.
 #pragma unroll
-    for (int i = 0; i < kSampPerThread; ++i) {
+    for (int i = 0; i < PT; ++i) {
       const double et = weight_e(zt[i], mti, invT, tbl);
       const double ed = weight_e(zd[i], mdi, invT, tbl);
       const double dlt = fma(-ed, g, et);
@@ -282,7 +315,7 @@ __device__ __forceinline__ void draw_prefetch(const ChunkRec* __restrict__ rb,
 // Barriers are few: the chunk holding t is found by every wave on its own
 // (a wave-wide blocked prefix over the chunk masses), and only the in-chunk
 // scan combines the four waves.
-template <typename T>
+template <typename T, int PT = kSampPerThread>
 __device__ __forceinline__ void draw_request(const T* __restrict__ tgt, const T* __restrict__ dft,
                                              float uf, int b, int K, int V, int nch, double invT,
                                              const Plan& pl, const ChunkRec* __restrict__ rb,
@@ -365,11 +398,12 @@ __device__ __forceinline__ void draw_request(const T* __restrict__ tgt, const T*
   const int nredo = s.nredo;
   for (int i = 0; i < nredo; ++i) {                  // each chunk's mass is order-independent
     const int cc = s.redo[i];
-    double w[kSampPerThread];
-    chunk_weights(trow, drow, (long)cc * kSampChunk, V, true, mti, mdi, invT, rSt, rSd, s.tbl, w);
+    double w[PT];
+    chunk_weights<T, PT>(trow, drow, (long)cc * (kSampThreads * PT), V, true, mti, mdi, invT, rSt,
+                         rSd, s.tbl, w);
     double sum = 0.0;
 #pragma unroll
-    for (int k = 0; k < kSampPerThread; ++k) sum += w[k];
+    for (int k = 0; k < PT; ++k) sum += w[k];
     sum = block_sum(sum, s.dl);
     if (tid == 0) s.wts[cc] = sum;
   }
@@ -428,13 +462,13 @@ __device__ __forceinline__ void draw_request(const T* __restrict__ tgt, const T*
   }
 
   // in-chunk scan of chunk cstar
-  const long e0 = (long)cstar * kSampChunk + (long)tid * kSampPerThread;
-  double w[kSampPerThread];
-  chunk_weights(trow, drow, (long)cstar * kSampChunk, V, resid, mti, mdi, invT, rSt, rSd, s.tbl,
-                w);
+  const long e0 = (long)cstar * (kSampThreads * PT) + (long)tid * PT;
+  double w[PT];
+  chunk_weights<T, PT>(trow, drow, (long)cstar * (kSampThreads * PT), V, resid, mti, mdi, invT,
+                       rSt, rSd, s.tbl, w);
   double mysum = 0.0;
 #pragma unroll
-  for (int i = 0; i < kSampPerThread; ++i) mysum += w[i];
+  for (int i = 0; i < PT; ++i) mysum += w[i];
   const double wincl = wave_incl_scan(mysum);
   const double wex = wave_shr1(wincl);
   if (lane == kWave - 1) s.dl[wid] = wincl;          // dl's last readers passed a barrier
@@ -446,7 +480,7 @@ __device__ __forceinline__ void draw_request(const T* __restrict__ tgt, const T*
   int vc = INT_MAX, vlast = -1;
   run = off + wex;
 #pragma unroll
-  for (int i = 0; i < kSampPerThread; ++i) {
+  for (int i = 0; i < PT; ++i) {
     run += w[i];
     if (vc == INT_MAX && tprime < run) vc = (int)(e0 + i);
     if (w[i] > 0.0) vlast = (int)(e0 + i);

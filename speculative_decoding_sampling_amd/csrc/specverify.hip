@@ -17,8 +17,7 @@ namespace specv {
 int row_stats_chunk(bool bf16);
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                             const int* tokens, int B, int K, int V, int nchunk, float c,
-                            float2* part, float* zx, hipStream_t stream, int row_lo = 0,
-                            int* arrivals = nullptr);
+                            float2* part, float* zx, hipStream_t stream, int row_lo = 0);
 int lm_head_tiles(int V);
 size_t lm_head_packed_elems(int V, int D);
 hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int D,
@@ -57,12 +56,13 @@ hipError_t launch_sample_finish(bool bf16, const void* tgt, const void* dft, con
                                 const ChunkRec* recs, const Tie* ties, int* out_tokens,
                                 double* rmass_out, hipStream_t stream);
 size_t small_blocks(int B, int K, int V);
+bool small_fits(int K, int V, int nch_row);
 hipError_t launch_verify_small(bool bf16, const void* tgt, const void* dft, const int* tokens,
                                const int* draft_len, const float* u, const float* u_final, int B,
                                int K, int V, int nch_row, float c, double invT, int eos_id,
-                               const float2* part, const float* zx, ChunkRec* recs, Tie* ties,
-                               PairStat* pstat, int* arrivals, const AcceptOut& out,
-                               hipStream_t stream);
+                               uint64_t* part, uint64_t* zxw, ChunkRec* recs, Tie* ties,
+                               PairStat* pstat, uint32_t* flags, uint32_t* calls,
+                               const AcceptOut& out, hipStream_t stream);
 hipError_t launch_exp64_selftest(const double* x, double* y, int n, hipStream_t stream);
 hipError_t launch_beta(bool bf16, bool filt, const void* tgt, const void* dft,
                        const int* draft_len, int B, int K, int V, int nch_row, float c,
@@ -89,8 +89,8 @@ const char* const kStageNames[kNumPaths][4] = {
     {"row_stats", "accept", "sample_pass", "sample_finish"},
     {"filter_cand", "filter_merge", "accept", "sample_list"},
     {"filter_rows", "accept", "sample_list", nullptr},
-    {"row_stats", "verify_small", nullptr, nullptr}};
-constexpr int kNumStages[kNumPaths] = {4, 4, 3, 2};
+    {"verify_small", nullptr, nullptr, nullptr}};
+constexpr int kNumStages[kNumPaths] = {4, 4, 3, 1};
 
 // Unfiltered calls with at most this many (request, row pair, 2048-token
 // chunk) triples, B (K+1) ceil(V/2048), take the small-batch path
@@ -115,10 +115,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 //   plans          Plan     [B]
 //   chunk records  ChunkRec [B][nch_samp]             (fp64 sums per sampler chunk)
 //   near ties      Tie      [B][nch_samp][kTieCap]
-// and on the small-batch path, where the chunk pass runs for every row pair,
-// chunk records and near ties [B][K+1][nch_samp](...) instead, plus
+// and on the small-batch path (one kernel), the row partials as tagged words
+// uint64 [B][2K+1][nch_row][2] and the drafted logits as tagged words uint64
+// [B][2K] in place of the first two, chunk records and near ties
+// [B][K+1][nch_samp](...) (the chunk pass runs for every row pair), plus
 //   pair statistics PairStat [B][K+1]
-//   arrival counters int     [B]
+//   pass flags      uint32   [B][K+1][nch_samp]
+//   call counters   uint32   [B]               (never cleared: see small.hip)
 // With top-k / top-p:
 //   plans          Plan     [B]
 //   candidates     uint64   [B][2K+1][row_stride]     (key, id); cap per chunk, >= 256 last
@@ -133,7 +136,7 @@ struct Layout {
   int nch_row = 0, nch_samp = 0, nch_filt = 0, cap = 0;
   size_t off_row = 0, off_zx = 0, off_beta = 0, off_plan = 0, off_recs = 0, off_ties = 0;
   size_t off_cand = 0, off_counts = 0, off_redo = 0, off_frows = 0, off_kept = 0, off_cmass = 0;
-  size_t off_pstat = 0, off_arrive = 0, total = 0;
+  size_t off_pstat = 0, off_flags = 0, off_calls = 0, total = 0;
 };
 
 bool filters_on(int V, int top_k, float top_p) { return (top_k > 0 && top_k < V) || top_p < 1.0f; }
@@ -146,14 +149,18 @@ bool candidate_path(int V, int top_k) {
   return nch <= kFiltMaxChunks && filter_row_stride(nch, top_k) <= kFiltSortMax;
 }
 
-// An unfiltered call small enough for the one-kernel tail.
+// An unfiltered call small enough for the one-kernel path (its row partials
+// counted for float32 rows, the smaller chunks: the same answer for either
+// dtype).
 bool small_path(int B, int K, int V) {
-  const size_t blocks = small_blocks(B, K, V);
-  return blocks > 0 && (long long)(blocks - B) <= g_small_limit.load(std::memory_order_relaxed);
+  const int ch = row_stats_chunk(false);
+  const long long triples = (long long)B * (K + 1) * ((V + kSampChunk - 1) / kSampChunk);
+  return small_blocks(B, K, V) > 0 && small_fits(K, V, (V + ch - 1) / ch) &&
+         triples <= g_small_limit.load(std::memory_order_relaxed);
 }
 
 // Stage-table index of a call: 0 unfiltered, 1 candidate select, 2 radix
-// select, 3 unfiltered through the small-batch tail.
+// select, 3 unfiltered through the one-kernel small-batch path.
 int path_kind(int B, int K, int V, int top_k, float top_p) {
   if (!filters_on(V, top_k, top_p)) return small_path(B, K, V) ? 3 : 0;
   return candidate_path(V, top_k) ? 1 : 2;
@@ -172,11 +179,11 @@ Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p,
     const size_t pairs = L.small ? (size_t)(K + 1) : 1;   // chunk-pass row pairs per request
     const int ch = row_stats_chunk(bf16);
     L.nch_row = (V + ch - 1) / ch;
-    L.nch_samp = (V + kSampChunk - 1) / kSampChunk;
+    L.nch_samp = L.small ? (V + kSmallChunk - 1) / kSmallChunk : (V + kSampChunk - 1) / kSampChunk;
     L.off_row = off;
-    off = align_up(off + (size_t)B * R * L.nch_row * sizeof(float2));
+    off = align_up(off + (size_t)B * R * L.nch_row * (L.small ? 2 * sizeof(uint64_t) : sizeof(float2)));
     L.off_zx = off;
-    off = align_up(off + (size_t)B * 2 * K * sizeof(float));
+    off = align_up(off + (size_t)B * 2 * K * (L.small ? sizeof(uint64_t) : sizeof(float)));
     L.off_beta = off;
     off = align_up(off + (size_t)B * K * L.nch_row * sizeof(float));
     L.off_plan = off;
@@ -188,8 +195,10 @@ Layout make_layout(int B, int K, int V, bool bf16, int top_k, float top_p,
     if (L.small) {
       L.off_pstat = off;
       off = align_up(off + (size_t)B * pairs * sizeof(PairStat));
-      L.off_arrive = off;
-      off = align_up(off + (size_t)B * sizeof(int));
+      L.off_flags = off;
+      off = align_up(off + (size_t)B * pairs * L.nch_samp * sizeof(uint32_t));
+      L.off_calls = off;
+      off = align_up(off + (size_t)B * sizeof(uint32_t));
     }
   } else {
     L.cand = candidate_path(V, top_k);
@@ -288,18 +297,20 @@ specv_status_t run(const void* target, const void* draft, specv_dtype_t dtype,
     float* zx = reinterpret_cast<float*>(ws + L.off_zx);
     ChunkRec* recs = reinterpret_cast<ChunkRec*>(ws + L.off_recs);
     Tie* ties = reinterpret_cast<Tie*>(ws + L.off_ties);
-    int* arrivals = L.small ? reinterpret_cast<int*>(ws + L.off_arrive) : nullptr;
-    e = launch_row_stats(bf16, target, draft, draft_len, tokens, B, K, V, L.nch_row, c, row_part,
-                         zx, stream, 0, arrivals);
-    if (e != hipSuccess || !mark(1)) return SPECV_EHIP;
     if (L.small) {
       PairStat* pstat = reinterpret_cast<PairStat*>(ws + L.off_pstat);
       e = launch_verify_small(bf16, target, draft, tokens, draft_len, u, u_final, B, K, V,
-                              L.nch_row, c, invT, eos_id, row_part, zx, recs, ties, pstat,
-                              arrivals, out, stream);
-      if (e != hipSuccess || !mark(2)) return SPECV_EHIP;
+                              L.nch_row, c, invT, eos_id,
+                              reinterpret_cast<uint64_t*>(ws + L.off_row),
+                              reinterpret_cast<uint64_t*>(ws + L.off_zx), recs, ties, pstat,
+                              reinterpret_cast<uint32_t*>(ws + L.off_flags),
+                              reinterpret_cast<uint32_t*>(ws + L.off_calls), out, stream);
+      if (e != hipSuccess || !mark(1)) return SPECV_EHIP;
       return SPECV_OK;
     }
+    e = launch_row_stats(bf16, target, draft, draft_len, tokens, B, K, V, L.nch_row, c, row_part,
+                         zx, stream, 0);
+    if (e != hipSuccess || !mark(1)) return SPECV_EHIP;
     e = launch_accept(bf16, false, target, draft, tokens, draft_len, u, u_final, B, K, V,
                       L.nch_row, c, invT, eos_id, row_part, zx, nullptr, out, stream);
     if (e != hipSuccess || !mark(2)) return SPECV_EHIP;

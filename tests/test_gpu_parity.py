@@ -122,6 +122,42 @@ def test_small_batch_tail_equals_four_kernel_path(cfg, B):
     assert not rep["mismatches"], rep["mismatches"][:3]
 
 
+def test_small_path_shares_one_workspace_across_sizes():
+    # The one-kernel small-batch path publishes row statistics and chunk-pass
+    # records through tagged words that no call clears.  One zeroed workspace
+    # (every request's call counter starting equal) serves, in turn,
+    # verifications of two sizes whose draft lengths change from call to call
+    # and draft-side sampling calls of a third size; every call must match the
+    # oracle, so no word left by another call -- of these sizes or of others
+    # -- passes for one of the current call's.
+    w1, w2 = make_workload(1), make_workload(2)
+    for w in (w1, w2):
+        assert binding.path_kind(w.B, w.K, w.V) == 3
+    R = w1.B * w1.K
+    assert binding.path_kind(R, 0, w1.V) == 3
+    nbytes = max(binding.workspace_bytes(w1.B, w1.K, w1.V, torch.float32),
+                 binding.workspace_bytes(w2.B, w2.K, w2.V, torch.bfloat16),
+                 binding.workspace_bytes(R, 0, w1.V, torch.float32))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(77)
+    drows = upload(w1, DEV)["draft_logits"].reshape(R, w1.V)
+    for step in range(6):
+        for w in (w1, w2):
+            # every drafted token was drawn from q, so any length up to K is valid
+            w.draft_len = rng.integers(0, w.K + 1, size=w.B).astype(np.int32)
+            print(f"[share] step={step} cfg={w.cfg} draft_len={w.draft_len.tolist()}", flush=True)
+            g = to_numpy(binding.verify(**upload(w, DEV), workspace=ws, debug=True))
+            torch.cuda.synchronize()
+            rep = compare(g, run_oracle(w), w.K)
+            assert not rep["mismatches"], (step, w.cfg, rep["mismatches"][:3])
+        un = ((rng.integers(0, 1 << 24, size=R)) * 2.0 ** -24).astype(np.float32)
+        tok = binding.sample(drows, torch.from_numpy(un).to(DEV), w1.T, workspace=ws)
+        torch.cuda.synchronize()
+        ref, fk = oracle_sample(w1.draft.reshape(R, w1.V), un, w1.T, 0, 1.0, w1.dtype)
+        sure = fk == O.FLAG_NONE
+        assert np.array_equal(tok.cpu().numpy()[sure], ref[sure]), step
+
+
 def test_p_equals_q_is_always_bonus_with_alpha_exactly_one(unfiltered_path):
     # EOS off: with p == q an accepted draft may itself be the EOS token.
     w = make_workload(5, B=16)
