@@ -78,17 +78,23 @@ constexpr uint32_t kIdFlag = 1u << 29;
 __device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t bits, uint32_t tag) {
   __hip_atomic_store(p, (uint64_t)tag << 32 | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Polls a tagged word until it carries tag; false if the wait ran out.
-__device__ __forceinline__ bool poll_tagged(const uint64_t* p, uint32_t tag, uint32_t& bits) {
+// Polls two tagged words until they carry tag0 and tag1 (false if the wait
+// ran out), both loads in flight at once: each poll is a round trip to
+// memory, so polling them one after the other takes two.
+__device__ __forceinline__ bool poll_tagged2(const uint64_t* p0, const uint64_t* p1,
+                                             uint32_t tag0, uint32_t tag1, uint32_t& bits0,
+                                             uint32_t& bits1) {
   for (int i = 0; i < kTinyMaxPoll; ++i) {
-    const uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(w >> 32) == tag) {
-      bits = (uint32_t)w;
+    const uint64_t w0 = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t w1 = __hip_atomic_load(p1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(w0 >> 32) == tag0 && (uint32_t)(w1 >> 32) == tag1) {
+      bits0 = (uint32_t)w0;
+      bits1 = (uint32_t)w1;
       return true;
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  bits = 0;
+  bits0 = bits1 = 0;
   return false;
 }
 __device__ __forceinline__ bool poll_flag(const uint32_t* p, uint32_t tag) {
@@ -101,23 +107,26 @@ __device__ __forceinline__ bool poll_flag(const uint32_t* p, uint32_t tag) {
 
 // Staging of row partials: entry i of the list (row slot i / nch_row, chunk
 // i % nch_row) polled from row row_of(i / nch_row) of request b into st[i]
-// as (max, sum).  Returns false, block-wide, if any wait ran out.
-template <typename RowOf>
+// as (max, sum).  extra() runs in every thread before the closing barrier
+// (other waits of the caller, overlapped with these), and returns false if
+// one of them ran out.  Returns false, block-wide, if any wait ran out.
+template <typename RowOf, typename Extra>
 __device__ __forceinline__ bool stage_partials(const uint64_t* __restrict__ part, int b, int R,
                                                int nch_row, int count, uint32_t nc,
                                                uint32_t salt, RowOf row_of, float2* st,
-                                               int* s_fail) {
+                                               int* s_fail, Extra extra) {
   if (threadIdx.x == 0) *s_fail = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < count; i += kSampThreads) {
     const int r = row_of(i / nch_row), ch = i % nch_row;
     const size_t pi = ((size_t)b * R + r) * nch_row + ch;
     uint32_t m, s;
-    const bool ok = poll_tagged(part + 2 * pi, tiny_tag(nc, 2 * (uint32_t)pi, salt), m) &&
-                    poll_tagged(part + 2 * pi + 1, tiny_tag(nc, 2 * (uint32_t)pi + 1, salt), s);
-    if (!ok) *s_fail = 1;
+    if (!poll_tagged2(part + 2 * pi, part + 2 * pi + 1, tiny_tag(nc, 2 * (uint32_t)pi, salt),
+                      tiny_tag(nc, 2 * (uint32_t)pi + 1, salt), m, s))
+      *s_fail = 1;
     st[i] = make_float2(__uint_as_float(m), __uint_as_float(s));
   }
+  if (!extra()) *s_fail = 1;
   __syncthreads();
   return *s_fail == 0;
 }
@@ -229,7 +238,7 @@ __global__ __launch_bounds__(kSampThreads) void verify_small_kernel(
     const bool rej = j < nb_raw;                     // j = n_b: the bonus row alone
     const bool ok = stage_partials(
         part, b, R, nch_row, (rej ? 2 : 1) * nch_row, nc, salt,
-        [&](int q) { return q == 0 ? j : K + 1 + j; }, st, &s_fail);
+        [&](int q) { return q == 0 ? j : K + 1 + j; }, st, &s_fail, [] { return true; });
     float Mt, St, Md = -INFINITY, Sd = 0.f;
     combine_staged(st, nch_row, c, Mt, St);
     if (rej) combine_staged(st + nch_row, nch_row, c, Md, Sd);
@@ -282,24 +291,31 @@ __global__ __launch_bounds__(kSampThreads) void verify_small_kernel(
     uk = u[(size_t)b * K + lane];
   }
   const bool xin = wid == 0 && lane < K && x >= 0 && x < V;
-  // the statistics of target rows 0..n_b, then of draft rows 0..n_b-1
+  // the statistics of target rows 0..n_b, then of draft rows 0..n_b-1, and
+  // (polled by the last wave meanwhile) the logits at the drafted tokens of
+  // rows 0..n_b-1, recorded with the statistics
+  __shared__ float2 zxs[kWave];
   bool ok = true;
   if (npair > 0)
     ok = stage_partials(
         part, b, R, nch_row, (2 * nb + 1) * nch_row, nc, salt,
-        [&](int q) { return q <= nb ? q : K + 1 + (q - nb - 1); }, st, &s_fail);
+        [&](int q) { return q <= nb ? q : K + 1 + (q - nb - 1); }, st, &s_fail, [&] {
+          const int zl = (int)threadIdx.x - (kSampThreads - kWave);
+          if (zl < 0 || zl >= nb) return true;
+          const int xz = tokens[(size_t)b * K + zl];
+          if (xz < 0 || xz >= V) return true;
+          const uint32_t zi = (uint32_t)((size_t)b * 2 * K + zl);
+          uint32_t bt, bd;
+          const bool zok = poll_tagged2(zxw + zi, zxw + zi + K, tiny_tag(nc, kIdZx | zi, salt),
+                                        tiny_tag(nc, kIdZx | (zi + K), salt), bt, bd);
+          zxs[zl] = make_float2(__uint_as_float(bt), __uint_as_float(bd));
+          return zok;
+        });
   if (wid == 0) {
-    // the logits at the drafted tokens, recorded with the statistics
-    bool zok = true;
     if (npair > 0 && lane < nb && xin) {
-      uint32_t bt, bd;
-      const uint32_t zi = (uint32_t)((size_t)b * 2 * K + lane);
-      zok = poll_tagged(zxw + zi, tiny_tag(nc, kIdZx | zi, salt), bt) &&
-            poll_tagged(zxw + zi + K, tiny_tag(nc, kIdZx | (zi + K), salt), bd);
-      zt = __uint_as_float(bt);
-      zd = __uint_as_float(bd);
+      zt = zxs[lane].x;
+      zd = zxs[lane].y;
     }
-    ok = ok && __ballot(!zok) == 0;
     LaneRows rs;
     if (npair > 0) {
       if (lane <= nb) combine_staged(st + lane * nch_row, nch_row, c, rs.Mt, rs.St);
