@@ -50,7 +50,7 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC = {
     "B64_K4_V128256_bf16": {
         "sources": ("row_stats.hip", "row_core.h", "common.h"),
-        "sources_sha256_16": "6d89c0f827d39f43", "bytes": 148139093},
+        "sources_sha256_16": "a9a4a3778ecb2f8c", "bytes": 148143669},
     "B256_K8_V152064_f32_topk50_topp0.9": {
         "sources": ("filter.hip", "filter_common.h", "radix_select.h", "wave_scan.h", "exp64.h",
                     "common.h"),
@@ -297,10 +297,10 @@ def bench_rates(args):
     w0 = hosts[0]
     B, K, V = w0.B, w0.K, w0.V
     positions = w0.positions
-    # one read of every needed row for the statistics, then one of each
-    # drafted (target, draft) row pair for the sums of min(p, q)
+    # two reads of each drafted (target, draft) row pair: one for the row
+    # statistics, one for the sums of min(p, q)
     drafted = int(np.sum(w0.draft_len))
-    alg_bytes = w0.algorithmic_bytes + 2 * drafted * V * 2
+    alg_bytes = 2 * (2 * drafted * V * 2)
     stream = torch.cuda.current_stream(dev)
     ws = torch.empty(binding.workspace_bytes(B, K, V, torch.bfloat16), dtype=torch.uint8,
                      device=dev)

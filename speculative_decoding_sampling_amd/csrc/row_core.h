@@ -14,9 +14,11 @@ namespace specv {
 
 // The chunk's raw 16-byte vectors of one thread: each wave reads one
 // contiguous segment of VECS * 1 KB (its loads 1 KB apart, so concurrent
-// loads spread over the HBM channels); nontemporal where the chunk is
-// interior and the row 16-byte aligned, element-checked otherwise.
-template <typename T, int VECS>
+// loads spread over the HBM channels); where the chunk is interior and the
+// row 16-byte aligned, nontemporal (STREAM: rows read once) or plain cached
+// loads (rows a later kernel of the call reads again, which then finds them
+// in the memory-side cache), element-checked otherwise.
+template <typename T, int VECS, bool STREAM = true>
 __device__ __forceinline__ void row_chunk_load(const T* __restrict__ row, long e_base, int V,
                                                uint4* w) {
   constexpr int N = Elem<T>::kPerVec;
@@ -26,7 +28,9 @@ __device__ __forceinline__ void row_chunk_load(const T* __restrict__ row, long e
   const bool aligned = aligned16(row);
   if (aligned && e_base + kChunk <= V) {              // uniform: interior chunk
 #pragma unroll
-    for (int j = 0; j < VECS; ++j) w[j] = load_raw_stream(row, e_wave + (long)j * kWave * N);
+    for (int j = 0; j < VECS; ++j)
+      w[j] = STREAM ? load_raw_stream(row, e_wave + (long)j * kWave * N)
+                    : *reinterpret_cast<const uint4*>(row + e_wave + (long)j * kWave * N);
   } else {
 #pragma unroll
     for (int j = 0; j < VECS; ++j)

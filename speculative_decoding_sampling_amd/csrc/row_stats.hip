@@ -19,32 +19,36 @@
 
 namespace specv {
 
-template <typename T, int VECS>
+template <typename T, int VECS, bool STREAM>
 __global__ __launch_bounds__(kRowThreads) void row_stats_kernel(
     const T* __restrict__ tgt, const T* __restrict__ dft, const int* __restrict__ draft_len,
-    const int* __restrict__ tokens, int K, int V, int nchunk, int row_lo, float c,
-    float2* __restrict__ part, float* __restrict__ zx) {
+    const int* __restrict__ tokens, int K, int V, int nchunk, int row_lo, int pairs_only,
+    float c, float2* __restrict__ part, float* __restrict__ zx) {
   constexpr int N = Elem<T>::kPerVec;
   constexpr int kChunk = kRowThreads * VECS * N;
   const int R = 2 * K + 1;
   // The grid covers rows row_lo .. 2K of every request (row_lo = K + 1: draft
-  // rows only, when the target rows' statistics come from elsewhere).
+  // rows only, when the target rows' statistics come from elsewhere), or with
+  // pairs_only the rows of drafted positions alone: target and draft rows
+  // k < n_b, never the bonus row K.
+  const int nrow = pairs_only ? 2 * K : R - row_lo;
   const int chunk = blockIdx.x % nchunk;
   const int rq = blockIdx.x / nchunk;
-  const int r = row_lo + rq % (R - row_lo);
-  const int b = rq / (R - row_lo);
+  const int q = rq % nrow;
+  const int r = pairs_only ? (q < K ? q : q + 1) : row_lo + q;
+  const int b = rq / nrow;
   const size_t rr = (size_t)b * R + r;
   const int nb = draft_len ? draft_len[b] : 0;      // null: no drafts (sampling)
   if (nb < 0 || nb > K) return;                      // the accept scan reports the error
   const bool is_target = r <= K;
   const int k = is_target ? r : r - (K + 1);
-  if (k > (is_target ? nb : nb - 1)) return;         // row not needed for this request
+  if (k > (is_target && !pairs_only ? nb : nb - 1)) return;   // row not needed
   const T* row = is_target ? tgt + target_row_off(b, k, K, V) : dft + draft_row_off(b, k, K, V);
 
   uint4 w[VECS];
   const long e_base = (long)chunk * kChunk;
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  row_chunk_load<T, VECS>(row, e_base, V, w);
+  row_chunk_load<T, VECS, STREAM>(row, e_base, V, w);
 
   // Arrival counter of the end-of-workgroup combine, cleared while the loads
   // are in flight: every wave waits on memory here anyway.
@@ -90,19 +94,22 @@ int row_stats_chunk(bool bf16) {
 
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                             const int* tokens, int B, int K, int V, int nchunk, float c,
-                            float2* part, float* zx, hipStream_t stream, int row_lo) {
-  if (row_lo < 0 || row_lo > 2 * K) return hipErrorInvalidValue;
-  const size_t blocks = (size_t)B * (2 * K + 1 - row_lo) * nchunk;
+                            float2* part, float* zx, hipStream_t stream, int row_lo, bool cached,
+                            bool pairs_only) {
+  if (row_lo < 0 || row_lo > 2 * K || (pairs_only && row_lo != 0)) return hipErrorInvalidValue;
+  const size_t blocks = (size_t)B * (pairs_only ? 2 * K : 2 * K + 1 - row_lo) * nchunk;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  if (bf16)
-    row_stats_kernel<bf16_t, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
-        static_cast<const bf16_t*>(tgt), static_cast<const bf16_t*>(dft), draft_len, tokens, K, V,
-        nchunk, row_lo, c, part, zx);
-  else
-    row_stats_kernel<float, kRowVecs><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>(
-        static_cast<const float*>(tgt), static_cast<const float*>(dft), draft_len, tokens, K, V,
-        nchunk, row_lo, c, part, zx);
+#define SPECV_ROWS(TT, ST)                                                                    \
+  row_stats_kernel<TT, kRowVecs, ST><<<dim3((unsigned)blocks), dim3(kRowThreads), 0, stream>>>( \
+      static_cast<const TT*>(tgt), static_cast<const TT*>(dft), draft_len, tokens, K, V, nchunk, \
+      row_lo, (int)pairs_only, c, part, zx)
+  if (bf16) {
+    if (cached) SPECV_ROWS(bf16_t, false); else SPECV_ROWS(bf16_t, true);
+  } else {
+    if (cached) SPECV_ROWS(float, false); else SPECV_ROWS(float, true);
+  }
+#undef SPECV_ROWS
   return hipGetLastError();
 }
 

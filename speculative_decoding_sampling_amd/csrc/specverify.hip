@@ -17,7 +17,8 @@ namespace specv {
 int row_stats_chunk(bool bf16);
 hipError_t launch_row_stats(bool bf16, const void* tgt, const void* dft, const int* draft_len,
                             const int* tokens, int B, int K, int V, int nchunk, float c,
-                            float2* part, float* zx, hipStream_t stream, int row_lo = 0);
+                            float2* part, float* zx, hipStream_t stream, int row_lo = 0,
+                            bool cached = false, bool pairs_only = false);
 int lm_head_tiles(int V);
 size_t lm_head_packed_elems(int V, int D);
 hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int D,
@@ -716,8 +717,10 @@ specv_status_t specv_acceptance_rates(const void* target_logits, const void* dra
   hipError_t e;
   if (!L.filt) {
     float2* row_part = reinterpret_cast<float2*>(ws + L.off_row);
+    // the rows of drafted positions only, through the cache: beta_pass reads
+    // them again right after
     e = launch_row_stats(bf16, target_logits, draft_logits, draft_len, nullptr, B, K, V,
-                         L.nch_row, c, row_part, nullptr, stream);
+                         L.nch_row, c, row_part, nullptr, stream, 0, true, true);
     if (e == hipSuccess)
       e = launch_beta(bf16, false, target_logits, draft_logits, draft_len, B, K, V, L.nch_row,
                       c, invT, row_part, nullptr, nullptr,
