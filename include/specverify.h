@@ -79,8 +79,12 @@ typedef enum {
  * statistics, per-request decisions and fp64 chunk partials; its contents
  * need no initialisation and are meaningless to the caller after the call.
  * (On path 3 it also keeps a per-request call counter from one call to the
- * next, which the library reads whatever it holds.)  Two calls that overlap
- * on one workspace race.  The size depends on the path the call takes
+ * next, which the library reads whatever it holds.  There a request whose
+ * internal wait ran out -- n_emitted = -1 for valid inputs, after some 2^18
+ * polls of a word another workgroup had not yet written -- may leave words
+ * that a replay of the same captured graph would accept: zero the workspace
+ * before replaying after such an error.)  Two calls that overlap on one
+ * workspace race.  The size depends on the path the call takes
  * (specv_path_kind), so query it after any specv_set_small_batch_limit.
  */
 SPECV_API size_t specv_workspace_bytes(int B, int K, int V, specv_dtype_t dtype, int top_k, float top_p);

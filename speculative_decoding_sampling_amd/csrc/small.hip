@@ -44,6 +44,15 @@
 // 2^-32 chance per word, does anything else: a fresh allocation, or words and
 // counters left by a call of other sizes that shared the memory (their
 // counters run on another stride, so they do not keep in step with these).
+// The salt also mixes in a sequence number of the launch: if a wait runs out
+// (its request then reports an error), the draw advances the counter before
+// every workgroup of the request may have read it, and one that reads it
+// late tags its words with the advanced counter -- under this launch's salt,
+// which no later launch shares.  A captured graph replays one launch's
+// arguments, so there only the counter tells replays apart, and after such
+// an error the workspace is to be zeroed before the next replay.
+#include <atomic>
+
 #include "accept_core.h"
 #include "row_core.h"
 #include "sample_core.h"
@@ -392,10 +401,13 @@ hipError_t launch_verify_small(bool bf16, const void* tgt, const void* dft, cons
   if (tail == 0 || !small_fits(K, V, nch_row) || nrs + tail > 0x7fffffffu)
     return hipErrorInvalidConfiguration;
   const int nch = (V + kSmallChunk - 1) / kSmallChunk;
-  // salt of these sizes (FNV-1a over B, K, V, the dtype and the chunk counts)
+  // salt of these sizes and this launch (FNV-1a over B, K, V, the dtype, the
+  // chunk counts and the launch's sequence number)
+  static std::atomic<uint32_t> launch_seq{0};
+  const uint32_t seq = launch_seq.fetch_add(1, std::memory_order_relaxed);
   uint32_t salt = 2166136261u;
   for (uint32_t v : {(uint32_t)B, (uint32_t)K, (uint32_t)V, (uint32_t)bf16, (uint32_t)nch_row,
-                     (uint32_t)nch})
+                     (uint32_t)nch, seq})
     for (int i = 0; i < 4; ++i) salt = (salt ^ ((v >> (8 * i)) & 0xffu)) * 16777619u;
 #define SPECV_SMALL(TT)                                                                        \
   verify_small_kernel<TT><<<dim3((unsigned)(nrs + tail)), dim3(kSampThreads), 0, stream>>>(    \
