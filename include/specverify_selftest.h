@@ -70,6 +70,16 @@ SPECV_API specv_status_t specv_bench_lm_head(const void *hidden, const void *pac
                                              hipStream_t stream, hipEvent_t start,
                                              hipEvent_t stop);
 
+/*
+ * Failure-handling hook: the number of times each internal wait of the
+ * one-kernel small-batch path (path kind 3) polls a word before it gives up
+ * and makes its request an error (n_emitted = -1, every output -1).  limit < 1
+ * restores the default (2^18).  Applies to launches made after the call, from
+ * any thread; returns the previous limit.  A small limit makes waits run out
+ * with every kernel still ending normally, so tests can exercise that path.
+ */
+SPECV_API int specv_selftest_set_small_poll_limit(int limit);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,7 @@ namespace specv {
 
 constexpr int kTinyMaxRecs = 1024;          // row partials one workgroup stages in LDS
 constexpr int kTinyMaxPoll = 1 << 18;       // polls of one word before a wait gives up
+std::atomic<int> g_small_poll_limit{kTinyMaxPoll};   // lowered only by a test hook
 
 // A bijective mix of 32-bit words (multiply-xorshift rounds).
 __device__ __forceinline__ uint32_t mix32(uint32_t h) {
@@ -92,8 +93,8 @@ __device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t bits, uint32_t 
 // memory, so polling them one after the other takes two.
 __device__ __forceinline__ bool poll_tagged2(const uint64_t* p0, const uint64_t* p1,
                                              uint32_t tag0, uint32_t tag1, uint32_t& bits0,
-                                             uint32_t& bits1) {
-  for (int i = 0; i < kTinyMaxPoll; ++i) {
+                                             uint32_t& bits1, int max_poll) {
+  for (int i = 0; i < max_poll; ++i) {
     const uint64_t w0 = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t w1 = __hip_atomic_load(p1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((uint32_t)(w0 >> 32) == tag0 && (uint32_t)(w1 >> 32) == tag1) {
@@ -106,8 +107,8 @@ __device__ __forceinline__ bool poll_tagged2(const uint64_t* p0, const uint64_t*
   bits0 = bits1 = 0;
   return false;
 }
-__device__ __forceinline__ bool poll_flag(const uint32_t* p, uint32_t tag) {
-  for (int i = 0; i < kTinyMaxPoll; ++i) {
+__device__ __forceinline__ bool poll_flag(const uint32_t* p, uint32_t tag, int max_poll) {
+  for (int i = 0; i < max_poll; ++i) {
     if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) return true;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -123,7 +124,7 @@ template <typename RowOf, typename Extra>
 __device__ __forceinline__ bool stage_partials(const uint64_t* __restrict__ part, int b, int R,
                                                int nch_row, int count, uint32_t nc,
                                                uint32_t salt, RowOf row_of, float2* st,
-                                               int* s_fail, Extra extra) {
+                                               int* s_fail, int max_poll, Extra extra) {
   if (threadIdx.x == 0) *s_fail = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < count; i += kSampThreads) {
@@ -131,7 +132,7 @@ __device__ __forceinline__ bool stage_partials(const uint64_t* __restrict__ part
     const size_t pi = ((size_t)b * R + r) * nch_row + ch;
     uint32_t m, s;
     if (!poll_tagged2(part + 2 * pi, part + 2 * pi + 1, tiny_tag(nc, 2 * (uint32_t)pi, salt),
-                      tiny_tag(nc, 2 * (uint32_t)pi + 1, salt), m, s))
+                      tiny_tag(nc, 2 * (uint32_t)pi + 1, salt), m, s, max_poll))
       *s_fail = 1;
     st[i] = make_float2(__uint_as_float(m), __uint_as_float(s));
   }
@@ -172,7 +173,8 @@ __global__ __launch_bounds__(kSampThreads) void verify_small_kernel(
     const float* __restrict__ u_final, int K, int V, int nch_row, int nch, float c, double invT,
     int eos_id, int nrs, uint64_t* __restrict__ part, uint64_t* __restrict__ zxw,
     ChunkRec* __restrict__ recs, Tie* __restrict__ ties, PairStat* __restrict__ pstat,
-    uint32_t* __restrict__ flags, uint32_t* __restrict__ calls, uint32_t salt, AcceptOut out) {
+    uint32_t* __restrict__ flags, uint32_t* __restrict__ calls, uint32_t salt, int max_poll,
+    AcceptOut out) {
   __shared__ DrawLds s;
   __shared__ Tie tl[kTieCap];
   __shared__ int tcnt[2];
@@ -247,7 +249,8 @@ __global__ __launch_bounds__(kSampThreads) void verify_small_kernel(
     const bool rej = j < nb_raw;                     // j = n_b: the bonus row alone
     const bool ok = stage_partials(
         part, b, R, nch_row, (rej ? 2 : 1) * nch_row, nc, salt,
-        [&](int q) { return q == 0 ? j : K + 1 + j; }, st, &s_fail, [] { return true; });
+        [&](int q) { return q == 0 ? j : K + 1 + j; }, st, &s_fail, max_poll,
+        [] { return true; });
     float Mt, St, Md = -INFINITY, Sd = 0.f;
     combine_staged(st, nch_row, c, Mt, St);
     if (rej) combine_staged(st + nch_row, nch_row, c, Md, Sd);
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(kSampThreads) void verify_small_kernel(
   if (npair > 0)
     ok = stage_partials(
         part, b, R, nch_row, (2 * nb + 1) * nch_row, nc, salt,
-        [&](int q) { return q <= nb ? q : K + 1 + (q - nb - 1); }, st, &s_fail, [&] {
+        [&](int q) { return q <= nb ? q : K + 1 + (q - nb - 1); }, st, &s_fail, max_poll, [&] {
           const int zl = (int)threadIdx.x - (kSampThreads - kWave);
           if (zl < 0 || zl >= nb) return true;
           const int xz = tokens[(size_t)b * K + zl];
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(kSampThreads) void verify_small_kernel(
           const uint32_t zi = (uint32_t)((size_t)b * 2 * K + zl);
           uint32_t bt, bd;
           const bool zok = poll_tagged2(zxw + zi, zxw + zi + K, tiny_tag(nc, kIdZx | zi, salt),
-                                        tiny_tag(nc, kIdZx | (zi + K), salt), bt, bd);
+                                        tiny_tag(nc, kIdZx | (zi + K), salt), bt, bd, max_poll);
           zxs[zl] = make_float2(__uint_as_float(bt), __uint_as_float(bd));
           return zok;
         });
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(kSampThreads) void verify_small_kernel(
   __syncthreads();
   for (int i = threadIdx.x; i < npair * nch; i += kSampThreads) {
     const size_t fi = (size_t)b * (K + 1) * nch + i;
-    if (!poll_flag(flags + fi, tiny_tag(nc, kIdFlag | (uint32_t)fi, salt))) s_fail = 1;
+    if (!poll_flag(flags + fi, tiny_tag(nc, kIdFlag | (uint32_t)fi, salt), max_poll)) s_fail = 1;
   }
   if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();                                   // records visible to every wave
@@ -374,6 +377,10 @@ __global__ __launch_bounds__(kSampThreads) void verify_small_kernel(
   }
   __syncthreads();
   if (threadIdx.x == 0) calls[b] = next_call(nc, salt);   // every word of this call is read
+}
+
+int set_small_poll_limit(int limit) {
+  return g_small_poll_limit.exchange(limit < 1 ? kTinyMaxPoll : limit);
 }
 
 // Whether the one-kernel path serves these sizes: its workgroups stage at
@@ -413,7 +420,7 @@ hipError_t launch_verify_small(bool bf16, const void* tgt, const void* dft, cons
   verify_small_kernel<TT><<<dim3((unsigned)(nrs + tail)), dim3(kSampThreads), 0, stream>>>(    \
       static_cast<const TT*>(tgt), static_cast<const TT*>(dft), tokens, draft_len, u, u_final, \
       K, V, nch_row, nch, c, invT, eos_id, (int)nrs, part, zxw, recs, ties, pstat, flags,      \
-      calls, salt, out)
+      calls, salt, g_small_poll_limit.load(std::memory_order_relaxed), out)
   if (bf16) SPECV_SMALL(bf16_t); else SPECV_SMALL(float);
 #undef SPECV_SMALL
   return hipGetLastError();

@@ -57,6 +57,7 @@ hipError_t launch_sample_finish(bool bf16, const void* tgt, const void* dft, con
                                 const ChunkRec* recs, const Tie* ties, int* out_tokens,
                                 double* rmass_out, hipStream_t stream);
 size_t small_blocks(int B, int K, int V);
+int set_small_poll_limit(int limit);
 bool small_fits(int K, int V, int nch_row);
 hipError_t launch_verify_small(bool bf16, const void* tgt, const void* dft, const int* tokens,
                                const int* draft_len, const float* u, const float* u_final, int B,
@@ -574,6 +575,8 @@ int specv_num_stages(int kind) {
 int specv_path_kind(int B, int K, int V, int top_k, float top_p) {
   return specv::path_kind(B, K, V, top_k, top_p);
 }
+
+int specv_selftest_set_small_poll_limit(int limit) { return specv::set_small_poll_limit(limit); }
 
 long long specv_set_small_batch_limit(long long limit) {
   return specv::g_small_limit.exchange(limit < 0 ? 0 : limit);

@@ -158,6 +158,46 @@ def test_small_path_shares_one_workspace_across_sizes():
         assert np.array_equal(tok.cpu().numpy()[sure], ref[sure]), step
 
 
+def test_small_path_waits_that_run_out_are_request_errors():
+    # The one-kernel path bounds every wait between its workgroups; a wait that
+    # runs out makes its request an error instead of hanging.  A test hook caps
+    # the polls at one, so most waits run out (every kernel still ends
+    # normally): each request is then an error (every output -1) or the
+    # oracle's.  The draws of such a call advance their call counters while
+    # workgroups of the request may not yet have read them, so those tag their
+    # words with the advanced counter; the next eager call on the same
+    # workspace, polling normally, must still match the oracle everywhere.
+    import ctypes
+    lib = binding.load_library()
+    lib.specv_selftest_set_small_poll_limit.restype = ctypes.c_int
+    lib.specv_selftest_set_small_poll_limit.argtypes = [ctypes.c_int]
+    w = make_workload(1)
+    assert binding.path_kind(w.B, w.K, w.V) == 3
+    ws = torch.zeros(binding.workspace_bytes(w.B, w.K, w.V, torch.float32), dtype=torch.uint8,
+                     device=DEV)
+    ora = run_oracle(w)
+    old = lib.specv_selftest_set_small_poll_limit(1)
+    try:
+        print("[timeout] one poll per wait", flush=True)
+        g = to_numpy(binding.verify(**upload(w, DEV), workspace=ws, debug=True))
+        torch.cuda.synchronize()
+    finally:
+        lib.specv_selftest_set_small_poll_limit(old)
+    err = g["n_emitted"] == -1
+    print(f"[timeout] {int(err.sum())} of {w.B} requests timed out", flush=True)
+    for b in np.nonzero(err)[0]:
+        assert np.all(g["out_tokens"][b] == -1) and g["path"][b] == -1, b
+    rep = compare(g, ora, w.K)
+    assert all(m[0] in set(np.nonzero(err)[0].tolist()) for m in rep["mismatches"]), \
+        rep["mismatches"][:3]
+    for step in range(3):
+        print(f"[timeout] normal call {step}", flush=True)
+        g = to_numpy(binding.verify(**upload(w, DEV), workspace=ws, debug=True))
+        torch.cuda.synchronize()
+        rep = compare(g, ora, w.K)
+        assert not rep["mismatches"], (step, rep["mismatches"][:3])
+
+
 def test_p_equals_q_is_always_bonus_with_alpha_exactly_one(unfiltered_path):
     # EOS off: with p == q an accepted draft may itself be the EOS token.
     w = make_workload(5, B=16)

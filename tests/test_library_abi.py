@@ -38,6 +38,7 @@ def test_header_declares_the_api():
                           "specv_path_kind", "specv_set_small_batch_limit",
                           "specv_verify_noalloc",
                           "specv_status_string", "specv_version", "specv_selftest_exp64",
+                          "specv_selftest_set_small_poll_limit",
                           "specv_bench_row_stats", "specv_sample",
                           "specv_acceptance_rates", "specv_round_stats",
                           "specv_monitor_state_bytes", "specv_monitor_reset",
